@@ -1,0 +1,169 @@
+"""Pins of the oracle's routing: brute force, hand-worked fixtures, token
+rounding invariants, SplitMix64 known answers.  CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from fine_grained_mixture_top_amd import inputs
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "route_hand_worked.json")
+
+
+def brute_force_route(z, K, tile):
+    """Routing written as plain Python loops over tiny inputs."""
+    T, E = len(z), len(z[0])
+    sets = []
+    for t in range(T):
+        pairs = sorted(((-float(z[t][e]), e) for e in range(E)))
+        sets.append([e for _, e in pairs[:K]])
+    counts = [sum(1 for t in range(T) if e in sets[t]) for e in range(E)]
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + counts[e])
+    row_token, row_expert = [], []
+    for e in range(E):
+        for t in range(T):
+            if e in sets[t]:
+                row_token.append(t)
+                row_expert.append(e)
+    tok_ptr, tok_row = [0], []
+    for t in range(T):
+        mine = [r for r in range(len(row_token)) if row_token[r] == t]
+        tok_row += mine
+        tok_ptr.append(tok_ptr[-1] + len(mine))
+    tiles = [0]
+    for e in range(E):
+        tiles.append(tiles[-1] + (counts[e] + tile - 1) // tile)
+    return dict(topk_idx=sets, counts=counts, offsets=offsets, row_token=row_token,
+                row_expert=row_expert, tok_ptr=tok_ptr, tok_row=tok_row, tile_offsets=tiles)
+
+
+@pytest.mark.parametrize("T,E,K,seed", [(7, 4, 2, 0), (33, 8, 3, 1), (50, 16, 1, 2), (40, 5, 5, 3)])
+@pytest.mark.parametrize("ties", [True, False])
+def test_route_matches_brute_force(T, E, K, seed, ties):
+    z = inputs.draw_logits(T, E, seed, ties=ties)
+    r = O.route_scores(z, K, tile=4)
+    b = brute_force_route(z.tolist(), K, 4)
+    assert r["topk_idx"].tolist() == b["topk_idx"]
+    for key in ("counts", "offsets", "row_token", "row_expert", "tok_ptr", "tok_row", "tile_offsets"):
+        assert np.asarray(r[key]).tolist() == b[key], key
+
+
+def test_route_hand_worked_fixtures():
+    cases = json.load(open(GOLDEN))["cases"]
+    for c in cases:
+        z = np.asarray(c["scores"], dtype=np.float32)
+        r = O.route_scores(z, c["K"], tile=c["tile"], round_mode=c["round_mode"])
+        for key in ("topk_idx", "counts", "counts_raw", "offsets", "tile_offsets", "row_token",
+                    "row_expert", "tok_ptr", "tok_row"):
+            if key in c:
+                assert np.asarray(r[key]).tolist() == c[key], (c["name"], key)
+        if "topk_gate" in c:
+            np.testing.assert_allclose(r["topk_gate"], np.asarray(c["topk_gate"]), rtol=1e-14)
+
+
+def test_splitmix64_known_answers():
+    # First three outputs of SplitMix64 started from state 0 (published test vector).
+    g = O.GOLDEN_GAMMA
+    assert O.splitmix64(0) == 0xE220A8397B1DCDAF
+    assert O.splitmix64(g) == 0x6E789E6AA1B965F4
+    assert O.splitmix64((2 * g) & O.MASK64) == 0x06C45D188009454F
+
+
+def _round_cases():
+    out = []
+    for T, E, K, M, seed in [(300, 8, 2, 16, 0), (1000, 32, 4, 32, 1), (517, 16, 3, 8, 2),
+                             (2048, 64, 8, 128, 3)]:
+        out.append((T, E, K, M, seed))
+    return out
+
+
+@pytest.mark.parametrize("T,E,K,M,seed", _round_cases())
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("ties", [True, False])
+def test_token_rounding_invariants(T, E, K, M, seed, mode, ties):
+    z = inputs.draw_logits(T, E, seed, ties=ties)
+    member = O.membership(O.topk(z, K), E)
+    new, c, r = O.token_round(z, member, M, mode, seed=seed + 11)
+    counts = new.sum(axis=0)
+    assert np.array_equal(counts, r)
+    assert np.all(r % M == 0)
+    assert np.all(r <= T)
+    dev = np.abs(r - c)
+    if mode == 1:
+        assert np.all(dev <= M // 2)
+    else:
+        assert np.all(dev < M)
+    for e in range(E):
+        key = lambda t: (float(z[t, e]), -t)  # noqa: E731  larger is better
+        if r[e] < c[e]:
+            kept = np.nonzero(new[:, e])[0]
+            dropped = np.nonzero(member[:, e] & ~new[:, e])[0]
+            assert not np.any(new[:, e] & ~member[:, e])
+            assert max(key(t) for t in dropped) < min(key(t) for t in kept)
+        elif r[e] > c[e]:
+            added = np.nonzero(new[:, e] & ~member[:, e])[0]
+            outside = np.nonzero(~new[:, e])[0]
+            assert np.all(new[:, e] >= member[:, e])
+            if len(outside):
+                assert min(key(t) for t in added) > max(key(t) for t in outside)
+        else:
+            assert np.array_equal(new[:, e], member[:, e])
+
+
+def test_token_rounding_mode2_unbiased():
+    """Across 1000 seeds the mean total deviation is within 4 sigma/sqrt(1000)
+    of zero; for every expert the empirical up-rate follows remainder/M."""
+    T, E, K, M = 4000, 64, 6, 128
+    z = inputs.draw_logits(T, E, 5, ties=False)
+    c = O.membership(O.topk(z, K), E).sum(axis=0)
+    totals = []
+    ups = np.zeros(E)
+    for s in range(1000):
+        r = np.array([O.rounded_count(int(c[e]), T, M, 2, O.round_uniform(s, e, M)) for e in range(E)])
+        totals.append(int((r - c).sum()))
+        ups += (r > c)
+    totals = np.asarray(totals, dtype=np.float64)
+    sigma = totals.std()
+    assert abs(totals.mean()) <= 4 * sigma / np.sqrt(1000)
+    rate = ups / 1000
+    expect = (c % M) / M
+    assert np.all(np.abs(rate - expect) <= 4 * np.sqrt(expect * (1 - expect) / 1000) + 1e-9)
+
+
+def test_rounded_count_cases():
+    # nearest: remainder >= M/2 rounds up; exact multiples unchanged; zero stays zero
+    assert O.rounded_count(0, 100, 8, 1) == 0
+    assert O.rounded_count(16, 100, 8, 1) == 16
+    assert O.rounded_count(19, 100, 8, 1) == 16
+    assert O.rounded_count(20, 100, 8, 1) == 24
+    # more rows than tokens: round down instead
+    assert O.rounded_count(98, 100, 8, 1) == 96
+    assert O.rounded_count(99, 100, 8, 2, u=0) == 96
+    # unbiased: up iff remainder > u
+    assert O.rounded_count(19, 100, 8, 2, u=2) == 24
+    assert O.rounded_count(19, 100, 8, 2, u=3) == 16
+
+
+def test_rounding_off_is_plain():
+    z = inputs.draw_logits(200, 16, 9, ties=True)
+    a = O.route_scores(z, 4, tile=16, round_mode=0)
+    member = O.membership(O.topk(z, 4), 16)
+    b = O.segments(member, 16)
+    for key in ("counts", "offsets", "row_token", "tok_ptr", "tok_row"):
+        assert np.array_equal(a[key], b[key])
+
+
+def test_gates_softmax_over_set():
+    z = inputs.draw_logits(64, 8, 4, ties=False)
+    r = O.route_scores(z, 3)
+    g = r["gate"]
+    assert np.allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert np.all((g > 0) == r["member"])
+    # ratio of two selected gates is exp of the score difference
+    t = 5
+    e0, e1 = r["topk_idx"][t, :2]
+    assert np.isclose(g[t, e0] / g[t, e1], np.exp(float(z[t, e0]) - float(z[t, e1])), rtol=1e-14)
