@@ -1,0 +1,208 @@
+"""Thin ctypes binding of the C ABI in include/moe.h.
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+The functions take torch tensors (device memory owned by the caller) and
+raise ``MoEError`` on a non-zero status.  ``Layer`` allocates the routing
+buffers, the cached H and the workspaces with torch and calls the three
+entry points in order.
+
+The library must be built (``fine_grained_mixture_top_amd.build``); there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_gfx950.so")
+
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EDTYPE, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
+MOE_F32, MOE_BF16 = 0, 1
+MOE_ROUND_OFF, MOE_ROUND_NEAREST, MOE_ROUND_STOCHASTIC = 0, 1, 2
+MOE_FLAG_SCORES_GIVEN = 1
+MOE_WS_ROUTE, MOE_WS_FWD, MOE_WS_BWD = 0, 1, 2
+MOE_ITEM_Y, MOE_ITEM_A, MOE_ITEM_DH, MOE_ITEM_AS, MOE_ITEM_DXT, MOE_ITEM_DS, MOE_ITEM_DZ = range(7)
+
+TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
+DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {moe_strerror(status)} ({status})")
+        self.status = status
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("n", ctypes.c_int32), ("K", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("round_mode", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("round_seed", ctypes.c_uint64), ("flags", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
+ROUTING_FIELDS = ["logits", "topk_idx", "topk_gate", "counts", "counts_raw", "offsets",
+                  "tile_offsets", "row_token", "row_expert", "row_gate", "tok_ptr", "tok_row"]
+
+
+class MoeRouting(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in ROUTING_FIELDS]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library {LIB_PATH} is not built; run "
+                               "`python -m fine_grained_mixture_top_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        pdesc, prout = ctypes.POINTER(MoeDesc), ctypes.POINTER(MoeRouting)
+        L.moe_row_capacity.argtypes, L.moe_row_capacity.restype = [pdesc], sz
+        L.moe_workspace_bytes.argtypes, L.moe_workspace_bytes.restype = [pdesc, i32], sz
+        L.moe_workspace_offset.argtypes, L.moe_workspace_offset.restype = [pdesc, i32], sz
+        L.moe_route.argtypes = [pdesc, vp, vp, vp, prout, vp, sz, vp]
+        L.moe_route.restype = i32
+        L.moe_fwd.argtypes = [pdesc, vp, vp, vp, prout, vp, vp, vp, sz, vp]
+        L.moe_fwd.restype = i32
+        L.moe_bwd.argtypes = [pdesc, vp, vp, vp, vp, prout, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_bwd.restype = i32
+        L.moe_strerror.argtypes, L.moe_strerror.restype = [i32], ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def make_desc(T, d, E, n, K, dtype="bf16", round_mode=0, tile=128, round_seed=0, flags=0) -> MoeDesc:
+    code = DTYPE_CODE[dtype] if isinstance(dtype, str) else int(dtype)
+    return MoeDesc(T, d, E, n, K, code, round_mode, tile, round_seed, flags, 0)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def moe_strerror(status: int) -> str:
+    return lib().moe_strerror(int(status)).decode()
+
+
+def moe_row_capacity(desc: MoeDesc) -> int:
+    return int(lib().moe_row_capacity(ctypes.byref(desc)))
+
+
+def moe_workspace_bytes(desc: MoeDesc, which: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(desc), which))
+
+
+def moe_workspace_offset(desc: MoeDesc, item: int) -> int:
+    v = int(lib().moe_workspace_offset(ctypes.byref(desc), item))
+    return -1 if v == (1 << 64) - 1 else v
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+class Routing:
+    """Device buffers of the routing metadata (caller-owned torch tensors)."""
+
+    def __init__(self, desc: MoeDesc, device="cuda"):
+        T, E, K = desc.T, desc.E, desc.K
+        cap = moe_row_capacity(desc)
+        i32, f32 = torch.int32, torch.float32
+        z = lambda n, dt: torch.zeros(max(n, 1), dtype=dt, device=device)  # noqa: E731
+        self.cap = cap
+        self.logits = z(T * E, f32)
+        self.topk_idx = z(T * K, i32)
+        self.topk_gate = z(T * K, f32)
+        self.counts = z(E, i32)
+        self.counts_raw = z(E, i32)
+        self.offsets = z(E + 1, i32)
+        self.tile_offsets = z(E + 1, i32)
+        self.row_token = z(cap, i32)
+        self.row_expert = z(cap, i32)
+        self.row_gate = z(cap, f32)
+        self.tok_ptr = z(T + 1, i32)
+        self.tok_row = z(cap, i32)
+        self.c = MoeRouting(*[t.data_ptr() for t in (getattr(self, f) for f in ROUTING_FIELDS)])
+
+
+def workspace(desc: MoeDesc, which: int, device="cuda") -> torch.Tensor:
+    n = moe_workspace_bytes(desc, which)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_route(desc, x, w_r, bias, routing: Routing, ws: torch.Tensor, stream=None):
+    _check("moe_route", lib().moe_route(ctypes.byref(desc), _p(x), _p(w_r), _p(bias),
+                                        ctypes.byref(routing.c), _p(ws), ws.numel(), _stream(stream)))
+
+
+def moe_fwd(desc, x, w1, w2, routing: Routing, o, h_cache, ws, stream=None):
+    _check("moe_fwd", lib().moe_fwd(ctypes.byref(desc), _p(x), _p(w1), _p(w2), ctypes.byref(routing.c),
+                                    _p(o), _p(h_cache), _p(ws), ws.numel(), _stream(stream)))
+
+
+def moe_bwd(desc, x, w_r, w1, w2, routing: Routing, h_cache, d_o, dx, dw_r, dw1, dw2, ds, db, ws,
+            stream=None):
+    _check("moe_bwd", lib().moe_bwd(ctypes.byref(desc), _p(x), _p(w_r), _p(w1), _p(w2),
+                                    ctypes.byref(routing.c), _p(h_cache), _p(d_o), _p(dx), _p(dw_r),
+                                    _p(dw1), _p(dw2), _p(ds), _p(db), _p(ws), ws.numel(),
+                                    _stream(stream)))
+
+
+class Layer:
+    """One MoE layer's buffers plus route / forward / backward calls.
+
+    Inputs are device tensors of the layer dtype: x [T,d], w_r [d,E],
+    w1 [E,d,2n], w2 [E,n,d], optional fp32 bias [E]."""
+
+    def __init__(self, desc: MoeDesc, device="cuda"):
+        self.desc = desc
+        dt = TORCH_DTYPE[desc.dtype]
+        T, d, E, n = desc.T, desc.d, desc.E, desc.n
+        self.routing = Routing(desc, device)
+        cap = self.routing.cap
+        self.h_cache = torch.empty((cap, 2 * n), dtype=dt, device=device)
+        self.o = torch.empty((T, d), dtype=dt, device=device)
+        self.dx = torch.empty((T, d), dtype=dt, device=device)
+        self.dw_r = torch.empty((d, E), dtype=dt, device=device)
+        self.dw1 = torch.empty((E, d, 2 * n), dtype=dt, device=device)
+        self.dw2 = torch.empty((E, n, d), dtype=dt, device=device)
+        self.ds = torch.empty(max(cap, 1), dtype=torch.float32, device=device)
+        self.db = torch.empty(E, dtype=torch.float32, device=device)
+        self.ws_route = workspace(desc, MOE_WS_ROUTE, device)
+        self.ws_fwd = workspace(desc, MOE_WS_FWD, device)
+        self.ws_bwd = workspace(desc, MOE_WS_BWD, device)
+
+    def route(self, x, w_r, bias=None, stream=None):
+        moe_route(self.desc, x, w_r, bias, self.routing, self.ws_route, stream)
+
+    def forward(self, x, w1, w2, stream=None):
+        moe_fwd(self.desc, x, w1, w2, self.routing, self.o, self.h_cache, self.ws_fwd, stream)
+        return self.o
+
+    def backward(self, x, w_r, w1, w2, d_o, stream=None):
+        moe_bwd(self.desc, x, w_r, w1, w2, self.routing, self.h_cache, d_o, self.dx, self.dw_r,
+                self.dw1, self.dw2, self.ds, self.db, self.ws_bwd, stream)
+        return self.dx
+
+    def ws_view(self, item: int, count: int, dtype) -> torch.Tensor:
+        """View of an internal workspace item (MOE_ITEM_*) of ``count`` elements."""
+        off = moe_workspace_offset(self.desc, item)
+        ws = self.ws_fwd if item in (MOE_ITEM_Y, MOE_ITEM_A) else self.ws_bwd
+        esz = torch.empty(0, dtype=dtype).element_size()
+        return ws[off:off + count * esz].view(dtype)

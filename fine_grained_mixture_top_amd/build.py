@@ -1,0 +1,65 @@
+"""Build the HIP shared library (libmoe_gfx950.so) in-tree with hipcc.
+
+Each .hip file under csrc/ compiles to an object in ``_build/`` (in parallel),
+then they link into ``fine_grained_mixture_top_amd/libmoe_gfx950.so``.
+Usage: ``python -m fine_grained_mixture_top_amd.build`` (or ``build()``).
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmoe_gfx950.so")
+ARCH = "gfx950"
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # packed fp32 instructions stay off: the compiler would otherwise form
+    # v_pk_* fp32 ops from plain float code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *FLAGS, "-I", CSRC, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    workers = min(len(srcs), max(1, (os.cpu_count() or 4)), 8)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,253 @@
+// Expert aggregation (O and dX) and the small router-backward kernels.
+//
+// Aggregation ([B] kernel-list paragraph: the expert-aggregation kernel; it
+// is the only non-GEMM kernel of the layer) is a gather-sum over each
+// token's rows: bandwidth-bound, so it is one wave per token, 16-byte loads,
+// several rows in flight per lane, fp32 accumulation in a fixed (ascending
+// row) order, no atomics.
+//
+// Router backward ([B] algorithm paragraph: the router gradient comes from
+// the reordered contraction, no cached Y): dS per row is the sum of the dH
+// kernel's per-column-tile partials; dz = gate * (dS - sum over the token's
+// set of gate * dS) is the softmax-over-set backward.
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void load_vec(const T* p, float (&v)[16 / sizeof(T)]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_vec(T* p, const float (&v)[16 / sizeof(T)]) {
+  uint4 u;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+    u = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    u = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+  }
+  *reinterpret_cast<uint4*>(p) = u;
+}
+
+constexpr int UNR = 4;  // rows in flight per lane
+
+// O[t] = sum over token t's rows (ascending) of gate_r * Y[r]
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_aggregate_o(const T* __restrict__ Y, const float* __restrict__ row_gate,
+              const int32_t* __restrict__ tok_ptr, const int32_t* __restrict__ tok_row, int Tn, int d,
+              T* __restrict__ O) {
+  constexpr int V = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (t >= Tn) return;
+  const int j0 = tok_ptr[t], j1 = tok_ptr[t + 1];
+  const int nch = d / V;
+  for (int ch = lane; ch < nch; ch += 64) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int j = j0; j < j1; j += UNR) {
+      float v[UNR][V];
+      float g[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        if (j + u < j1) {
+          const int r = tok_row[j + u];
+          g[u] = row_gate[r];
+          load_vec<T>(Y + (size_t)r * d + ch * V, v[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+        if (j + u < j1)
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] = fmaf(g[u], v[u][i], acc[i]);
+    }
+    store_vec<T>(O + (size_t)t * d + ch * V, acc);
+  }
+}
+
+// dX[t] = sum over token t's rows (ascending) of dXt[r] + dz_r * W_r^T[e_r]
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_aggregate_dx(const T* __restrict__ dXt, const float* __restrict__ dz_row,
+               const int32_t* __restrict__ row_expert, const T* __restrict__ w_rT,
+               const int32_t* __restrict__ tok_ptr, const int32_t* __restrict__ tok_row, int Tn, int d,
+               T* __restrict__ dX) {
+  constexpr int V = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (t >= Tn) return;
+  const int j0 = tok_ptr[t], j1 = tok_ptr[t + 1];
+  const int nch = d / V;
+  for (int ch = lane; ch < nch; ch += 64) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int j = j0; j < j1; j += UNR) {
+      float v[UNR][V], w[UNR][V];
+      float g[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        if (j + u < j1) {
+          const int r = tok_row[j + u];
+          g[u] = dz_row[r];
+          load_vec<T>(dXt + (size_t)r * d + ch * V, v[u]);
+          load_vec<T>(w_rT + (size_t)row_expert[r] * d + ch * V, w[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u)
+        if (j + u < j1)
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] = fmaf(g[u], w[u][i], acc[i] + v[u][i]);
+    }
+    store_vec<T>(dX + (size_t)t * d + ch * V, acc);
+  }
+}
+
+// One wave per token.  dS_r = sum of the row's partials (fixed order);
+// dz_r = g_r (dS_r - sum_j g_j dS_j).  Also writes the token's dense row of dz
+// (zeros outside its set) for the router weight-gradient GEMM.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_router_grad(const float* __restrict__ dS_part, int nparts, const float* __restrict__ row_gate,
+              const int32_t* __restrict__ row_expert, const int32_t* __restrict__ tok_ptr,
+              const int32_t* __restrict__ tok_row, int Tn, int E, float* __restrict__ dS_row,
+              float* __restrict__ dz_row, T* __restrict__ dz_dense) {
+  __shared__ float dense[4][1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  const bool live = t < Tn;
+  for (int e = lane; e < E; e += 64) dense[wave][e] = 0.f;
+  __syncthreads();
+  if (live) {
+    const int j0 = tok_ptr[t], j1 = tok_ptr[t + 1];
+    float part = 0.f;
+    for (int j = j0 + lane; j < j1; j += 64) {
+      const int r = tok_row[j];
+      float s = 0.f;
+      for (int p = 0; p < nparts; ++p) s += dS_part[(size_t)r * nparts + p];
+      part += row_gate[r] * s;
+    }
+    const float mean = wave_sum(part);
+    for (int j = j0 + lane; j < j1; j += 64) {
+      const int r = tok_row[j];
+      float s = 0.f;
+      for (int p = 0; p < nparts; ++p) s += dS_part[(size_t)r * nparts + p];
+      const float dz = row_gate[r] * (s - mean);
+      dS_row[r] = s;
+      dz_row[r] = dz;
+      dense[wave][row_expert[r]] = dz;
+    }
+  }
+  __syncthreads();
+  if (live)
+    for (int e = lane; e < E; e += 64) dz_dense[(size_t)t * E + e] = Elem<T>::from_f(dense[wave][e]);
+}
+
+// db[e] = sum of dz over expert e's rows (fixed per-thread split and tree).
+__global__ void __launch_bounds__(256)
+k_bias_grad(const float* __restrict__ dz_row, const int32_t* __restrict__ offsets, float* __restrict__ db) {
+  __shared__ float red[4];
+  const int e = blockIdx.x;
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  float s = 0.f;
+  for (int r = r0 + threadIdx.x; r < r1; r += 256) s += dz_row[r];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) db[e] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// dst[c][r] = src[r][c]
+template <typename T>
+__global__ void k_transpose(const T* __restrict__ src, int rows, int cols, T* __restrict__ dst) {
+  __shared__ T tile[32][33];
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int i = ty; i < 32; i += 8) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = src[(size_t)r * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int c = c0 + i, r = r0 + tx;
+    if (r < rows && c < cols) dst[(size_t)c * rows + r] = tile[tx][i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_aggregate_o(int dtype, const void* Y, const float* row_gate, const int32_t* tok_ptr,
+                              const int32_t* tok_row, int T, int d, void* O, hipStream_t st) {
+  dim3 grid((T + 3) / 4), block(256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(k_aggregate_o<bf16_t>, grid, block, 0, st, (const bf16_t*)Y, row_gate, tok_ptr,
+                       tok_row, T, d, (bf16_t*)O);
+  else
+    hipLaunchKernelGGL(k_aggregate_o<float>, grid, block, 0, st, (const float*)Y, row_gate, tok_ptr,
+                       tok_row, T, d, (float*)O);
+  return hipGetLastError();
+}
+
+hipError_t launch_aggregate_dx(int dtype, const void* dXt, const float* dz_row, const int32_t* row_expert,
+                               const void* w_rT, const int32_t* tok_ptr, const int32_t* tok_row, int T,
+                               int d, void* dX, hipStream_t st) {
+  dim3 grid((T + 3) / 4), block(256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(k_aggregate_dx<bf16_t>, grid, block, 0, st, (const bf16_t*)dXt, dz_row, row_expert,
+                       (const bf16_t*)w_rT, tok_ptr, tok_row, T, d, (bf16_t*)dX);
+  else
+    hipLaunchKernelGGL(k_aggregate_dx<float>, grid, block, 0, st, (const float*)dXt, dz_row, row_expert,
+                       (const float*)w_rT, tok_ptr, tok_row, T, d, (float*)dX);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_grad(int dtype, const float* dS_part, int nparts, const float* row_gate,
+                              const int32_t* row_expert, const int32_t* tok_ptr, const int32_t* tok_row,
+                              int T, int E, float* dS_row, float* dz_row, void* dz_dense, hipStream_t st) {
+  dim3 grid((T + 3) / 4), block(256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(k_router_grad<bf16_t>, grid, block, 0, st, dS_part, nparts, row_gate, row_expert,
+                       tok_ptr, tok_row, T, E, dS_row, dz_row, (bf16_t*)dz_dense);
+  else
+    hipLaunchKernelGGL(k_router_grad<float>, grid, block, 0, st, dS_part, nparts, row_gate, row_expert,
+                       tok_ptr, tok_row, T, E, dS_row, dz_row, (float*)dz_dense);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_grad(const float* dz_row, const int32_t* offsets, int E, float* db, hipStream_t st) {
+  hipLaunchKernelGGL(k_bias_grad, dim3(E), dim3(256), 0, st, dz_row, offsets, db);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(int dtype, const void* src, int rows, int cols, void* dst, hipStream_t st) {
+  dim3 grid((cols + 31) / 32, (rows + 31) / 32), block(256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(k_transpose<bf16_t>, grid, block, 0, st, (const bf16_t*)src, rows, cols, (bf16_t*)dst);
+  else
+    hipLaunchKernelGGL(k_transpose<float>, grid, block, 0, st, (const float*)src, rows, cols, (float*)dst);
+  return hipGetLastError();
+}
+
+}  // namespace moe

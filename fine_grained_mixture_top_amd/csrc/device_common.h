@@ -1,0 +1,79 @@
+// Device-side helpers shared by the MoE kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bf16 storage (bit pattern)
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int VEC = 4;   // elements per 16-byte vector
+  static constexpr int BK = 32;   // k elements per main-loop step (128 bytes)
+  __device__ static float to_f(float v) { return v; }
+  __device__ static float from_f(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int VEC = 8;
+  static constexpr int BK = 64;
+  __device__ static float to_f(bf16_t v) { return bf2f(v); }
+  __device__ static bf16_t from_f(float v) { return f2bf(v); }
+};
+
+// Round a value through the storage type (identity for fp32).
+template <typename T> __device__ __forceinline__ float through(float v) {
+  return Elem<T>::to_f(Elem<T>::from_f(v));
+}
+
+__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+// Largest i in [0, n) with a[i] <= v (a non-decreasing, a[0] <= v).
+__device__ __forceinline__ int upper_index(const int32_t* a, int n, int v) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= v) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Sum over the 16 lanes that share lane/16 (xor butterfly inside a row of 16).
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Map a workgroup id so that consecutive virtual ids land on the same XCD.
+// Workgroups are dispatched round-robin over the 8 XCDs, so physical id b runs
+// on XCD b % 8; virtual id (b % 8) * (G / 8) + b / 8 gives each XCD one
+// contiguous run of G / 8 virtual ids (G a multiple of 8).
+__device__ __forceinline__ int xcd_virtual_id(int b, int G) {
+  if ((G & 7) != 0) return b;
+  return (b & 7) * (G >> 3) + (b >> 3);
+}
+
+}  // namespace moe

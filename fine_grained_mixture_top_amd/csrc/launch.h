@@ -1,0 +1,83 @@
+// Internal launchers shared by the translation units of the MoE library.
+// Every launcher only enqueues work on `st` and returns the runtime status of
+// the launch; all shapes were validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
+
+// Column tile of the dH GEMM, which decides how many fp32 score-gradient
+// partials each row gets (n / dh_block(dtype)).
+int dh_block(int dtype);
+inline int dh_partials(int dtype, int n) { return n / dh_block(dtype); }
+
+// ---- grouped GEMMs (gemm_kernels.hip) ----
+hipError_t launch_router_logits(int dtype, const void* x, const void* w_r, const float* bias,
+                                float* logits, int T, int d, int E, hipStream_t st);
+hipError_t launch_up_swiglu(int dtype, const void* x, const void* w1, const int32_t* row_token,
+                            const int32_t* offsets, const int32_t* tile_offsets, int E, int d,
+                            int n, size_t cap, void* H, void* A, hipStream_t st);
+hipError_t launch_down(int dtype, const void* A, const void* w2, const int32_t* offsets,
+                       const int32_t* tile_offsets, int E, int d, int n, size_t cap, void* Y,
+                       hipStream_t st);
+hipError_t launch_dh(int dtype, const void* d_o, const void* w2, const void* H,
+                     const int32_t* row_token, const float* row_gate, const int32_t* offsets,
+                     const int32_t* tile_offsets, int E, int d, int n, size_t cap, void* dH,
+                     void* As, float* dS_part, hipStream_t st);
+hipError_t launch_dxt(int dtype, const void* dH, const void* w1, const int32_t* offsets,
+                      const int32_t* tile_offsets, int E, int d, int n, size_t cap, void* dXt,
+                      hipStream_t st);
+hipError_t launch_dw1(int dtype, const void* x, const void* dH, const int32_t* row_token,
+                      const int32_t* offsets, int E, int d, int n, void* dW1, hipStream_t st);
+hipError_t launch_dw2(int dtype, const void* As, const void* d_o, const int32_t* row_token,
+                      const int32_t* offsets, int E, int d, int n, void* dW2, hipStream_t st);
+hipError_t launch_dwr(int dtype, const void* x, const void* dz_dense, int T, int d, int E,
+                      void* dWr, hipStream_t st);
+
+// ---- routing (route_kernels.hip) ----
+struct RouteBufs {
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* counts;
+  int32_t* counts_raw;
+  int32_t* offsets;
+  int32_t* tile_offsets;
+  int32_t* row_token;
+  int32_t* row_expert;
+  float* row_gate;
+  int32_t* tok_ptr;
+  int32_t* tok_row;
+};
+struct RouteScratch {
+  uint8_t* mask;       // [E][T] membership
+  float* scoresT;      // [E][T] scores, expert-major (token rounding only)
+  int32_t* rowmap;     // [E][T] row of (e, t)
+  int32_t* tokcnt;     // [T]
+};
+hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int T, int E, int K,
+                               int tile, int round_mode, uint64_t round_seed, hipStream_t st);
+
+// ---- aggregation and router backward (aggregate_kernels.hip) ----
+hipError_t launch_aggregate_o(int dtype, const void* Y, const float* row_gate,
+                              const int32_t* tok_ptr, const int32_t* tok_row, int T, int d,
+                              void* O, hipStream_t st);
+hipError_t launch_router_grad(int dtype, const float* dS_part, int nparts, const float* row_gate,
+                              const int32_t* row_expert, const int32_t* tok_ptr,
+                              const int32_t* tok_row, int T, int E, float* dS_row, float* dz_row,
+                              void* dz_dense, hipStream_t st);
+hipError_t launch_bias_grad(const float* dz_row, const int32_t* offsets, int E, float* db,
+                            hipStream_t st);
+hipError_t launch_transpose(int dtype, const void* src, int rows, int cols, void* dst,
+                            hipStream_t st);
+hipError_t launch_aggregate_dx(int dtype, const void* dXt, const float* dz_row,
+                               const int32_t* row_expert, const void* w_rT,
+                               const int32_t* tok_ptr, const int32_t* tok_row, int T, int d,
+                               void* dX, hipStream_t st);
+
+}  // namespace moe

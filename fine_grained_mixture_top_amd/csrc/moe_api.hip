@@ -1,0 +1,242 @@
+// C ABI of the MoE layer (declared in include/moe.h): argument validation,
+// workspace layout and the launch sequence of each phase.  Everything here
+// runs on the host; it only enqueues kernels on the caller's stream.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+size_t elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+int validate_desc(const moe_desc* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->reserved != 0) return MOE_EINVAL;
+  if ((d->flags & ~MOE_FLAG_SCORES_GIVEN) != 0) return MOE_EINVAL;
+  if (d->T < 1 || d->d < 1 || d->E < 1 || d->n < 1 || d->K < 1 || d->K > d->E) return MOE_EINVAL;
+  if (d->round_mode < MOE_ROUND_OFF || d->round_mode > MOE_ROUND_STOCHASTIC) return MOE_EINVAL;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_EDTYPE;
+  if (d->tile != 128) return MOE_ESHAPE;
+  if (d->E % 8 != 0 || d->E > 1024) return MOE_ESHAPE;
+  if (d->d % 128 != 0 || d->n % 64 != 0) return MOE_ESHAPE;
+  if ((int64_t)d->T * d->E > INT32_MAX - 1) return MOE_ESHAPE;  // rows are int32
+  return MOE_OK;
+}
+
+size_t capacity(const moe_desc* d) {
+  size_t base = (size_t)d->T * d->K;
+  size_t extra = 0;
+  if (d->round_mode == MOE_ROUND_NEAREST) extra = (size_t)d->E * (d->tile / 2);
+  if (d->round_mode == MOE_ROUND_STOCHASTIC) extra = (size_t)d->E * (d->tile - 1);
+  size_t cap = base + extra;
+  size_t all = (size_t)d->T * d->E;
+  return cap < all ? cap : all;
+}
+
+// Workspace items, in order, for each phase.
+struct Layout {
+  size_t off[8];
+  size_t total;
+};
+
+Layout route_layout(const moe_desc* d) {
+  Layout L{};
+  size_t o = 0;
+  const size_t TE = (size_t)d->T * d->E;
+  L.off[0] = o; o = up(o + TE);                                   // mask
+  L.off[1] = o; o = up(o + (d->round_mode ? TE * 4 : 0));         // scoresT
+  L.off[2] = o; o = up(o + TE * 4);                               // rowmap
+  L.off[3] = o; o = up(o + (size_t)d->T * 4);                     // tokcnt
+  L.total = o;
+  return L;
+}
+
+Layout fwd_layout(const moe_desc* d) {
+  Layout L{};
+  const size_t cap = capacity(d), es = elem_size(d->dtype);
+  size_t o = 0;
+  L.off[0] = o; o = up(o + cap * d->n * es);   // A
+  L.off[1] = o; o = up(o + cap * d->d * es);   // Y
+  L.total = o;
+  return L;
+}
+
+Layout bwd_layout(const moe_desc* d) {
+  Layout L{};
+  const size_t cap = capacity(d), es = elem_size(d->dtype);
+  const size_t np = (size_t)dh_partials(d->dtype, d->n);
+  size_t o = 0;
+  L.off[0] = o; o = up(o + cap * 2 * d->n * es);          // dH
+  L.off[1] = o; o = up(o + cap * d->n * es);              // A_s
+  L.off[2] = o; o = up(o + cap * np * 4);                 // dS partials
+  L.off[3] = o; o = up(o + cap * 4);                      // dS per row
+  L.off[4] = o; o = up(o + cap * 4);                      // dz per row
+  L.off[5] = o; o = up(o + (size_t)d->T * d->E * es);     // dz dense [T][E]
+  L.off[6] = o; o = up(o + (size_t)d->E * d->d * es);     // W_r^T [E][d]
+  L.off[7] = o; o = up(o + cap * d->d * es);              // dXt
+  L.total = o;
+  return L;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (!ws) return MOE_EINVAL;
+  if (((uintptr_t)ws & (ALIGN - 1)) != 0) return MOE_EINVAL;
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+bool routing_ok(const moe_routing* r) {
+  return r && r->logits && r->topk_idx && r->topk_gate && r->counts && r->counts_raw && r->offsets &&
+         r->tile_offsets && r->row_token && r->row_expert && r->row_gate && r->tok_ptr && r->tok_row;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+#define MOE_TRY(expr)                         \
+  do {                                        \
+    hipError_t _e = (expr);                   \
+    if (_e != hipSuccess) return MOE_EHIP;    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_row_capacity(const moe_desc* desc) {
+  if (validate_desc(desc) != MOE_OK) return 0;
+  return capacity(desc);
+}
+
+size_t moe_workspace_bytes(const moe_desc* desc, int which) {
+  if (validate_desc(desc) != MOE_OK) return 0;
+  switch (which) {
+    case MOE_WS_ROUTE: return route_layout(desc).total;
+    case MOE_WS_FWD: return fwd_layout(desc).total;
+    case MOE_WS_BWD: return bwd_layout(desc).total;
+    default: return 0;
+  }
+}
+
+size_t moe_workspace_offset(const moe_desc* desc, int item) {
+  if (validate_desc(desc) != MOE_OK) return (size_t)-1;
+  switch (item) {
+    case MOE_ITEM_A: return fwd_layout(desc).off[0];
+    case MOE_ITEM_Y: return fwd_layout(desc).off[1];
+    case MOE_ITEM_DH: return bwd_layout(desc).off[0];
+    case MOE_ITEM_AS: return bwd_layout(desc).off[1];
+    case MOE_ITEM_DS: return bwd_layout(desc).off[3];
+    case MOE_ITEM_DZ: return bwd_layout(desc).off[4];
+    case MOE_ITEM_DXT: return bwd_layout(desc).off[7];
+    default: return (size_t)-1;
+  }
+}
+
+int moe_route(const moe_desc* desc, const void* x, const void* w_r, const float* bias,
+              const moe_routing* routing, void* ws, size_t ws_bytes, void* stream) {
+  int s = validate_desc(desc);
+  if (s != MOE_OK) return s;
+  const bool given = (desc->flags & MOE_FLAG_SCORES_GIVEN) != 0;
+  if (!routing_ok(routing)) return MOE_EINVAL;
+  if (!given && (!x || !w_r)) return MOE_EINVAL;
+  const Layout L = route_layout(desc);
+  if ((s = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  if (!given)
+    MOE_TRY(launch_router_logits(desc->dtype, x, w_r, bias, routing->logits, desc->T, desc->d, desc->E, st));
+  RouteBufs rb{routing->logits,     routing->topk_idx,  routing->topk_gate, routing->counts,
+               routing->counts_raw, routing->offsets,   routing->tile_offsets, routing->row_token,
+               routing->row_expert, routing->row_gate,  routing->tok_ptr,   routing->tok_row};
+  RouteScratch sc{(uint8_t*)(w + L.off[0]), desc->round_mode ? (float*)(w + L.off[1]) : nullptr,
+                  (int32_t*)(w + L.off[2]), (int32_t*)(w + L.off[3])};
+  return hip_status(launch_route_select(rb, sc, desc->T, desc->E, desc->K, desc->tile, desc->round_mode,
+                                        desc->round_seed, st));
+}
+
+int moe_fwd(const moe_desc* desc, const void* x, const void* w1, const void* w2,
+            const moe_routing* routing, void* o, void* h_cache, void* ws, size_t ws_bytes, void* stream) {
+  int s = validate_desc(desc);
+  if (s != MOE_OK) return s;
+  if (!x || !w1 || !w2 || !o || !h_cache || !routing_ok(routing)) return MOE_EINVAL;
+  const Layout L = fwd_layout(desc);
+  if ((s = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  void* A = w + L.off[0];
+  void* Y = w + L.off[1];
+  const size_t cap = capacity(desc);
+  const moe_desc& D = *desc;
+  MOE_TRY(launch_up_swiglu(D.dtype, x, w1, routing->row_token, routing->offsets, routing->tile_offsets, D.E,
+                           D.d, D.n, cap, h_cache, A, st));
+  MOE_TRY(launch_down(D.dtype, A, w2, routing->offsets, routing->tile_offsets, D.E, D.d, D.n, cap, Y, st));
+  MOE_TRY(launch_aggregate_o(D.dtype, Y, routing->row_gate, routing->tok_ptr, routing->tok_row, D.T, D.d, o,
+                             st));
+  return MOE_OK;
+}
+
+int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1, const void* w2,
+            const moe_routing* routing, const void* h_cache, const void* d_o, void* dx, void* dw_r,
+            void* dw1, void* dw2, float* ds, float* db, void* ws, size_t ws_bytes, void* stream) {
+  int s = validate_desc(desc);
+  if (s != MOE_OK) return s;
+  if (!x || !w_r || !w1 || !w2 || !h_cache || !d_o || !dx || !dw_r || !dw1 || !dw2 || !routing_ok(routing))
+    return MOE_EINVAL;
+  const Layout L = bwd_layout(desc);
+  if ((s = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  const moe_desc& D = *desc;
+  const size_t cap = capacity(desc);
+  void* dH = w + L.off[0];
+  void* As = w + L.off[1];
+  float* dS_part = (float*)(w + L.off[2]);
+  float* dS_row = ds ? ds : (float*)(w + L.off[3]);
+  float* dz_row = (float*)(w + L.off[4]);
+  void* dz_dense = w + L.off[5];
+  void* w_rT = w + L.off[6];
+  void* dXt = w + L.off[7];
+  const moe_routing& R = *routing;
+
+  // dH kernel: dA' = dO W2^T with the recompute-A epilogue (dH, A_s, dS parts)
+  MOE_TRY(launch_dh(D.dtype, d_o, w2, h_cache, R.row_token, R.row_gate, R.offsets, R.tile_offsets, D.E, D.d,
+                    D.n, cap, dH, As, dS_part, st));
+  // router gradient: dS -> dz (per row and dense), dW_r = X^T dz
+  MOE_TRY(launch_router_grad(D.dtype, dS_part, dh_partials(D.dtype, D.n), R.row_gate, R.row_expert, R.tok_ptr,
+                             R.tok_row, D.T, D.E, dS_row, dz_row, dz_dense, st));
+  MOE_TRY(launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, st));
+  // activation gradient: dXt = dH W1^T, then dX = sum of dXt + dz W_r^T
+  MOE_TRY(launch_transpose(D.dtype, w_r, D.d, D.E, w_rT, st));
+  MOE_TRY(launch_dxt(D.dtype, dH, w1, R.offsets, R.tile_offsets, D.E, D.d, D.n, cap, dXt, st));
+  MOE_TRY(launch_aggregate_dx(D.dtype, dXt, dz_row, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T, D.d, dx,
+                              st));
+  // weight gradients
+  MOE_TRY(launch_dw1(D.dtype, x, dH, R.row_token, R.offsets, D.E, D.d, D.n, dw1, st));
+  MOE_TRY(launch_dw2(D.dtype, As, d_o, R.row_token, R.offsets, D.E, D.d, D.n, dw2, st));
+  if (db) MOE_TRY(launch_bias_grad(dz_row, R.offsets, D.E, db, st));
+  return MOE_OK;
+}
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_ESHAPE: return "unsupported shape";
+    case MOE_EDTYPE: return "unsupported dtype";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

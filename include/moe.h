@@ -1,0 +1,205 @@
+/*
+ * moe.h -- C ABI of the fine-grained MoE layer for MI355X (gfx950).
+ *
+ * One MoE layer on one GPU: top-K token-choice routing (optionally with token
+ * rounding), the gather-fused grouped GEMMs of the forward (up-projection with
+ * SwiGLU, down-projection), the weighted expert aggregation, and the
+ * memory-efficient backward that keeps only the up-projection output H
+ * between forward and backward and recomputes the router gradient from dO and
+ * the recomputed activations instead of from a cached down-projection output.
+ *
+ * Sources (web pages about SonicMoE, cited by title and section):
+ *   [A] "DeepSeek做大→Mega MoE，Tri Dao团队加快→SonicMoE" (article on the
+ *       authors' Blackwell blog): "MoE 与它的隐患" (standard MoE workflow
+ *       figures, routing metadata), "核心创新：一次算法级的重新设计" (reordered
+ *       contraction, gather fusion, SwiGLU epilogue, dH kernel), "实验结果"
+ *       (problem dimensions T, d, n, E, K).
+ *   [B] "SonicMoE：突破细粒度MoE硬件效率瓶颈，实现高稀疏性下的极致训练加速":
+ *       algorithm paragraph (router gradient without cached activations),
+ *       scheduling paragraph (token rounding to tile multiples), kernel-list
+ *       paragraph (up-proj A, down-proj Y, aggregation O; dH, up-proj
+ *       gradient, dX, dW1, dW2; host launches kernels by GEMM configuration).
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense row-major.  x [T,d], w_r [d,E], w1 [E,d,2n]
+ *     (columns 0..n-1 of each expert feed SiLU, columns n..2n-1 are the
+ *     "up" half), w2 [E,n,d], o / d_o / dx [T,d], dw_r [d,E], dw1 / dw2 as
+ *     w1 / w2.  Element type: desc->dtype (fp32 or bf16) for all of these.
+ *     Router scores, gates, per-row score gradients and bias are fp32.
+ *   - Every pointer except the host-side moe_desc is a device pointer owned
+ *     by the caller.  The library never allocates or frees memory; scratch
+ *     space comes from the caller's workspace (moe_workspace_bytes).
+ *   - Calls are stream-ordered and asynchronous on the hipStream_t passed in
+ *     (NULL = the default stream); buffers must stay valid until the stream
+ *     work completes.  No call synchronises the host.
+ *   - Arguments are validated on the host before anything is launched: an
+ *     error return means nothing was enqueued.  A launch failure reported by
+ *     the runtime returns MOE_EHIP (work enqueued before it may have run).
+ *   - Results are bit-identical from run to run (no floating-point atomics).
+ *   - Gradients are written, never accumulated.  Every expert's dw1 / dw2
+ *     slice is written, zeros for an expert that received no rows.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK          0
+#define MOE_EINVAL     -1  /* null pointer, K < 1, K > E, T < 1, bad flag/mode */
+#define MOE_ESHAPE     -2  /* dims the kernels do not support (see moe_desc) */
+#define MOE_EDTYPE     -3  /* unknown dtype */
+#define MOE_EWORKSPACE -4  /* workspace smaller than moe_workspace_bytes */
+#define MOE_EHIP       -5  /* the HIP runtime reported an error */
+
+/* element types */
+#define MOE_F32  0
+#define MOE_BF16 1
+
+/* token rounding modes ([B] scheduling paragraph) */
+#define MOE_ROUND_OFF        0
+#define MOE_ROUND_NEAREST    1  /* up when count mod tile >= tile/2 */
+#define MOE_ROUND_STOCHASTIC 2  /* up with probability (count mod tile)/tile */
+
+/* desc->flags */
+#define MOE_FLAG_SCORES_GIVEN 1u  /* moe_route reads routing->logits as the
+                                     router scores instead of computing them */
+
+/* workspace phases */
+#define MOE_WS_ROUTE 0
+#define MOE_WS_FWD   1
+#define MOE_WS_BWD   2
+
+/* internal workspace items exposed for inspection (moe_workspace_offset) */
+#define MOE_ITEM_Y        0  /* fwd: down-proj output Y [cap, d] (dtype)          */
+#define MOE_ITEM_A        1  /* fwd: SwiGLU output A [cap, n] (dtype)             */
+#define MOE_ITEM_DH       2  /* bwd: dH [cap, 2n] (dtype)                         */
+#define MOE_ITEM_AS       3  /* bwd: gate-scaled A [cap, n] (dtype)               */
+#define MOE_ITEM_DXT      4  /* bwd: per-row input gradient dXt [cap, d] (dtype)  */
+#define MOE_ITEM_DS       5  /* bwd: per-row score gradient dS [cap] (fp32)       */
+#define MOE_ITEM_DZ       6  /* bwd: per-row router-logit gradient dz [cap] (fp32) */
+
+/*
+ * Layer description (host struct).
+ *   T, d, E, n, K: tokens, hidden size, experts, expert intermediate size,
+ *     experts per token ([A] "实验结果" uses these names).
+ *   Supported by the kernels: T >= 1, 1 <= K <= E, E % 8 == 0, E <= 1024,
+ *     d % 128 == 0, n % 64 == 0, tile == 128 (else MOE_ESHAPE).
+ *   dtype: MOE_F32 or MOE_BF16.
+ *   round_mode / tile / round_seed: token rounding ([B] scheduling
+ *     paragraph); round_seed drives MOE_ROUND_STOCHASTIC only.
+ *   flags: MOE_FLAG_* bits.
+ */
+typedef struct moe_desc {
+    int32_t  T, d, E, n, K;
+    int32_t  dtype;
+    int32_t  round_mode;
+    int32_t  tile;
+    uint64_t round_seed;
+    uint32_t flags;
+    uint32_t reserved;   /* must be 0 */
+} moe_desc;
+
+/*
+ * Routing metadata, written by moe_route and read by moe_fwd / moe_bwd.
+ * All device pointers, caller-allocated; cap = moe_row_capacity(desc).
+ * This compact form replaces the pages' binary T x E routing mask ([A]
+ * "MoE 与它的隐患").  Rows are grouped by expert ("expert-sorted"), and inside
+ * an expert in ascending token id.
+ *   logits      [T*E] fp32  router scores z = x w_r + bias (an input when
+ *                           MOE_FLAG_SCORES_GIVEN is set)
+ *   topk_idx    [T*K] int32 per token, the K experts of largest score in
+ *                           descending order; equal scores: smaller id first
+ *   topk_gate   [T*K] fp32  softmax of the K selected scores, same order
+ *   counts      [E]   int32 rows per expert after token rounding
+ *   counts_raw  [E]   int32 rows per expert of plain top-K
+ *   offsets     [E+1] int32 exclusive prefix sum of counts; offsets[E] = P
+ *   tile_offsets[E+1] int32 exclusive prefix sum of ceil(counts/tile)
+ *   row_token   [cap] int32 token of each row
+ *   row_expert  [cap] int32 expert of each row
+ *   row_gate    [cap] fp32  gate of each row: softmax of the token's scores
+ *                           over its final expert set
+ *   tok_ptr     [T+1] int32 CSR over tokens: rows of token t are
+ *   tok_row     [cap] int32 tok_row[tok_ptr[t] .. tok_ptr[t+1]), ascending
+ */
+typedef struct moe_routing {
+    float*   logits;
+    int32_t* topk_idx;
+    float*   topk_gate;
+    int32_t* counts;
+    int32_t* counts_raw;
+    int32_t* offsets;
+    int32_t* tile_offsets;
+    int32_t* row_token;
+    int32_t* row_expert;
+    float*   row_gate;
+    int32_t* tok_ptr;
+    int32_t* tok_row;
+} moe_routing;
+
+/* Upper bound on routed rows P: T*K without rounding, T*K + E*tile/2
+ * (nearest) or T*K + E*(tile-1) (stochastic), never above T*E.
+ * Returns 0 for an invalid descriptor.  Host only. */
+size_t moe_row_capacity(const moe_desc* desc);
+
+/* Bytes of device workspace the phase `which` (MOE_WS_*) needs; 0 for an
+ * invalid descriptor.  Host only.  The workspace must be 256-byte aligned. */
+size_t moe_workspace_bytes(const moe_desc* desc, int which);
+
+/* Byte offset of an internal item (MOE_ITEM_*) inside the workspace of its
+ * phase, or (size_t)-1 when the item does not exist.  Host only.  The item
+ * holds the value computed by the most recent call of that phase. */
+size_t moe_workspace_offset(const moe_desc* desc, int item);
+
+/*
+ * Routing ([A] "MoE 与它的隐患": routing metadata; [B] scheduling paragraph).
+ *   x [T,d], w_r [d,E] (dtype), bias [E] fp32 or NULL; ignored when
+ *   MOE_FLAG_SCORES_GIVEN is set (then routing->logits is read).
+ *   Computes the scores, the top-K selection, token rounding when
+ *   desc->round_mode != 0, and every other field of *routing.
+ *   ws: MOE_WS_ROUTE workspace (ws_bytes >= moe_workspace_bytes).
+ *   Integer outputs are exact: the same scores always give the same rows.
+ */
+int moe_route(const moe_desc* desc, const void* x, const void* w_r, const float* bias,
+              const moe_routing* routing, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Forward ([B] kernel-list paragraph: up-proj A, down-proj Y, aggregation O;
+ * [A] second point: gather fusion and SwiGLU in the GEMM epilogue).
+ *   x [T,d], w1 [E,d,2n], w2 [E,n,d] (dtype); routing from moe_route.
+ *   o [T,d] (dtype): O_t = sum over token t's rows of gate * Y.
+ *   h_cache [cap,2n] (dtype): H = x[row_token] w1[e] per row, the only
+ *     activation kept for the backward.
+ *   ws: MOE_WS_FWD workspace (holds A and Y while the call runs).
+ */
+int moe_fwd(const moe_desc* desc, const void* x, const void* w1, const void* w2,
+            const moe_routing* routing, void* o, void* h_cache, void* ws, size_t ws_bytes,
+            void* stream);
+
+/*
+ * Backward of L = <d_o, O> ([A] first point: reordered contraction, no Y
+ * cached, no extra GEMM; [B] algorithm and kernel-list paragraphs).
+ *   Reads x, w_r, w1, w2, routing, h_cache (from moe_fwd), d_o [T,d].
+ *   Writes dx [T,d], dw_r [d,E], dw1 [E,d,2n], dw2 [E,n,d] (dtype), and when
+ *   non-NULL ds [cap] fp32 (per-row score gradient <dO_t, Y_r>) and
+ *   db [E] fp32 (bias gradient; the bias itself is not a trained input).
+ *   ws: MOE_WS_BWD workspace.
+ */
+int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1,
+            const void* w2, const moe_routing* routing, const void* h_cache, const void* d_o,
+            void* dx, void* dw_r, void* dw1, void* dw2, float* ds, float* db, void* ws,
+            size_t ws_bytes, void* stream);
+
+/* Static text for a status code.  Host only. */
+const char* moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

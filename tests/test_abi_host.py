@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI (no GPU needed): every symbol declared in
+include/moe.h is exported, and argument validation rejects bad calls before
+anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fine_grained_mixture_top_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("HIP library not built: run python -m fine_grained_mixture_top_amd.build")
+    return B.lib()
+
+
+def test_header_functions_exported(lib):
+    names = declared_functions()
+    assert set(names) == {"moe_row_capacity", "moe_workspace_bytes", "moe_workspace_offset",
+                          "moe_route", "moe_fwd", "moe_bwd", "moe_strerror"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define\s+(MOE_[A-Z0-9_]+)\s+(-?\d+)u?", text))
+    for k, v in consts.items():
+        assert getattr(B, k) == int(v), k
+
+
+def test_capacity_and_workspace():
+    d = B.make_desc(256, 128, 8, 64, 2, "f32")
+    assert B.moe_row_capacity(d) == 512
+    dn = B.make_desc(1000, 128, 16, 64, 2, "bf16", round_mode=1)
+    assert B.moe_row_capacity(dn) == 2000 + 16 * 64
+    ds = B.make_desc(1000, 128, 16, 64, 2, "bf16", round_mode=2)
+    assert B.moe_row_capacity(ds) == 2000 + 16 * 127
+    dcap = B.make_desc(10, 128, 16, 64, 2, "bf16", round_mode=2)
+    assert B.moe_row_capacity(dcap) == 10 * 16
+    for which in (0, 1, 2):
+        assert B.moe_workspace_bytes(d, which) > 0
+        assert B.moe_workspace_bytes(d, which) % 256 == 0
+    assert B.moe_workspace_bytes(d, 7) == 0
+    for item in range(7):
+        off = B.moe_workspace_offset(d, item)
+        assert off >= 0 and off % 256 == 0
+    assert B.moe_workspace_offset(d, 99) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), B.MOE_EINVAL), (dict(K=0), B.MOE_EINVAL), (dict(K=9), B.MOE_EINVAL),
+    (dict(dtype=7), B.MOE_EDTYPE), (dict(round_mode=3), B.MOE_EINVAL), (dict(tile=64), B.MOE_ESHAPE),
+    (dict(d=100), B.MOE_ESHAPE), (dict(n=48), B.MOE_ESHAPE), (dict(E=12, K=2), B.MOE_ESHAPE),
+    (dict(flags=4), B.MOE_EINVAL),
+])
+def test_invalid_descriptors_rejected(lib, kw, code):
+    a = dict(T=256, d=128, E=8, n=64, K=2, dtype="f32")
+    a.update(kw)
+    d = B.make_desc(**a)
+    assert B.moe_row_capacity(d) == 0
+    assert B.moe_workspace_bytes(d, 0) == 0
+    st = lib.moe_route(ctypes.byref(d), None, None, None, None, None, 0, None)
+    assert st == code
+    st = lib.moe_fwd(ctypes.byref(d), None, None, None, None, None, None, None, 0, None)
+    assert st == code
+
+
+def test_null_pointers_and_workspace_rejected_before_launch(lib):
+    d = B.make_desc(256, 128, 8, 64, 2, "f32")
+    # null routing
+    assert lib.moe_route(ctypes.byref(d), 16, 16, None, None, None, 0, None) == B.MOE_EINVAL
+    # fake (never dereferenced) device pointers: validation fails on the workspace first
+    r = B.MoeRouting(*([4096] * len(B.ROUTING_FIELDS)))
+    need = B.moe_workspace_bytes(d, B.MOE_WS_ROUTE)
+    assert lib.moe_route(ctypes.byref(d), 4096, 4096, None, ctypes.byref(r), 4096, need - 1,
+                         None) == B.MOE_EWORKSPACE
+    assert lib.moe_route(ctypes.byref(d), 4096, 4096, None, ctypes.byref(r), 4097, need,
+                         None) == B.MOE_EINVAL  # misaligned
+    assert lib.moe_route(ctypes.byref(d), None, 4096, None, ctypes.byref(r), 4096, need,
+                         None) == B.MOE_EINVAL  # x missing without given scores
+    r2 = B.MoeRouting(*([4096] * (len(B.ROUTING_FIELDS) - 1) + [0]))
+    assert lib.moe_fwd(ctypes.byref(d), 4096, 4096, 4096, ctypes.byref(r2), 4096, 4096, 4096,
+                       1 << 30, None) == B.MOE_EINVAL
+    need_b = B.moe_workspace_bytes(d, B.MOE_WS_BWD)
+    assert lib.moe_bwd(ctypes.byref(d), *([4096] * 4), ctypes.byref(r), *([4096] * 6), None, None,
+                       4096, need_b - 256, None) == B.MOE_EWORKSPACE
+
+
+def test_strerror():
+    assert B.moe_strerror(0) == "ok"
+    assert "workspace" in B.moe_strerror(B.MOE_EWORKSPACE)
+    assert B.moe_strerror(12345) == "unknown status"
