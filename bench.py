@@ -1,0 +1,184 @@
+"""Benchmark of one fine-grained MoE layer step (route + forward + backward) on
+one MI355X through the C ABI.
+
+Prints one JSON line: whole-step TFLOPS (useful FLOPs 18*P*d*n per step, P =
+routed rows) and its fraction of the bf16 MFMA peak, the roofline position of
+the dominant kernel (per-launch durations from HIP events the library records
+on its stream during the timed steps), every kernel's time and roofline
+fraction, and the fp64 CPU oracle timed on a bounded sample of the same
+workload as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload fg7b_bf16]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16
+MFMA_PEAK_F32 = 157.3     # TFLOP/s, MI355X fp32 (MFMA fp32 reuses this figure)
+HBM_PEAK = 8000.0         # GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fg7b_bf16")
+    ap.add_argument("--round-mode", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
+                    help="tokens of the oracle's CPU baseline sample (0 = skip)")
+    return ap.parse_args()
+
+
+def kernel_work(name, w, P, es):
+    """Algorithmic work of one launch: (amount, kind) with kind 'flop' or 'byte'."""
+    T, d, E, n = w.T, w.d, w.E, w.n
+    flops = {
+        "router_logits": 2.0 * T * d * E, "up": 4.0 * P * d * n, "down": 2.0 * P * n * d,
+        "dh": 2.0 * P * d * n, "dxt": 4.0 * P * d * n, "dw1": 4.0 * P * d * n,
+        "dw2": 2.0 * P * n * d, "dwr": 2.0 * T * d * E,
+    }
+    if name in flops:
+        return flops[name], "flop"
+    # bandwidth-bound kernels: bytes that must cross HBM once
+    bytes_ = {
+        "agg_o": P * d * es + T * d * es + P * 8 + (T + 1) * 4,
+        "agg_dx": P * d * es + T * d * es + P * 12 + (T + 1) * 4 + E * d * es,
+        "route_select": T * E * 4 + T * w.K * 8 + P * 16 + T * E * (1 + 1 + 4),
+        "router_grad": P * (8 + 4 + 4 + 4) + T * E * es,
+        "wr_t": 2 * E * d * es, "db": P * 4,
+    }
+    return float(bytes_.get(name, 0)), "byte"
+
+
+def cpu_baseline(w, a, tokens):
+    """fp64 oracle (as it stands) on the first `tokens` tokens of the workload."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    tk = min(tokens, w.T)
+    t0 = time.perf_counter()
+    r = O.layer(a["x"][:tk], a["w_r"], a["w1"], a["w2"], a["d_o"][:tk], w.dtype, w.K, bias=a["bias"])
+    dt = time.perf_counter() - t0
+    rows = int(r["n_rows"])
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = min(cores, int(omp))
+    del np
+    return {"value": 18.0 * rows * w.d * w.n / dt / 1e12, "unit": "TFLOPS", "cores": cores,
+            "kind": "oracle",
+            "sample": f"route+fwd+bwd of {tk} of {w.T} tokens ({rows} rows), same weights, "
+                      f"fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is built and measured on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from fine_grained_mixture_top_amd import binding as B
+    from fine_grained_mixture_top_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    a = I.draw_all(w)
+    dt = B.TORCH_DTYPE[B.DTYPE_CODE[w.dtype]]
+
+    def dev(v):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).cuda()
+
+    x, wr, w1, w2, do = (dev(a[k]) for k in ("x", "w_r", "w1", "w2", "d_o"))
+    bias = None if a["bias"] is None else torch.from_numpy(a["bias"]).cuda()
+    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=args.round_mode)
+    L = B.Layer(desc)
+
+    def step():
+        L.route(x, wr, bias)
+        L.forward(x, w1, w2)
+        L.backward(x, wr, w1, w2, do)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    prof = B.Profiler(capacity=(B.MOE_K_COUNT + 2) * args.steps)
+    prof.attach(L.desc)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    B.Profiler.detach(L.desc)
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    P = int(L.routing.offsets[-1].item())
+    es = 2 if w.dtype == "bf16" else 4
+    peak_mfma = MFMA_PEAK_BF16 if w.dtype == "bf16" else MFMA_PEAK_F32
+    per = {}
+    for kid, ms in prof.records():
+        per.setdefault(B.KERNEL_NAMES[kid], []).append(ms)
+    prof.close()
+    kernels = {}
+    for name, lst in per.items():
+        avg = sum(lst) / len(lst)
+        work, kind = kernel_work(name, w, P, es)
+        if kind == "flop":
+            ach = work / (avg * 1e-3) / 1e12
+            kernels[name] = {"ms": round(avg, 4), "bound": "mfma", "achieved": round(ach, 1),
+                             "peak": peak_mfma, "unit": "TFLOP/s", "frac": round(ach / peak_mfma, 4),
+                             "work": work}
+        else:
+            ach = work / (avg * 1e-3) / 1e9
+            kernels[name] = {"ms": round(avg, 4), "bound": "hbm", "achieved": round(ach, 1),
+                             "peak": HBM_PEAK, "unit": "GB/s", "frac": round(ach / HBM_PEAK, 4),
+                             "work": work}
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    dk = kernels[dom]
+    useful = w.flops_fwd_bwd(P if args.round_mode else None)
+    tflops = useful / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": "MoE layer fwd+bwd TFLOPS and % of bf16 MFMA peak, 7B fine-grained shape, 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "n": w.n, "K": w.K,
+                   "round_mode": args.round_mode, "rows": P, "parallelism": "single GPU"},
+        "mfma_peak_frac": round(tflops / peak_mfma, 4),
+        "tokens_per_s": round(w.T / (ms_step * 1e-3), 1),
+        "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
+                     "unit": dk["unit"], "frac": dk["frac"], "traffic": None},
+        "kernels": {k: {kk: v for kk, v in d.items() if kk != "work"} for k, d in kernels.items()},
+    }
+    if args.cpu_tokens > 0:
+        out["cpu_baseline"] = cpu_baseline(w, a, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,6 +26,12 @@ MOE_ROUND_OFF, MOE_ROUND_NEAREST, MOE_ROUND_STOCHASTIC = 0, 1, 2
 MOE_FLAG_SCORES_GIVEN = 1
 MOE_WS_ROUTE, MOE_WS_FWD, MOE_WS_BWD = 0, 1, 2
 MOE_ITEM_Y, MOE_ITEM_A, MOE_ITEM_DH, MOE_ITEM_AS, MOE_ITEM_DXT, MOE_ITEM_DS, MOE_ITEM_DZ = range(7)
+KERNEL_NAMES = ["router_logits", "route_select", "up", "down", "agg_o", "dh", "router_grad", "dwr",
+                "wr_t", "dxt", "agg_dx", "dw1", "dw2", "db"]
+(MOE_K_ROUTER_LOGITS, MOE_K_ROUTE_SELECT, MOE_K_UP, MOE_K_DOWN, MOE_K_AGG_O, MOE_K_DH,
+ MOE_K_ROUTER_GRAD, MOE_K_DWR, MOE_K_WR_T, MOE_K_DXT, MOE_K_AGG_DX, MOE_K_DW1, MOE_K_DW2,
+ MOE_K_DB) = range(14)
+MOE_K_COUNT = 14
 
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16}
@@ -37,12 +43,18 @@ class MoEError(RuntimeError):
         self.status = status
 
 
+class MoeProfile(ctypes.Structure):
+    _fields_ = [("capacity", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("start", ctypes.POINTER(ctypes.c_void_p)), ("stop", ctypes.POINTER(ctypes.c_void_p)),
+                ("kernel", ctypes.POINTER(ctypes.c_int32))]
+
+
 class MoeDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("n", ctypes.c_int32), ("K", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("round_mode", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("round_seed", ctypes.c_uint64), ("flags", ctypes.c_uint32),
-                ("reserved", ctypes.c_uint32)]
+                ("reserved", ctypes.c_uint32), ("profile", ctypes.POINTER(MoeProfile))]
 
 
 ROUTING_FIELDS = ["logits", "topk_idx", "topk_gate", "counts", "counts_raw", "offsets",
@@ -82,7 +94,70 @@ def lib() -> ctypes.CDLL:
 
 def make_desc(T, d, E, n, K, dtype="bf16", round_mode=0, tile=128, round_seed=0, flags=0) -> MoeDesc:
     code = DTYPE_CODE[dtype] if isinstance(dtype, str) else int(dtype)
-    return MoeDesc(T, d, E, n, K, code, round_mode, tile, round_seed, flags, 0)
+    return MoeDesc(T, d, E, n, K, code, round_mode, tile, round_seed, flags, 0, None)
+
+
+_hip = None
+
+
+def hip_runtime() -> ctypes.CDLL:
+    global _hip
+    if _hip is None:
+        lib()  # the library pulls in the HIP runtime
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                             ctypes.c_void_p]
+    return _hip
+
+
+class Profiler:
+    """Per-launch timing: HIP event pairs the library records around each
+    kernel it launches (moe_desc.profile)."""
+
+    def __init__(self, capacity: int):
+        h = hip_runtime()
+        self.capacity = capacity
+        self._start = (ctypes.c_void_p * capacity)()
+        self._stop = (ctypes.c_void_p * capacity)()
+        self._kernel = (ctypes.c_int32 * capacity)()
+        for i in range(capacity):
+            for arr in (self._start, self._stop):
+                ev = ctypes.c_void_p()
+                if h.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = ev.value
+        self.c = MoeProfile(capacity, 0, self._start, self._stop, self._kernel)
+
+    def attach(self, desc: MoeDesc):
+        desc.profile = ctypes.pointer(self.c)
+
+    @staticmethod
+    def detach(desc: MoeDesc):
+        desc.profile = None
+
+    def reset(self):
+        self.c.count = 0
+
+    def records(self):
+        """[(kernel id, milliseconds)] of the recorded launches (stream must be done)."""
+        h = hip_runtime()
+        out = []
+        for i in range(min(self.c.count, self.capacity)):
+            ms = ctypes.c_float()
+            if h.hipEventElapsedTime(ctypes.byref(ms), self._start[i], self._stop[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append((int(self._kernel[i]), float(ms.value)))
+        return out
+
+    def close(self):
+        h = hip_runtime()
+        for arr in (self._start, self._stop):
+            for i in range(self.capacity):
+                if arr[i]:
+                    h.hipEventDestroy(arr[i])
+                    arr[i] = None
 
 
 def _p(t: Optional[torch.Tensor]):

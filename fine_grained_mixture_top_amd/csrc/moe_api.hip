@@ -100,8 +100,26 @@ bool routing_ok(const moe_routing* r) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
-#define MOE_TRY(expr)                         \
+// Event pair around one launch when the caller asked for timing.
+struct Timed {
+  moe_profile* p;
+  hipStream_t st;
+  int slot;
+  Timed(const moe_desc* d, hipStream_t s, int kernel) : p(d->profile), st(s), slot(-1) {
+    if (p && p->count < p->capacity && p->start && p->stop) {
+      slot = p->count++;
+      if (p->kernel) p->kernel[slot] = kernel;
+      (void)hipEventRecord((hipEvent_t)p->start[slot], st);
+    }
+  }
+  ~Timed() {
+    if (slot >= 0) (void)hipEventRecord((hipEvent_t)p->stop[slot], st);
+  }
+};
+
+#define MOE_TRY(kid, expr)                    \
   do {                                        \
+    Timed _t(desc, st, (kid));                \
     hipError_t _e = (expr);                   \
     if (_e != hipSuccess) return MOE_EHIP;    \
   } while (0)
@@ -152,14 +170,16 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_r, const float*
   hipStream_t st = (hipStream_t)stream;
   char* w = (char*)ws;
   if (!given)
-    MOE_TRY(launch_router_logits(desc->dtype, x, w_r, bias, routing->logits, desc->T, desc->d, desc->E, st));
+    MOE_TRY(MOE_K_ROUTER_LOGITS,
+            launch_router_logits(desc->dtype, x, w_r, bias, routing->logits, desc->T, desc->d, desc->E, st));
   RouteBufs rb{routing->logits,     routing->topk_idx,  routing->topk_gate, routing->counts,
                routing->counts_raw, routing->offsets,   routing->tile_offsets, routing->row_token,
                routing->row_expert, routing->row_gate,  routing->tok_ptr,   routing->tok_row};
   RouteScratch sc{(uint8_t*)(w + L.off[0]), desc->round_mode ? (float*)(w + L.off[1]) : nullptr,
                   (int32_t*)(w + L.off[2]), (int32_t*)(w + L.off[3])};
-  return hip_status(launch_route_select(rb, sc, desc->T, desc->E, desc->K, desc->tile, desc->round_mode,
-                                        desc->round_seed, st));
+  MOE_TRY(MOE_K_ROUTE_SELECT, launch_route_select(rb, sc, desc->T, desc->E, desc->K, desc->tile,
+                                                  desc->round_mode, desc->round_seed, st));
+  return MOE_OK;
 }
 
 int moe_fwd(const moe_desc* desc, const void* x, const void* w1, const void* w2,
@@ -176,10 +196,10 @@ int moe_fwd(const moe_desc* desc, const void* x, const void* w1, const void* w2,
   void* Y = w + L.off[1];
   const size_t cap = capacity(desc);
   const moe_desc& D = *desc;
-  MOE_TRY(launch_up_swiglu(D.dtype, x, w1, routing->row_token, routing->offsets, routing->tile_offsets, D.E,
+  MOE_TRY(MOE_K_UP, launch_up_swiglu(D.dtype, x, w1, routing->row_token, routing->offsets, routing->tile_offsets, D.E,
                            D.d, D.n, cap, h_cache, A, st));
-  MOE_TRY(launch_down(D.dtype, A, w2, routing->offsets, routing->tile_offsets, D.E, D.d, D.n, cap, Y, st));
-  MOE_TRY(launch_aggregate_o(D.dtype, Y, routing->row_gate, routing->tok_ptr, routing->tok_row, D.T, D.d, o,
+  MOE_TRY(MOE_K_DOWN, launch_down(D.dtype, A, w2, routing->offsets, routing->tile_offsets, D.E, D.d, D.n, cap, Y, st));
+  MOE_TRY(MOE_K_AGG_O, launch_aggregate_o(D.dtype, Y, routing->row_gate, routing->tok_ptr, routing->tok_row, D.T, D.d, o,
                              st));
   return MOE_OK;
 }
@@ -209,21 +229,21 @@ int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1
   const moe_routing& R = *routing;
 
   // dH kernel: dA' = dO W2^T with the recompute-A epilogue (dH, A_s, dS parts)
-  MOE_TRY(launch_dh(D.dtype, d_o, w2, h_cache, R.row_token, R.row_gate, R.offsets, R.tile_offsets, D.E, D.d,
+  MOE_TRY(MOE_K_DH, launch_dh(D.dtype, d_o, w2, h_cache, R.row_token, R.row_gate, R.offsets, R.tile_offsets, D.E, D.d,
                     D.n, cap, dH, As, dS_part, st));
   // router gradient: dS -> dz (per row and dense), dW_r = X^T dz
-  MOE_TRY(launch_router_grad(D.dtype, dS_part, dh_partials(D.dtype, D.n), R.row_gate, R.row_expert, R.tok_ptr,
+  MOE_TRY(MOE_K_ROUTER_GRAD, launch_router_grad(D.dtype, dS_part, dh_partials(D.dtype, D.n), R.row_gate, R.row_expert, R.tok_ptr,
                              R.tok_row, D.T, D.E, dS_row, dz_row, dz_dense, st));
-  MOE_TRY(launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, st));
+  MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, st));
   // activation gradient: dXt = dH W1^T, then dX = sum of dXt + dz W_r^T
-  MOE_TRY(launch_transpose(D.dtype, w_r, D.d, D.E, w_rT, st));
-  MOE_TRY(launch_dxt(D.dtype, dH, w1, R.offsets, R.tile_offsets, D.E, D.d, D.n, cap, dXt, st));
-  MOE_TRY(launch_aggregate_dx(D.dtype, dXt, dz_row, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T, D.d, dx,
+  MOE_TRY(MOE_K_WR_T, launch_transpose(D.dtype, w_r, D.d, D.E, w_rT, st));
+  MOE_TRY(MOE_K_DXT, launch_dxt(D.dtype, dH, w1, R.offsets, R.tile_offsets, D.E, D.d, D.n, cap, dXt, st));
+  MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, dXt, dz_row, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T, D.d, dx,
                               st));
   // weight gradients
-  MOE_TRY(launch_dw1(D.dtype, x, dH, R.row_token, R.offsets, D.E, D.d, D.n, dw1, st));
-  MOE_TRY(launch_dw2(D.dtype, As, d_o, R.row_token, R.offsets, D.E, D.d, D.n, dw2, st));
-  if (db) MOE_TRY(launch_bias_grad(dz_row, R.offsets, D.E, db, st));
+  MOE_TRY(MOE_K_DW1, launch_dw1(D.dtype, x, dH, R.row_token, R.offsets, D.E, D.d, D.n, dw1, st));
+  MOE_TRY(MOE_K_DW2, launch_dw2(D.dtype, As, d_o, R.row_token, R.offsets, D.E, D.d, D.n, dw2, st));
+  if (db) MOE_TRY(MOE_K_DB, launch_bias_grad(dz_row, R.offsets, D.E, db, st));
   return MOE_OK;
 }
 

@@ -70,6 +70,23 @@ extern "C" {
 #define MOE_FLAG_SCORES_GIVEN 1u  /* moe_route reads routing->logits as the
                                      router scores instead of computing them */
 
+/* kernel ids reported in moe_profile.kernel (one per launch, in order) */
+#define MOE_K_ROUTER_LOGITS 0   /* z = x w_r + b                                  */
+#define MOE_K_ROUTE_SELECT  1   /* top-K, token rounding, segments, token CSR      */
+#define MOE_K_UP            2   /* K1: gathered x w1 with the SwiGLU epilogue -> H, A */
+#define MOE_K_DOWN          3   /* K2: A w2 -> Y                                   */
+#define MOE_K_AGG_O         4   /* K3: O = sum of gate * Y                         */
+#define MOE_K_DH            5   /* K4: dO w2^T with the dH epilogue -> dH, A_s, dS */
+#define MOE_K_ROUTER_GRAD   6   /* dS -> dz (softmax over the token's set)         */
+#define MOE_K_DWR           7   /* dw_r = x^T dz                                   */
+#define MOE_K_WR_T          8   /* w_r transposed for the dX aggregation           */
+#define MOE_K_DXT           9   /* K5: dH w1^T -> dXt                              */
+#define MOE_K_AGG_DX       10   /* K6: dX = sum of dXt + dz w_r^T                  */
+#define MOE_K_DW1          11   /* K7: dw1 = x_g^T dH                              */
+#define MOE_K_DW2          12   /* K8: dw2 = A_s^T dO_g                            */
+#define MOE_K_DB           13   /* db = per-expert sum of dz                       */
+#define MOE_K_COUNT        14
+
 /* workspace phases */
 #define MOE_WS_ROUTE 0
 #define MOE_WS_FWD   1
@@ -94,7 +111,24 @@ extern "C" {
  *   round_mode / tile / round_seed: token rounding ([B] scheduling
  *     paragraph); round_seed drives MOE_ROUND_STOCHASTIC only.
  *   flags: MOE_FLAG_* bits.
+ *   profile: NULL, or where to record per-kernel launch timing.
  */
+/*
+ * Optional launch timing (for measurement only).  When moe_desc.profile is
+ * non-NULL, each entry point records start[count] / stop[count] (hipEvent_t
+ * handles created by the caller) on its stream around every kernel it
+ * launches, stores the kernel's MOE_K_* id in kernel[count] and increments
+ * count; entries beyond capacity are not recorded.  The caller reads the
+ * elapsed times after the stream has completed.
+ */
+typedef struct moe_profile {
+    int32_t  capacity;
+    int32_t  count;
+    void**   start;    /* [capacity] hipEvent_t */
+    void**   stop;     /* [capacity] hipEvent_t */
+    int32_t* kernel;   /* [capacity] host array */
+} moe_profile;
+
 typedef struct moe_desc {
     int32_t  T, d, E, n, K;
     int32_t  dtype;
@@ -102,7 +136,8 @@ typedef struct moe_desc {
     int32_t  tile;
     uint64_t round_seed;
     uint32_t flags;
-    uint32_t reserved;   /* must be 0 */
+    uint32_t reserved;      /* must be 0 */
+    moe_profile* profile;   /* NULL, or launch timing (see moe_profile) */
 } moe_desc;
 
 /*
