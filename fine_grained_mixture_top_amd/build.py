@@ -21,7 +21,7 @@ ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 instructions stay off: the compiler would otherwise form
     # v_pk_* fp32 ops from plain float code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,30 +1,21 @@
 // Epilogues of the grouped GEMM: what each MoE kernel does with its
-// accumulator tile while it is still in registers ([A] "核心创新" second
-// point: SwiGLU fused into the up-projection epilogue; the dH kernel's
-// epilogue recomputes the activation and forms the score gradient).
+// accumulator tile ([A] "核心创新" second point: SwiGLU fused into the
+// up-projection epilogue; the dH kernel's epilogue recomputes the activation
+// and forms the score gradient).
+//
+// The main loop parks the fp32 tile in LDS ([BM][BN + 4], see stage_acc);
+// every epilogue then walks it in 8-column chunks of whole rows, 256 threads
+// at a time, so its global reads and writes are coalesced 16-byte accesses
+// and the element-wise math keeps few values live.
 #pragma once
 
 #include "grouped_gemm.h"
 
 namespace moe {
 
-// Copy rows of a staged tile (row pitch LD elements) to global memory in
-// 16-byte pieces.  dst(r) -> destination of row r (null = skip); only the
-// first `cols` columns exist.
-template <typename TO, class F>
-__device__ __forceinline__ void store_rows(const TO* s, int LD, int rows, int cols, int tid, F dst) {
-  constexpr int V = 16 / (int)sizeof(TO);
-  const int cpr = cols / V;
-  for (int v = tid; v < rows * cpr; v += 256) {
-    int r = v / cpr, ch = v - r * cpr;
-    TO* d = dst(r);
-    if (d) *reinterpret_cast<uint4*>(d + ch * V) = *reinterpret_cast<const uint4*>(s + r * LD + ch * V);
-  }
-}
-
 // C[row, n0 + col] = acc (+ bias[col]), converted to TO.
-// ROW mode: row = routed row; WGT mode: row = e*M + m (rows of all experts'
-// [M][N] slices are contiguous).
+// ROW mode: row = routed row; WGT mode: row = slice*M + m (rows of all
+// slices' [M][N] blocks are contiguous).
 template <typename T, typename TO, int BM, int BN>
 struct EpiStore {
   struct Params {
@@ -32,36 +23,32 @@ struct EpiStore {
     long long ldc;
     const float* bias;  // per column, may be null
   };
-  static constexpr int V = 16 / (int)sizeof(TO);
-  static constexpr int LD = BN + V;
-  static constexpr int SMEM = BM * LD * (int)sizeof(TO);
-  using G = TileGeom<T, BM, BN>;
+  static constexpr int SMEM = 0;
 
-  __device__ static void run(const Params& p, const GemmShape& s, const TileCtx& c,
-                             f32x4_v (&acc)[G::FM][G::FN], char* smem) {
-    TO* Cs = reinterpret_cast<TO*>(smem);
+  __device__ __forceinline__ static void run(const Params& p, const GemmShape& s, const TileCtx& c,
+                                             const float* Cs, char*) {
+    constexpr int LDC = BN + 4, CPR = BN / 8;
     const int cols = min(BN, s.n_valid - c.n0);
+    for (int v = c.tid; v < BM * CPR; v += 256) {
+      const int r = v / CPR, ch = v % CPR;
+      if (r < c.m_valid && ch * 8 < cols) {
+        float x[8];
+        ld8(Cs + r * LDC + ch * 8, x);
+        if (p.bias) {
 #pragma unroll
-    for (int fn = 0; fn < G::FN; ++fn) {
-      const int col = frag_col<T, BM, BN>(c, fn);
-      const float b = (p.bias && col < cols) ? p.bias[c.n0 + col] : 0.f;
-#pragma unroll
-      for (int fm = 0; fm < G::FM; ++fm)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          Cs[frag_row<T, BM, BN>(c, fm, j) * LD + col] = Elem<TO>::from_f(acc[fm][fn][j] + b);
+          for (int i = 0; i < 8; ++i) x[i] += p.bias[c.n0 + ch * 8 + i];
+        }
+        st8<TO>(p.C + (c.out_row0 + r) * p.ldc + c.n0 + ch * 8, x);
+      }
     }
-    __syncthreads();
-    store_rows<TO>(Cs, LD, BM, cols, c.tid, [&](int r) -> TO* {
-      return r < c.m_valid ? p.C + (c.out_row0 + r) * p.ldc + c.n0 : nullptr;
-    });
   }
 };
 
-// Up-projection epilogue (K1): the tile holds matching gate / up columns
-// (ColPaired).  H is rounded to the storage type first and A = silu(G)*U is
-// formed from the rounded values, so the backward's recomputation of A from
-// the cached H reproduces it exactly.
+// Up-projection epilogue (K1).  The staged tile holds BN/2 gate columns then
+// the matching BN/2 "up" columns (global columns j0.. and n + j0..).  H is
+// rounded to the storage type first and A = silu(G)*U is formed from the
+// rounded values, so the backward's recomputation of A from the cached H
+// reproduces it exactly.
 template <typename T, int BM, int BN>
 struct EpiSwiGLU {
   struct Params {
@@ -69,52 +56,41 @@ struct EpiSwiGLU {
     T* A;     // [rows, n]
     int n;
   };
-  static constexpr int V = 16 / (int)sizeof(T);
-  static constexpr int LDH = BN + V, LDA = BN / 2 + V;
-  static constexpr int SMEM = BM * (LDH + LDA) * (int)sizeof(T);
-  using G = TileGeom<T, BM, BN>;
-  static_assert(G::FN % 2 == 0, "paired tile needs an even fragment count");
+  static constexpr int SMEM = 0;
 
-  __device__ static void run(const Params& p, const GemmShape&, const TileCtx& c,
-                             f32x4_v (&acc)[G::FM][G::FN], char* smem) {
-    T* Hs = reinterpret_cast<T*>(smem);
-    T* As = Hs + BM * LDH;
-#pragma unroll
-    for (int q = 0; q < G::FN / 2; ++q) {
-      const int jj = (c.wn * (G::FN / 2) + q) * 16 + (c.lane & 15);
-#pragma unroll
-      for (int fm = 0; fm < G::FM; ++fm)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = frag_row<T, BM, BN>(c, fm, j);
-          const float g = through<T>(acc[fm][2 * q][j]);
-          const float u = through<T>(acc[fm][2 * q + 1][j]);
-          const float a = g * sigmoidf_(g) * u;
-          Hs[r * LDH + jj] = Elem<T>::from_f(g);
-          Hs[r * LDH + BN / 2 + jj] = Elem<T>::from_f(u);
-          As[r * LDA + jj] = Elem<T>::from_f(a);
-        }
-    }
-    __syncthreads();
+  __device__ __forceinline__ static void run(const Params& p, const GemmShape&, const TileCtx& c,
+                                             const float* Cs, char*) {
+    constexpr int LDC = BN + 4, CPR = BN / 16;
     const int j0 = c.nt * (BN / 2);
     const long long ldh = 2LL * p.n;
-    store_rows<T>(Hs, LDH, BM, BN / 2, c.tid, [&](int r) -> T* {
-      return r < c.m_valid ? p.H + (c.out_row0 + r) * ldh + j0 : nullptr;
-    });
-    store_rows<T>(Hs + BN / 2, LDH, BM, BN / 2, c.tid, [&](int r) -> T* {
-      return r < c.m_valid ? p.H + (c.out_row0 + r) * ldh + p.n + j0 : nullptr;
-    });
-    store_rows<T>(As, LDA, BM, BN / 2, c.tid, [&](int r) -> T* {
-      return r < c.m_valid ? p.A + (c.out_row0 + r) * (long long)p.n + j0 : nullptr;
-    });
+    for (int v = c.tid; v < BM * CPR; v += 256) {
+      const int r = v / CPR, jj = (v % CPR) * 8;
+      if (r < c.m_valid) {
+        float g[8], u[8], a[8];
+        ld8(Cs + r * LDC + jj, g);
+        ld8(Cs + r * LDC + BN / 2 + jj, u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          g[i] = through<T>(g[i]);
+          u[i] = through<T>(u[i]);
+          a[i] = g[i] * sigmoidf_(g[i]) * u[i];
+        }
+        const long long row = c.out_row0 + r;
+        st8<T>(p.H + row * ldh + j0 + jj, g);
+        st8<T>(p.H + row * ldh + p.n + j0 + jj, u);
+        st8<T>(p.A + row * (long long)p.n + j0 + jj, a);
+      }
+    }
   }
 };
 
-// dH epilogue (K4).  acc = dA' = dO[tok] W2^T for columns j of this tile.
-// From the cached H it recomputes A = silu(G)*U, then
+// dH epilogue (K4).  The staged tile is dA' = dO[tok] W2^T for columns
+// j = n0 .. n0+BN-1.  From the cached H it recomputes A = silu(G)*U, then
 //   dS partial = sum_j dA'_j A_j          (the reordered router contraction)
 //   dA = gate * dA',  dG = dA*U*s*(1+G*(1-s)),  dU = dA*silu(G)
 //   A_s = gate * A                        (operand of the dW2 GEMM)
+// The BN/8 chunks of a row sit on consecutive lanes, which sum the row's
+// partial with shuffles.
 template <typename T, int BM, int BN>
 struct EpiDH {
   struct Params {
@@ -126,64 +102,45 @@ struct EpiDH {
     int n;
     int NT;
   };
-  static constexpr int V = 16 / (int)sizeof(T);
-  static constexpr int LDD = 2 * BN + V, LDS_ = BN + V;
-  static constexpr int SMEM = BM * (LDD + LDS_) * (int)sizeof(T) + 2 * BM * 4;
-  using G = TileGeom<T, BM, BN>;
+  static constexpr int SMEM = 0;
+  static_assert((BN / 8) <= 64 && (64 % (BN / 8)) == 0, "row chunks must tile a wave");
 
-  __device__ static void run(const Params& p, const GemmShape&, const TileCtx& c,
-                             f32x4_v (&acc)[G::FM][G::FN], char* smem) {
-    T* dHs = reinterpret_cast<T*>(smem);
-    T* Ass = dHs + BM * LDD;
-    float* red = reinterpret_cast<float*>(Ass + BM * LDS_);
+  __device__ __forceinline__ static void run(const Params& p, const GemmShape&, const TileCtx& c,
+                                             const float* Cs, char*) {
+    constexpr int LDC = BN + 4, CPR = BN / 8;
     const long long ldh = 2LL * p.n;
-    float psum[G::FM][4];
+    for (int v = c.tid; v < BM * CPR; v += 256) {
+      const int r = v / CPR, ch = v % CPR;
+      const bool valid = r < c.m_valid;
+      const long long grow = c.out_row0 + (valid ? r : c.m_valid - 1);
+      const int col = c.n0 + ch * 8;
+      float dap[8], g[8], u[8];
+      ld8(Cs + r * LDC + ch * 8, dap);
+      ld8g<T>(p.H + grow * ldh + col, g);
+      ld8g<T>(p.H + grow * ldh + p.n + col, u);
+      const float gt = p.gate[grow];
+      float dg[8], du[8], as[8];
+      float ps = 0.f;
 #pragma unroll
-    for (int fm = 0; fm < G::FM; ++fm)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = frag_row<T, BM, BN>(c, fm, j);
-        const long long grow = c.out_row0 + (r < c.m_valid ? r : c.m_valid - 1);
-        const float gt = p.gate[grow];
-        const T* hrow = p.H + grow * ldh + c.n0;
-        float ps = 0.f;
-#pragma unroll
-        for (int fn = 0; fn < G::FN; ++fn) {
-          const int col = frag_col<T, BM, BN>(c, fn);
-          const float g = Elem<T>::to_f(hrow[col]);
-          const float u = Elem<T>::to_f(hrow[p.n + col]);
-          const float sg = sigmoidf_(g);
-          const float sl = g * sg;
-          const float a = sl * u;
-          const float dap = acc[fm][fn][j];
-          ps += dap * a;
-          const float da = gt * dap;
-          dHs[r * LDD + col] = Elem<T>::from_f(da * u * sg * (1.f + g * (1.f - sg)));
-          dHs[r * LDD + BN + col] = Elem<T>::from_f(da * sl);
-          Ass[r * LDS_ + col] = Elem<T>::from_f(gt * a);
-        }
-        psum[fm][j] = ps;
+      for (int i = 0; i < 8; ++i) {
+        const float sg = sigmoidf_(g[i]);
+        const float sl = g[i] * sg;
+        const float a = sl * u[i];
+        ps += dap[i] * a;
+        const float da = gt * dap[i];
+        dg[i] = da * u[i] * sg * (1.f + g[i] * (1.f - sg));
+        du[i] = da * sl;
+        as[i] = gt * a;
       }
-    // row sums over this wave's columns, then over the two column waves
-#pragma unroll
-    for (int fm = 0; fm < G::FM; ++fm)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = sum16(psum[fm][j]);
-        if ((c.lane & 15) == 0) red[c.wn * BM + frag_row<T, BM, BN>(c, fm, j)] = v;
+      if (valid) {
+        st8<T>(p.dH + grow * ldh + col, dg);
+        st8<T>(p.dH + grow * ldh + p.n + col, du);
+        st8<T>(p.As + grow * (long long)p.n + col, as);
       }
-    __syncthreads();
-    for (int r = c.tid; r < c.m_valid; r += 256)
-      p.dS_part[(c.out_row0 + r) * p.NT + c.nt] = red[r] + red[BM + r];
-    store_rows<T>(dHs, LDD, BM, BN, c.tid, [&](int r) -> T* {
-      return r < c.m_valid ? p.dH + (c.out_row0 + r) * ldh + c.n0 : nullptr;
-    });
-    store_rows<T>(dHs + BN, LDD, BM, BN, c.tid, [&](int r) -> T* {
-      return r < c.m_valid ? p.dH + (c.out_row0 + r) * ldh + p.n + c.n0 : nullptr;
-    });
-    store_rows<T>(Ass, LDS_, BM, BN, c.tid, [&](int r) -> T* {
-      return r < c.m_valid ? p.As + (c.out_row0 + r) * (long long)p.n + c.n0 : nullptr;
-    });
+#pragma unroll
+      for (int o = 1; o < CPR; o <<= 1) ps += __shfl_xor(ps, o, 64);
+      if (valid && ch == 0) p.dS_part[grow * p.NT + c.nt] = ps;
+    }
   }
 };
 

@@ -2,6 +2,7 @@
 // host-side choice of tile configuration per GEMM ([B] kernel-list paragraph:
 // the host launches each kernel with its chosen GEMM configuration).
 #include <algorithm>
+#include <type_traits>
 
 #include "epilogues.h"
 #include "launch.h"
@@ -43,27 +44,31 @@ hipError_t run_gemm(const GemmShape& s, const Operand& A, const Operand& B,
 long long row_tiles_bound(size_t cap, int E, int BM) { return (long long)(cap + BM - 1) / BM + E; }
 
 // ---------------------------------------------------------------------------
-// per-dtype configurations
+// configurations: bf16 uses 128 x 128 tiles (two workgroups per CU), 128 x 64
+// where a dimension is only a multiple of 64; the fp32 path (small checks)
+// uses 128 x 64 tiles.
 // ---------------------------------------------------------------------------
 
 template <typename T> struct Cfg;
 template <> struct Cfg<bf16_t> {
-  static constexpr int UP_BN = 128, DOWN_BN = 128, DH_BN = 64, DXT_BN = 128;
-  static constexpr int DW1_BN = 128, DW2_BN = 128, R_BN = 64, DWR_BN = 64;
+  static constexpr int BIG = 128, SMALL = 128;   // column tile of down / dXt
+  __host__ static int bm_rows() { return 256; }
 };
 template <> struct Cfg<float> {
-  static constexpr int UP_BN = 64, DOWN_BN = 64, DH_BN = 32, DXT_BN = 64;
-  static constexpr int DW1_BN = 64, DW2_BN = 64, R_BN = 64, DWR_BN = 64;
+  static constexpr int BIG = 64, SMALL = 64;
+  __host__ static int bm_rows() { return 128; }
 };
 
-constexpr int BM = 128;  // routed-row tile; equals the token-rounding tile
+// rows tile of the ROW-mode GEMMs
+constexpr int ROWS_TILE = 128;
+template <typename T> constexpr int ROWS = ROWS_TILE;
 
 template <typename T>
 hipError_t router_logits(const void* x, const void* w_r, const float* bias, float* logits, int T_,
                          int d, int E, hipStream_t st) {
-  constexpr int BN = Cfg<T>::R_BN;
+  constexpr int BM = ROWS<T>, BN = std::is_same<T, bf16_t>::value ? 128 : 64;
   using Epi = EpiStore<T, float, BM, BN>;
-  GemmShape s{nullptr, nullptr, 1, T_, (E + BN - 1) / BN * BN, d, E};
+  GemmShape s{nullptr, 1, T_, (E + BN - 1) / BN * BN, d, E, 1};
   Operand A{x, nullptr, 0, d};
   Operand B{w_r, nullptr, 0, E};
   typename Epi::Params ep{logits, E, bias};
@@ -71,109 +76,187 @@ hipError_t router_logits(const void* x, const void* w_r, const float* bias, floa
   return run_gemm<T, BM, BN, false, B_KN, false, Epi>(s, A, B, ep, tiles, st);
 }
 
-template <typename T>
-hipError_t up_swiglu(const void* x, const void* w1, const int32_t* row_token, const int32_t* offsets,
-                     const int32_t* tile_offsets, int E, int d, int n, size_t cap, void* H, void* A,
-                     hipStream_t st) {
-  constexpr int BN = Cfg<T>::UP_BN;
+template <typename T, int BN>
+hipError_t up_swiglu_t(const void* x, const void* w1, const int32_t* row_token, const int32_t* offsets, int E,
+                       int d, int n, size_t cap, void* H, void* A, hipStream_t st) {
+  constexpr int BM = ROWS<T>;
   using Epi = EpiSwiGLU<T, BM, BN>;
-  GemmShape s{offsets, tile_offsets, E, 0, 2 * n, d, 2 * n};
+  GemmShape s{offsets, E, 0, 2 * n, d, 2 * n, 1};
   Operand a{x, row_token, 0, d};
   Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
   typename Epi::Params ep{reinterpret_cast<T*>(H), reinterpret_cast<T*>(A), n};
   return run_gemm<T, BM, BN, false, B_KN, true, Epi>(s, a, b, ep,
                                                       row_tiles_bound(cap, E, BM) * (2 * n / BN), st);
 }
-
 template <typename T>
-hipError_t down(const void* A, const void* w2, const int32_t* offsets, const int32_t* tile_offsets,
-                int E, int d, int n, size_t cap, void* Y, hipStream_t st) {
-  constexpr int BN = Cfg<T>::DOWN_BN;
+hipError_t up_swiglu(const void* x, const void* w1, const int32_t* row_token, const int32_t* offsets,
+                     const int32_t*, int E, int d, int n, size_t cap, void* H, void* A, hipStream_t st) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    return up_swiglu_t<T, 128>(x, w1, row_token, offsets, E, d, n, cap, H, A, st);
+  } else {
+    return up_swiglu_t<T, 64>(x, w1, row_token, offsets, E, d, n, cap, H, A, st);
+  }
+}
+
+template <typename T, int BN>
+hipError_t down_t(const void* A, const void* w2, const int32_t* offsets, int E, int d, int n, size_t cap,
+                  void* Y, hipStream_t st) {
+  constexpr int BM = ROWS<T>;
   using Epi = EpiStore<T, T, BM, BN>;
-  GemmShape s{offsets, tile_offsets, E, 0, d, n, d};
+  GemmShape s{offsets, E, 0, d, n, d, 1};
   Operand a{A, nullptr, 0, n};
   Operand b{w2, nullptr, (long long)n * d, d};
   typename Epi::Params ep{reinterpret_cast<T*>(Y), d, nullptr};
-  return run_gemm<T, BM, BN, false, B_KN, false, Epi>(s, a, b, ep,
-                                                       row_tiles_bound(cap, E, BM) * (d / BN), st);
+  return run_gemm<T, BM, BN, false, B_KN, false, Epi>(s, a, b, ep, row_tiles_bound(cap, E, BM) * (d / BN), st);
+}
+template <typename T>
+hipError_t down(const void* A, const void* w2, const int32_t* offsets, const int32_t*, int E, int d, int n,
+                size_t cap, void* Y, hipStream_t st) {
+  if (d % Cfg<T>::BIG == 0) return down_t<T, Cfg<T>::BIG>(A, w2, offsets, E, d, n, cap, Y, st);
+  return down_t<T, Cfg<T>::SMALL>(A, w2, offsets, E, d, n, cap, Y, st);
 }
 
-template <typename T>
-hipError_t dh(const void* d_o, const void* w2, const void* H, const int32_t* row_token,
-              const float* row_gate, const int32_t* offsets, const int32_t* tile_offsets, int E, int d,
-              int n, size_t cap, void* dH, void* As, float* dS_part, hipStream_t st) {
-  constexpr int BN = Cfg<T>::DH_BN;
+// dH: the column tile decides the number of score-gradient partials per row
+template <typename T> int dh_bn(int n);
+template <> int dh_bn<bf16_t>(int n) { return n % 128 == 0 ? 128 : 64; }
+template <> int dh_bn<float>(int) { return 32; }
+
+template <typename T, int BN>
+hipError_t dh_t(const void* d_o, const void* w2, const void* H, const int32_t* row_token, const float* row_gate,
+                const int32_t* offsets, int E, int d, int n, size_t cap, void* dH, void* As, float* dS_part,
+                hipStream_t st) {
+  constexpr int BM = ROWS<T>;
   using Epi = EpiDH<T, BM, BN>;
-  GemmShape s{offsets, tile_offsets, E, 0, n, d, n};
+  GemmShape s{offsets, E, 0, n, d, n, 1};
   Operand a{d_o, row_token, 0, d};
   Operand b{w2, nullptr, (long long)n * d, d};  // W2[e] is [n][d]: row j holds k = 0..d-1
   typename Epi::Params ep{reinterpret_cast<const T*>(H), row_gate, reinterpret_cast<T*>(dH),
                           reinterpret_cast<T*>(As), dS_part, n, n / BN};
-  return run_gemm<T, BM, BN, false, B_NK, false, Epi>(s, a, b, ep,
-                                                       row_tiles_bound(cap, E, BM) * (n / BN), st);
+  return run_gemm<T, BM, BN, false, B_NK, false, Epi>(s, a, b, ep, row_tiles_bound(cap, E, BM) * (n / BN), st);
+}
+template <typename T>
+hipError_t dh(const void* d_o, const void* w2, const void* H, const int32_t* row_token, const float* row_gate,
+              const int32_t* offsets, const int32_t*, int E, int d, int n, size_t cap, void* dH, void* As,
+              float* dS_part, hipStream_t st) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (dh_bn<T>(n) == 128)
+      return dh_t<T, 128>(d_o, w2, H, row_token, row_gate, offsets, E, d, n, cap, dH, As, dS_part, st);
+    return dh_t<T, 64>(d_o, w2, H, row_token, row_gate, offsets, E, d, n, cap, dH, As, dS_part, st);
+  } else {
+    return dh_t<T, 32>(d_o, w2, H, row_token, row_gate, offsets, E, d, n, cap, dH, As, dS_part, st);
+  }
 }
 
-template <typename T>
-hipError_t dxt(const void* dH, const void* w1, const int32_t* offsets, const int32_t* tile_offsets,
-               int E, int d, int n, size_t cap, void* dXt, hipStream_t st) {
-  constexpr int BN = Cfg<T>::DXT_BN;
+template <typename T, int BN>
+hipError_t dxt_t(const void* dH, const void* w1, const int32_t* offsets, int E, int d, int n, size_t cap,
+                 void* dXt, hipStream_t st) {
+  constexpr int BM = ROWS<T>;
   using Epi = EpiStore<T, T, BM, BN>;
-  GemmShape s{offsets, tile_offsets, E, 0, d, 2 * n, d};
+  GemmShape s{offsets, E, 0, d, 2 * n, d, 1};
   Operand a{dH, nullptr, 0, 2 * n};
   Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};  // W1[e] is [d][2n]: row i holds k = 0..2n-1
   typename Epi::Params ep{reinterpret_cast<T*>(dXt), d, nullptr};
-  return run_gemm<T, BM, BN, false, B_NK, false, Epi>(s, a, b, ep,
-                                                       row_tiles_bound(cap, E, BM) * (d / BN), st);
+  return run_gemm<T, BM, BN, false, B_NK, false, Epi>(s, a, b, ep, row_tiles_bound(cap, E, BM) * (d / BN), st);
+}
+template <typename T>
+hipError_t dxt(const void* dH, const void* w1, const int32_t* offsets, const int32_t*, int E, int d, int n,
+               size_t cap, void* dXt, hipStream_t st) {
+  if (d % Cfg<T>::BIG == 0) return dxt_t<T, Cfg<T>::BIG>(dH, w1, offsets, E, d, n, cap, dXt, st);
+  return dxt_t<T, Cfg<T>::SMALL>(dH, w1, offsets, E, d, n, cap, dXt, st);
 }
 
-template <typename T>
-hipError_t dw1(const void* x, const void* dH, const int32_t* row_token, const int32_t* offsets, int E,
-               int d, int n, void* dW1, hipStream_t st) {
-  constexpr int BN = Cfg<T>::DW1_BN;
-  using Epi = EpiStore<T, T, BM, BN>;
-  GemmShape s{offsets, nullptr, E, d, 2 * n, 0, 2 * n};
+template <typename T, int BMW, int BN>
+hipError_t dw1_t(const void* x, const void* dH, const int32_t* row_token, const int32_t* offsets, int E, int d,
+                 int n, void* dW1, hipStream_t st) {
+  using Epi = EpiStore<T, T, BMW, BN>;
+  GemmShape s{offsets, E, d, 2 * n, 0, 2 * n, 1};
   Operand a{x, row_token, 0, d};
   Operand b{dH, nullptr, 0, 2 * n};
   typename Epi::Params ep{reinterpret_cast<T*>(dW1), 2 * n, nullptr};
-  return run_gemm<T, BM, BN, true, B_KN, false, Epi>(s, a, b, ep,
-                                                      (long long)E * (d / BM) * (2 * n / BN), st);
+  return run_gemm<T, BMW, BN, true, B_KN, false, Epi>(s, a, b, ep, (long long)E * (d / BMW) * (2 * n / BN), st);
+}
+template <typename T>
+hipError_t dw1(const void* x, const void* dH, const int32_t* row_token, const int32_t* offsets, int E, int d,
+               int n, void* dW1, hipStream_t st) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    return dw1_t<T, 128, 128>(x, dH, row_token, offsets, E, d, n, dW1, st);
+  } else {
+    return dw1_t<T, 128, 64>(x, dH, row_token, offsets, E, d, n, dW1, st);
+  }
 }
 
-template <typename T, int BMW>
-hipError_t dw2_impl(const void* As, const void* d_o, const int32_t* row_token, const int32_t* offsets,
-                    int E, int d, int n, void* dW2, hipStream_t st) {
-  constexpr int BN = Cfg<T>::DW2_BN;
+template <typename T, int BMW, int BN>
+hipError_t dw2_t(const void* As, const void* d_o, const int32_t* row_token, const int32_t* offsets, int E,
+                 int d, int n, void* dW2, hipStream_t st) {
   using Epi = EpiStore<T, T, BMW, BN>;
-  GemmShape s{offsets, nullptr, E, n, d, 0, d};
+  GemmShape s{offsets, E, n, d, 0, d, 1};
   Operand a{As, nullptr, 0, n};
   Operand b{d_o, row_token, 0, d};
   typename Epi::Params ep{reinterpret_cast<T*>(dW2), d, nullptr};
-  return run_gemm<T, BMW, BN, true, B_KN, false, Epi>(s, a, b, ep,
-                                                       (long long)E * (n / BMW) * (d / BN), st);
+  return run_gemm<T, BMW, BN, true, B_KN, false, Epi>(s, a, b, ep, (long long)E * (n / BMW) * (d / BN), st);
+}
+template <typename T>
+hipError_t dw2(const void* As, const void* d_o, const int32_t* row_token, const int32_t* offsets, int E, int d,
+               int n, void* dW2, hipStream_t st) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (n % 128 == 0) return dw2_t<T, 128, 128>(As, d_o, row_token, offsets, E, d, n, dW2, st);
+    return dw2_t<T, 64, 128>(As, d_o, row_token, offsets, E, d, n, dW2, st);
+  } else {
+    if (n % 128 == 0) return dw2_t<T, 128, 64>(As, d_o, row_token, offsets, E, d, n, dW2, st);
+    return dw2_t<T, 64, 64>(As, d_o, row_token, offsets, E, d, n, dW2, st);
+  }
+}
+
+// Router weight gradient dW_r = X^T dz: one dense reduction over all T
+// tokens with only (d/BM) x (E/BN) output tiles, so the reduction is split
+// into chunks whose fp32 partials are summed in a fixed order afterwards.
+template <typename TO>
+__global__ void k_sum_partials(const float* __restrict__ part, int splits, long long count,
+                               TO* __restrict__ out) {
+  const long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= count) return;
+  float4 acc = *reinterpret_cast<const float4*>(part + i);
+  for (int s = 1; s < splits; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (long long)s * count + i);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  out[i] = Elem<TO>::from_f(acc.x);
+  out[i + 1] = Elem<TO>::from_f(acc.y);
+  out[i + 2] = Elem<TO>::from_f(acc.z);
+  out[i + 3] = Elem<TO>::from_f(acc.w);
 }
 
 template <typename T>
-hipError_t dw2(const void* As, const void* d_o, const int32_t* row_token, const int32_t* offsets, int E,
-               int d, int n, void* dW2, hipStream_t st) {
-  if (n % 128 == 0) return dw2_impl<T, 128>(As, d_o, row_token, offsets, E, d, n, dW2, st);
-  return dw2_impl<T, 64>(As, d_o, row_token, offsets, E, d, n, dW2, st);
-}
-
-template <typename T>
-hipError_t dwr(const void* x, const void* dz, int T_, int d, int E, void* dWr, hipStream_t st) {
-  constexpr int BN = Cfg<T>::DWR_BN;
-  using Epi = EpiStore<T, T, BM, BN>;
-  GemmShape s{nullptr, nullptr, 1, d, (E + BN - 1) / BN * BN, T_, E};
+hipError_t dwr(const void* x, const void* dz, int T_, int d, int E, void* dWr, float* part, hipStream_t st) {
+  constexpr int BM = 128, BN = 64;
+  using Epi = EpiStore<T, float, BM, BN>;
+  const int NT = (E + BN - 1) / BN;
+  const int splits = dwr_splits(T_, d, E);
+  GemmShape s{nullptr, 1, d, NT * BN, T_, E, splits};
   Operand a{x, nullptr, 0, d};
   Operand b{dz, nullptr, 0, E};
-  typename Epi::Params ep{reinterpret_cast<T*>(dWr), E, nullptr};
-  return run_gemm<T, BM, BN, true, B_KN, false, Epi>(s, a, b, ep,
-                                                      (long long)(d / BM) * ((E + BN - 1) / BN), st);
+  typename Epi::Params ep{part, E, nullptr};
+  hipError_t err = run_gemm<T, BM, BN, true, B_KN, false, Epi>(s, a, b, ep,
+                                                               (long long)splits * (d / BM) * NT, st);
+  if (err != hipSuccess) return err;
+  const long long count = (long long)d * E;  // multiple of 4: d % 128 == 0
+  hipLaunchKernelGGL(k_sum_partials<T>, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0, st, part,
+                     splits, count, reinterpret_cast<T*>(dWr));
+  return hipGetLastError();
 }
 
 }  // namespace
 
-int dh_block(int dtype) { return dtype == DT_BF16 ? Cfg<bf16_t>::DH_BN : Cfg<float>::DH_BN; }
+int dh_block(int dtype, int n) { return dtype == DT_BF16 ? dh_bn<bf16_t>(n) : dh_bn<float>(n); }
+
+int dwr_splits(int T, int d, int E) {
+  const int tiles = (d / 128) * ((E + 63) / 64);
+  int s = (512 + tiles - 1) / tiles;           // about two resident tiles per CU
+  const int kmax = (T + 255) / 256;            // at least 4 k steps of 64 per chunk
+  if (s > kmax) s = kmax;
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : s;
+}
 
 #define MOE_DISPATCH(dtype, fn, ...) \
   ((dtype) == DT_BF16 ? fn<bf16_t>(__VA_ARGS__) : fn<float>(__VA_ARGS__))
@@ -213,8 +296,8 @@ hipError_t launch_dw2(int dtype, const void* As, const void* d_o, const int32_t*
   return MOE_DISPATCH(dtype, dw2, As, d_o, row_token, offsets, E, d, n, dW2, st);
 }
 hipError_t launch_dwr(int dtype, const void* x, const void* dz_dense, int T, int d, int E, void* dWr,
-                      hipStream_t st) {
-  return MOE_DISPATCH(dtype, dwr, x, dz_dense, T, d, E, dWr, st);
+                      float* partials, hipStream_t st) {
+  return MOE_DISPATCH(dtype, dwr, x, dz_dense, T, d, E, dWr, partials, st);
 }
 
 }  // namespace moe

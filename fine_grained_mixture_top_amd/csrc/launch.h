@@ -12,9 +12,9 @@ namespace moe {
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
 
 // Column tile of the dH GEMM, which decides how many fp32 score-gradient
-// partials each row gets (n / dh_block(dtype)).
-int dh_block(int dtype);
-inline int dh_partials(int dtype, int n) { return n / dh_block(dtype); }
+// partials each row gets (n / dh_block(dtype, n)).
+int dh_block(int dtype, int n);
+inline int dh_partials(int dtype, int n) { return n / dh_block(dtype, n); }
 
 // ---- grouped GEMMs (gemm_kernels.hip) ----
 hipError_t launch_router_logits(int dtype, const void* x, const void* w_r, const float* bias,
@@ -36,8 +36,11 @@ hipError_t launch_dw1(int dtype, const void* x, const void* dH, const int32_t* r
                       const int32_t* offsets, int E, int d, int n, void* dW1, hipStream_t st);
 hipError_t launch_dw2(int dtype, const void* As, const void* d_o, const int32_t* row_token,
                       const int32_t* offsets, int E, int d, int n, void* dW2, hipStream_t st);
+// dW_r = x^T dz_dense, reduction split in dwr_splits() chunks whose fp32
+// partials ([splits][d][E]) go to `partials` and are then summed in order.
+int dwr_splits(int T, int d, int E);
 hipError_t launch_dwr(int dtype, const void* x, const void* dz_dense, int T, int d, int E,
-                      void* dWr, hipStream_t st);
+                      void* dWr, float* partials, hipStream_t st);
 
 // ---- routing (route_kernels.hip) ----
 struct RouteBufs {
@@ -54,10 +57,12 @@ struct RouteBufs {
   int32_t* tok_ptr;
   int32_t* tok_row;
 };
+// Membership rows are padded to mask_pitch(T) tokens (16-byte aligned).
+int mask_pitch(int T);
 struct RouteScratch {
-  uint8_t* mask;       // [E][T] membership
+  uint8_t* mask;       // [E][pitch] membership bytes
   float* scoresT;      // [E][T] scores, expert-major (token rounding only)
-  int32_t* rowmap;     // [E][T] row of (e, t)
+  int32_t* rowmap;     // [E][pitch] row of (e, t)
   int32_t* tokcnt;     // [T]
 };
 hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int T, int E, int K,

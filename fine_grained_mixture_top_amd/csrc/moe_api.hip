@@ -42,7 +42,7 @@ size_t capacity(const moe_desc* d) {
 
 // Workspace items, in order, for each phase.
 struct Layout {
-  size_t off[8];
+  size_t off[9];
   size_t total;
 };
 
@@ -50,9 +50,10 @@ Layout route_layout(const moe_desc* d) {
   Layout L{};
   size_t o = 0;
   const size_t TE = (size_t)d->T * d->E;
-  L.off[0] = o; o = up(o + TE);                                   // mask
+  const size_t TEp = (size_t)mask_pitch(d->T) * d->E;
+  L.off[0] = o; o = up(o + TEp);                                  // mask
   L.off[1] = o; o = up(o + (d->round_mode ? TE * 4 : 0));         // scoresT
-  L.off[2] = o; o = up(o + TE * 4);                               // rowmap
+  L.off[2] = o; o = up(o + TEp * 4);                              // rowmap
   L.off[3] = o; o = up(o + (size_t)d->T * 4);                     // tokcnt
   L.total = o;
   return L;
@@ -81,6 +82,7 @@ Layout bwd_layout(const moe_desc* d) {
   L.off[5] = o; o = up(o + (size_t)d->T * d->E * es);     // dz dense [T][E]
   L.off[6] = o; o = up(o + (size_t)d->E * d->d * es);     // W_r^T [E][d]
   L.off[7] = o; o = up(o + cap * d->d * es);              // dXt
+  L.off[8] = o; o = up(o + (size_t)dwr_splits(d->T, d->d, d->E) * d->d * d->E * 4);  // dW_r partials
   L.total = o;
   return L;
 }
@@ -234,7 +236,7 @@ int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1
   // router gradient: dS -> dz (per row and dense), dW_r = X^T dz
   MOE_TRY(MOE_K_ROUTER_GRAD, launch_router_grad(D.dtype, dS_part, dh_partials(D.dtype, D.n), R.row_gate, R.row_expert, R.tok_ptr,
                              R.tok_row, D.T, D.E, dS_row, dz_row, dz_dense, st));
-  MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, st));
+  MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, (float*)(w + L.off[8]), st));
   // activation gradient: dXt = dH W1^T, then dX = sum of dXt + dz W_r^T
   MOE_TRY(MOE_K_WR_T, launch_transpose(D.dtype, w_r, D.d, D.E, w_rT, st));
   MOE_TRY(MOE_K_DXT, launch_dxt(D.dtype, dH, w1, R.offsets, R.tile_offsets, D.E, D.d, D.n, cap, dXt, st));

@@ -82,24 +82,26 @@ __device__ __forceinline__ int block_scan1024(int v, int* lds /* >= 16 ints */, 
   return base + incl - v;
 }
 
-// One wave per token: K rounds of a wave-wide arg-max over the token's
-// scores.  Writes the slot-ordered experts, their softmax gates and the
-// membership bytes.  Slot k's score is kept by lane k % 64.
+// G lanes per token (G = 16 or 64): K rounds of an arg-max over the token's
+// scores held E/G per lane.  Writes the slot-ordered experts, their softmax
+// gates and the membership bytes; with fixed_ptr also tok_ptr[t] = t*K (every
+// token keeps exactly K rows when there is no token rounding).  Slot k's score
+// is kept by lane k % G of the group.
+template <int G>
 __global__ void __launch_bounds__(256)
-k_topk(const float* __restrict__ scores, int T, int E, int K, int32_t* __restrict__ topk_idx,
-       float* __restrict__ topk_gate, uint8_t* __restrict__ mask) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;  // whole wave; no block barrier below
-  const float* z = scores + (size_t)t * E;
-  constexpr int MAXV = 16;  // E <= 1024
+k_topk(const float* __restrict__ scores, int T, int E, int K, int mpitch, int32_t* __restrict__ topk_idx,
+       float* __restrict__ topk_gate, uint8_t* __restrict__ mask, int32_t* __restrict__ tok_ptr) {
+  constexpr int MAXV = 16;  // E <= 16 * G
+  const int lane = threadIdx.x & (G - 1);
+  const int t = (blockIdx.x * 256 + threadIdx.x) / G;
+  const bool live = t < T;  // groups never straddle a wave, so shuffles stay inside live groups
+  const float* z = scores + (size_t)(live ? t : 0) * E;
   float v[MAXV], zs[MAXV];
   uint32_t taken = 0;
-  const int nv = (E + 63) / 64;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
-    int e = lane + 64 * i;
-    const bool ok = i < nv && e < E;
+    const int e = lane + G * i;
+    const bool ok = live && e < E;
     v[i] = ok ? z[e] : 0.f;
     zs[i] = 0.f;
     if (!ok) taken |= 1u << i;
@@ -110,48 +112,60 @@ k_topk(const float* __restrict__ scores, int T, int E, int K, int32_t* __restric
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
       if (!(taken & (1u << i))) {
-        int e = lane + 64 * i;
+        const int e = lane + G * i;
         if (be == 0x7fffffff || beats(v[i], e, bv, be)) { bv = v[i]; be = e; }
       }
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oe = __shfl_xor(be, o, 64);
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
       if (oe != 0x7fffffff && (be == 0x7fffffff || beats(ov, oe, bv, be))) { bv = ov; be = oe; }
     }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if ((k & 63) == lane) {
+    if (live && (be & (G - 1)) == lane) taken |= 1u << (be / G);
+    if ((k & (G - 1)) == lane) {
 #pragma unroll
       for (int i = 0; i < MAXV; ++i)
-        if (i == (k >> 6)) zs[i] = bv;
+        if (i == k / G) zs[i] = bv;
     }
-    if (lane == 0) {
+    if (lane == 0 && live) {
       topk_idx[(size_t)t * K + k] = be;
-      mask[(size_t)be * T + t] = 1;
+      mask[(size_t)be * mpitch + t] = 1;
     }
   }
-  const float m = __shfl(zs[0], 0, 64);  // slot 0 holds the largest score
+  const float m = __shfl(zs[0], (threadIdx.x & 63) & ~(G - 1), 64);  // slot 0: largest score
   float part = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i)
-    if (lane + 64 * i < K) part += __expf(zs[i] - m);
-  const float sum = wave_sum(part);
+    if (lane + G * i < K) part += __expf(zs[i] - m);
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+  if (!live) return;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
-    const int k = lane + 64 * i;
-    if (k < K) topk_gate[(size_t)t * K + k] = __expf(zs[i] - m) / sum;
+    const int k = lane + G * i;
+    if (k < K) topk_gate[(size_t)t * K + k] = __expf(zs[i] - m) / part;
+  }
+  if (tok_ptr && lane == 0) {
+    tok_ptr[t] = t * K;
+    if (t == T - 1) tok_ptr[T] = T * K;
   }
 }
 
-// counts[e] = number of member tokens of expert e (one workgroup per expert).
+// counts[e] = number of member tokens of expert e (one workgroup per expert;
+// mask rows are 16-byte aligned and zero past T).
 __global__ void __launch_bounds__(256)
-k_expert_count(const uint8_t* __restrict__ mask, int T, int32_t* __restrict__ counts,
+k_expert_count(const uint8_t* __restrict__ mask, int mpitch, int32_t* __restrict__ counts,
                int32_t* __restrict__ counts2) {
   __shared__ int lds[8];
   const int e = blockIdx.x;
-  const uint8_t* m = mask + (size_t)e * T;
+  const uint4* m = reinterpret_cast<const uint4*>(mask + (size_t)e * mpitch);
   int c = 0;
-  for (int t = threadIdx.x; t < T; t += 256) c += m[t];
+  for (int i = threadIdx.x; i < mpitch / 16; i += 256) {
+    const uint4 u = m[i];
+    // each byte is 0 or 1: the byte sum of a word is its popcount
+    c += __popc(u.x) + __popc(u.y) + __popc(u.z) + __popc(u.w);
+  }
   int total;
   block_scan256(c, lds, &total);
   if (threadIdx.x == 0) {
@@ -183,7 +197,7 @@ __global__ void k_transpose_scores(const float* __restrict__ in, int T, int E, f
 // select over the order-preserving score keys; equal-key candidates are then
 // taken in ascending token order.
 __global__ void __launch_bounds__(256)
-k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask,
+k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int mpitch,
               const int32_t* __restrict__ counts_raw, int T, int M, int mode, uint64_t seed) {
   __shared__ int hist[256];
   __shared__ int sh[8];
@@ -208,7 +222,7 @@ k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask,
   const bool drop = r < c;
   const uint8_t want = drop ? 1 : 0;         // candidates: routed (drop) or not (add)
   const int k_sel = drop ? r : r - c;        // candidates to select
-  uint8_t* m = mask + (size_t)e * T;
+  uint8_t* m = mask + (size_t)e * mpitch;
   const float* z = scoresT + (size_t)e * T;
 
   uint32_t prefix = 0, pmask = 0;
@@ -285,38 +299,64 @@ k_scan_experts(const int32_t* __restrict__ counts, int E, int tile, int32_t* __r
 }
 
 // Rows of expert e: its member tokens in ascending order, at offsets[e].
-// Each thread takes 16 consecutive tokens per sweep.
+// Each thread takes 16 consecutive tokens (one 16-byte mask load) per sweep.
+// rowmap[e][t] = row of (e, t); tokcnt (token rounding only) counts rows per
+// token.
 __global__ void __launch_bounds__(256)
-k_compact(const uint8_t* __restrict__ mask, const int32_t* __restrict__ offsets, int T,
+k_compact(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restrict__ offsets, int T,
           int32_t* __restrict__ row_token, int32_t* __restrict__ row_expert,
           int32_t* __restrict__ rowmap, int32_t* __restrict__ tokcnt) {
   __shared__ int sh[8];
   const int e = blockIdx.x;
-  const uint8_t* m = mask + (size_t)e * T;
-  int32_t* rm = rowmap + (size_t)e * T;
+  const uint8_t* m = mask + (size_t)e * mpitch;
+  int32_t* rm = rowmap + (size_t)e * mpitch;
   int carry = offsets[e];
-  for (int base = 0; base < T; base += 256 * 16) {
+  for (int base = 0; base < mpitch; base += 256 * 16) {
     const int t0 = base + threadIdx.x * 16;
-    uint8_t f[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) f[i] = (t0 + i < T) ? m[t0 + i] : 0;
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cnt += f[i];
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (t0 < mpitch) u = *reinterpret_cast<const uint4*>(m + t0);
+    const int cnt = __popc(u.x) + __popc(u.y) + __popc(u.z) + __popc(u.w);
     int tot;
     int row = carry + block_scan256(cnt, sh, &tot);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (f[i]) {
+      if ((w[i >> 2] >> (8 * (i & 3))) & 0xffu) {
         const int t = t0 + i;
         row_token[row] = t;
         row_expert[row] = e;
         rm[t] = row;
-        atomicAdd(&tokcnt[t], 1);
+        if (tokcnt) atomicAdd(&tokcnt[t], 1);
         ++row;
       }
     }
     carry += tot;
+  }
+}
+
+// Plain top-K: each token's rows are its K slots sorted by expert id; the
+// row gate is the slot's top-K gate.
+__global__ void __launch_bounds__(256)
+k_tok_fill_topk(const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_gate,
+                const int32_t* __restrict__ rowmap, int mpitch, int T, int K,
+                int32_t* __restrict__ tok_row, float* __restrict__ row_gate) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  const int32_t* idx = topk_idx + (size_t)t * K;
+  const float* g = topk_gate + (size_t)t * K;
+  int32_t* out = tok_row + (size_t)t * K;
+  // selection sort by expert id; K is small (<= E) and ids are distinct
+  int prev = -1;
+  for (int j = 0; j < K; ++j) {
+    int best = 0x7fffffff, bk = 0;
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[k];
+      if (e > prev && e < best) { best = e; bk = k; }
+    }
+    const int row = rowmap[(size_t)best * mpitch + t];
+    out[j] = row;
+    row_gate[row] = g[bk];
+    prev = best;
   }
 }
 
@@ -340,10 +380,10 @@ k_tok_scan(const int32_t* __restrict__ tokcnt, int T, int32_t* __restrict__ tok_
   if (threadIdx.x == 0) tok_ptr[T] = tot;
 }
 
-// Per token: its rows in ascending expert order (= ascending row index) and
-// each row's gate, the softmax of the token's scores over its final set.
+// Token rounding: per token, its rows in ascending expert order and each
+// row's gate, the softmax of the token's scores over its final set.
 __global__ void __launch_bounds__(256)
-k_tok_fill(const uint8_t* __restrict__ mask, const int32_t* __restrict__ rowmap,
+k_tok_fill(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restrict__ rowmap,
            const float* __restrict__ scores, const int32_t* __restrict__ tok_ptr, int T, int E,
            int32_t* __restrict__ tok_row, float* __restrict__ row_gate) {
   const int t = blockIdx.x * 256 + threadIdx.x;
@@ -351,14 +391,14 @@ k_tok_fill(const uint8_t* __restrict__ mask, const int32_t* __restrict__ rowmap,
   const float* z = scores + (size_t)t * E;
   float mx = -INFINITY;
   for (int e = 0; e < E; ++e)
-    if (mask[(size_t)e * T + t]) mx = fmaxf(mx, z[e]);
+    if (mask[(size_t)e * mpitch + t]) mx = fmaxf(mx, z[e]);
   float sum = 0.f;
   for (int e = 0; e < E; ++e)
-    if (mask[(size_t)e * T + t]) sum += __expf(z[e] - mx);
+    if (mask[(size_t)e * mpitch + t]) sum += __expf(z[e] - mx);
   int j = tok_ptr[t];
   for (int e = 0; e < E; ++e)
-    if (mask[(size_t)e * T + t]) {
-      const int row = rowmap[(size_t)e * T + t];
+    if (mask[(size_t)e * mpitch + t]) {
+      const int row = rowmap[(size_t)e * mpitch + t];
       tok_row[j++] = row;
       row_gate[row] = __expf(z[e] - mx) / sum;
     }
@@ -366,32 +406,50 @@ k_tok_fill(const uint8_t* __restrict__ mask, const int32_t* __restrict__ rowmap,
 
 }  // namespace
 
+int mask_pitch(int T) { return (T + 15) / 16 * 16; }
+
 hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int T, int E, int K,
                                int tile, int round_mode, uint64_t round_seed, hipStream_t st) {
   hipError_t err;
-  if ((err = hipMemsetAsync(sc.mask, 0, (size_t)E * T, st)) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, st, rb.logits, T, E, K, rb.topk_idx,
-                     rb.topk_gate, sc.mask);
-  if (round_mode == 0) {
-    hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, T, rb.counts_raw, rb.counts);
+  const int mp = mask_pitch(T);
+  if ((err = hipMemsetAsync(sc.mask, 0, (size_t)E * mp, st)) != hipSuccess) return err;
+  int32_t* fixed_ptr = round_mode == 0 ? rb.tok_ptr : nullptr;
+  if (E <= 256) {
+    const long long threads = (long long)T * 16;
+    hipLaunchKernelGGL(k_topk<16>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, rb.logits, T, E,
+                       K, mp, rb.topk_idx, rb.topk_gate, sc.mask, fixed_ptr);
   } else {
-    hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, T, rb.counts_raw,
+    const long long threads = (long long)T * 64;
+    hipLaunchKernelGGL(k_topk<64>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, rb.logits, T, E,
+                       K, mp, rb.topk_idx, rb.topk_gate, sc.mask, fixed_ptr);
+  }
+  if (round_mode == 0) {
+    hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.counts_raw, rb.counts);
+  } else {
+    hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.counts_raw,
                        (int32_t*)nullptr);
     hipLaunchKernelGGL(k_transpose_scores, dim3((T + 31) / 32, (E + 31) / 32), dim3(256), 0, st,
                        rb.logits, T, E, sc.scoresT);
-    hipLaunchKernelGGL(k_token_round, dim3(E), dim3(256), 0, st, sc.scoresT, sc.mask, rb.counts_raw, T,
-                       tile, round_mode, round_seed);
-    hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, T, rb.counts,
+    hipLaunchKernelGGL(k_token_round, dim3(E), dim3(256), 0, st, sc.scoresT, sc.mask, mp, rb.counts_raw,
+                       T, tile, round_mode, round_seed);
+    hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.counts,
                        (int32_t*)nullptr);
   }
   hipLaunchKernelGGL(k_scan_experts, dim3(1), dim3(1024), 0, st, rb.counts, E, tile, rb.offsets,
                      rb.tile_offsets);
-  if ((err = hipMemsetAsync(sc.tokcnt, 0, (size_t)T * sizeof(int32_t), st)) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_compact, dim3(E), dim3(256), 0, st, sc.mask, rb.offsets, T, rb.row_token,
-                     rb.row_expert, sc.rowmap, sc.tokcnt);
-  hipLaunchKernelGGL(k_tok_scan, dim3(1), dim3(1024), 0, st, sc.tokcnt, T, rb.tok_ptr);
-  hipLaunchKernelGGL(k_tok_fill, dim3((T + 255) / 256), dim3(256), 0, st, sc.mask, sc.rowmap, rb.logits,
-                     rb.tok_ptr, T, E, rb.tok_row, rb.row_gate);
+  if (round_mode == 0) {
+    hipLaunchKernelGGL(k_compact, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.offsets, T, rb.row_token,
+                       rb.row_expert, sc.rowmap, (int32_t*)nullptr);
+    hipLaunchKernelGGL(k_tok_fill_topk, dim3((T + 255) / 256), dim3(256), 0, st, rb.topk_idx, rb.topk_gate,
+                       sc.rowmap, mp, T, K, rb.tok_row, rb.row_gate);
+  } else {
+    if ((err = hipMemsetAsync(sc.tokcnt, 0, (size_t)T * sizeof(int32_t), st)) != hipSuccess) return err;
+    hipLaunchKernelGGL(k_compact, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.offsets, T, rb.row_token,
+                       rb.row_expert, sc.rowmap, sc.tokcnt);
+    hipLaunchKernelGGL(k_tok_scan, dim3(1), dim3(1024), 0, st, sc.tokcnt, T, rb.tok_ptr);
+    hipLaunchKernelGGL(k_tok_fill, dim3((T + 255) / 256), dim3(256), 0, st, sc.mask, mp, sc.rowmap, rb.logits,
+                       rb.tok_ptr, T, E, rb.tok_row, rb.row_gate);
+  }
   return hipGetLastError();
 }
 
