@@ -32,7 +32,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fg7b_bf16")
     ap.add_argument("--round-mode", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=8192,
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the oracle's CPU baseline sample (0 = skip)")
     return ap.parse_args()
 

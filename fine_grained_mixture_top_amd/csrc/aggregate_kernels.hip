@@ -48,8 +48,33 @@ __device__ __forceinline__ void store_vec(T* p, const float (&v)[16 / sizeof(T)]
 }
 
 constexpr int UNR = 4;  // rows in flight per lane
+constexpr int CPL = 4;  // 16-byte column chunks per lane per pass
 
-// O[t] = sum over token t's rows (ascending) of gate_r * Y[r]
+// Streaming 16-byte load (read once: keep it out of the caches' way).
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4_v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_v*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack(const uint4 u, float (&v)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+  }
+}
+
+// O[t] = sum over token t's rows (ascending) of gate_r * Y[r].  One wave per
+// token; each lane owns up to CPL 16-byte column chunks per pass and keeps
+// UNR rows x CPL chunks of loads in flight.
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_aggregate_o(const T* __restrict__ Y, const float* __restrict__ row_gate,
@@ -61,28 +86,41 @@ k_aggregate_o(const T* __restrict__ Y, const float* __restrict__ row_gate,
   if (t >= Tn) return;
   const int j0 = tok_ptr[t], j1 = tok_ptr[t + 1];
   const int nch = d / V;
-  for (int ch = lane; ch < nch; ch += 64) {
-    float acc[V];
+  for (int cb = 0; cb < nch; cb += 64 * CPL) {
+    float acc[CPL][V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[c][i] = 0.f;
     for (int j = j0; j < j1; j += UNR) {
-      float v[UNR][V];
+      uint4 raw[UNR][CPL];
       float g[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        if (j + u < j1) {
-          const int r = tok_row[j + u];
-          g[u] = row_gate[r];
-          load_vec<T>(Y + (size_t)r * d + ch * V, v[u]);
+        const bool ok = j + u < j1;
+        const int r = ok ? tok_row[j + u] : 0;
+        g[u] = ok ? row_gate[r] : 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int ch = cb + lane + 64 * c;
+          raw[u][c] = (ok && ch < nch) ? ld_stream(Y + (size_t)r * d + ch * V) : make_uint4(0, 0, 0, 0);
         }
       }
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
-        if (j + u < j1)
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] = fmaf(g[u], v[u][i], acc[i]);
+        for (int c = 0; c < CPL; ++c) {
+          float v[V];
+          unpack<T>(raw[u][c], v);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[c][i] = fmaf(g[u], v[i], acc[c][i]);
+        }
     }
-    store_vec<T>(O + (size_t)t * d + ch * V, acc);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = cb + lane + 64 * c;
+      if (ch < nch) store_vec<T>(O + (size_t)t * d + ch * V, acc[c]);
+    }
   }
 }
 
@@ -99,29 +137,45 @@ k_aggregate_dx(const T* __restrict__ dXt, const float* __restrict__ dz_row,
   if (t >= Tn) return;
   const int j0 = tok_ptr[t], j1 = tok_ptr[t + 1];
   const int nch = d / V;
-  for (int ch = lane; ch < nch; ch += 64) {
-    float acc[V];
+  for (int cb = 0; cb < nch; cb += 64 * CPL) {
+    float acc[CPL][V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[c][i] = 0.f;
     for (int j = j0; j < j1; j += UNR) {
-      float v[UNR][V], w[UNR][V];
+      uint4 raw[UNR][CPL], wr[UNR][CPL];
       float g[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        if (j + u < j1) {
-          const int r = tok_row[j + u];
-          g[u] = dz_row[r];
-          load_vec<T>(dXt + (size_t)r * d + ch * V, v[u]);
-          load_vec<T>(w_rT + (size_t)row_expert[r] * d + ch * V, w[u]);
+        const bool ok = j + u < j1;
+        const int r = ok ? tok_row[j + u] : 0;
+        g[u] = ok ? dz_row[r] : 0.f;
+        const int e = ok ? row_expert[r] : 0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int ch = cb + lane + 64 * c;
+          const bool in = ok && ch < nch;
+          raw[u][c] = in ? ld_stream(dXt + (size_t)r * d + ch * V) : make_uint4(0, 0, 0, 0);
+          wr[u][c] = in ? *reinterpret_cast<const uint4*>(w_rT + (size_t)e * d + ch * V) : make_uint4(0, 0, 0, 0);
         }
       }
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
-        if (j + u < j1)
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] = fmaf(g[u], w[u][i], acc[i] + v[u][i]);
+        for (int c = 0; c < CPL; ++c) {
+          float v[V], ww[V];
+          unpack<T>(raw[u][c], v);
+          unpack<T>(wr[u][c], ww);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[c][i] = fmaf(g[u], ww[i], acc[c][i] + v[i]);
+        }
     }
-    store_vec<T>(dX + (size_t)t * d + ch * V, acc);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = cb + lane + 64 * c;
+      if (ch < nch) store_vec<T>(dX + (size_t)t * d + ch * V, acc[c]);
+    }
   }
 }
 

@@ -28,10 +28,10 @@ int occupancy(K kernel) {
 }
 
 // Persistent launch: one workgroup per resident slot, never more than tiles.
-template <typename T, int BM, int BN, bool WGT, int BL, bool PAIRED, class Epi>
+template <typename T, int BM, int BN, bool WGT, int BL, bool PAIRED, class Epi, int PF = 1>
 hipError_t run_gemm(const GemmShape& s, const Operand& A, const Operand& B,
                     const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
-  auto kern = grouped_gemm_kernel<T, BM, BN, WGT, BL, PAIRED, Epi>;
+  auto kern = grouped_gemm_kernel<T, BM, BN, WGT, BL, PAIRED, Epi, PF>;
   static const int occ = occupancy(kern);  // per instantiation, fixed for the process
   long long slots = (long long)num_cus() * occ;
   long long grid = std::min(max_tiles, slots);
@@ -85,8 +85,9 @@ hipError_t up_swiglu_t(const void* x, const void* w1, const int32_t* row_token, 
   Operand a{x, row_token, 0, d};
   Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
   typename Epi::Params ep{reinterpret_cast<T*>(H), reinterpret_cast<T*>(A), n};
-  return run_gemm<T, BM, BN, false, B_KN, true, Epi>(s, a, b, ep,
-                                                      row_tiles_bound(cap, E, BM) * (2 * n / BN), st);
+  // two k steps of loads in flight: the gathered token rows come from L2 / MALL
+  return run_gemm<T, BM, BN, false, B_KN, true, Epi, 2>(s, a, b, ep,
+                                                         row_tiles_bound(cap, E, BM) * (2 * n / BN), st);
 }
 template <typename T>
 hipError_t up_swiglu(const void* x, const void* w1, const int32_t* row_token, const int32_t* offsets,

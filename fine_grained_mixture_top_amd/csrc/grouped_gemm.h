@@ -138,18 +138,19 @@ struct KMajorLoad {
       ptr[p] = (v < NV) ? rowptr(r < R ? r : 0) + c * VEC : nullptr;
     }
   }
+  static constexpr bool FULL = NV % 256 == 0;  // every thread has PER chunks
   template <int S>
   __device__ __forceinline__ void load(int k0) {
 #pragma unroll
     for (int p = 0; p < PER; ++p)
-      if (ptr[p]) reg[S][p] = *reinterpret_cast<const uint4*>(ptr[p] + k0);
+      if (FULL || ptr[p]) reg[S][p] = *reinterpret_cast<const uint4*>(ptr[p] + k0);
   }
   template <int S>
   __device__ __forceinline__ void store(T* lds, int tid) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int v = tid + p * 256;
-      if (v < NV) {
+      if (FULL || v < NV) {
         const int r = v / CPR, c = v % CPR;
         *reinterpret_cast<uint4*>(lds + r * LD + c * VEC) = reg[S][p];
       }
@@ -208,7 +209,7 @@ struct NatLoad {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int v = tid + p * 256;
-      if (v < NV) *reinterpret_cast<uint4*>(lds + (v / CPR) * LD + (v % CPR) * VEC) = reg[S][p];
+      if (NV % 256 == 0 || v < NV) *reinterpret_cast<uint4*>(lds + (v / CPR) * LD + (v % CPR) * VEC) = reg[S][p];
     }
   }
 };
@@ -315,20 +316,27 @@ struct Mma;
 template <int BM, int BN, bool AMN, bool BMN>
 struct Mma<bf16_t, BM, BN, AMN, BMN> {
   using G = TileGeom<bf16_t, BM, BN, AMN, BMN>;
+  static constexpr int KS = G::BK / 32;  // MFMA k steps per LDS stage
+  __device__ __forceinline__ static void fetch(const bf16_t* As, const bf16_t* Bs, bf16x8_v (&a)[G::FM],
+                                               bf16x8_v (&b)[G::FN], int ks, int lane, int wm, int wn) {
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm) a[fm] = frag<bf16_t, BM, AMN>(As, wm * G::WM + fm * 16, ks, lane);
+#pragma unroll
+    for (int fn = 0; fn < G::FN; ++fn) b[fn] = frag<bf16_t, BN, BMN>(Bs, wn * G::WN + fn * 16, ks, lane);
+  }
+  // The fragments of k step ks+1 are read from LDS while the MFMAs of step ks run.
   __device__ __forceinline__ static void step(const bf16_t* As, const bf16_t* Bs, f32x4_v (&acc)[G::FM][G::FN],
                                               int lane, int wm, int wn) {
+    bf16x8_v a[2][G::FM], b[2][G::FN];
+    fetch(As, Bs, a[0], b[0], 0, lane, wm, wn);
 #pragma unroll
-    for (int ks = 0; ks < G::BK; ks += 32) {
-      bf16x8_v a[G::FM], b[G::FN];
-#pragma unroll
-      for (int fm = 0; fm < G::FM; ++fm) a[fm] = frag<bf16_t, BM, AMN>(As, wm * G::WM + fm * 16, ks, lane);
-#pragma unroll
-      for (int fn = 0; fn < G::FN; ++fn) b[fn] = frag<bf16_t, BN, BMN>(Bs, wn * G::WN + fn * 16, ks, lane);
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) fetch(As, Bs, a[(s + 1) & 1], b[(s + 1) & 1], (s + 1) * 32, lane, wm, wn);
 #pragma unroll
       for (int fm = 0; fm < G::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < G::FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s & 1][fm], b[s & 1][fn], acc[fm][fn], 0, 0, 0);
     }
   }
 };
@@ -470,7 +478,7 @@ enum BLayout { B_NK = 0, B_KN = 1 };  // ROW-mode weight: [N][K] (k-contiguous) 
 constexpr int MAX_E = 1024;
 
 template <typename T, int BM, int BN, bool WGT, int BL, bool PAIRED, class Epi, int PF = 1>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 grouped_gemm_kernel(GemmShape s, Operand A, Operand B, typename Epi::Params ep) {
   constexpr bool AMN = WGT;
   constexpr bool BMN = WGT || BL == B_KN;

@@ -22,8 +22,10 @@ bf16 tensors are returned as ``uint16`` bit patterns (numpy has no bf16).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -112,14 +114,26 @@ def draw_w2_expert(w: Workload, e: int) -> np.ndarray:
     return _draw(ss, (w.n, w.d), W_STD, w.dtype)
 
 
+def _draw_experts(kids, shape, dtype) -> np.ndarray:
+    """One array per expert child stream, drawn in parallel threads (numpy
+    releases the GIL while filling); the values do not depend on threading."""
+    out = np.empty((len(kids),) + shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def one(e):
+        out[e] = _draw(kids[e], shape, W_STD, dtype)
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, range(len(kids))))
+    return out
+
+
 def draw_w1(w: Workload) -> np.ndarray:
-    kids = _children(w.seed)[2].spawn(w.E)
-    return np.stack([_draw(kids[e], (w.d, 2 * w.n), W_STD, w.dtype) for e in range(w.E)])
+    return _draw_experts(_children(w.seed)[2].spawn(w.E), (w.d, 2 * w.n), w.dtype)
 
 
 def draw_w2(w: Workload) -> np.ndarray:
-    kids = _children(w.seed)[3].spawn(w.E)
-    return np.stack([_draw(kids[e], (w.n, w.d), W_STD, w.dtype) for e in range(w.E)])
+    return _draw_experts(_children(w.seed)[3].spawn(w.E), (w.n, w.d), w.dtype)
 
 
 def draw_do(w: Workload) -> np.ndarray:

@@ -1,0 +1,218 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (one route + forward + backward through the C ABI).
+
+The oracle cannot run whole 32k-token layers in seconds, so outputs are
+checked on samples it computes exactly:
+  * token-subset check (all workloads but the production-shaped one): the
+    oracle runs on U = (sampled tokens) + (every token of two sampled experts)
+    with the full routing restricted to U.  Tokens are independent, so O and
+    dX of the sampled tokens, H of their rows, and dW1 / dW2 / dW_r columns /
+    db of the sampled experts are exact.
+  * expert-subset check (production-shaped layer, whose fp64 weights would
+    not fit in host memory): the oracle runs the two sampled experts over all
+    their rows: per-row H, A, Y, dH, dXt, dS and the experts' dW1 / dW2.
+Routing is compared in full.  Scores are computed on both sides in different
+summation orders, so a token whose K-th and (K+1)-th scores are closer than
+the measured score error may legitimately flip; such flips are checked to be
+near-ties, and flipped tokens / affected experts are left out of the samples.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fine_grained_mixture_top_amd import binding as B
+from fine_grained_mixture_top_amd import inputs as I
+from oracle import moe_oracle as O
+
+from gpu_util import dev, host64, host_int, relF, tol
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def inputs_of(name):
+    if name not in _CACHE:
+        _CACHE.clear()
+        _CACHE[name] = I.draw_all(I.WORKLOADS[name])
+    return _CACHE[name]
+
+
+def run_layer(w, a, round_mode, round_seed):
+    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=round_mode, round_seed=round_seed)
+    L = B.Layer(desc)
+    X, WR, W1, W2, DO = (dev(a[k], w.dtype) for k in ("x", "w_r", "w1", "w2", "d_o"))
+    bias = None if a["bias"] is None else torch.from_numpy(a["bias"]).cuda()
+    L.route(X, WR, bias)
+    L.forward(X, W1, W2)
+    L.backward(X, WR, W1, W2, DO)
+    torch.cuda.synchronize()
+    del W1, W2
+    return L
+
+
+def gpu_membership(L, w):
+    P = int(L.routing.offsets[-1].item())
+    tok = host_int(L.routing.row_token[:P])
+    exp = host_int(L.routing.row_expert[:P])
+    m = np.zeros((w.T, w.E), dtype=bool)
+    m[tok, exp] = True
+    return m, P
+
+
+def check_routing(L, w, rt, x64, wr64, bias):
+    """Full routing comparison; returns (bad tokens, bad experts)."""
+    z_gpu = host64(L.routing.logits).reshape(w.T, w.E)
+    z64 = rt["logits64"]
+    err = np.abs(z_gpu - z64)
+    assert np.linalg.norm(z_gpu - z64) / np.linalg.norm(z64) < 1e-5
+    g_idx = host_int(L.routing.topk_idx).reshape(w.T, w.K)
+    o_idx = rt["topk_idx"]
+    flip = np.nonzero(np.any(np.sort(g_idx, axis=1) != np.sort(o_idx, axis=1), axis=1))[0]
+    z32 = rt["scores"].astype(np.float64)
+    for t in flip:  # every flip must be a near-tie within the measured score error
+        s = np.sort(z32[t])[::-1]
+        gap = s[w.K - 1] - s[w.K]
+        assert gap <= 2.0 * err[t].max() + 1e-7, (t, gap, err[t].max())
+    assert len(flip) <= max(3, w.T // 10000), f"{len(flip)} routing flips"
+    g_mem, P = gpu_membership(L, w)
+    bad_e = np.nonzero(np.any(g_mem != rt["member"], axis=0))[0]
+    bad_t = np.nonzero(np.any(g_mem != rt["member"], axis=1))[0]
+    if len(flip) == 0:
+        # identical decisions: every integer output must be identical
+        r = L.routing
+        assert np.array_equal(g_idx, o_idx)
+        assert np.array_equal(host_int(r.counts), rt["counts"])
+        assert np.array_equal(host_int(r.counts_raw), rt["counts_raw"])
+        assert np.array_equal(host_int(r.offsets), rt["offsets"])
+        assert np.array_equal(host_int(r.tile_offsets), rt["tile_offsets"])
+        assert np.array_equal(host_int(r.row_token[:P]), rt["row_token"])
+        assert np.array_equal(host_int(r.tok_ptr), rt["tok_ptr"])
+        assert np.array_equal(host_int(r.tok_row[:P]), rt["tok_row"])
+        assert len(bad_e) == 0 and len(bad_t) == 0
+    return set(bad_t.tolist()) | set(flip.tolist()), set(bad_e.tolist())
+
+
+def sub_routing(rt, tokens, experts=None):
+    """The oracle's full routing restricted to a token subset (and optionally
+    to a subset of experts, re-indexed 0..len-1)."""
+    member = rt["member"][tokens]
+    gate = rt["gate"][tokens]
+    if experts is not None:
+        member = member[:, experts]
+        gate = gate[:, experts]
+    seg = O.segments(member, 128)
+    seg.update(member=member, gate=gate, row_gate=gate[seg["row_token"], seg["row_expert"]])
+    return seg
+
+
+def gpu_rows_of(L, w, tok, exp):
+    """GPU row index of each (token, expert) pair."""
+    P = int(L.routing.offsets[-1].item())
+    rt = host_int(L.routing.row_token[:P])
+    re = host_int(L.routing.row_expert[:P])
+    key = {(int(a), int(b)): i for i, (a, b) in enumerate(zip(rt, re))}
+    return np.array([key[(int(t), int(e))] for t, e in zip(tok, exp)], dtype=np.int64)
+
+
+def rows_host(t: torch.Tensor, rows, width):
+    idx = torch.from_numpy(rows).to(t.device)
+    return host64(t.view(-1, width).index_select(0, idx))
+
+
+def ws_rows(L, item, rows, width, dtype):
+    cap = L.routing.cap
+    return rows_host(L.ws_view(item, cap * width, dtype), rows, width)
+
+
+FULL = [("fg7b_bf16", 0), ("sweep_e32", 0), ("sweep_e64", 0), ("sweep_e128", 0), ("sweep_e256", 0),
+        ("zipf_e256", 0), ("zipf_e256", 1), ("zipf_e256", 2)]
+
+
+@pytest.mark.parametrize("name,mode", FULL, ids=[f"{n}-round{m}" for n, m in FULL])
+def test_full_size_token_sample(name, mode):
+    w = I.WORKLOADS[name]
+    a = inputs_of(name)
+    L = run_layer(w, a, mode, 0)
+    x64, wr64 = O.to_f64(a["x"], w.dtype), O.to_f64(a["w_r"], w.dtype)
+    rt = O.route(x64, wr64, a["bias"], w.K, 128, mode, 0)
+    bad_t, bad_e = check_routing(L, w, rt, x64, wr64, a["bias"])
+    if mode:
+        cnt = host_int(L.routing.counts)
+        assert np.all(cnt % 128 == 0)
+        assert np.all(np.abs(cnt - host_int(L.routing.counts_raw)) < 128)
+
+    rng = np.random.default_rng(1234)
+    counts = rt["counts"]
+    ok_e = [e for e in range(w.E) if e not in bad_e and counts[e] > 0]
+    heavy = max(ok_e, key=lambda e: counts[e])
+    other = int(rng.choice([e for e in ok_e if e != heavy]))
+    S_E = [heavy, other]
+    ok_t = np.array([t for t in range(w.T) if t not in bad_t])
+    S_T = np.sort(rng.choice(ok_t, size=128, replace=False))
+    U = np.unique(np.concatenate([S_T] + [np.nonzero(rt["member"][:, e])[0] for e in S_E]))
+    rtU = sub_routing(rt, U)
+    w1_64, w2_64, dO64 = O.to_f64(a["w1"], w.dtype), O.to_f64(a["w2"], w.dtype), O.to_f64(a["d_o"], w.dtype)
+    f = O.forward(x64[U], w1_64, w2_64, rtU)
+    b = O.backward(x64[U], wr64, w1_64, w2_64, rtU, f["H"], dO64[U])
+    del w1_64, w2_64
+    pos = np.searchsorted(U, S_T)
+    errs = {}
+    errs["O"] = relF(rows_host(L.o, S_T, w.d), f["O"][pos])
+    errs["dX"] = relF(rows_host(L.dx, S_T, w.d), b["dX"][pos])
+    e_t = torch.tensor(S_E, device="cuda")
+    errs["dW1"] = relF(host64(L.dw1.index_select(0, e_t)), b["dW1"][S_E])
+    errs["dW2"] = relF(host64(L.dw2.index_select(0, e_t)), b["dW2"][S_E])
+    errs["dWr"] = relF(host64(L.dw_r)[:, S_E], b["dWr"][:, S_E])
+    # db sums per-row dz values that largely cancel (each token's dz sums to
+    # zero), so its error is measured against the size of its summands
+    dz_abs = np.abs(b["dz"]).sum(axis=0)[S_E]
+    errs["db"] = float(np.linalg.norm(host64(L.db)[S_E] - b["db"][S_E]) / np.linalg.norm(dz_abs))
+    # per-row values of the sampled tokens' rows, matched by (token, expert)
+    sel = np.isin(rtU["row_token"], pos)
+    o_rows = np.nonzero(sel)[0]
+    g_rows = gpu_rows_of(L, w, U[rtU["row_token"][o_rows]], rtU["row_expert"][o_rows])
+    errs["H"] = relF(rows_host(L.h_cache, g_rows, 2 * w.n), f["H"][o_rows])
+    errs["dS"] = relF(host64(L.ds)[g_rows], b["dS"][o_rows])
+    print(name, mode, {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if not v <= tol(w.dtype)}
+    assert not bad, (bad, errs)
+
+
+def test_full_size_production_expert_sample():
+    name = "prod_e256"
+    w = I.WORKLOADS[name]
+    a = inputs_of(name)
+    L = run_layer(w, a, 0, 0)
+    x64, wr64 = O.to_f64(a["x"], w.dtype), O.to_f64(a["w_r"], w.dtype)
+    rt = O.route(x64, wr64, None, w.K, 128, 0, 0)
+    bad_t, bad_e = check_routing(L, w, rt, x64, wr64, None)
+    counts = rt["counts"]
+    rng = np.random.default_rng(99)
+    ok_e = [e for e in range(w.E) if e not in bad_e and counts[e] > 0]
+    S_E = [max(ok_e, key=lambda e: counts[e]), int(rng.choice(ok_e))]
+    if S_E[0] == S_E[1]:
+        S_E[1] = min(ok_e, key=lambda e: counts[e])
+    toks = np.arange(w.T)
+    rtE = sub_routing(rt, toks, S_E)
+    w1E = O.to_f64(a["w1"][S_E], w.dtype)
+    w2E = O.to_f64(a["w2"][S_E], w.dtype)
+    dO64 = O.to_f64(a["d_o"], w.dtype)
+    f = O.forward(x64, w1E, w2E, rtE)
+    # router columns of the sampled experts only (dz / dX here are partial and unused)
+    b = O.backward(x64, wr64[:, S_E], w1E, w2E, rtE, f["H"], dO64)
+    g_rows = gpu_rows_of(L, w, rtE["row_token"], np.asarray(S_E)[rtE["row_expert"]])
+    dt = torch.bfloat16
+    errs = dict(
+        H=relF(rows_host(L.h_cache, g_rows, 2 * w.n), f["H"]),
+        A=relF(ws_rows(L, B.MOE_ITEM_A, g_rows, w.n, dt), f["A"]),
+        Y=relF(ws_rows(L, B.MOE_ITEM_Y, g_rows, w.d, dt), f["Y"]),
+        dH=relF(ws_rows(L, B.MOE_ITEM_DH, g_rows, 2 * w.n, dt), b["dH"]),
+        dXt=relF(ws_rows(L, B.MOE_ITEM_DXT, g_rows, w.d, dt), b["dXt"]),
+        dS=relF(host64(L.ds)[g_rows], b["dS"]),
+        dW1=relF(host64(L.dw1.index_select(0, torch.tensor(S_E, device="cuda"))), b["dW1"]),
+        dW2=relF(host64(L.dw2.index_select(0, torch.tensor(S_E, device="cuda"))), b["dW2"]),
+    )
+    print(name, {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if not v <= tol(w.dtype)}
+    assert not bad, (bad, errs)
