@@ -34,7 +34,24 @@ def parse():
     ap.add_argument("--round-mode", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of the oracle's CPU baseline sample (0 = skip)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many bytes "
+                         "(calibration dispatch for HBM counter passes)")
     return ap.parse_args()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter passes, or
+    None when they are missing or were taken on different kernel sources."""
+    from fine_grained_mixture_top_amd import hbm_traffic
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != hbm_traffic.source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else round(k["bytes"])
 
 
 def kernel_work(name, w, P, es):
@@ -128,6 +145,12 @@ def main():
     torch.cuda.synchronize()
     B.Profiler.detach(L.desc)
     ms_step = t0.elapsed_time(t1) / args.steps
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     P = int(L.routing.offsets[-1].item())
     es = 2 if w.dtype == "bf16" else 4
@@ -172,7 +195,7 @@ def main():
         "mfma_peak_frac": round(tflops / peak_mfma, 4),
         "tokens_per_s": round(w.T / (ms_step * 1e-3), 1),
         "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
-                     "unit": dk["unit"], "frac": dk["frac"], "traffic": None},
+                     "unit": dk["unit"], "frac": dk["frac"], "traffic": measured_traffic(w.name, dom)},
         "kernels": {k: {kk: v for kk, v in d.items() if kk != "work"} for k, d in kernels.items()},
     }
     if args.cpu_tokens > 0:

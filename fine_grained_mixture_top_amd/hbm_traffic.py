@@ -1,0 +1,110 @@
+"""HBM traffic per kernel from rocprofv3 counter passes.
+
+Two counter passes over the same benchmark command, one with FETCH_SIZE and
+one with WRITE_SIZE (KiB per dispatch), each also running a plain device copy
+of a known size (bench.py --copy-bytes).  The copy calibrates the counters:
+factor = bytes the copy must move / bytes the counter reports for it.  Each
+MoE kernel's traffic is its counter value times that factor, averaged over its
+dispatches.
+
+    python -m fine_grained_mixture_top_amd.hbm_traffic FETCH.csv WRITE.csv COPY_BYTES OUT.json
+
+The result records a hash of the kernel sources; bench.py reports the traffic
+only while the sources still hash the same.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".h", ".hip")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def classify(name: str, wgt_seen: dict) -> str:
+    """Bench kernel name of one dispatch (None for kernels that are not tracked)."""
+    if "grouped_gemm_kernel" in name:
+        m = re.search(r"grouped_gemm_kernel<([^,]+), (\d+), (\d+), (true|false), (\d), (true|false), moe::(\w+)<([^>]*)>", name)
+        if not m:
+            return None
+        wgt, bl, epi, args = m.group(4) == "true", m.group(5), m.group(7), m.group(8)
+        if epi == "EpiSwiGLU":
+            return "up"
+        if epi == "EpiDH":
+            return "dh"
+        to_float = args.split(",")[1].strip() == "float"
+        if to_float:
+            return "dwr" if wgt else "router_logits"
+        if wgt:  # dw1 and dw2 share an instantiation: first per step is dw1
+            k = wgt_seen["n"] % 2
+            wgt_seen["n"] += 1
+            return "dw1" if k == 0 else "dw2"
+        return "down" if bl == "1" else "dxt"
+    if "k_aggregate_o" in name:
+        return "agg_o"
+    if "k_aggregate_dx" in name:
+        return "agg_dx"
+    if "copyBuffer" in name or "elementwise_kernel" in name and "copy" in name.lower():
+        return "copy"
+    return None
+
+
+def per_kernel(path: str, counter: str):
+    """{kernel: [KiB per dispatch]} from one counter-collection CSV."""
+    rows = list(csv.DictReader(open(path)))
+    by = collections.defaultdict(float)
+    names = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        did = int(r["Dispatch_Id"])
+        by[did] += float(r["Counter_Value"])  # summed over the reporting instances
+        names[did] = r["Kernel_Name"]
+    out = collections.defaultdict(list)
+    seen = {"n": 0}
+    for did in sorted(by):
+        k = classify(names[did], seen)
+        if k:
+            out[k].append(by[did])
+    return out
+
+
+def main(fetch_csv, write_csv, copy_bytes, out_json):
+    copy_bytes = float(copy_bytes)
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    if not f.get("copy") or not w.get("copy"):
+        raise SystemExit("no calibration copy dispatch found")
+    # the calibration copy is the largest copy dispatch of the run
+    f_copy = max(f["copy"]) * 1024.0
+    w_copy = max(w["copy"]) * 1024.0
+    kf, kw = copy_bytes / f_copy, copy_bytes / w_copy
+    res = {"source_hash": source_hash(), "copy_bytes": copy_bytes, "fetch_factor": kf, "write_factor": kw,
+           "kernels": {}}
+    for k in sorted(set(f) | set(w)):
+        if k == "copy":
+            continue
+        fb = sum(f.get(k, [0])) / max(1, len(f.get(k, []))) * 1024.0 * kf
+        wb = sum(w.get(k, [0])) / max(1, len(w.get(k, []))) * 1024.0 * kw
+        res["kernels"][k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb,
+                             "dispatches": len(f.get(k, []))}
+    with open(out_json, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main(*sys.argv[1:5])
