@@ -24,6 +24,7 @@ MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EDTYPE, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUND_OFF, MOE_ROUND_NEAREST, MOE_ROUND_STOCHASTIC = 0, 1, 2
 MOE_FLAG_SCORES_GIVEN = 1
+MOE_FLAG_GEMM_128 = 2
 MOE_WS_ROUTE, MOE_WS_FWD, MOE_WS_BWD = 0, 1, 2
 MOE_ITEM_Y, MOE_ITEM_A, MOE_ITEM_DH, MOE_ITEM_AS, MOE_ITEM_DXT, MOE_ITEM_DS, MOE_ITEM_DZ = range(7)
 KERNEL_NAMES = ["router_logits", "route_select", "up", "down", "agg_o", "dh", "router_grad", "dwr",

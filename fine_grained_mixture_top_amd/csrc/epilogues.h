@@ -4,7 +4,7 @@
 // and forms the score gradient).
 //
 // The main loop parks the fp32 tile in LDS ([BM][BN + 4], see stage_acc);
-// every epilogue then walks it in 8-column chunks of whole rows, 256 threads
+// every epilogue then walks it in 8-column chunks of whole rows, NTH threads
 // at a time, so its global reads and writes are coalesced 16-byte accesses
 // and the element-wise math keeps few values live.
 #pragma once
@@ -16,7 +16,7 @@ namespace moe {
 // C[row, n0 + col] = acc (+ bias[col]), converted to TO.
 // ROW mode: row = routed row; WGT mode: row = slice*M + m (rows of all
 // slices' [M][N] blocks are contiguous).
-template <typename T, typename TO, int BM, int BN>
+template <typename T, typename TO, int BM, int BN, int NTH = 256>
 struct EpiStore {
   struct Params {
     TO* C;
@@ -29,7 +29,7 @@ struct EpiStore {
                                              const float* Cs, char*) {
     constexpr int LDC = BN + 4, CPR = BN / 8;
     const int cols = min(BN, s.n_valid - c.n0);
-    for (int v = c.tid; v < BM * CPR; v += 256) {
+    for (int v = c.tid; v < BM * CPR; v += NTH) {
       const int r = v / CPR, ch = v % CPR;
       if (r < c.m_valid && ch * 8 < cols) {
         float x[8];
@@ -49,7 +49,7 @@ struct EpiStore {
 // rounded to the storage type first and A = silu(G)*U is formed from the
 // rounded values, so the backward's recomputation of A from the cached H
 // reproduces it exactly.
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, int NTH = 256>
 struct EpiSwiGLU {
   struct Params {
     T* H;     // [rows, 2n]
@@ -63,7 +63,7 @@ struct EpiSwiGLU {
     constexpr int LDC = BN + 4, CPR = BN / 16;
     const int j0 = c.nt * (BN / 2);
     const long long ldh = 2LL * p.n;
-    for (int v = c.tid; v < BM * CPR; v += 256) {
+    for (int v = c.tid; v < BM * CPR; v += NTH) {
       const int r = v / CPR, jj = (v % CPR) * 8;
       if (r < c.m_valid) {
         float g[8], u[8], a[8];
@@ -91,7 +91,7 @@ struct EpiSwiGLU {
 //   A_s = gate * A                        (operand of the dW2 GEMM)
 // The BN/8 chunks of a row sit on consecutive lanes, which sum the row's
 // partial with shuffles.
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, int NTH = 256>
 struct EpiDH {
   struct Params {
     const T* H;           // [rows, 2n]
@@ -109,7 +109,7 @@ struct EpiDH {
                                              const float* Cs, char*) {
     constexpr int LDC = BN + 4, CPR = BN / 8;
     const long long ldh = 2LL * p.n;
-    for (int v = c.tid; v < BM * CPR; v += 256) {
+    for (int v = c.tid; v < BM * CPR; v += NTH) {
       const int r = v / CPR, ch = v % CPR;
       const bool valid = r < c.m_valid;
       const long long grow = c.out_row0 + (valid ? r : c.m_valid - 1);

@@ -5,6 +5,7 @@
 #include <type_traits>
 
 #include "epilogues.h"
+#include "grouped_gemm4.h"
 #include "launch.h"
 
 namespace moe {
@@ -40,6 +41,25 @@ hipError_t run_gemm(const GemmShape& s, const Operand& A, const Operand& B,
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, s, A, B, ep);
   return hipGetLastError();
 }
+
+// 256 x 256 tile kernel: one 512-thread workgroup per CU (LDS-bound).
+template <bool WGT, bool BMN, bool PAIRED, class Epi>
+hipError_t run_gemm4(const GemmShape& s, const Operand& A, const Operand& B, size_t a_bytes, size_t b_bytes,
+                     const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
+  auto kern = g4::grouped_gemm4_kernel<WGT, BMN, PAIRED, Epi>;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, g4::SMEM);
+  if (attr != hipSuccess) return attr;
+  long long grid = std::min<long long>(max_tiles, num_cus());
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(g4::NTH), g4::SMEM, st, s, A, B, (uint32_t)a_bytes,
+                     (uint32_t)b_bytes, ep);
+  return hipGetLastError();
+}
+
+// Buffer-addressed operands use 32-bit byte offsets with the top half of the
+// range kept as the out-of-bounds marker.
+bool fits_g4(size_t bytes) { return bytes < (size_t)g4::OOB; }
 
 long long row_tiles_bound(size_t cap, int E, int BM) { return (long long)(cap + BM - 1) / BM + E; }
 
@@ -77,9 +97,10 @@ hipError_t router_logits(const void* x, const void* w_r, const float* bias, floa
 }
 
 template <typename T, int BN>
-hipError_t up_swiglu_t(const void* x, const void* w1, const int32_t* row_token, const int32_t* offsets, int E,
-                       int d, int n, size_t cap, void* H, void* A, hipStream_t st) {
+hipError_t up_swiglu_t(const GemmDims& g, const void* x, const void* w1, const int32_t* row_token,
+                       const int32_t* offsets, void* H, void* A, hipStream_t st) {
   constexpr int BM = ROWS<T>;
+  const int n = g.n, d = g.d, E = g.E;
   using Epi = EpiSwiGLU<T, BM, BN>;
   GemmShape s{offsets, E, 0, 2 * n, d, 2 * n, 1};
   Operand a{x, row_token, 0, d};
@@ -87,88 +108,154 @@ hipError_t up_swiglu_t(const void* x, const void* w1, const int32_t* row_token, 
   typename Epi::Params ep{reinterpret_cast<T*>(H), reinterpret_cast<T*>(A), n};
   // two k steps of loads in flight: the gathered token rows come from L2 / MALL
   return run_gemm<T, BM, BN, false, B_KN, true, Epi, 2>(s, a, b, ep,
-                                                         row_tiles_bound(cap, E, BM) * (2 * n / BN), st);
+                                                         row_tiles_bound(g.cap, E, BM) * (2 * n / BN), st);
+}
+hipError_t up_swiglu_g4(const GemmDims& g, const void* x, const void* w1, const int32_t* row_token,
+                        const int32_t* offsets, void* H, void* A, hipStream_t st) {
+  const int n = g.n, d = g.d, E = g.E;
+  using Epi = EpiSwiGLU<bf16_t, g4::HALF, g4::BN, g4::NTH>;
+  GemmShape s{offsets, E, 0, 2 * n, d, 2 * n, 1};
+  Operand a{x, row_token, 0, d};
+  Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
+  typename Epi::Params ep{reinterpret_cast<bf16_t*>(H), reinterpret_cast<bf16_t*>(A), n};
+  return run_gemm4<false, true, true, Epi>(s, a, b, (size_t)g.T * d * 2, (size_t)d * 2 * n * 2, ep,
+                                           row_tiles_bound(g.cap, E, g4::BM) * (2 * n / g4::BN), st);
+}
+bool up_g4(const GemmDims& g) {
+  return g.dtype == DT_BF16 && !g.small_tiles && (2 * g.n) % 256 == 0 && g.d % 32 == 0 &&
+         fits_g4((size_t)g.T * g.d * 2) && fits_g4((size_t)g.d * 2 * g.n * 2);
 }
 template <typename T>
-hipError_t up_swiglu(const void* x, const void* w1, const int32_t* row_token, const int32_t* offsets,
-                     const int32_t*, int E, int d, int n, size_t cap, void* H, void* A, hipStream_t st) {
+hipError_t up_swiglu(const GemmDims& g, const void* x, const void* w1, const int32_t* row_token,
+                     const int32_t* offsets, void* H, void* A, hipStream_t st) {
   if constexpr (std::is_same<T, bf16_t>::value) {
-    return up_swiglu_t<T, 128>(x, w1, row_token, offsets, E, d, n, cap, H, A, st);
+    if (up_g4(g)) return up_swiglu_g4(g, x, w1, row_token, offsets, H, A, st);
+    return up_swiglu_t<T, 128>(g, x, w1, row_token, offsets, H, A, st);
   } else {
-    return up_swiglu_t<T, 64>(x, w1, row_token, offsets, E, d, n, cap, H, A, st);
+    return up_swiglu_t<T, 64>(g, x, w1, row_token, offsets, H, A, st);
   }
 }
 
 template <typename T, int BN>
-hipError_t down_t(const void* A, const void* w2, const int32_t* offsets, int E, int d, int n, size_t cap,
-                  void* Y, hipStream_t st) {
+hipError_t down_t(const GemmDims& g, const void* A, const void* w2, const int32_t* offsets, void* Y,
+                  hipStream_t st) {
   constexpr int BM = ROWS<T>;
+  const int n = g.n, d = g.d, E = g.E;
   using Epi = EpiStore<T, T, BM, BN>;
   GemmShape s{offsets, E, 0, d, n, d, 1};
   Operand a{A, nullptr, 0, n};
   Operand b{w2, nullptr, (long long)n * d, d};
   typename Epi::Params ep{reinterpret_cast<T*>(Y), d, nullptr};
-  return run_gemm<T, BM, BN, false, B_KN, false, Epi>(s, a, b, ep, row_tiles_bound(cap, E, BM) * (d / BN), st);
+  return run_gemm<T, BM, BN, false, B_KN, false, Epi>(s, a, b, ep, row_tiles_bound(g.cap, E, BM) * (d / BN), st);
+}
+bool down_g4(const GemmDims& g) {
+  return g.dtype == DT_BF16 && !g.small_tiles && g.d % 256 == 0 && g.n % 32 == 0 &&
+         fits_g4(g.cap * g.n * 2) && fits_g4((size_t)g.n * g.d * 2);
 }
 template <typename T>
-hipError_t down(const void* A, const void* w2, const int32_t* offsets, const int32_t*, int E, int d, int n,
-                size_t cap, void* Y, hipStream_t st) {
-  if (d % Cfg<T>::BIG == 0) return down_t<T, Cfg<T>::BIG>(A, w2, offsets, E, d, n, cap, Y, st);
-  return down_t<T, Cfg<T>::SMALL>(A, w2, offsets, E, d, n, cap, Y, st);
+hipError_t down(const GemmDims& g, const void* A, const void* w2, const int32_t* offsets, void* Y, hipStream_t st) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (down_g4(g)) {
+      const int n = g.n, d = g.d, E = g.E;
+      using Epi = EpiStore<bf16_t, bf16_t, g4::HALF, g4::BN, g4::NTH>;
+      GemmShape s{offsets, E, 0, d, n, d, 1};
+      Operand a{A, nullptr, 0, n};
+      Operand b{w2, nullptr, (long long)n * d, d};
+      typename Epi::Params ep{reinterpret_cast<bf16_t*>(Y), d, nullptr};
+      return run_gemm4<false, true, false, Epi>(s, a, b, g.cap * n * 2, (size_t)n * d * 2, ep,
+                                                row_tiles_bound(g.cap, E, g4::BM) * (d / g4::BN), st);
+    }
+  }
+  if (g.d % Cfg<T>::BIG == 0) return down_t<T, Cfg<T>::BIG>(g, A, w2, offsets, Y, st);
+  return down_t<T, Cfg<T>::SMALL>(g, A, w2, offsets, Y, st);
 }
 
 // dH: the column tile decides the number of score-gradient partials per row
-template <typename T> int dh_bn(int n);
-template <> int dh_bn<bf16_t>(int n) { return n % 128 == 0 ? 128 : 64; }
-template <> int dh_bn<float>(int) { return 32; }
+bool dh_g4(const GemmDims& g) {
+  return g.dtype == DT_BF16 && !g.small_tiles && g.n % 256 == 0 && g.d % 32 == 0 &&
+         fits_g4((size_t)g.T * g.d * 2) && fits_g4((size_t)g.n * g.d * 2);
+}
+int dh_bn(const GemmDims& g) {
+  if (g.dtype != DT_BF16) return 32;
+  if (dh_g4(g)) return g4::BN;
+  return g.n % 128 == 0 ? 128 : 64;
+}
 
 template <typename T, int BN>
-hipError_t dh_t(const void* d_o, const void* w2, const void* H, const int32_t* row_token, const float* row_gate,
-                const int32_t* offsets, int E, int d, int n, size_t cap, void* dH, void* As, float* dS_part,
-                hipStream_t st) {
+hipError_t dh_t(const GemmDims& g, const void* d_o, const void* w2, const void* H, const int32_t* row_token,
+                const float* row_gate, const int32_t* offsets, void* dH, void* As, float* dS_part, hipStream_t st) {
   constexpr int BM = ROWS<T>;
+  const int n = g.n, d = g.d, E = g.E;
   using Epi = EpiDH<T, BM, BN>;
   GemmShape s{offsets, E, 0, n, d, n, 1};
   Operand a{d_o, row_token, 0, d};
   Operand b{w2, nullptr, (long long)n * d, d};  // W2[e] is [n][d]: row j holds k = 0..d-1
   typename Epi::Params ep{reinterpret_cast<const T*>(H), row_gate, reinterpret_cast<T*>(dH),
                           reinterpret_cast<T*>(As), dS_part, n, n / BN};
-  return run_gemm<T, BM, BN, false, B_NK, false, Epi>(s, a, b, ep, row_tiles_bound(cap, E, BM) * (n / BN), st);
+  return run_gemm<T, BM, BN, false, B_NK, false, Epi>(s, a, b, ep, row_tiles_bound(g.cap, E, BM) * (n / BN), st);
 }
 template <typename T>
-hipError_t dh(const void* d_o, const void* w2, const void* H, const int32_t* row_token, const float* row_gate,
-              const int32_t* offsets, const int32_t*, int E, int d, int n, size_t cap, void* dH, void* As,
-              float* dS_part, hipStream_t st) {
+hipError_t dh(const GemmDims& g, const void* d_o, const void* w2, const void* H, const int32_t* row_token,
+              const float* row_gate, const int32_t* offsets, void* dH, void* As, float* dS_part, hipStream_t st) {
   if constexpr (std::is_same<T, bf16_t>::value) {
-    if (dh_bn<T>(n) == 128)
-      return dh_t<T, 128>(d_o, w2, H, row_token, row_gate, offsets, E, d, n, cap, dH, As, dS_part, st);
-    return dh_t<T, 64>(d_o, w2, H, row_token, row_gate, offsets, E, d, n, cap, dH, As, dS_part, st);
+    const int bn = dh_bn(g);
+    if (bn == g4::BN) {
+      const int n = g.n, d = g.d, E = g.E;
+      using Epi = EpiDH<bf16_t, g4::HALF, g4::BN, g4::NTH>;
+      GemmShape s{offsets, E, 0, n, d, n, 1};
+      Operand a{d_o, row_token, 0, d};
+      Operand b{w2, nullptr, (long long)n * d, d};
+      typename Epi::Params ep{reinterpret_cast<const bf16_t*>(H), row_gate, reinterpret_cast<bf16_t*>(dH),
+                              reinterpret_cast<bf16_t*>(As), dS_part, n, n / g4::BN};
+      return run_gemm4<false, false, false, Epi>(s, a, b, (size_t)g.T * d * 2, (size_t)n * d * 2, ep,
+                                                 row_tiles_bound(g.cap, E, g4::BM) * (n / g4::BN), st);
+    }
+    if (bn == 128) return dh_t<T, 128>(g, d_o, w2, H, row_token, row_gate, offsets, dH, As, dS_part, st);
+    return dh_t<T, 64>(g, d_o, w2, H, row_token, row_gate, offsets, dH, As, dS_part, st);
   } else {
-    return dh_t<T, 32>(d_o, w2, H, row_token, row_gate, offsets, E, d, n, cap, dH, As, dS_part, st);
+    return dh_t<T, 32>(g, d_o, w2, H, row_token, row_gate, offsets, dH, As, dS_part, st);
   }
 }
 
 template <typename T, int BN>
-hipError_t dxt_t(const void* dH, const void* w1, const int32_t* offsets, int E, int d, int n, size_t cap,
-                 void* dXt, hipStream_t st) {
+hipError_t dxt_t(const GemmDims& g, const void* dH, const void* w1, const int32_t* offsets, void* dXt,
+                 hipStream_t st) {
   constexpr int BM = ROWS<T>;
+  const int n = g.n, d = g.d, E = g.E;
   using Epi = EpiStore<T, T, BM, BN>;
   GemmShape s{offsets, E, 0, d, 2 * n, d, 1};
   Operand a{dH, nullptr, 0, 2 * n};
   Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};  // W1[e] is [d][2n]: row i holds k = 0..2n-1
   typename Epi::Params ep{reinterpret_cast<T*>(dXt), d, nullptr};
-  return run_gemm<T, BM, BN, false, B_NK, false, Epi>(s, a, b, ep, row_tiles_bound(cap, E, BM) * (d / BN), st);
+  return run_gemm<T, BM, BN, false, B_NK, false, Epi>(s, a, b, ep, row_tiles_bound(g.cap, E, BM) * (d / BN), st);
+}
+bool dxt_g4(const GemmDims& g) {
+  return g.dtype == DT_BF16 && !g.small_tiles && g.d % 256 == 0 && (2 * g.n) % 32 == 0 &&
+         fits_g4(g.cap * 2 * g.n * 2) && fits_g4((size_t)g.d * 2 * g.n * 2);
 }
 template <typename T>
-hipError_t dxt(const void* dH, const void* w1, const int32_t* offsets, const int32_t*, int E, int d, int n,
-               size_t cap, void* dXt, hipStream_t st) {
-  if (d % Cfg<T>::BIG == 0) return dxt_t<T, Cfg<T>::BIG>(dH, w1, offsets, E, d, n, cap, dXt, st);
-  return dxt_t<T, Cfg<T>::SMALL>(dH, w1, offsets, E, d, n, cap, dXt, st);
+hipError_t dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t* offsets, void* dXt,
+               hipStream_t st) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (dxt_g4(g)) {
+      const int n = g.n, d = g.d, E = g.E;
+      using Epi = EpiStore<bf16_t, bf16_t, g4::HALF, g4::BN, g4::NTH>;
+      GemmShape s{offsets, E, 0, d, 2 * n, d, 1};
+      Operand a{dH, nullptr, 0, 2 * n};
+      Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
+      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dXt), d, nullptr};
+      return run_gemm4<false, false, false, Epi>(s, a, b, g.cap * 2 * n * 2, (size_t)d * 2 * n * 2, ep,
+                                                 row_tiles_bound(g.cap, E, g4::BM) * (d / g4::BN), st);
+    }
+  }
+  if (g.d % Cfg<T>::BIG == 0) return dxt_t<T, Cfg<T>::BIG>(g, dH, w1, offsets, dXt, st);
+  return dxt_t<T, Cfg<T>::SMALL>(g, dH, w1, offsets, dXt, st);
 }
 
 template <typename T, int BMW, int BN>
-hipError_t dw1_t(const void* x, const void* dH, const int32_t* row_token, const int32_t* offsets, int E, int d,
-                 int n, void* dW1, hipStream_t st) {
+hipError_t dw1_t(const GemmDims& g, const void* x, const void* dH, const int32_t* row_token,
+                 const int32_t* offsets, void* dW1, hipStream_t st) {
+  const int n = g.n, d = g.d, E = g.E;
   using Epi = EpiStore<T, T, BMW, BN>;
   GemmShape s{offsets, E, d, 2 * n, 0, 2 * n, 1};
   Operand a{x, row_token, 0, d};
@@ -176,19 +263,34 @@ hipError_t dw1_t(const void* x, const void* dH, const int32_t* row_token, const 
   typename Epi::Params ep{reinterpret_cast<T*>(dW1), 2 * n, nullptr};
   return run_gemm<T, BMW, BN, true, B_KN, false, Epi>(s, a, b, ep, (long long)E * (d / BMW) * (2 * n / BN), st);
 }
+bool dw1_g4(const GemmDims& g) {
+  return g.dtype == DT_BF16 && !g.small_tiles && g.d % 256 == 0 && (2 * g.n) % 256 == 0 &&
+         fits_g4((size_t)g.T * g.d * 2) && fits_g4(g.cap * 2 * g.n * 2);
+}
 template <typename T>
-hipError_t dw1(const void* x, const void* dH, const int32_t* row_token, const int32_t* offsets, int E, int d,
-               int n, void* dW1, hipStream_t st) {
+hipError_t dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* row_token, const int32_t* offsets,
+               void* dW1, hipStream_t st) {
   if constexpr (std::is_same<T, bf16_t>::value) {
-    return dw1_t<T, 128, 128>(x, dH, row_token, offsets, E, d, n, dW1, st);
+    if (dw1_g4(g)) {
+      const int n = g.n, d = g.d, E = g.E;
+      using Epi = EpiStore<bf16_t, bf16_t, g4::HALF, g4::BN, g4::NTH>;
+      GemmShape s{offsets, E, d, 2 * n, 0, 2 * n, 1};
+      Operand a{x, row_token, 0, d};
+      Operand b{dH, nullptr, 0, 2 * n};
+      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dW1), 2 * n, nullptr};
+      return run_gemm4<true, true, false, Epi>(s, a, b, (size_t)g.T * d * 2, g.cap * 2 * n * 2, ep,
+                                               (long long)E * (d / g4::BM) * (2 * n / g4::BN), st);
+    }
+    return dw1_t<T, 128, 128>(g, x, dH, row_token, offsets, dW1, st);
   } else {
-    return dw1_t<T, 128, 64>(x, dH, row_token, offsets, E, d, n, dW1, st);
+    return dw1_t<T, 128, 64>(g, x, dH, row_token, offsets, dW1, st);
   }
 }
 
 template <typename T, int BMW, int BN>
-hipError_t dw2_t(const void* As, const void* d_o, const int32_t* row_token, const int32_t* offsets, int E,
-                 int d, int n, void* dW2, hipStream_t st) {
+hipError_t dw2_t(const GemmDims& g, const void* As, const void* d_o, const int32_t* row_token,
+                 const int32_t* offsets, void* dW2, hipStream_t st) {
+  const int n = g.n, d = g.d, E = g.E;
   using Epi = EpiStore<T, T, BMW, BN>;
   GemmShape s{offsets, E, n, d, 0, d, 1};
   Operand a{As, nullptr, 0, n};
@@ -196,15 +298,29 @@ hipError_t dw2_t(const void* As, const void* d_o, const int32_t* row_token, cons
   typename Epi::Params ep{reinterpret_cast<T*>(dW2), d, nullptr};
   return run_gemm<T, BMW, BN, true, B_KN, false, Epi>(s, a, b, ep, (long long)E * (n / BMW) * (d / BN), st);
 }
+bool dw2_g4(const GemmDims& g) {
+  return g.dtype == DT_BF16 && !g.small_tiles && g.n % 256 == 0 && g.d % 256 == 0 &&
+         fits_g4(g.cap * g.n * 2) && fits_g4((size_t)g.T * g.d * 2);
+}
 template <typename T>
-hipError_t dw2(const void* As, const void* d_o, const int32_t* row_token, const int32_t* offsets, int E, int d,
-               int n, void* dW2, hipStream_t st) {
+hipError_t dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t* row_token, const int32_t* offsets,
+               void* dW2, hipStream_t st) {
   if constexpr (std::is_same<T, bf16_t>::value) {
-    if (n % 128 == 0) return dw2_t<T, 128, 128>(As, d_o, row_token, offsets, E, d, n, dW2, st);
-    return dw2_t<T, 64, 128>(As, d_o, row_token, offsets, E, d, n, dW2, st);
+    if (dw2_g4(g)) {
+      const int n = g.n, d = g.d, E = g.E;
+      using Epi = EpiStore<bf16_t, bf16_t, g4::HALF, g4::BN, g4::NTH>;
+      GemmShape s{offsets, E, n, d, 0, d, 1};
+      Operand a{As, nullptr, 0, n};
+      Operand b{d_o, row_token, 0, d};
+      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dW2), d, nullptr};
+      return run_gemm4<true, true, false, Epi>(s, a, b, g.cap * n * 2, (size_t)g.T * d * 2, ep,
+                                               (long long)E * (n / g4::BM) * (d / g4::BN), st);
+    }
+    if (g.n % 128 == 0) return dw2_t<T, 128, 128>(g, As, d_o, row_token, offsets, dW2, st);
+    return dw2_t<T, 64, 128>(g, As, d_o, row_token, offsets, dW2, st);
   } else {
-    if (n % 128 == 0) return dw2_t<T, 128, 64>(As, d_o, row_token, offsets, E, d, n, dW2, st);
-    return dw2_t<T, 64, 64>(As, d_o, row_token, offsets, E, d, n, dW2, st);
+    if (g.n % 128 == 0) return dw2_t<T, 128, 64>(g, As, d_o, row_token, offsets, dW2, st);
+    return dw2_t<T, 64, 64>(g, As, d_o, row_token, offsets, dW2, st);
   }
 }
 
@@ -248,7 +364,7 @@ hipError_t dwr(const void* x, const void* dz, int T_, int d, int E, void* dWr, f
 
 }  // namespace
 
-int dh_block(int dtype, int n) { return dtype == DT_BF16 ? dh_bn<bf16_t>(n) : dh_bn<float>(n); }
+int dh_block(const GemmDims& g) { return dh_bn(g); }
 
 int dwr_splits(int T, int d, int E) {
   const int tiles = (d / 128) * ((E + 63) / 64);
@@ -266,35 +382,33 @@ hipError_t launch_router_logits(int dtype, const void* x, const void* w_r, const
                                 float* logits, int T, int d, int E, hipStream_t st) {
   return MOE_DISPATCH(dtype, router_logits, x, w_r, bias, logits, T, d, E, st);
 }
-hipError_t launch_up_swiglu(int dtype, const void* x, const void* w1, const int32_t* row_token,
-                            const int32_t* offsets, const int32_t* tile_offsets, int E, int d, int n,
-                            size_t cap, void* H, void* A, hipStream_t st) {
-  return MOE_DISPATCH(dtype, up_swiglu, x, w1, row_token, offsets, tile_offsets, E, d, n, cap, H, A, st);
+#define MOE_GDISPATCH(g, fn, ...) \
+  ((g).dtype == DT_BF16 ? fn<bf16_t>(g, __VA_ARGS__) : fn<float>(g, __VA_ARGS__))
+
+hipError_t launch_up_swiglu(const GemmDims& g, const void* x, const void* w1, const int32_t* row_token,
+                            const int32_t* offsets, void* H, void* A, hipStream_t st) {
+  return MOE_GDISPATCH(g, up_swiglu, x, w1, row_token, offsets, H, A, st);
 }
-hipError_t launch_down(int dtype, const void* A, const void* w2, const int32_t* offsets,
-                       const int32_t* tile_offsets, int E, int d, int n, size_t cap, void* Y,
+hipError_t launch_down(const GemmDims& g, const void* A, const void* w2, const int32_t* offsets, void* Y,
                        hipStream_t st) {
-  return MOE_DISPATCH(dtype, down, A, w2, offsets, tile_offsets, E, d, n, cap, Y, st);
+  return MOE_GDISPATCH(g, down, A, w2, offsets, Y, st);
 }
-hipError_t launch_dh(int dtype, const void* d_o, const void* w2, const void* H,
-                     const int32_t* row_token, const float* row_gate, const int32_t* offsets,
-                     const int32_t* tile_offsets, int E, int d, int n, size_t cap, void* dH, void* As,
-                     float* dS_part, hipStream_t st) {
-  return MOE_DISPATCH(dtype, dh, d_o, w2, H, row_token, row_gate, offsets, tile_offsets, E, d, n, cap,
-                      dH, As, dS_part, st);
+hipError_t launch_dh(const GemmDims& g, const void* d_o, const void* w2, const void* H,
+                     const int32_t* row_token, const float* row_gate, const int32_t* offsets, void* dH,
+                     void* As, float* dS_part, hipStream_t st) {
+  return MOE_GDISPATCH(g, dh, d_o, w2, H, row_token, row_gate, offsets, dH, As, dS_part, st);
 }
-hipError_t launch_dxt(int dtype, const void* dH, const void* w1, const int32_t* offsets,
-                      const int32_t* tile_offsets, int E, int d, int n, size_t cap, void* dXt,
+hipError_t launch_dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t* offsets, void* dXt,
                       hipStream_t st) {
-  return MOE_DISPATCH(dtype, dxt, dH, w1, offsets, tile_offsets, E, d, n, cap, dXt, st);
+  return MOE_GDISPATCH(g, dxt, dH, w1, offsets, dXt, st);
 }
-hipError_t launch_dw1(int dtype, const void* x, const void* dH, const int32_t* row_token,
-                      const int32_t* offsets, int E, int d, int n, void* dW1, hipStream_t st) {
-  return MOE_DISPATCH(dtype, dw1, x, dH, row_token, offsets, E, d, n, dW1, st);
+hipError_t launch_dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* row_token,
+                      const int32_t* offsets, void* dW1, hipStream_t st) {
+  return MOE_GDISPATCH(g, dw1, x, dH, row_token, offsets, dW1, st);
 }
-hipError_t launch_dw2(int dtype, const void* As, const void* d_o, const int32_t* row_token,
-                      const int32_t* offsets, int E, int d, int n, void* dW2, hipStream_t st) {
-  return MOE_DISPATCH(dtype, dw2, As, d_o, row_token, offsets, E, d, n, dW2, st);
+hipError_t launch_dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t* row_token,
+                      const int32_t* offsets, void* dW2, hipStream_t st) {
+  return MOE_GDISPATCH(g, dw2, As, d_o, row_token, offsets, dW2, st);
 }
 hipError_t launch_dwr(int dtype, const void* x, const void* dz_dense, int T, int d, int E, void* dWr,
                       float* partials, hipStream_t st) {

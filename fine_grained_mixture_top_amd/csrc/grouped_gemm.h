@@ -47,6 +47,7 @@
 //    (optionally split into chunks written as separate fp32 slices).
 #pragma once
 
+#include <type_traits>
 #include <utility>
 
 #include "device_common.h"
@@ -379,10 +380,12 @@ template <int V> struct Slot { static constexpr int value = V; };
 
 // LDS holds two stages (A tile then B tile, STAGE elements each); D register
 // slots hold the global loads of the next D k steps.  Stage k lives in slot
-// k % D.  Top of step k: LDS[k&1] = stage k, slot (k+1)%D = stage k+1.
-// Step k: write stage k+1 to LDS[(k+1)&1], refill its slot with stage
-// k+1+D, run the MFMAs of stage k, barrier.  The loop is unrolled D times so
-// slot indices are compile-time constants.
+// k % D.  The caller has already issued the loads of stage 0 into slot 0
+// (for the next tile, before the current tile's epilogue, so that their
+// latency hides behind it).  Top of step k: LDS[k&1] = stage k, slot
+// (k+1)%D = stage k+1.  Step k: write stage k+1 to LDS[(k+1)&1], refill its
+// slot with stage k+1+D, run the MFMAs of stage k, barrier.  The loop is
+// unrolled D times so slot indices are compile-time constants.
 template <int D, typename T, int BM, int BN, bool AMN, bool BMN, class Load, class Store>
 __device__ __forceinline__ void pipeline(int nk, f32x4_v (&acc)[BM / 32][BN / 32], T* lds, const TileCtx& c,
                                          Load load, Store store) {
@@ -390,7 +393,6 @@ __device__ __forceinline__ void pipeline(int nk, f32x4_v (&acc)[BM / 32][BN / 32
   auto a_of = [&](int st) { return lds + st * G::STAGE; };
   auto b_of = [&](int st) { return lds + st * G::STAGE + G::TA::SIZE; };
   if (nk <= 0) return;
-  load(Slot<0>(), 0);
   store(Slot<0>(), a_of(0), b_of(0));
   [&]<int... I>(std::integer_sequence<int, I...>) {
     ((1 + I < nk ? (load(Slot<(1 + I) % D>(), 1 + I), 0) : 0), ...);
@@ -533,103 +535,131 @@ grouped_gemm_kernel(GemmShape s, Operand A, Operand B, typename Epi::Params ep) 
 
   T* lds = reinterpret_cast<T*>(smem);
   float* Cs = reinterpret_cast<float*>(smem);
-  for (int t = xcd_virtual_id(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
-    // ---- decode the tile ----
+
+  // tile t -> expert, m tile, n tile and the rows it covers
+  auto decode = [&](int t, TileCtx& d) {
     if (!WGT) {
       const int mg = t / NT;
-      c.nt = t % NT;
+      d.nt = t % NT;
       if (s.offsets) {
-        c.e = upper_index(tprefix, s.E + 1, mg);
-        c.mt = mg - tprefix[c.e];
-        c.seg0 = s.offsets[c.e];
-        c.segn = s.offsets[c.e + 1] - c.seg0;
+        d.e = upper_index(tprefix, s.E + 1, mg);
+        d.mt = mg - tprefix[d.e];
+        d.seg0 = s.offsets[d.e];
+        d.segn = s.offsets[d.e + 1] - d.seg0;
       } else {
-        c.e = 0; c.mt = mg; c.seg0 = 0; c.segn = s.M;
+        d.e = 0; d.mt = mg; d.seg0 = 0; d.segn = s.M;
       }
-      c.m_valid = min(BM, c.segn - c.mt * BM);
-      c.out_row0 = (long long)c.seg0 + (long long)c.mt * BM;
+      d.m_valid = min(BM, d.segn - d.mt * BM);
+      d.out_row0 = (long long)d.seg0 + (long long)d.mt * BM;
     } else {
       const int MT = s.M / BM;
       const int es = t / (MT * NT);  // (expert, split)
-      c.e = es / s.ksplit;
+      d.e = es / s.ksplit;
       const int sp = es % s.ksplit;
       const int rem = t % (MT * NT);
-      c.mt = rem / NT;
-      c.nt = rem % NT;
-      c.seg0 = s.offsets ? s.offsets[c.e] : 0;
-      c.segn = s.offsets ? s.offsets[c.e + 1] - c.seg0 : s.K;
+      d.mt = rem / NT;
+      d.nt = rem % NT;
+      d.seg0 = s.offsets ? s.offsets[d.e] : 0;
+      d.segn = s.offsets ? s.offsets[d.e + 1] - d.seg0 : s.K;
       if (s.ksplit > 1) {  // chunk sp of the segment, a whole number of k steps
-        const int steps = (c.segn + G::BK - 1) / G::BK;
+        const int steps = (d.segn + G::BK - 1) / G::BK;
         const int per = (steps + s.ksplit - 1) / s.ksplit * G::BK;
-        const int lo = min(c.segn, sp * per);
-        c.seg0 += lo;
-        c.segn = min(c.segn, lo + per) - lo;
+        const int lo = min(d.segn, sp * per);
+        d.seg0 += lo;
+        d.segn = min(d.segn, lo + per) - lo;
       }
-      c.m_valid = BM;
-      c.out_row0 = (long long)es * s.M + (long long)c.mt * BM;
+      d.m_valid = BM;
+      d.out_row0 = (long long)es * s.M + (long long)d.mt * BM;
     }
-    c.n0 = c.nt * BN;
+    d.n0 = d.nt * BN;
+  };
 
+  // loaders live across tiles: the next tile's first k step is fetched
+  // before the current tile's epilogue
+  using LA = typename std::conditional<WGT, MNLoad<T, BM, PF>, KMajorLoad<T, BM, PF>>::type;
+  using LB = typename std::conditional<(!WGT && BL == B_NK), KMajorLoad<T, BN, PF>, MNLoad<T, BN, PF>>::type;
+  LA la;
+  LB lb;
+  const T* abase = reinterpret_cast<const T*>(A.ptr);
+  auto setup = [&](const TileCtx& d) {
+    if constexpr (!WGT) {
+      la.setup(d.tid, [&](int r) {
+        const int m = d.mt * BM + r;
+        const int row = d.seg0 + (m < d.segn ? m : d.segn - 1);  // rows past the end repeat the last one
+        const long long src = A.idx ? A.idx[row] : row;
+        return abase + src * A.ld;
+      });
+      const T* bbase = reinterpret_cast<const T*>(B.ptr) + (long long)d.e * B.estride;
+      if constexpr (BL == B_NK) {
+        lb.setup(d.tid, [&](int r) {
+          int col = d.n0 + r;
+          if (col >= s.n_valid) col = s.n_valid - 1;
+          return bbase + (long long)col * B.ld;
+        });
+      } else {
+        const int half = s.N / 2, n0p = d.nt * (BN / 2);
+        lb.setup(d.tid, [&](int cc) {
+          const int col = PAIRED ? ColPaired::map(cc, n0p, half) : d.n0 + cc;
+          return (PAIRED || col < s.n_valid) ? col : -1;
+        }, bbase, nullptr, B.ld, 0, s.K);
+      }
+    } else {
+      const T* bbase = reinterpret_cast<const T*>(B.ptr);
+      const int m0 = d.mt * BM;
+      la.setup(d.tid, [&](int cc) { return m0 + cc; }, abase, A.idx, A.ld, d.seg0, d.segn);
+      lb.setup(d.tid, [&](int cc) { const int col = d.n0 + cc; return col < s.n_valid ? col : -1; }, bbase, B.idx,
+               B.ld, d.seg0, d.segn);
+    }
+  };
+  auto load = [&](auto S, int k) {
+    constexpr int SV = decltype(S)::value;
+    if constexpr (!WGT && BL == B_NK) {
+      la.template load<SV>(k * G::BK);
+      lb.template load<SV>(k * G::BK);
+    } else if constexpr (!WGT) {
+      la.template load<SV>(k * G::BK);
+      lb.template load<SV>(c.tid, k * G::BK);
+    } else {
+      la.template load<SV>(c.tid, k * G::BK);
+      lb.template load<SV>(c.tid, k * G::BK);
+    }
+  };
+  auto store = [&](auto S, T* a, T* b) {
+    constexpr int SV = decltype(S)::value;
+    la.template store<SV>(a, c.tid);
+    lb.template store<SV>(b, c.tid);
+  };
+  auto ksteps = [&](const TileCtx& d) { return WGT ? (d.segn + G::BK - 1) / G::BK : s.K / G::BK; };
+
+  int t = xcd_virtual_id(blockIdx.x, gridDim.x);
+  if (t < total) {
+    decode(t, c);
+    setup(c);
+    if (ksteps(c) > 0) load(Slot<0>(), 0);
+  }
+  while (t < total) {
     f32x4_v acc[G::FM][G::FN];
 #pragma unroll
     for (int i = 0; i < G::FM; ++i)
 #pragma unroll
       for (int j = 0; j < G::FN; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+    pipeline<PF, T, BM, BN, AMN, BMN>(ksteps(c), acc, lds, c, load, store);
 
-    if constexpr (!WGT) {
-      // ---------------- ROW mode ----------------
-      const T* abase = reinterpret_cast<const T*>(A.ptr);
-      const T* bbase = reinterpret_cast<const T*>(B.ptr) + (long long)c.e * B.estride;
-      KMajorLoad<T, BM, PF> la;
-      la.setup(c.tid, [&](int r) {
-        const int m = c.mt * BM + r;
-        const int row = c.seg0 + (m < c.segn ? m : c.segn - 1);  // rows past the end repeat the last one
-        const long long src = A.idx ? A.idx[row] : row;
-        return abase + src * A.ld;
-      });
-      const int nk = s.K / G::BK;
-      if constexpr (BL == B_NK) {
-        KMajorLoad<T, BN, PF> lb;
-        lb.setup(c.tid, [&](int r) {
-          int col = c.n0 + r;
-          if (col >= s.n_valid) col = s.n_valid - 1;
-          return bbase + (long long)col * B.ld;
-        });
-        pipeline<PF, T, BM, BN, AMN, BMN>(nk, acc, lds, c,
-            [&](auto S, int k) { la.template load<decltype(S)::value>(k * G::BK); lb.template load<decltype(S)::value>(k * G::BK); },
-            [&](auto S, T* a, T* b) { la.template store<decltype(S)::value>(a, c.tid); lb.template store<decltype(S)::value>(b, c.tid); });
-      } else {
-        MNLoad<T, BN, PF> lb;
-        const int half = s.N / 2, n0p = c.nt * (BN / 2);
-        lb.setup(c.tid, [&](int cc) {
-          const int col = PAIRED ? ColPaired::map(cc, n0p, half) : c.n0 + cc;
-          return (PAIRED || col < s.n_valid) ? col : -1;
-        }, bbase, nullptr, B.ld, 0, s.K);
-        pipeline<PF, T, BM, BN, AMN, BMN>(nk, acc, lds, c,
-            [&](auto S, int k) { la.template load<decltype(S)::value>(k * G::BK); lb.template load<decltype(S)::value>(c.tid, k * G::BK); },
-            [&](auto S, T* a, T* b) { la.template store<decltype(S)::value>(a, c.tid); lb.template store<decltype(S)::value>(b, c.tid); });
-      }
-    } else {
-      // ---------------- WGT mode ----------------
-      const T* abase = reinterpret_cast<const T*>(A.ptr);
-      const T* bbase = reinterpret_cast<const T*>(B.ptr);
-      MNLoad<T, BM, PF> la;
-      MNLoad<T, BN, PF> lb;
-      const int m0 = c.mt * BM;
-      la.setup(c.tid, [&](int cc) { return m0 + cc; }, abase, A.idx, A.ld, c.seg0, c.segn);
-      lb.setup(c.tid, [&](int cc) { const int col = c.n0 + cc; return col < s.n_valid ? col : -1; }, bbase, B.idx,
-               B.ld, c.seg0, c.segn);
-      const int nk = (c.segn + G::BK - 1) / G::BK;
-      pipeline<PF, T, BM, BN, AMN, BMN>(nk, acc, lds, c,
-          [&](auto S, int k) { la.template load<decltype(S)::value>(c.tid, k * G::BK); lb.template load<decltype(S)::value>(c.tid, k * G::BK); },
-          [&](auto S, T* a, T* b) { la.template store<decltype(S)::value>(a, c.tid); lb.template store<decltype(S)::value>(b, c.tid); });
-    }
-
-    // ---- epilogue: park the fp32 tile in LDS, then the functor's pass ----
+    // park the fp32 tile in LDS, fetch the next tile's first k step, then
+    // run the functor's pass over the parked tile
     stage_acc<BM, BN, PAIRED>(Cs, acc, c);
+    const int tn = t + gridDim.x;
+    TileCtx cn = c;
+    if (tn < total) {
+      decode(tn, cn);
+      setup(cn);
+      if (ksteps(cn) > 0) load(Slot<0>(), 0);
+    }
     __syncthreads();
     Epi::run(ep, s, c, Cs, smem + G::STAGE_C);
     __syncthreads();  // LDS is reused by the next tile's main loop
+    c = cn;
+    t = tn;
   }
 }
 

@@ -1,0 +1,418 @@
+// Large-tile grouped GEMM for bf16 on gfx950 (the MoE layer's six grouped
+// GEMMs when their dimensions are multiples of 256).  Same contract as the
+// kernel in grouped_gemm.h (ROW and WGT modes, gathered rows, the epilogue
+// functors of epilogues.h), different machinery:
+//
+//  * 256 x 256 output tile, 512 threads = 8 waves in a 2 (m) x 4 (n) grid;
+//    each wave owns 128 x 64 outputs as 4 x 2 blocks of
+//    v_mfma_f32_32x32x16_bf16.  The MFMA's first operand is the N-side
+//    fragment and its second the M-side one, so accumulator element e of a
+//    block holds (m = lane % 32, n = 8*(e/4) + 4*(lane/32) + e%4): four
+//    consecutive columns of one row per lane.
+//  * Operand tiles go from memory straight into LDS with buffer loads that
+//    write LDS (16 bytes per lane, 1 KB per instruction, no registers);
+//    rows outside a segment are addressed past the buffer's record count and
+//    read as zeros.  Four LDS stages of k = 32 (32 KB each): three are in
+//    flight while the MFMAs of the fourth run, which covers HBM latency
+//    without spending registers.
+//  * Layouts (16-byte chunks XOR-swizzled so that fragment reads hit
+//    distinct banks):
+//      k-contiguous operands: [256 rows][32 k], 64-byte rows, chunk c of row
+//        r in slot c ^ ((r >> 2) & 3); a fragment is one ds_read_b128;
+//      m/n-contiguous operands: [32 k-rows][256 cols], 512-byte rows, chunk
+//        c of k-row kr in slot c ^ (4 * (kr & 3)); a fragment is two
+//        ds_read_b64_tr_b16 (the LDS transpose read).
+//  * Epilogue: the tile is parked in LDS as fp32 in two halves of 128 rows
+//    (the waves of one m half write, then all 512 threads run the functor on
+//    that half), so the functors of the 128-row kernel apply unchanged.
+#pragma once
+
+#include <type_traits>
+
+#include "epilogues.h"
+
+namespace moe {
+namespace g4 {
+
+constexpr int BM = 256, BN = 256, BK = 32, NS = 4, NTH = 512;
+constexpr int OPB = 256 * BK * 2;            // bytes of one operand tile per stage
+constexpr int STAGE = 2 * OPB;               // 32 KB
+constexpr int HALF = 128;                    // epilogue rows per pass
+constexpr int LDC = BN + 4;                  // fp32 staging pitch (floats)
+constexpr int STAGE_C = HALF * LDC * 4;      // 133120 bytes
+constexpr int SMEM = NS * STAGE > STAGE_C ? NS * STAGE : STAGE_C;
+constexpr uint32_t OOB = 0x80000000u;        // byte offset past every record count
+constexpr int LPS = 4;                       // 16-byte loads per thread per stage
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef float f32x16_v __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ int swz_kc(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_mn(int kr) { return 4 * (kr & 3); }
+
+// s_waitcnt with vmcnt(n) only (expcnt and lgkmcnt at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// ---------------------------------------------------------------------------
+// operand loaders: each wave issues two 1 KB instructions per operand per stage
+// ---------------------------------------------------------------------------
+
+// k-contiguous rows.  Instruction i of wave w covers tile rows
+// (2w + i) * 16 .. +15; lane l takes row rb + l/4, slot l%4.
+struct KCLoad {
+  uint32_t off[2];  // byte offset of this lane's chunk at k = 0 (OOB when absent)
+  template <class F>
+  __device__ __forceinline__ void setup(int w, int lane, F rowoff) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = (2 * w + i) * 16 + (lane >> 2);
+      const uint32_t ro = rowoff(r);
+      off[i] = ro == OOB ? OOB : ro + (uint32_t)(((lane & 3) ^ swz_kc(r)) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* op, int w, int k0) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(rs, op + (2 * w + i) * 1024, off[i] + (uint32_t)k0 * 2u);
+  }
+};
+
+// m/n-contiguous rows (k-rows of 256 columns).  Instruction i of wave w
+// covers k-rows (2w + i) * 2 and +1 (lanes 0..31 and 32..63), slot l % 32.
+// The column part of the offset is fixed per tile; the row part is either
+// (k0 + kr) * ld (weights) or idx[seg0 + k0 + kr] * ld (gathered rows, the
+// indices of the next stage fetched one stage ahead).
+struct MNLoad4 {
+  uint32_t coff[2];   // column byte offset of this lane's chunk (OOB if absent)
+  int kr[2];          // k-row of each instruction within the stage
+  // gathered / segment rows
+  const int32_t* idx;
+  int seg0, segn;
+  uint32_t ldb;       // row pitch in bytes
+  uint32_t rcur[2], rnext[2];  // row byte offsets of this stage / the next (OOB past the segment)
+
+  template <class F>
+  __device__ __forceinline__ void setup_cols(int w, int lane, F colmap) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      kr[i] = (2 * w + i) * 2 + (lane >> 5);
+      const int chunk = (lane & 31) ^ swz_mn(kr[i]);
+      const int col = colmap(chunk * 8);
+      coff[i] = col < 0 ? OOB : (uint32_t)col * 2u;
+    }
+  }
+  // row byte offset of segment row k (OOB past the end)
+  __device__ __forceinline__ uint32_t seg_row(int k) const {
+    if (k >= segn) return OOB;
+    const int src = idx ? idx[seg0 + k] : seg0 + k;
+    return (uint32_t)src * ldb;
+  }
+  __device__ __forceinline__ void setup_rows(const int32_t* idx_, int seg0_, int segn_, uint32_t ldb_) {
+    idx = idx_; seg0 = seg0_; segn = segn_; ldb = ldb_;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) rnext[i] = seg_row(kr[i]);
+  }
+  // weights: k-row kr of stage k0 sits at (k0 + kr) * ldb
+  __device__ __forceinline__ void issue_w(__amdgpu_buffer_rsrc_t rs, char* op, int w, int k0) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t o = coff[i] == OOB ? OOB : coff[i] + (uint32_t)(k0 + kr[i]) * ldb;
+      dma16(rs, op + (2 * w + i) * 1024, o);
+    }
+  }
+  // segment rows, in two calls per stage: next_rows() takes the rows of
+  // stage k0 (fetched by the previous call) and fetches those of stage
+  // k0 + BK; dma() then issues the data loads.  Every index load of a stage
+  // is issued before any of its data loads.
+  __device__ __forceinline__ void next_rows(int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) rcur[i] = rnext[i];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k = k0 + BK + kr[i];
+      const int kc = k < segn ? k : (segn > 0 ? segn - 1 : 0);  // keeps the index load inside the segment
+      const int src = idx ? idx[seg0 + kc] : seg0 + kc;
+      rnext[i] = k < segn ? (uint32_t)src * ldb : OOB;
+    }
+  }
+  __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, char* op, int w) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t o = (coff[i] == OOB || rcur[i] == OOB) ? OOB : rcur[i] + coff[i];
+      dma16(rs, op + (2 * w + i) * 1024, o);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// fragments (32 rows / columns by 8 consecutive k per lane)
+// ---------------------------------------------------------------------------
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// k-contiguous tile: row rb + lane%32, k = 16s + 8*(lane/32) .. +7
+__device__ __forceinline__ bf16x8_v frag_kc(const char* op, int rb, int s, int lane) {
+  const int r = rb + (lane & 31);
+  const int c = 2 * s + (lane >> 5);
+  return *reinterpret_cast<const bf16x8_v*>(op + r * 64 + ((c ^ swz_kc(r)) * 16));
+}
+
+// m/n-contiguous tile: column cb + lane%32, k = 16s + 8*(lane/32) .. +7.
+// Lane q of each 16-lane group addresses k-row (q/4) of a 4 x 16 block and
+// column chunk (q%4)*4; the transpose read hands it column q of the block.
+__device__ __forceinline__ bf16x8_v frag_mn(const char* op, int cb, int s, int lane) {
+  const int q = lane & 15, g = lane >> 4;
+  const int col = cb + 16 * (g & 1) + (q & 3) * 4;
+  const int k0 = 16 * s + 8 * (g >> 1) + (q >> 2);
+  auto addr = [&](int kr) { return op + kr * 512 + ((((col >> 3) ^ swz_mn(kr)) * 16) + (col & 7) * 2); };
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)addr(k0));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)addr(k0 + 4));
+  return __builtin_bit_cast(bf16x8_v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <bool MN>
+__device__ __forceinline__ bf16x8_v frag(const char* op, int base, int s, int lane) {
+  if constexpr (MN) return frag_mn(op, base, s, lane);
+  else return frag_kc(op, base, s, lane);
+}
+
+template <bool AMN, bool BMN>
+struct Frags {
+  bf16x8_v m[4], n[2];
+  __device__ __forceinline__ void read(const char* st, int s, int lane, int wm, int wn) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = frag<AMN>(st, wm * 128 + 32 * j, s, lane);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) n[i] = frag<BMN>(st + OPB, wn * 64 + 32 * i, s, lane);
+  }
+};
+
+template <bool AMN, bool BMN>
+__device__ __forceinline__ void mma(f32x16_v (&acc)[2][4], const Frags<AMN, BMN>& f) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.n[i], f.m[j], acc[i][j], 0, 0, 0);
+}
+
+#define G4_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+
+// WGT: weight-gradient mode (both operands m/n-contiguous segment rows);
+// otherwise ROW mode with A k-contiguous and B [N][K] (BMN = false) or [K][N]
+// (BMN = true).  PAIRED: B columns are gate j0.. then up n + j0.. (SwiGLU).
+template <bool WGT, bool BMN, bool PAIRED, class Epi>
+__global__ void __launch_bounds__(NTH, 1)
+grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32_t b_bytes,
+                     typename Epi::Params ep) {
+  constexpr bool AMN = WGT;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  __shared__ int tprefix[WGT ? 1 : MAX_E + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 2, wn = w & 3;
+
+  const int NT = s.N / BN;
+  int total;
+  if constexpr (!WGT) {
+    __shared__ int wsum[8];
+    int carry = 0;
+    for (int e0 = 0; e0 < s.E; e0 += NTH) {
+      const int e = e0 + tid;
+      const int tiles = e < s.E ? (s.offsets[e + 1] - s.offsets[e] + BM - 1) / BM : 0;
+      int incl = tiles;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      if (lane == 63) wsum[w] = incl;
+      __syncthreads();
+      int base = carry, tot = 0;
+      for (int x = 0; x < NTH / 64; ++x) {
+        if (x < w) base += wsum[x];
+        tot += wsum[x];
+      }
+      if (e < s.E) tprefix[e] = base + incl - tiles;
+      carry += tot;
+      __syncthreads();
+    }
+    if (tid == 0) tprefix[s.E] = carry;
+    __syncthreads();
+    total = tprefix[s.E] * NT;
+  } else {
+    total = s.E * (s.M / BM) * NT;
+  }
+
+  float* Cs = reinterpret_cast<float*>(smem);
+  const char* abase = reinterpret_cast<const char*>(A.ptr);
+  const char* bbase = reinterpret_cast<const char*>(B.ptr);
+
+  for (int t = xcd_virtual_id(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
+    TileCtx c;
+    c.tid = tid; c.lane = lane; c.wm = wm; c.wn = wn;
+    if constexpr (!WGT) {
+      const int mg = t / NT;
+      c.nt = t % NT;
+      c.e = upper_index(tprefix, s.E + 1, mg);
+      c.mt = mg - tprefix[c.e];
+      c.seg0 = s.offsets[c.e];
+      c.segn = s.offsets[c.e + 1] - c.seg0;
+      c.m_valid = min(BM, c.segn - c.mt * BM);
+      c.out_row0 = (long long)c.seg0 + (long long)c.mt * BM;
+    } else {
+      const int MT = s.M / BM;
+      c.e = t / (MT * NT);
+      const int rem = t % (MT * NT);
+      c.mt = rem / NT;
+      c.nt = rem % NT;
+      c.seg0 = s.offsets[c.e];
+      c.segn = s.offsets[c.e + 1] - c.seg0;
+      c.m_valid = BM;
+      c.out_row0 = (long long)c.e * s.M + (long long)c.mt * BM;
+    }
+    c.n0 = c.nt * BN;
+    const int nk = WGT ? (c.segn + BK - 1) / BK : s.K / BK;
+
+    // ---- operand set-up ----
+    __amdgpu_buffer_rsrc_t ra, rb;
+    KCLoad la_kc, lb_kc;
+    MNLoad4 la_mn, lb_mn;
+    if constexpr (!WGT) {
+      ra = make_rsrc(abase, a_bytes);
+      la_kc.setup(w, lane, [&](int r) -> uint32_t {
+        const int m = c.mt * BM + r;
+        const int row = c.seg0 + (m < c.segn ? m : c.segn - 1);  // rows past the end repeat the last one
+        const uint32_t src = A.idx ? (uint32_t)A.idx[row] : (uint32_t)row;
+        return src * (uint32_t)A.ld * 2u;
+      });
+      const char* be = bbase + (long long)c.e * B.estride * 2;
+      rb = make_rsrc(be, b_bytes);
+      if constexpr (!BMN) {
+        lb_kc.setup(w, lane, [&](int r) -> uint32_t { return (uint32_t)(c.n0 + r) * (uint32_t)B.ld * 2u; });
+      } else {
+        const int half = s.N / 2, j0 = c.nt * (BN / 2);
+        lb_mn.setup_cols(w, lane, [&](int cc) {
+          if (PAIRED) return cc < BN / 2 ? j0 + cc : half + j0 + (cc - BN / 2);
+          return c.n0 + cc;
+        });
+        lb_mn.ldb = (uint32_t)B.ld * 2u;
+      }
+    } else {
+      ra = make_rsrc(abase, a_bytes);
+      rb = make_rsrc(bbase, b_bytes);
+      const int m0 = c.mt * BM;
+      la_mn.setup_cols(w, lane, [&](int cc) { return m0 + cc; });
+      lb_mn.setup_cols(w, lane, [&](int cc) { return c.n0 + cc; });
+      la_mn.setup_rows(A.idx, c.seg0, c.segn, (uint32_t)A.ld * 2u);
+      lb_mn.setup_rows(B.idx, c.seg0, c.segn, (uint32_t)B.ld * 2u);
+    }
+    auto issue = [&](int k) {
+      char* st = smem + (k % NS) * STAGE;
+      const int k0 = k * BK;
+      if constexpr (!WGT) {
+        la_kc.issue(ra, st, w, k0);
+        if constexpr (!BMN) lb_kc.issue(rb, st + OPB, w, k0);
+        else lb_mn.issue_w(rb, st + OPB, w, k0);
+      } else {
+        la_mn.next_rows(k0);
+        lb_mn.next_rows(k0);
+        la_mn.dma(ra, st, w);
+        lb_mn.dma(rb, st + OPB, w);
+      }
+    };
+
+    f32x16_v acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    if (nk > 0) {
+      // prologue: stages 0 .. NS-2 in flight, then wait for stage 0
+      for (int k = 0; k < NS - 1 && k < nk; ++k) issue(k);
+      wait_vm<0>();
+      __syncthreads();
+      Frags<AMN, BMN> f0, f1;
+      f0.read(smem, 0, lane, wm, wn);
+      // one k step: MFMAs of sub-step 0 while sub-step 1's fragments load,
+      // barrier (stage k+1 landed, stage k-1's buffer free), next stage's
+      // loads, MFMAs of sub-step 1 while the next stage's first fragments load
+      auto body = [&](int k, auto MAIN) {
+        const char* cur = smem + (k % NS) * STAGE;
+        f1.read(cur, 1, lane, wm, wn);
+        mma(acc, f0);
+#pragma unroll
+        for (int i = 0; i < 6; ++i) { G4_SCHED(0x008, 1); G4_SCHED(0x100, 1); }
+        G4_SCHED(0x008, 2);
+        if constexpr (decltype(MAIN)::value) {
+          // stage k+1 complete: at least the LPS data loads of stage k+2
+          // were issued after its last load (index loads only add to that)
+          wait_vm<LPS>();
+        } else {
+          wait_vm<0>();
+        }
+        __syncthreads();
+        if constexpr (decltype(MAIN)::value) issue(k + NS - 1);
+        if (k + 1 < nk) f0.read(smem + ((k + 1) % NS) * STAGE, 0, lane, wm, wn);
+        mma(acc, f1);
+        if constexpr (decltype(MAIN)::value) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { G4_SCHED(0x008, 1); G4_SCHED(0x020, 1); G4_SCHED(0x100, 1); }
+          G4_SCHED(0x100, 2);
+          G4_SCHED(0x008, 4);
+        }
+      };
+      int k = 0;
+      for (; k + NS - 1 < nk; ++k) body(k, std::true_type());
+      for (; k < nk; ++k) body(k, std::false_type());
+      __syncthreads();  // every wave is done reading the stages
+    }
+
+    // ---- epilogue: two halves of 128 rows ----
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      TileCtx ch = c;
+      ch.out_row0 = c.out_row0 + h * HALF;
+      ch.m_valid = min(HALF, c.m_valid - h * HALF);
+      if (ch.m_valid <= 0) break;  // uniform over the workgroup
+      if (wm == h) {
+        const int cl = lane & 31, hl = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int eg = 0; eg < 4; ++eg) {
+              float4 v = make_float4(acc[i][j][4 * eg], acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2],
+                                     acc[i][j][4 * eg + 3]);
+              *reinterpret_cast<float4*>(Cs + (32 * j + cl) * LDC + wn * 64 + 32 * i + 8 * eg + 4 * hl) = v;
+            }
+      }
+      __syncthreads();
+      Epi::run(ep, s, ch, Cs, nullptr);
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace g4
+}  // namespace moe

@@ -11,31 +11,37 @@ namespace moe {
 
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
 
+// Sizes every grouped GEMM launcher needs: element type, layer sizes, row
+// capacity of the per-row buffers, and whether to keep to the 128-row tile
+// kernels.
+struct GemmDims {
+  int dtype;
+  int T, d, E, n;
+  size_t cap;
+  bool small_tiles;
+};
+
 // Column tile of the dH GEMM, which decides how many fp32 score-gradient
-// partials each row gets (n / dh_block(dtype, n)).
-int dh_block(int dtype, int n);
-inline int dh_partials(int dtype, int n) { return n / dh_block(dtype, n); }
+// partials each row gets (n / dh_block(g)).
+int dh_block(const GemmDims& g);
+inline int dh_partials(const GemmDims& g) { return g.n / dh_block(g); }
 
 // ---- grouped GEMMs (gemm_kernels.hip) ----
 hipError_t launch_router_logits(int dtype, const void* x, const void* w_r, const float* bias,
                                 float* logits, int T, int d, int E, hipStream_t st);
-hipError_t launch_up_swiglu(int dtype, const void* x, const void* w1, const int32_t* row_token,
-                            const int32_t* offsets, const int32_t* tile_offsets, int E, int d,
-                            int n, size_t cap, void* H, void* A, hipStream_t st);
-hipError_t launch_down(int dtype, const void* A, const void* w2, const int32_t* offsets,
-                       const int32_t* tile_offsets, int E, int d, int n, size_t cap, void* Y,
+hipError_t launch_up_swiglu(const GemmDims& g, const void* x, const void* w1, const int32_t* row_token,
+                            const int32_t* offsets, void* H, void* A, hipStream_t st);
+hipError_t launch_down(const GemmDims& g, const void* A, const void* w2, const int32_t* offsets, void* Y,
                        hipStream_t st);
-hipError_t launch_dh(int dtype, const void* d_o, const void* w2, const void* H,
-                     const int32_t* row_token, const float* row_gate, const int32_t* offsets,
-                     const int32_t* tile_offsets, int E, int d, int n, size_t cap, void* dH,
+hipError_t launch_dh(const GemmDims& g, const void* d_o, const void* w2, const void* H,
+                     const int32_t* row_token, const float* row_gate, const int32_t* offsets, void* dH,
                      void* As, float* dS_part, hipStream_t st);
-hipError_t launch_dxt(int dtype, const void* dH, const void* w1, const int32_t* offsets,
-                      const int32_t* tile_offsets, int E, int d, int n, size_t cap, void* dXt,
+hipError_t launch_dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t* offsets, void* dXt,
                       hipStream_t st);
-hipError_t launch_dw1(int dtype, const void* x, const void* dH, const int32_t* row_token,
-                      const int32_t* offsets, int E, int d, int n, void* dW1, hipStream_t st);
-hipError_t launch_dw2(int dtype, const void* As, const void* d_o, const int32_t* row_token,
-                      const int32_t* offsets, int E, int d, int n, void* dW2, hipStream_t st);
+hipError_t launch_dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* row_token,
+                      const int32_t* offsets, void* dW1, hipStream_t st);
+hipError_t launch_dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t* row_token,
+                      const int32_t* offsets, void* dW2, hipStream_t st);
 // dW_r = x^T dz_dense, reduction split in dwr_splits() chunks whose fp32
 // partials ([splits][d][E]) go to `partials` and are then summed in order.
 int dwr_splits(int T, int d, int E);

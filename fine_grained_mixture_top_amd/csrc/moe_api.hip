@@ -19,7 +19,7 @@ size_t elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 int validate_desc(const moe_desc* d) {
   if (!d) return MOE_EINVAL;
   if (d->reserved != 0) return MOE_EINVAL;
-  if ((d->flags & ~MOE_FLAG_SCORES_GIVEN) != 0) return MOE_EINVAL;
+  if ((d->flags & ~(MOE_FLAG_SCORES_GIVEN | MOE_FLAG_GEMM_128)) != 0) return MOE_EINVAL;
   if (d->T < 1 || d->d < 1 || d->E < 1 || d->n < 1 || d->K < 1 || d->K > d->E) return MOE_EINVAL;
   if (d->round_mode < MOE_ROUND_OFF || d->round_mode > MOE_ROUND_STOCHASTIC) return MOE_EINVAL;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_EDTYPE;
@@ -59,6 +59,10 @@ Layout route_layout(const moe_desc* d) {
   return L;
 }
 
+GemmDims gemm_dims(const moe_desc* d) {
+  return GemmDims{d->dtype, d->T, d->d, d->E, d->n, capacity(d), (d->flags & MOE_FLAG_GEMM_128) != 0};
+}
+
 Layout fwd_layout(const moe_desc* d) {
   Layout L{};
   const size_t cap = capacity(d), es = elem_size(d->dtype);
@@ -72,7 +76,7 @@ Layout fwd_layout(const moe_desc* d) {
 Layout bwd_layout(const moe_desc* d) {
   Layout L{};
   const size_t cap = capacity(d), es = elem_size(d->dtype);
-  const size_t np = (size_t)dh_partials(d->dtype, d->n);
+  const size_t np = (size_t)dh_partials(gemm_dims(d));
   size_t o = 0;
   L.off[0] = o; o = up(o + cap * 2 * d->n * es);          // dH
   L.off[1] = o; o = up(o + cap * d->n * es);              // A_s
@@ -198,9 +202,9 @@ int moe_fwd(const moe_desc* desc, const void* x, const void* w1, const void* w2,
   void* Y = w + L.off[1];
   const size_t cap = capacity(desc);
   const moe_desc& D = *desc;
-  MOE_TRY(MOE_K_UP, launch_up_swiglu(D.dtype, x, w1, routing->row_token, routing->offsets, routing->tile_offsets, D.E,
-                           D.d, D.n, cap, h_cache, A, st));
-  MOE_TRY(MOE_K_DOWN, launch_down(D.dtype, A, w2, routing->offsets, routing->tile_offsets, D.E, D.d, D.n, cap, Y, st));
+  const GemmDims g = gemm_dims(desc);
+  MOE_TRY(MOE_K_UP, launch_up_swiglu(g, x, w1, routing->row_token, routing->offsets, h_cache, A, st));
+  MOE_TRY(MOE_K_DOWN, launch_down(g, A, w2, routing->offsets, Y, st));
   MOE_TRY(MOE_K_AGG_O, launch_aggregate_o(D.dtype, Y, routing->row_gate, routing->tok_ptr, routing->tok_row, D.T, D.d, o,
                              st));
   return MOE_OK;
@@ -231,20 +235,20 @@ int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1
   const moe_routing& R = *routing;
 
   // dH kernel: dA' = dO W2^T with the recompute-A epilogue (dH, A_s, dS parts)
-  MOE_TRY(MOE_K_DH, launch_dh(D.dtype, d_o, w2, h_cache, R.row_token, R.row_gate, R.offsets, R.tile_offsets, D.E, D.d,
-                    D.n, cap, dH, As, dS_part, st));
+  const GemmDims g = gemm_dims(desc);
+  MOE_TRY(MOE_K_DH, launch_dh(g, d_o, w2, h_cache, R.row_token, R.row_gate, R.offsets, dH, As, dS_part, st));
   // router gradient: dS -> dz (per row and dense), dW_r = X^T dz
-  MOE_TRY(MOE_K_ROUTER_GRAD, launch_router_grad(D.dtype, dS_part, dh_partials(D.dtype, D.n), R.row_gate, R.row_expert, R.tok_ptr,
+  MOE_TRY(MOE_K_ROUTER_GRAD, launch_router_grad(D.dtype, dS_part, dh_partials(g), R.row_gate, R.row_expert, R.tok_ptr,
                              R.tok_row, D.T, D.E, dS_row, dz_row, dz_dense, st));
   MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, (float*)(w + L.off[8]), st));
   // activation gradient: dXt = dH W1^T, then dX = sum of dXt + dz W_r^T
   MOE_TRY(MOE_K_WR_T, launch_transpose(D.dtype, w_r, D.d, D.E, w_rT, st));
-  MOE_TRY(MOE_K_DXT, launch_dxt(D.dtype, dH, w1, R.offsets, R.tile_offsets, D.E, D.d, D.n, cap, dXt, st));
+  MOE_TRY(MOE_K_DXT, launch_dxt(g, dH, w1, R.offsets, dXt, st));
   MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, dXt, dz_row, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T, D.d, dx,
                               st));
   // weight gradients
-  MOE_TRY(MOE_K_DW1, launch_dw1(D.dtype, x, dH, R.row_token, R.offsets, D.E, D.d, D.n, dw1, st));
-  MOE_TRY(MOE_K_DW2, launch_dw2(D.dtype, As, d_o, R.row_token, R.offsets, D.E, D.d, D.n, dw2, st));
+  MOE_TRY(MOE_K_DW1, launch_dw1(g, x, dH, R.row_token, R.offsets, dw1, st));
+  MOE_TRY(MOE_K_DW2, launch_dw2(g, As, d_o, R.row_token, R.offsets, dw2, st));
   if (db) MOE_TRY(MOE_K_DB, launch_bias_grad(dz_row, R.offsets, D.E, db, st));
   return MOE_OK;
 }

@@ -69,6 +69,11 @@ extern "C" {
 /* desc->flags */
 #define MOE_FLAG_SCORES_GIVEN 1u  /* moe_route reads routing->logits as the
                                      router scores instead of computing them */
+#define MOE_FLAG_GEMM_128     2u  /* run every grouped GEMM with the 128-row
+                                     tile kernels (by default bf16 layers whose
+                                     sizes are multiples of 256 use 256 x 256
+                                     tiles); results agree to rounding, the
+                                     workspace size may differ */
 
 /* kernel ids reported in moe_profile.kernel (one per launch, in order) */
 #define MOE_K_ROUTER_LOGITS 0   /* z = x w_r + b                                  */

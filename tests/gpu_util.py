@@ -42,9 +42,9 @@ def relF(gpu: np.ndarray, ref: np.ndarray) -> float:
 
 
 def run_gpu(w: I.Workload, x, w_r, w1, w2, d_o, bias=None, round_mode=0, round_seed=0,
-            scores=None, backward=True):
+            scores=None, backward=True, flags=0):
     """Route + forward (+ backward) on the GPU; returns the Layer and device inputs."""
-    flags = B.MOE_FLAG_SCORES_GIVEN if scores is not None else 0
+    flags |= B.MOE_FLAG_SCORES_GIVEN if scores is not None else 0
     desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=round_mode,
                        round_seed=round_seed, flags=flags)
     L = B.Layer(desc)

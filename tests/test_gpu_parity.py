@@ -67,6 +67,12 @@ LAYER_CASES = [
     W("bf16_top1", 500, 128, 16, 64, 1, "bf16", seed=5),
     W("bf16_sparse_experts", 40, 256, 64, 128, 1, "bf16", seed=6),
     W("f32_one_token", 1, 128, 8, 64, 2, "f32", seed=7),
+    # d and n multiples of 256: every bf16 grouped GEMM takes the 256 x 256
+    # tile kernel (ragged T, partial 256-row tiles, experts of very different
+    # sizes, experts with no rows)
+    W("bf16_big_tiles", 1500, 512, 16, 256, 4, "bf16", seed=13),
+    W("bf16_big_tiles_sparse", 90, 256, 64, 256, 2, "bf16", seed=14),
+    W("bf16_big_tiles_skewed", 3000, 256, 32, 512, 3, "bf16", seed=15, zipf=1.2),
 ]
 
 
@@ -100,6 +106,35 @@ def test_layer_token_rounding_matches_oracle(mode):
     assert np.all(g_rt["counts"] % 128 == 0)
     g = layer_outputs(L, w)
     compare_layer(g, o, w.dtype)
+
+
+def test_layer_token_rounding_big_tiles():
+    w = W("bf16_tr_big", 1800, 256, 16, 256, 2, "bf16", seed=16)
+    a = I.draw_all(w)
+    L, _ = run_gpu(w, a["x"], a["w_r"], a["w1"], a["w2"], a["d_o"], round_mode=2, round_seed=9)
+    g_rt = routing_host(L, w)
+    o = oracle_layer(w, a["x"], a["w_r"], a["w1"], a["w2"], a["d_o"], round_mode=2, round_seed=9)
+    assert_routing_equal(g_rt, o)
+    g = layer_outputs(L, w)
+    compare_layer(g, o, w.dtype)
+
+
+@pytest.mark.parametrize("w", [W("bf16_tiles_ab", 1200, 512, 16, 256, 4, "bf16", seed=17)], ids=lambda w: w.name)
+def test_tile_kernels_agree(w):
+    """The 256 x 256 and the 128-row tile kernels compute the same layer: both
+    within tolerance of the oracle, and of each other."""
+    a = I.draw_all(w)
+    o = oracle_layer(w, a["x"], a["w_r"], a["w1"], a["w2"], a["d_o"], a["bias"])
+    outs = []
+    for flags in (0, B.MOE_FLAG_GEMM_128):
+        L, _ = run_gpu(w, a["x"], a["w_r"], a["w1"], a["w2"], a["d_o"], a["bias"], flags=flags)
+        assert_routing_equal(routing_host(L, w), o)
+        g = layer_outputs(L, w)
+        compare_layer(g, o, w.dtype)
+        outs.append(g)
+    from gpu_util import relF
+    for k in ("O", "H", "A", "Y", "dH", "dXt", "dS", "dX", "dWr", "dW1", "dW2"):
+        assert relF(outs[0][k], outs[1][k]) < 1e-2, k
 
 
 def test_layer_is_deterministic():
