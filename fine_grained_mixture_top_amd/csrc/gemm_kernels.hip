@@ -113,7 +113,7 @@ hipError_t up_swiglu_t(const GemmDims& g, const void* x, const void* w1, const i
 hipError_t up_swiglu_g4(const GemmDims& g, const void* x, const void* w1, const int32_t* row_token,
                         const int32_t* offsets, void* H, void* A, hipStream_t st) {
   const int n = g.n, d = g.d, E = g.E;
-  using Epi = EpiSwiGLU<bf16_t, g4::HALF, g4::BN, g4::NTH>;
+  using Epi = EpiSwiGLU<bf16_t, g4::EROWS, g4::BN, g4::NTH>;
   GemmShape s{offsets, E, 0, 2 * n, d, 2 * n, 1};
   Operand a{x, row_token, 0, d};
   Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
@@ -157,7 +157,7 @@ hipError_t down(const GemmDims& g, const void* A, const void* w2, const int32_t*
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (down_g4(g)) {
       const int n = g.n, d = g.d, E = g.E;
-      using Epi = EpiStore<bf16_t, bf16_t, g4::HALF, g4::BN, g4::NTH>;
+      using Epi = EpiStore<bf16_t, bf16_t, g4::EROWS, g4::BN, g4::NTH>;
       GemmShape s{offsets, E, 0, d, n, d, 1};
       Operand a{A, nullptr, 0, n};
       Operand b{w2, nullptr, (long long)n * d, d};
@@ -201,7 +201,7 @@ hipError_t dh(const GemmDims& g, const void* d_o, const void* w2, const void* H,
     const int bn = dh_bn(g);
     if (bn == g4::BN) {
       const int n = g.n, d = g.d, E = g.E;
-      using Epi = EpiDH<bf16_t, g4::HALF, g4::BN, g4::NTH>;
+      using Epi = EpiDH<bf16_t, g4::EROWS, g4::BN, g4::NTH>;
       GemmShape s{offsets, E, 0, n, d, n, 1};
       Operand a{d_o, row_token, 0, d};
       Operand b{w2, nullptr, (long long)n * d, d};
@@ -239,7 +239,7 @@ hipError_t dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t*
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (dxt_g4(g)) {
       const int n = g.n, d = g.d, E = g.E;
-      using Epi = EpiStore<bf16_t, bf16_t, g4::HALF, g4::BN, g4::NTH>;
+      using Epi = EpiStore<bf16_t, bf16_t, g4::EROWS, g4::BN, g4::NTH>;
       GemmShape s{offsets, E, 0, d, 2 * n, d, 1};
       Operand a{dH, nullptr, 0, 2 * n};
       Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
@@ -273,7 +273,7 @@ hipError_t dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* 
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (dw1_g4(g)) {
       const int n = g.n, d = g.d, E = g.E;
-      using Epi = EpiStore<bf16_t, bf16_t, g4::HALF, g4::BN, g4::NTH>;
+      using Epi = EpiStore<bf16_t, bf16_t, g4::EROWS, g4::BN, g4::NTH>;
       GemmShape s{offsets, E, d, 2 * n, 0, 2 * n, 1};
       Operand a{x, row_token, 0, d};
       Operand b{dH, nullptr, 0, 2 * n};
@@ -308,7 +308,7 @@ hipError_t dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (dw2_g4(g)) {
       const int n = g.n, d = g.d, E = g.E;
-      using Epi = EpiStore<bf16_t, bf16_t, g4::HALF, g4::BN, g4::NTH>;
+      using Epi = EpiStore<bf16_t, bf16_t, g4::EROWS, g4::BN, g4::NTH>;
       GemmShape s{offsets, E, n, d, 0, d, 1};
       Operand a{As, nullptr, 0, n};
       Operand b{d_o, row_token, 0, d};

@@ -22,9 +22,12 @@
 //      m/n-contiguous operands: [32 k-rows][256 cols], 512-byte rows, chunk
 //        c of k-row kr in slot c ^ (4 * (kr & 3)); a fragment is two
 //        ds_read_b64_tr_b16 (the LDS transpose read).
-//  * Epilogue: the tile is parked in LDS as fp32 in two halves of 128 rows
-//    (the waves of one m half write, then all 512 threads run the functor on
-//    that half), so the functors of the 128-row kernel apply unchanged.
+//  * Epilogue: the tile is parked in LDS as fp32 in eight passes of 32 rows
+//    (the four waves holding those rows write, then all 512 threads run the
+//    functor on them), so the functors of the 128-row kernel apply
+//    unchanged.  The staging area lies over the last stage only: before the
+//    epilogue of a tile, the first three stages of the workgroup's next tile
+//    are already being loaded, so that tile's start does not wait for memory.
 #pragma once
 
 #include <type_traits>
@@ -37,10 +40,11 @@ namespace g4 {
 constexpr int BM = 256, BN = 256, BK = 32, NS = 4, NTH = 512;
 constexpr int OPB = 256 * BK * 2;            // bytes of one operand tile per stage
 constexpr int STAGE = 2 * OPB;               // 32 KB
-constexpr int HALF = 128;                    // epilogue rows per pass
+constexpr int EROWS = 32;                    // epilogue rows per pass
 constexpr int LDC = BN + 4;                  // fp32 staging pitch (floats)
-constexpr int STAGE_C = HALF * LDC * 4;      // 133120 bytes
-constexpr int SMEM = NS * STAGE > STAGE_C ? NS * STAGE : STAGE_C;
+constexpr int CS_OFF = (NS - 1) * STAGE;     // staging area: over the last stage
+constexpr int STAGE_C = EROWS * LDC * 4;     // 33280 bytes
+constexpr int SMEM = NS * STAGE > CS_OFF + STAGE_C ? NS * STAGE : CS_OFF + STAGE_C;
 constexpr uint32_t OOB = 0x80000000u;        // byte offset past every record count
 constexpr int LPS = 4;                       // 16-byte loads per thread per stage
 
@@ -260,12 +264,12 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     total = s.E * (s.M / BM) * NT;
   }
 
-  float* Cs = reinterpret_cast<float*>(smem);
+  float* Cs = reinterpret_cast<float*>(smem + CS_OFF);
   const char* abase = reinterpret_cast<const char*>(A.ptr);
   const char* bbase = reinterpret_cast<const char*>(B.ptr);
 
-  for (int t = xcd_virtual_id(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
-    TileCtx c;
+  // tile t -> expert, m tile, n tile, rows
+  auto decode = [&](int t, TileCtx& c) {
     c.tid = tid; c.lane = lane; c.wm = wm; c.wn = wn;
     if constexpr (!WGT) {
       const int mg = t / NT;
@@ -288,12 +292,14 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       c.out_row0 = (long long)c.e * s.M + (long long)c.mt * BM;
     }
     c.n0 = c.nt * BN;
-    const int nk = WGT ? (c.segn + BK - 1) / BK : s.K / BK;
+  };
+  auto ksteps = [&](const TileCtx& c) { return WGT ? (c.segn + BK - 1) / BK : s.K / BK; };
 
-    // ---- operand set-up ----
-    __amdgpu_buffer_rsrc_t ra, rb;
-    KCLoad la_kc, lb_kc;
-    MNLoad4 la_mn, lb_mn;
+  // operand loaders (state of the tile whose loads are being issued)
+  __amdgpu_buffer_rsrc_t ra, rb;
+  KCLoad la_kc, lb_kc;
+  MNLoad4 la_mn, lb_mn;
+  auto setup = [&](const TileCtx& c) {
     if constexpr (!WGT) {
       ra = make_rsrc(abase, a_bytes);
       la_kc.setup(w, lane, [&](int r) -> uint32_t {
@@ -323,21 +329,36 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       la_mn.setup_rows(A.idx, c.seg0, c.segn, (uint32_t)A.ld * 2u);
       lb_mn.setup_rows(B.idx, c.seg0, c.segn, (uint32_t)B.ld * 2u);
     }
-    auto issue = [&](int k) {
-      char* st = smem + (k % NS) * STAGE;
-      const int k0 = k * BK;
-      if constexpr (!WGT) {
-        la_kc.issue(ra, st, w, k0);
-        if constexpr (!BMN) lb_kc.issue(rb, st + OPB, w, k0);
-        else lb_mn.issue_w(rb, st + OPB, w, k0);
-      } else {
-        la_mn.next_rows(k0);
-        lb_mn.next_rows(k0);
-        la_mn.dma(ra, st, w);
-        lb_mn.dma(rb, st + OPB, w);
-      }
-    };
+  };
+  auto issue = [&](int k) {
+    char* st = smem + (k % NS) * STAGE;
+    const int k0 = k * BK;
+    if constexpr (!WGT) {
+      la_kc.issue(ra, st, w, k0);
+      if constexpr (!BMN) lb_kc.issue(rb, st + OPB, w, k0);
+      else lb_mn.issue_w(rb, st + OPB, w, k0);
+    } else {
+      la_mn.next_rows(k0);
+      lb_mn.next_rows(k0);
+      la_mn.dma(ra, st, w);
+      lb_mn.dma(rb, st + OPB, w);
+    }
+  };
+  // first stages of a tile (stages 0 .. NS-2, fewer for short reductions)
+  auto prime = [&](const TileCtx& c) {
+    const int nk = ksteps(c);
+    for (int k = 0; k < NS - 1 && k < nk; ++k) issue(k);
+  };
 
+  int t = xcd_virtual_id(blockIdx.x, gridDim.x);
+  TileCtx c;
+  if (t < total) {
+    decode(t, c);
+    setup(c);
+    prime(c);
+  }
+  while (t < total) {
+    const int nk = ksteps(c);
     f32x16_v acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -347,9 +368,13 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     if (nk > 0) {
-      // prologue: stages 0 .. NS-2 in flight, then wait for stage 0
-      for (int k = 0; k < NS - 1 && k < nk; ++k) issue(k);
-      wait_vm<0>();
+      // stage 0 complete: at least LPS data loads were issued after it by
+      // every later stage of this tile and, for tiles after the first, the
+      // previous epilogue's stores came after those (they only add to it)
+      static_assert(NS == 4, "the waits below assume three stages in flight");
+      if (nk >= 3) wait_vm<2 * LPS>();
+      else if (nk == 2) wait_vm<LPS>();
+      else wait_vm<0>();
       __syncthreads();
       Frags<AMN, BMN> f0, f1;
       f0.read(smem, 0, lane, wm, wn);
@@ -365,7 +390,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
         G4_SCHED(0x008, 2);
         if constexpr (decltype(MAIN)::value) {
           // stage k+1 complete: at least the LPS data loads of stage k+2
-          // were issued after its last load (index loads only add to that)
+          // were issued after its last load (other loads only add to that)
           wait_vm<LPS>();
         } else {
           wait_vm<0>();
@@ -387,30 +412,44 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       __syncthreads();  // every wave is done reading the stages
     }
 
-    // ---- epilogue: two halves of 128 rows ----
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      TileCtx ch = c;
-      ch.out_row0 = c.out_row0 + h * HALF;
-      ch.m_valid = min(HALF, c.m_valid - h * HALF);
-      if (ch.m_valid <= 0) break;  // uniform over the workgroup
-      if (wm == h) {
+    // ---- next tile's first stages, then this tile's epilogue ----
+    const int tn = t + gridDim.x;
+    TileCtx cn = c;
+    if (tn < total) {
+      decode(tn, cn);
+      setup(cn);
+      prime(cn);
+    }
+    // eight passes of 32 rows: pass p holds block j = p % 4 of the waves of
+    // m half p / 4
+#pragma unroll 1
+    for (int p = 0; p < BM / EROWS; ++p) {
+      TileCtx cp = c;
+      cp.out_row0 = c.out_row0 + p * EROWS;
+      cp.m_valid = min(EROWS, c.m_valid - p * EROWS);
+      if (cp.m_valid <= 0) break;  // uniform over the workgroup
+      if (wm == (p >> 2)) {
+        const int jp = p & 3;
         const int cl = lane & 31, hl = lane >> 5;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 4; ++j) {
+          if (j != jp) continue;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int eg = 0; eg < 4; ++eg) {
-              float4 v = make_float4(acc[i][j][4 * eg], acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2],
-                                     acc[i][j][4 * eg + 3]);
-              *reinterpret_cast<float4*>(Cs + (32 * j + cl) * LDC + wn * 64 + 32 * i + 8 * eg + 4 * hl) = v;
+              const float4 v = make_float4(acc[i][j][4 * eg], acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2],
+                                           acc[i][j][4 * eg + 3]);
+              *reinterpret_cast<float4*>(Cs + cl * LDC + wn * 64 + 32 * i + 8 * eg + 4 * hl) = v;
             }
+        }
       }
       __syncthreads();
-      Epi::run(ep, s, ch, Cs, nullptr);
+      Epi::run(ep, s, cp, Cs, nullptr);
       __syncthreads();
     }
+    c = cn;
+    t = tn;
   }
 }
 

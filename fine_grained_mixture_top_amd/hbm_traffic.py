@@ -36,6 +36,20 @@ def source_hash() -> str:
 
 def classify(name: str, wgt_seen: dict) -> str:
     """Bench kernel name of one dispatch (None for kernels that are not tracked)."""
+    if "grouped_gemm4_kernel" in name:
+        m = re.search(r"grouped_gemm4_kernel<(true|false), (true|false), (true|false), moe::(\w+)<", name)
+        if not m:
+            return None
+        wgt, bmn, epi = m.group(1) == "true", m.group(2) == "true", m.group(4)
+        if epi == "EpiSwiGLU":
+            return "up"
+        if epi == "EpiDH":
+            return "dh"
+        if wgt:  # dw1 and dw2 share an instantiation: first per step is dw1
+            k = wgt_seen["n"] % 2
+            wgt_seen["n"] += 1
+            return "dw1" if k == 0 else "dw2"
+        return "down" if bmn else "dxt"
     if "grouped_gemm_kernel" in name:
         m = re.search(r"grouped_gemm_kernel<([^,]+), (\d+), (\d+), (true|false), (\d), (true|false), moe::(\w+)<([^>]*)>", name)
         if not m:
