@@ -113,7 +113,7 @@ hipError_t up_swiglu_t(const GemmDims& g, const void* x, const void* w1, const i
 hipError_t up_swiglu_g4(const GemmDims& g, const void* x, const void* w1, const int32_t* row_token,
                         const int32_t* offsets, void* H, void* A, hipStream_t st) {
   const int n = g.n, d = g.d, E = g.E;
-  using Epi = EpiSwiGLU<bf16_t, g4::EROWS, g4::BN, g4::NTH>;
+  using Epi = g4::G4SwiGLU;
   GemmShape s{offsets, E, 0, 2 * n, d, 2 * n, 1};
   Operand a{x, row_token, 0, d};
   Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
@@ -157,11 +157,11 @@ hipError_t down(const GemmDims& g, const void* A, const void* w2, const int32_t*
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (down_g4(g)) {
       const int n = g.n, d = g.d, E = g.E;
-      using Epi = EpiStore<bf16_t, bf16_t, g4::EROWS, g4::BN, g4::NTH>;
+      using Epi = g4::G4Store;
       GemmShape s{offsets, E, 0, d, n, d, 1};
       Operand a{A, nullptr, 0, n};
       Operand b{w2, nullptr, (long long)n * d, d};
-      typename Epi::Params ep{reinterpret_cast<bf16_t*>(Y), d, nullptr};
+      typename Epi::Params ep{reinterpret_cast<bf16_t*>(Y), d};
       return run_gemm4<false, true, false, Epi>(s, a, b, g.cap * n * 2, (size_t)n * d * 2, ep,
                                                 row_tiles_bound(g.cap, E, g4::BM) * (d / g4::BN), st);
     }
@@ -239,11 +239,11 @@ hipError_t dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t*
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (dxt_g4(g)) {
       const int n = g.n, d = g.d, E = g.E;
-      using Epi = EpiStore<bf16_t, bf16_t, g4::EROWS, g4::BN, g4::NTH>;
+      using Epi = g4::G4Store;
       GemmShape s{offsets, E, 0, d, 2 * n, d, 1};
       Operand a{dH, nullptr, 0, 2 * n};
       Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
-      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dXt), d, nullptr};
+      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dXt), d};
       return run_gemm4<false, false, false, Epi>(s, a, b, g.cap * 2 * n * 2, (size_t)d * 2 * n * 2, ep,
                                                  row_tiles_bound(g.cap, E, g4::BM) * (d / g4::BN), st);
     }
@@ -273,11 +273,11 @@ hipError_t dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* 
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (dw1_g4(g)) {
       const int n = g.n, d = g.d, E = g.E;
-      using Epi = EpiStore<bf16_t, bf16_t, g4::EROWS, g4::BN, g4::NTH>;
+      using Epi = g4::G4Store;
       GemmShape s{offsets, E, d, 2 * n, 0, 2 * n, 1};
       Operand a{x, row_token, 0, d};
       Operand b{dH, nullptr, 0, 2 * n};
-      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dW1), 2 * n, nullptr};
+      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dW1), 2 * n};
       return run_gemm4<true, true, false, Epi>(s, a, b, (size_t)g.T * d * 2, g.cap * 2 * n * 2, ep,
                                                (long long)E * (d / g4::BM) * (2 * n / g4::BN), st);
     }
@@ -308,11 +308,11 @@ hipError_t dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (dw2_g4(g)) {
       const int n = g.n, d = g.d, E = g.E;
-      using Epi = EpiStore<bf16_t, bf16_t, g4::EROWS, g4::BN, g4::NTH>;
+      using Epi = g4::G4Store;
       GemmShape s{offsets, E, n, d, 0, d, 1};
       Operand a{As, nullptr, 0, n};
       Operand b{d_o, row_token, 0, d};
-      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dW2), d, nullptr};
+      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dW2), d};
       return run_gemm4<true, true, false, Epi>(s, a, b, g.cap * n * 2, (size_t)g.T * d * 2, ep,
                                                (long long)E * (n / g4::BM) * (d / g4::BN), st);
     }

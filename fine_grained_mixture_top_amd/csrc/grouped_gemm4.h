@@ -44,7 +44,11 @@ constexpr int EROWS = 32;                    // epilogue rows per pass
 constexpr int LDC = BN + 4;                  // fp32 staging pitch (floats)
 constexpr int CS_OFF = (NS - 1) * STAGE;     // staging area: over the last stage
 constexpr int STAGE_C = EROWS * LDC * 4;     // 33280 bytes
-constexpr int SMEM = NS * STAGE > CS_OFF + STAGE_C ? NS * STAGE : CS_OFF + STAGE_C;
+constexpr int WAVE_LDS = 7168;              // private epilogue area per wave
+constexpr int WE_OFF = (NS - 1) * STAGE;     // wave areas: over the last stage and above
+constexpr int SMEM_PASS = NS * STAGE > CS_OFF + STAGE_C ? NS * STAGE : CS_OFF + STAGE_C;
+constexpr int SMEM_WAVE = NS * STAGE > WE_OFF + 8 * WAVE_LDS ? NS * STAGE : WE_OFF + 8 * WAVE_LDS;
+constexpr int SMEM = SMEM_PASS > SMEM_WAVE ? SMEM_PASS : SMEM_WAVE;
 constexpr uint32_t OOB = 0x80000000u;        // byte offset past every record count
 constexpr int LPS = 4;                       // 16-byte loads per thread per stage
 
@@ -212,6 +216,115 @@ __device__ __forceinline__ void mma(f32x16_v (&acc)[2][4], const Frags<AMN, BMN>
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.n[i], f.m[j], acc[i][j], 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// wave-local epilogues: each wave converts its own 128 x 64 block, 32 rows at a
+// time, stages it as bf16 in a private LDS area and stores whole row segments;
+// no workgroup barrier.  (Epilogues that need whole rows, such as the dH one,
+// use the workgroup-wide passes instead.)
+// ---------------------------------------------------------------------------
+
+template <class E, class = void> struct is_wave_epi : std::false_type {};
+template <class E> struct is_wave_epi<E, std::void_t<decltype(E::WAVE)>> : std::bool_constant<E::WAVE> {};
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16), (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16));
+}
+
+// C[row, n0 + col] = acc as bf16.
+struct G4Store {
+  static constexpr bool WAVE = true;
+  struct Params {
+    bf16_t* C;
+    long long ldc;
+  };
+  __device__ __forceinline__ static void run(const Params& p, const TileCtx& c, const f32x16_v (&acc)[2][4],
+                                             char* area) {
+    constexpr int LD = 72;  // [32][64 + 8] bf16
+    bf16_t* L = reinterpret_cast<bf16_t*>(area);
+    const int cl = c.lane & 31, hl = c.lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rb = c.wm * 128 + 32 * j;  // tile row of the block's first row
+      if (rb >= c.m_valid) break;          // uniform over the wave
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int eg = 0; eg < 4; ++eg)
+          *reinterpret_cast<uint2*>(L + cl * LD + 32 * i + 8 * eg + 4 * hl) =
+              pack4(acc[i][j][4 * eg], acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2], acc[i][j][4 * eg + 3]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int v = c.lane + 64 * q, r = v >> 3, ch = v & 7;
+        const uint4 x = *reinterpret_cast<const uint4*>(L + r * LD + ch * 8);
+        if (rb + r < c.m_valid)
+          *reinterpret_cast<uint4*>(p.C + (c.out_row0 + rb + r) * p.ldc + c.n0 + c.wn * 64 + ch * 8) = x;
+      }
+    }
+  }
+};
+
+// Up-projection: the B tile's columns are arranged so that wave wn holds the
+// gate columns j0 + 32 wn .. +31 in its first 32 columns and the matching up
+// columns in its last 32 (j0 = 128 * nt), so gate and up of one element sit in
+// the same lane.  H is rounded to bf16 first and A = silu(G) * U is formed
+// from the rounded values (the backward recomputes A from the cached H).
+struct G4SwiGLU {
+  static constexpr bool WAVE = true;
+  struct Params {
+    bf16_t* H;  // [rows, 2n]
+    bf16_t* A;  // [rows, n]
+    int n;
+  };
+  // tile column of the B tile (chunk-aligned) -> global column of W1
+  __device__ __forceinline__ static int col(int cc, int nt, int n) {
+    const int wv = cc >> 6, cw = cc & 63;
+    const int j = nt * 128 + wv * 32 + (cw & 31);
+    return cw < 32 ? j : n + j;
+  }
+  __device__ __forceinline__ static void run(const Params& p, const TileCtx& c, const f32x16_v (&acc)[2][4],
+                                             char* area) {
+    constexpr int LH = 72, LA = 40;  // H block [32][32 gate + 32 up + 8], A block [32][32 + 8]
+    bf16_t* Lh = reinterpret_cast<bf16_t*>(area);
+    bf16_t* La = Lh + 32 * LH;
+    const int cl = c.lane & 31, hl = c.lane >> 5;
+    const int j0 = c.nt * 128 + c.wn * 32;
+    const long long ldh = 2LL * p.n;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rb = c.wm * 128 + 32 * j;
+      if (rb >= c.m_valid) break;
+#pragma unroll
+      for (int eg = 0; eg < 4; ++eg) {
+        float g[4], u[4], a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          g[e] = through<bf16_t>(acc[0][j][4 * eg + e]);
+          u[e] = through<bf16_t>(acc[1][j][4 * eg + e]);
+          a[e] = g[e] * sigmoidf_(g[e]) * u[e];
+        }
+        const int cc = 8 * eg + 4 * hl;
+        *reinterpret_cast<uint2*>(Lh + cl * LH + cc) = pack4(g[0], g[1], g[2], g[3]);
+        *reinterpret_cast<uint2*>(Lh + cl * LH + 32 + cc) = pack4(u[0], u[1], u[2], u[3]);
+        *reinterpret_cast<uint2*>(La + cl * LA + cc) = pack4(a[0], a[1], a[2], a[3]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // H: 32 rows x (4 gate + 4 up) chunks
+        const int v = c.lane + 64 * q, r = v >> 3, ch = v & 7;
+        const uint4 x = *reinterpret_cast<const uint4*>(Lh + r * LH + ch * 8);
+        const int gc = ch < 4 ? j0 + ch * 8 : p.n + j0 + (ch - 4) * 8;
+        if (rb + r < c.m_valid) *reinterpret_cast<uint4*>(p.H + (c.out_row0 + rb + r) * ldh + gc) = x;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {  // A: 32 rows x 4 chunks
+        const int v = c.lane + 64 * q, r = v >> 2, ch = v & 3;
+        const uint4 x = *reinterpret_cast<const uint4*>(La + r * LA + ch * 8);
+        if (rb + r < c.m_valid)
+          *reinterpret_cast<uint4*>(p.A + (c.out_row0 + rb + r) * (long long)p.n + j0 + ch * 8) = x;
+      }
+    }
+  }
+};
+
 #define G4_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
 
 // ---------------------------------------------------------------------------
@@ -220,7 +333,8 @@ __device__ __forceinline__ void mma(f32x16_v (&acc)[2][4], const Frags<AMN, BMN>
 
 // WGT: weight-gradient mode (both operands m/n-contiguous segment rows);
 // otherwise ROW mode with A k-contiguous and B [N][K] (BMN = false) or [K][N]
-// (BMN = true).  PAIRED: B columns are gate j0.. then up n + j0.. (SwiGLU).
+// (BMN = true).  PAIRED: B columns arranged for G4SwiGLU (gate and up of the
+// same j in the same wave).
 template <bool WGT, bool BMN, bool PAIRED, class Epi>
 __global__ void __launch_bounds__(NTH, 1)
 grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32_t b_bytes,
@@ -313,9 +427,8 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       if constexpr (!BMN) {
         lb_kc.setup(w, lane, [&](int r) -> uint32_t { return (uint32_t)(c.n0 + r) * (uint32_t)B.ld * 2u; });
       } else {
-        const int half = s.N / 2, j0 = c.nt * (BN / 2);
         lb_mn.setup_cols(w, lane, [&](int cc) {
-          if (PAIRED) return cc < BN / 2 ? j0 + cc : half + j0 + (cc - BN / 2);
+          if constexpr (PAIRED) return G4SwiGLU::col(cc, c.nt, s.N / 2);
           return c.n0 + cc;
         });
         lb_mn.ldb = (uint32_t)B.ld * 2u;
@@ -420,6 +533,9 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       setup(cn);
       prime(cn);
     }
+    if constexpr (is_wave_epi<Epi>::value) {
+      Epi::run(ep, c, acc, smem + WE_OFF + w * WAVE_LDS);
+    } else {
     // eight passes of 32 rows: pass p holds block j = p % 4 of the waves of
     // m half p / 4
 #pragma unroll 1
@@ -447,6 +563,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       __syncthreads();
       Epi::run(ep, s, cp, Cs, nullptr);
       __syncthreads();
+    }
     }
     c = cn;
     t = tn;
