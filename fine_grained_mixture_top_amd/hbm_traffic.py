@@ -37,13 +37,13 @@ def source_hash() -> str:
 def classify(name: str, wgt_seen: dict) -> str:
     """Bench kernel name of one dispatch (None for kernels that are not tracked)."""
     if "grouped_gemm4_kernel" in name:
-        m = re.search(r"grouped_gemm4_kernel<(true|false), (true|false), (true|false), moe::(\w+)<", name)
+        m = re.search(r"grouped_gemm4_kernel<(true|false), (true|false), (true|false), moe::(?:g4::)?(\w+)", name)
         if not m:
             return None
         wgt, bmn, epi = m.group(1) == "true", m.group(2) == "true", m.group(4)
-        if epi == "EpiSwiGLU":
+        if epi in ("EpiSwiGLU", "G4SwiGLU"):
             return "up"
-        if epi == "EpiDH":
+        if epi in ("EpiDH", "G4DH"):
             return "dh"
         if wgt:  # dw1 and dw2 share an instantiation: first per step is dw1
             k = wgt_seen["n"] % 2
