@@ -23,6 +23,7 @@ if ROOT not in sys.path:
 MFMA_PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16
 MFMA_PEAK_F32 = 157.3     # TFLOP/s, MI355X fp32 (MFMA fp32 reuses this figure)
 HBM_PEAK = 8000.0         # GB/s
+CPU_FLOP_BUDGET = 4.0e12  # useful FLOPs of the default CPU oracle sample
 
 
 def parse():
@@ -32,8 +33,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fg7b_bf16")
     ap.add_argument("--round-mode", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=32768,
-                    help="tokens of the oracle's CPU baseline sample (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=-1,
+                    help="tokens of the oracle's CPU baseline sample (0 = skip, -1 = as many as "
+                         "fit a 4 TFLOP budget, about 20 s of fp64 work, capped at the workload's T)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many bytes "
                          "(calibration dispatch for HBM counter passes)")
@@ -73,6 +75,24 @@ def kernel_work(name, w, P, es):
         "wr_t": 2 * E * d * es, "db": P * 4,
     }
     return float(bytes_.get(name, 0)), "byte"
+
+
+def memory_report(w, L, es):
+    """Bytes the layer keeps between forward and backward (the cached H plus the
+    routing metadata), the transient workspaces, and what a layer that caches
+    the usual backward activations (gathered X, H, A and Y per routed row)
+    would keep instead."""
+    from fine_grained_mixture_top_amd import binding as B
+    P = w.P
+    cap = int(L.routing.cap)
+    routing = sum(t.numel() * t.element_size() for t in L.routing.tensors())
+    return {
+        "cached_bytes": cap * 2 * w.n * es + routing,
+        "h_cache_bytes": cap * 2 * w.n * es,
+        "workspace_fwd_bytes": B.moe_workspace_bytes(L.desc, B.MOE_WS_FWD),
+        "workspace_bwd_bytes": B.moe_workspace_bytes(L.desc, B.MOE_WS_BWD),
+        "naive_cache_bytes": P * (w.d + 2 * w.n + w.n + w.d) * es,
+    }
 
 
 def cpu_baseline(w, a, tokens):
@@ -197,9 +217,13 @@ def main():
         "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
                      "unit": dk["unit"], "frac": dk["frac"], "traffic": measured_traffic(w.name, dom)},
         "kernels": {k: {kk: v for kk, v in d.items() if kk != "work"} for k, d in kernels.items()},
+        "memory": memory_report(w, L, es),
     }
-    if args.cpu_tokens > 0:
-        out["cpu_baseline"] = cpu_baseline(w, a, args.cpu_tokens)
+    cpu_tokens = args.cpu_tokens
+    if cpu_tokens < 0:
+        cpu_tokens = max(1, min(w.T, int(CPU_FLOP_BUDGET // (18.0 * w.K * w.d * w.n))))
+    if cpu_tokens > 0:
+        out["cpu_baseline"] = cpu_baseline(w, a, cpu_tokens)
     print(json.dumps(out), flush=True)
 
 

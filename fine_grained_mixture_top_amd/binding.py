@@ -214,7 +214,11 @@ class Routing:
         self.row_gate = z(cap, f32)
         self.tok_ptr = z(T + 1, i32)
         self.tok_row = z(cap, i32)
-        self.c = MoeRouting(*[t.data_ptr() for t in (getattr(self, f) for f in ROUTING_FIELDS)])
+        self.c = MoeRouting(*[t.data_ptr() for t in self.tensors()])
+
+    def tensors(self):
+        """The routing buffers, in the order of the C struct."""
+        return [getattr(self, f) for f in ROUTING_FIELDS]
 
 
 def workspace(desc: MoeDesc, which: int, device="cuda") -> torch.Tensor:

@@ -67,6 +67,8 @@ WORKLOADS = {
     "zipf_e256": Workload("zipf_e256", T=32768, d=2048, E=256, n=256, K=8, dtype="bf16",
                           zipf_s=1.1),
     "prod_e256": Workload("prod_e256", T=16384, d=7168, E=256, n=2048, K=8, dtype="bf16"),
+    # the OLMoE-shaped layer the pages break down per kernel
+    "olmoe_bf16": Workload("olmoe_bf16", T=32768, d=2048, E=64, n=1024, K=8, dtype="bf16"),
 }
 
 

@@ -79,9 +79,14 @@ def check_routing(L, w, rt, x64, wr64, bias):
     bad_e = np.nonzero(np.any(g_mem != rt["member"], axis=0))[0]
     bad_t = np.nonzero(np.any(g_mem != rt["member"], axis=1))[0]
     if len(flip) == 0:
-        # identical decisions: every integer output must be identical
+        # identical sets: the slot order within a token may differ only where
+        # two selected scores are within the measured score error of each other
         r = L.routing
-        assert np.array_equal(g_idx, o_idx)
+        order = np.nonzero(np.any(g_idx != o_idx, axis=1))[0]
+        for t in order:
+            s = np.sort(z32[t][o_idx[t]])[::-1]
+            assert np.min(s[:-1] - s[1:]) <= 2.0 * err[t].max() + 1e-7, (t, g_idx[t], o_idx[t])
+        assert len(order) <= max(3, w.T // 10000), f"{len(order)} order flips"
         assert np.array_equal(host_int(r.counts), rt["counts"])
         assert np.array_equal(host_int(r.counts_raw), rt["counts_raw"])
         assert np.array_equal(host_int(r.offsets), rt["offsets"])
@@ -126,7 +131,7 @@ def ws_rows(L, item, rows, width, dtype):
 
 
 FULL = [("fg7b_bf16", 0), ("sweep_e32", 0), ("sweep_e64", 0), ("sweep_e128", 0), ("sweep_e256", 0),
-        ("zipf_e256", 0), ("zipf_e256", 1), ("zipf_e256", 2)]
+        ("zipf_e256", 0), ("zipf_e256", 1), ("zipf_e256", 2), ("olmoe_bf16", 0)]
 
 
 @pytest.mark.parametrize("name,mode", FULL, ids=[f"{n}-round{m}" for n, m in FULL])
