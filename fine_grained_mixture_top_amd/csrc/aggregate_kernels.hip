@@ -220,17 +220,29 @@ k_router_grad(const float* __restrict__ dS_part, int nparts, const float* __rest
 }
 
 // db[e] = sum of dz over expert e's rows (fixed per-thread split and tree).
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(1024)
 k_bias_grad(const float* __restrict__ dz_row, const int32_t* __restrict__ offsets, float* __restrict__ db) {
-  __shared__ float red[4];
+  __shared__ float red[16];
   const int e = blockIdx.x;
   const int r0 = offsets[e], r1 = offsets[e + 1];
-  float s = 0.f;
-  for (int r = r0 + threadIdx.x; r < r1; r += 256) s += dz_row[r];
-  s = wave_sum(s);
+  // four independent partial sums per thread keep four loads in flight
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int r = r0 + threadIdx.x;
+  for (; r + 3 * 1024 < r1; r += 4 * 1024) {
+    s0 += dz_row[r];
+    s1 += dz_row[r + 1024];
+    s2 += dz_row[r + 2 * 1024];
+    s3 += dz_row[r + 3 * 1024];
+  }
+  for (; r < r1; r += 1024) s0 += dz_row[r];
+  float s = wave_sum((s0 + s1) + (s2 + s3));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) db[e] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < 16; ++w) t += red[w];
+    db[e] = t;
+  }
 }
 
 // dst[c][r] = src[r][c]
@@ -291,7 +303,7 @@ hipError_t launch_router_grad(int dtype, const float* dS_part, int nparts, const
 }
 
 hipError_t launch_bias_grad(const float* dz_row, const int32_t* offsets, int E, float* db, hipStream_t st) {
-  hipLaunchKernelGGL(k_bias_grad, dim3(E), dim3(256), 0, st, dz_row, offsets, db);
+  hipLaunchKernelGGL(k_bias_grad, dim3(E), dim3(1024), 0, st, dz_row, offsets, db);
   return hipGetLastError();
 }
 

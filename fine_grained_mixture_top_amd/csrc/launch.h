@@ -67,9 +67,10 @@ struct RouteBufs {
 int mask_pitch(int T);
 struct RouteScratch {
   uint8_t* mask;       // [E][pitch] membership bytes
-  float* scoresT;      // [E][T] scores, expert-major (token rounding only)
+  float* scoresT;      // [E][pitch] scores, expert-major (token rounding only)
   int32_t* rowmap;     // [E][pitch] row of (e, t)
-  int32_t* tokcnt;     // [T]
+  int32_t* tokcnt;     // [T] rows per token (token rounding only)
+  float* tstat;        // [2][T] set-softmax max and sum per token (token rounding only)
 };
 hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int T, int E, int K,
                                int tile, int round_mode, uint64_t round_seed, hipStream_t st);

@@ -49,12 +49,13 @@ struct Layout {
 Layout route_layout(const moe_desc* d) {
   Layout L{};
   size_t o = 0;
-  const size_t TE = (size_t)d->T * d->E;
   const size_t TEp = (size_t)mask_pitch(d->T) * d->E;
+  const size_t tr = d->round_mode ? 1 : 0;
   L.off[0] = o; o = up(o + TEp);                                  // mask
-  L.off[1] = o; o = up(o + (d->round_mode ? TE * 4 : 0));         // scoresT
+  L.off[1] = o; o = up(o + tr * TEp * 4);                         // scoresT
   L.off[2] = o; o = up(o + TEp * 4);                              // rowmap
-  L.off[3] = o; o = up(o + (size_t)d->T * 4);                     // tokcnt
+  L.off[3] = o; o = up(o + tr * (size_t)d->T * 4);                // tokcnt
+  L.off[4] = o; o = up(o + tr * (size_t)d->T * 8);                // tstat
   L.total = o;
   return L;
 }
@@ -181,8 +182,9 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_r, const float*
   RouteBufs rb{routing->logits,     routing->topk_idx,  routing->topk_gate, routing->counts,
                routing->counts_raw, routing->offsets,   routing->tile_offsets, routing->row_token,
                routing->row_expert, routing->row_gate,  routing->tok_ptr,   routing->tok_row};
-  RouteScratch sc{(uint8_t*)(w + L.off[0]), desc->round_mode ? (float*)(w + L.off[1]) : nullptr,
-                  (int32_t*)(w + L.off[2]), (int32_t*)(w + L.off[3])};
+  const bool tr = desc->round_mode != 0;
+  RouteScratch sc{(uint8_t*)(w + L.off[0]), tr ? (float*)(w + L.off[1]) : nullptr, (int32_t*)(w + L.off[2]),
+                  tr ? (int32_t*)(w + L.off[3]) : nullptr, tr ? (float*)(w + L.off[4]) : nullptr};
   MOE_TRY(MOE_K_ROUTE_SELECT, launch_route_select(rb, sc, desc->T, desc->E, desc->K, desc->tile,
                                                   desc->round_mode, desc->round_seed, st));
   return MOE_OK;

@@ -174,8 +174,9 @@ k_expert_count(const uint8_t* __restrict__ mask, int mpitch, int32_t* __restrict
   }
 }
 
-// scores [T][E] -> scoresT [E][T]
-__global__ void k_transpose_scores(const float* __restrict__ in, int T, int E, float* __restrict__ out) {
+// scores [T][E] -> scoresT [E][pitch]
+__global__ void k_transpose_scores(const float* __restrict__ in, int T, int E, int pitch,
+                                   float* __restrict__ out) {
   __shared__ float tile[32][33];
   const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 256 threads: ty 0..7
@@ -186,21 +187,56 @@ __global__ void k_transpose_scores(const float* __restrict__ in, int T, int E, f
   __syncthreads();
   for (int r = ty; r < 32; r += 8) {
     int e = e0 + r, t = t0 + tx;
-    if (t < T && e < E) out[(size_t)e * T + t] = tile[tx][r];
+    if (t < T && e < E) out[(size_t)e * pitch + t] = tile[tx][r];
+  }
+}
+
+// Token rounding works on 16-token groups: one 16-byte load of membership
+// bytes and four 16-byte loads of expert-major scores per thread.
+constexpr int TR_THREADS = 1024;
+constexpr int TR_GROUP = 16;
+
+// Candidate bits of one 16-token group (bit i: token t0 + i is a candidate,
+// i.e. inside [0, T) with membership byte == want) and their score keys.
+struct TrGroup {
+  uint4 mbytes;
+  uint32_t cand;
+  uint32_t key[TR_GROUP];
+};
+
+__device__ __forceinline__ void tr_load(const uint8_t* m, const float* z, int t0, int T, uint32_t want,
+                                        TrGroup& g) {
+  g.mbytes = *reinterpret_cast<const uint4*>(m + t0);
+  const uint32_t w[4] = {g.mbytes.x, g.mbytes.y, g.mbytes.z, g.mbytes.w};
+  g.cand = 0;
+#pragma unroll
+  for (int i = 0; i < TR_GROUP; ++i)
+    if (t0 + i < T && ((w[i >> 2] >> (8 * (i & 3))) & 0xffu) == want) g.cand |= 1u << i;
+  if (g.cand) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(z + t0 + 4 * q);
+      g.key[4 * q + 0] = score_key(v.x);
+      g.key[4 * q + 1] = score_key(v.y);
+      g.key[4 * q + 2] = score_key(v.z);
+      g.key[4 * q + 3] = score_key(v.w);
+    }
   }
 }
 
 // Token rounding of one expert per workgroup.  c = plain count; r = rounded
 // count.  r < c: keep the r best-ranked routed tokens; r > c: add the r - c
 // best-ranked tokens not routed to this expert.  Rank: score descending, then
-// token id ascending.  The threshold score is found by an MSB-first radix
-// select over the order-preserving score keys; equal-key candidates are then
-// taken in ascending token order.
-__global__ void __launch_bounds__(256)
+// token id ascending.  The threshold key is found by an MSB-first radix select
+// over the order-preserving score keys (digits of 12, 10 and 10 bits, counted
+// in an LDS histogram); candidates with exactly the threshold key are then
+// taken in ascending token order.  Counts are exact, so the result does not
+// depend on the order in which the histogram atomics land.
+__global__ void __launch_bounds__(TR_THREADS)
 k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int mpitch,
               const int32_t* __restrict__ counts_raw, int T, int M, int mode, uint64_t seed) {
-  __shared__ int hist[256];
-  __shared__ int sh[8];
+  __shared__ int hist[4096];
+  __shared__ int sh[20];
   const int e = blockIdx.x;
   const int c = counts_raw[e];
   const int rem = c % M;
@@ -220,59 +256,96 @@ k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int
     if (r > T) r = down;
   }
   const bool drop = r < c;
-  const uint8_t want = drop ? 1 : 0;         // candidates: routed (drop) or not (add)
-  const int k_sel = drop ? r : r - c;        // candidates to select
+  const uint32_t want = drop ? 1u : 0u;  // candidates: routed (drop) or not (add)
+  const int k_sel = drop ? r : r - c;    // candidates to select
   uint8_t* m = mask + (size_t)e * mpitch;
-  const float* z = scoresT + (size_t)e * T;
+  const float* z = scoresT + (size_t)e * mpitch;
+  const int tid = threadIdx.x;
+  constexpr int SWEEP = TR_THREADS * TR_GROUP;
 
   uint32_t prefix = 0, pmask = 0;
   int kk = k_sel;
   if (k_sel > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = threadIdx.x; i < 256; i += 256) hist[i] = 0;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int width = pass == 0 ? 12 : 10;
+      const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+      const int nb = 1 << width;
+      for (int i = tid; i < nb; i += TR_THREADS) hist[i] = 0;
       __syncthreads();
-      for (int t = threadIdx.x; t < T; t += 256) {
-        if (m[t] == want) {
-          uint32_t key = score_key(z[t]);
-          if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      for (int base = 0; base < mpitch; base += SWEEP) {
+        const int t0 = base + tid * TR_GROUP;
+        if (t0 >= mpitch) continue;
+        TrGroup g;
+        tr_load(m, z, t0, T, want, g);
+#pragma unroll
+        for (int i = 0; i < TR_GROUP; ++i)
+          if (((g.cand >> i) & 1u) && (g.key[i] & pmask) == prefix)
+            atomicAdd(&hist[(g.key[i] >> shift) & (nb - 1)], 1);
+      }
+      __syncthreads();
+      // Bins in descending order: thread tid owns bins nb-1-per*tid down to
+      // nb-per*(tid+1); a scan in thread order counts the candidates above.
+      const int per = nb / TR_THREADS;
+      int cnt[4] = {0, 0, 0, 0};
+      int s = 0;
+      for (int j = 0; j < per; ++j) {
+        cnt[j] = hist[nb - 1 - per * tid - j];
+        s += cnt[j];
+      }
+      int tot;
+      int above = block_scan1024(s, sh, &tot);
+      if (above < kk && above + s >= kk) {
+        for (int j = 0; j < per; ++j) {
+          if (above + cnt[j] >= kk) {
+            sh[16] = nb - 1 - per * tid - j;
+            sh[17] = kk - above;
+            break;
+          }
+          above += cnt[j];
         }
       }
       __syncthreads();
-      if (threadIdx.x == 0) {
-        int above = 0, dsel = 0;
-        for (int dgt = 255; dgt >= 0; --dgt) {
-          if (above + hist[dgt] >= kk) { dsel = dgt; break; }
-          above += hist[dgt];
-        }
-        sh[0] = dsel;
-        sh[1] = kk - above;
-      }
-      __syncthreads();
-      prefix |= (uint32_t)sh[0] << shift;
-      pmask |= 0xffu << shift;
-      kk = sh[1];
+      prefix |= (uint32_t)sh[16] << shift;
+      pmask |= (uint32_t)(nb - 1) << shift;
+      kk = sh[17];
       __syncthreads();
     }
   }
-  // prefix = threshold key; kk = how many equal-key candidates to take
+  // prefix = threshold key; kk = how many threshold-key candidates to take
   int carry = 0;
-  for (int base = 0; base < T; base += 256) {
-    const int t = base + threadIdx.x;
-    bool cand = false, gt = false, eq = false;
-    if (t < T) {
-      cand = m[t] == want;
-      if (cand && k_sel > 0) {
-        uint32_t key = score_key(z[t]);
-        gt = key > prefix;
-        eq = key == prefix;
+  for (int base = 0; base < mpitch; base += SWEEP) {
+    const int t0 = base + tid * TR_GROUP;
+    TrGroup g;
+    g.cand = 0;
+    uint32_t gt = 0, eq = 0;
+    if (t0 < mpitch) {
+      tr_load(m, z, t0, T, want, g);
+      if (k_sel > 0) {
+#pragma unroll
+        for (int i = 0; i < TR_GROUP; ++i)
+          if ((g.cand >> i) & 1u) {
+            if (g.key[i] > prefix) gt |= 1u << i;
+            if (g.key[i] == prefix) eq |= 1u << i;
+          }
       }
     }
     int tot;
-    const int rank = block_scan256(eq ? 1 : 0, sh, &tot);
-    const bool sel = gt || (eq && carry + rank < kk);
-    if (t < T && cand) {
-      if (drop && !sel) m[t] = 0;
-      if (!drop && sel) m[t] = 1;
+    int run = carry + block_scan1024(__popc(eq), sh, &tot);
+    uint32_t sel = gt;
+#pragma unroll
+    for (int i = 0; i < TR_GROUP; ++i)
+      if ((eq >> i) & 1u) {
+        if (run < kk) sel |= 1u << i;
+        ++run;
+      }
+    // drop: unselected candidates leave; add: selected candidates join
+    const uint32_t flip = drop ? (g.cand & ~sel) : (g.cand & sel);
+    if (flip) {
+      uint32_t w[4] = {g.mbytes.x, g.mbytes.y, g.mbytes.z, g.mbytes.w};
+#pragma unroll
+      for (int i = 0; i < TR_GROUP; ++i)
+        if ((flip >> i) & 1u) w[i >> 2] ^= 1u << (8 * (i & 3));
+      *reinterpret_cast<uint4*>(m + t0) = make_uint4(w[0], w[1], w[2], w[3]);
     }
     carry += tot;
   }
@@ -300,24 +373,22 @@ k_scan_experts(const int32_t* __restrict__ counts, int E, int tile, int32_t* __r
 
 // Rows of expert e: its member tokens in ascending order, at offsets[e].
 // Each thread takes 16 consecutive tokens (one 16-byte mask load) per sweep.
-// rowmap[e][t] = row of (e, t); tokcnt (token rounding only) counts rows per
-// token.
-__global__ void __launch_bounds__(256)
-k_compact(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restrict__ offsets, int T,
-          int32_t* __restrict__ row_token, int32_t* __restrict__ row_expert,
-          int32_t* __restrict__ rowmap, int32_t* __restrict__ tokcnt) {
-  __shared__ int sh[8];
+// rowmap[e][t] = row of (e, t).
+__global__ void __launch_bounds__(1024)
+k_compact(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restrict__ offsets,
+          int32_t* __restrict__ row_token, int32_t* __restrict__ row_expert, int32_t* __restrict__ rowmap) {
+  __shared__ int sh[16];
   const int e = blockIdx.x;
   const uint8_t* m = mask + (size_t)e * mpitch;
   int32_t* rm = rowmap + (size_t)e * mpitch;
   int carry = offsets[e];
-  for (int base = 0; base < mpitch; base += 256 * 16) {
+  for (int base = 0; base < mpitch; base += 1024 * 16) {
     const int t0 = base + threadIdx.x * 16;
     uint4 u = make_uint4(0, 0, 0, 0);
     if (t0 < mpitch) u = *reinterpret_cast<const uint4*>(m + t0);
     const int cnt = __popc(u.x) + __popc(u.y) + __popc(u.z) + __popc(u.w);
     int tot;
-    int row = carry + block_scan256(cnt, sh, &tot);
+    int row = carry + block_scan1024(cnt, sh, &tot);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -326,7 +397,6 @@ k_compact(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restric
         row_token[row] = t;
         row_expert[row] = e;
         rm[t] = row;
-        if (tokcnt) atomicAdd(&tokcnt[t], 1);
         ++row;
       }
     }
@@ -360,48 +430,118 @@ k_tok_fill_topk(const int32_t* __restrict__ topk_idx, const float* __restrict__ 
   }
 }
 
-// tok_ptr = exclusive scan of per-token row counts (one 1024-thread block,
-// each thread a contiguous run of tokens).
+// Per-token pass over the final membership (token rounding only).  A
+// workgroup takes 64 tokens (one per lane); wave s of its four takes the
+// contiguous expert range [s*ceil(E/4), (s+1)*ceil(E/4)), so the waves'
+// results in wave order follow ascending expert id.
+struct TokSlice {
+  int lo, hi;
+};
+__device__ __forceinline__ TokSlice tok_slice(int E, int s) {
+  const int q = (E + 3) / 4;
+  const int lo = min(E, s * q);
+  return TokSlice{lo, min(E, lo + q)};
+}
+
+// tokcnt[t] = rows of token t; tstat[t], tstat[T + t] = max and sum of
+// exp(score - max) over the token's final expert set (the set softmax).
+__global__ void __launch_bounds__(256)
+k_tok_stats(const uint8_t* __restrict__ mask, int mpitch, const float* __restrict__ scoresT, int T, int E,
+            int32_t* __restrict__ tokcnt, float* __restrict__ tstat) {
+  __shared__ float smx[4][64], ssum[4][64];
+  __shared__ int scnt[4][64];
+  const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
+  const int t = blockIdx.x * 64 + lane;
+  const TokSlice sl = tok_slice(E, s);
+  int cnt = 0;
+  float mx = -INFINITY, sum = 0.f;
+  if (t < T) {
+#pragma unroll 8
+    for (int e = sl.lo; e < sl.hi; ++e) {
+      if (mask[(size_t)e * mpitch + t]) {
+        const float z = scoresT[(size_t)e * mpitch + t];
+        ++cnt;
+        if (z > mx) {
+          sum = sum * __expf(mx - z) + 1.f;
+          mx = z;
+        } else {
+          sum += __expf(z - mx);
+        }
+      }
+    }
+  }
+  smx[s][lane] = mx;
+  ssum[s][lane] = sum;
+  scnt[s][lane] = cnt;
+  __syncthreads();
+  if (s != 0 || t >= T) return;
+  float M = smx[0][lane];
+  int C = scnt[0][lane];
+  for (int j = 1; j < 4; ++j) {
+    M = fmaxf(M, smx[j][lane]);
+    C += scnt[j][lane];
+  }
+  float S = 0.f;
+  for (int j = 0; j < 4; ++j)
+    if (scnt[j][lane]) S += ssum[j][lane] * __expf(smx[j][lane] - M);
+  tokcnt[t] = C;
+  tstat[t] = M;
+  tstat[(size_t)T + t] = S;
+}
+
+// tok_ptr = exclusive scan of per-token row counts (one 1024-thread block;
+// each sweep takes 4096 consecutive tokens, four per thread).
 __global__ void __launch_bounds__(1024)
 k_tok_scan(const int32_t* __restrict__ tokcnt, int T, int32_t* __restrict__ tok_ptr) {
   __shared__ int lds[16];
-  const int per = (T + 1023) / 1024;
-  const int t0 = threadIdx.x * per;
-  int s = 0;
-  for (int i = 0; i < per; ++i)
-    if (t0 + i < T) s += tokcnt[t0 + i];
-  int tot;
-  int run = block_scan1024(s, lds, &tot);
-  for (int i = 0; i < per; ++i)
-    if (t0 + i < T) {
-      tok_ptr[t0 + i] = run;
-      run += tokcnt[t0 + i];
-    }
-  if (threadIdx.x == 0) tok_ptr[T] = tot;
+  int carry = 0;
+  for (int base = 0; base < T; base += 4096) {
+    const int t0 = base + threadIdx.x * 4;
+    int v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = t0 + j < T ? tokcnt[t0 + j] : 0;
+    int tot;
+    int run = carry + block_scan1024(v[0] + v[1] + v[2] + v[3], lds, &tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (t0 + j < T) {
+        tok_ptr[t0 + j] = run;
+        run += v[j];
+      }
+    carry += tot;
+  }
+  if (threadIdx.x == 0) tok_ptr[T] = carry;
 }
 
 // Token rounding: per token, its rows in ascending expert order and each
 // row's gate, the softmax of the token's scores over its final set.
 __global__ void __launch_bounds__(256)
 k_tok_fill(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restrict__ rowmap,
-           const float* __restrict__ scores, const int32_t* __restrict__ tok_ptr, int T, int E,
-           int32_t* __restrict__ tok_row, float* __restrict__ row_gate) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
-  const float* z = scores + (size_t)t * E;
-  float mx = -INFINITY;
-  for (int e = 0; e < E; ++e)
-    if (mask[(size_t)e * mpitch + t]) mx = fmaxf(mx, z[e]);
-  float sum = 0.f;
-  for (int e = 0; e < E; ++e)
-    if (mask[(size_t)e * mpitch + t]) sum += __expf(z[e] - mx);
+           const float* __restrict__ scoresT, const float* __restrict__ tstat,
+           const int32_t* __restrict__ tok_ptr, int T, int E, int32_t* __restrict__ tok_row,
+           float* __restrict__ row_gate) {
+  __shared__ int scnt[4][64];
+  const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
+  const int t = blockIdx.x * 64 + lane;
+  const TokSlice sl = tok_slice(E, s);
+  int cnt = 0;
+  if (t < T) {
+#pragma unroll 8
+    for (int e = sl.lo; e < sl.hi; ++e) cnt += mask[(size_t)e * mpitch + t];
+  }
+  scnt[s][lane] = cnt;
+  __syncthreads();
+  if (t >= T || cnt == 0) return;
   int j = tok_ptr[t];
-  for (int e = 0; e < E; ++e)
+  for (int q = 0; q < s; ++q) j += scnt[q][lane];
+  const float mx = tstat[t], inv = 1.f / tstat[(size_t)T + t];
+  for (int e = sl.lo; e < sl.hi; ++e) {
     if (mask[(size_t)e * mpitch + t]) {
       const int row = rowmap[(size_t)e * mpitch + t];
       tok_row[j++] = row;
-      row_gate[row] = __expf(z[e] - mx) / sum;
+      row_gate[row] = __expf(scoresT[(size_t)e * mpitch + t] - mx) * inv;
     }
+  }
 }
 
 }  // namespace
@@ -429,26 +569,26 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
     hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.counts_raw,
                        (int32_t*)nullptr);
     hipLaunchKernelGGL(k_transpose_scores, dim3((T + 31) / 32, (E + 31) / 32), dim3(256), 0, st,
-                       rb.logits, T, E, sc.scoresT);
-    hipLaunchKernelGGL(k_token_round, dim3(E), dim3(256), 0, st, sc.scoresT, sc.mask, mp, rb.counts_raw,
-                       T, tile, round_mode, round_seed);
+                       rb.logits, T, E, mp, sc.scoresT);
+    hipLaunchKernelGGL(k_token_round, dim3(E), dim3(TR_THREADS), 0, st, sc.scoresT, sc.mask, mp,
+                       rb.counts_raw, T, tile, round_mode, round_seed);
     hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.counts,
                        (int32_t*)nullptr);
   }
   hipLaunchKernelGGL(k_scan_experts, dim3(1), dim3(1024), 0, st, rb.counts, E, tile, rb.offsets,
                      rb.tile_offsets);
+  hipLaunchKernelGGL(k_compact, dim3(E), dim3(1024), 0, st, sc.mask, mp, rb.offsets, rb.row_token,
+                     rb.row_expert, sc.rowmap);
   if (round_mode == 0) {
-    hipLaunchKernelGGL(k_compact, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.offsets, T, rb.row_token,
-                       rb.row_expert, sc.rowmap, (int32_t*)nullptr);
     hipLaunchKernelGGL(k_tok_fill_topk, dim3((T + 255) / 256), dim3(256), 0, st, rb.topk_idx, rb.topk_gate,
                        sc.rowmap, mp, T, K, rb.tok_row, rb.row_gate);
   } else {
-    if ((err = hipMemsetAsync(sc.tokcnt, 0, (size_t)T * sizeof(int32_t), st)) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_compact, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.offsets, T, rb.row_token,
-                       rb.row_expert, sc.rowmap, sc.tokcnt);
+    const unsigned blocks = (unsigned)((T + 63) / 64);
+    hipLaunchKernelGGL(k_tok_stats, dim3(blocks), dim3(256), 0, st, sc.mask, mp, sc.scoresT, T, E, sc.tokcnt,
+                       sc.tstat);
     hipLaunchKernelGGL(k_tok_scan, dim3(1), dim3(1024), 0, st, sc.tokcnt, T, rb.tok_ptr);
-    hipLaunchKernelGGL(k_tok_fill, dim3((T + 255) / 256), dim3(256), 0, st, sc.mask, mp, sc.rowmap, rb.logits,
-                       rb.tok_ptr, T, E, rb.tok_row, rb.row_gate);
+    hipLaunchKernelGGL(k_tok_fill, dim3(blocks), dim3(256), 0, st, sc.mask, mp, sc.rowmap, sc.scoresT,
+                       sc.tstat, rb.tok_ptr, T, E, rb.tok_row, rb.row_gate);
   }
   return hipGetLastError();
 }
