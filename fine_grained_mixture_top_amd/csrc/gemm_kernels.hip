@@ -252,6 +252,230 @@ hipError_t dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t*
   return dxt_t<T, Cfg<T>::SMALL>(g, dH, w1, offsets, dXt, st);
 }
 
+// ---------------------------------------------------------------------------
+// Weight gradients.  An expert's weight-gradient tiles each reduce over all of
+// the expert's rows, so under skewed routing a few tiles are far longer than
+// the rest.  Before the GEMM, k_wgt_plan (one workgroup) builds its tile plan:
+//  * an expert with more than `split` rows has its reduction cut into equal
+//    chunks of at most `split` rows; each chunk's tiles write fp32 partial
+//    sums to their own slot, and k_wgt_reduce adds them in chunk order (a
+//    fixed order: results do not depend on timing);
+//  * units (MU m tiles x all n tiles of one chunk) are sorted by rows, largest
+//    first; the GEMM deals their tiles to its workgroups round by round in
+//    alternating direction, so every workgroup gets a similar share of large
+//    and small tiles, and the tiles of one unit run side by side on one XCD
+//    (they share the chunk's rows in that XCD's L2).
+// ---------------------------------------------------------------------------
+
+struct WgtPolicy {
+  int MT, NT, MU;
+  int split;          // rows above which an expert is split (also the chunk bound); 0 = never
+  size_t max_slots;   // partial slots needed at most
+  size_t max_units;   // plan units at most
+};
+
+WgtPolicy wgt_policy(const GemmDims& g, int M, int N) {
+  WgtPolicy p{};
+  p.MT = M / g4::BM;
+  p.NT = N / g4::BN;
+  p.MU = 1;
+  for (int mu = p.MT; mu >= 1; --mu)
+    if (p.MT % mu == 0 && mu * p.NT <= 64) { p.MU = mu; break; }
+  // half the rows a workgroup would reduce with the work spread evenly over
+  // 256 workgroups (one per CU), never below 2048; a fixed count keeps the
+  // workspace size a function of the shapes alone
+  const long long tiles = (long long)p.MT * p.NT;
+  long long sp = (long long)g.cap * tiles / (2LL * 256);
+  sp = std::max<long long>(2048, (sp + 255) / 256 * 256);
+  p.split = (sp >= (long long)g.cap || sp > (1LL << 30)) ? 0 : (int)sp;
+  // every split expert has more than `split` rows and at most ceil(c/split) chunks
+  const size_t whole = p.split ? g.cap / (size_t)p.split : 0;
+  p.max_slots = p.split ? whole + std::min<size_t>((size_t)g.E, whole) : 0;
+  p.max_units = ((size_t)g.E + p.max_slots) * (size_t)(p.MT / p.MU);
+  return p;
+}
+
+// Plan buffer: [0] units, [16] split experts, then the split list (int4
+// {e, first slot, chunks, 0} per split expert) and the sorted units.
+struct WgtPlanLayout {
+  size_t split_off, units_off, plan_bytes, partial_off, total;
+};
+WgtPlanLayout wgt_layout(const GemmDims& g, const WgtPolicy& p, int M, int N) {
+  WgtPlanLayout L{};
+  L.split_off = 256;
+  L.units_off = L.split_off + ((size_t)g.E * 16 + 255) / 256 * 256;
+  L.plan_bytes = L.units_off + p.max_units * sizeof(PlanUnit);
+  L.partial_off = (L.plan_bytes + 255) / 256 * 256;
+  L.total = L.partial_off + p.max_slots * (size_t)M * N * 4;
+  return L;
+}
+
+__device__ __forceinline__ int plan_scan1024(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) lds[wave] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int x = 0; x < 16; ++x) {
+    const int sv = lds[x];
+    if (x < wave) base += sv;
+    tot += sv;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// One 1024-thread workgroup (E <= 1024).
+__global__ void __launch_bounds__(1024)
+k_wgt_plan(const int32_t* __restrict__ offsets, int E, int MT, int MU, int split, int* __restrict__ plan,
+           int4* __restrict__ split_list, PlanUnit* __restrict__ units) {
+  __shared__ int gp[MAX_E + 1];     // chunk groups of experts before e
+  __shared__ int base_rows[MAX_E];  // rows per chunk (split experts)
+  __shared__ int slot0[MAX_E];      // first partial slot, -1 if not split
+  __shared__ int hist[1024];
+  __shared__ int sc[16];
+  const int tid = threadIdx.x;
+  const int e = tid;
+  int q = 0, brows = 0, cnt = 0;
+  if (e < E) {
+    cnt = offsets[e + 1] - offsets[e];
+    q = 1;
+    if (split > 0 && cnt > split) {
+      const int q0 = (cnt + split - 1) / split;
+      brows = ((cnt + q0 - 1) / q0 + 31) / 32 * 32;
+      q = (cnt + brows - 1) / brows;  // chunks that hold rows
+    }
+  }
+  int ngroups, nsplit, nslots;
+  const int g0 = plan_scan1024(q, sc, &ngroups);
+  const int isz = q > 1 ? 1 : 0;
+  const int si = plan_scan1024(isz, sc, &nsplit);
+  const int s0 = plan_scan1024(q > 1 ? q : 0, sc, &nslots);
+  if (e < E) {
+    gp[e] = g0;
+    base_rows[e] = brows;
+    slot0[e] = q > 1 ? s0 : -1;
+    if (q > 1) split_list[si] = make_int4(e, s0, q, 0);
+  }
+  if (tid == 0) {
+    gp[E] = ngroups;
+    plan[16] = nsplit;
+  }
+  hist[tid] = 0;
+  __syncthreads();
+  const int UPG = MT / MU;
+  const int U = ngroups * UPG;
+  // group g -> (expert, chunk, rows); sort key: k steps of 32 rows, descending
+  auto group_of = [&](int g, int& ge, int& ch, int& r0, int& rn) {
+    int lo = 0, hi = E - 1;  // largest e with gp[e] <= g
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (gp[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    ge = lo;
+    ch = g - gp[lo];
+    const int c = offsets[lo + 1] - offsets[lo];
+    if (slot0[lo] < 0) {
+      r0 = offsets[lo];
+      rn = c;
+    } else {
+      r0 = offsets[lo] + ch * base_rows[lo];
+      rn = min(base_rows[lo], c - ch * base_rows[lo]);
+    }
+  };
+  for (int g = tid; g < ngroups; g += 1024) {
+    int ge, ch, r0, rn;
+    group_of(g, ge, ch, r0, rn);
+    atomicAdd(&hist[1023 - min(1023, rn >> 5)], 1);
+  }
+  __syncthreads();
+  int tot;
+  const int start = plan_scan1024(hist[tid], sc, &tot);
+  __syncthreads();
+  hist[tid] = start;  // next free position of bucket tid
+  __syncthreads();
+  for (int g = tid; g < ngroups; g += 1024) {
+    int ge, ch, r0, rn;
+    group_of(g, ge, ch, r0, rn);
+    // position among the sorted groups (groups of equal key in arrival
+    // order: the order only decides which workgroup runs a tile, never its
+    // result); a group's units stay together
+    const int i = atomicAdd(&hist[1023 - min(1023, rn >> 5)], 1);
+    PlanUnit pu;
+    pu.e = ge;
+    pu.seg0 = r0;
+    pu.segn = rn;
+    pu.slot = slot0[ge] < 0 ? -1 : slot0[ge] + ch;
+    pu.pad[0] = pu.pad[1] = pu.pad[2] = 0;
+    for (int m = 0; m < UPG; ++m) {
+      pu.mt0 = m * MU;
+      units[(size_t)i * UPG + m] = pu;
+    }
+  }
+  if (tid == 0) plan[0] = U;
+}
+
+// out[e] = sum over chunks c of P[first slot of e + c] for every split
+// expert (M x N elements each, bf16 out), in chunk order.  Workgroups stride
+// over (split expert, 2048-element block) items.
+__global__ void __launch_bounds__(256)
+k_wgt_reduce(const int* __restrict__ plan, const int4* __restrict__ split_list, int M, int N,
+             const float* __restrict__ P, bf16_t* __restrict__ out) {
+  const int nsplit = plan[16];
+  const long long mn = (long long)M * N;
+  const long long per = mn / 2048;  // M and N are multiples of 256
+  const long long items = (long long)nsplit * per;
+  for (long long u = blockIdx.x; u < items; u += gridDim.x) {
+    const int4 sl = split_list[u / per];
+    const long long off = (u % per) * 2048 + threadIdx.x * 8;
+    const float* src = P + (long long)sl.y * mn + off;
+    float4 a0 = *reinterpret_cast<const float4*>(src), a1 = *reinterpret_cast<const float4*>(src + 4);
+    for (int c = 1; c < sl.z; ++c) {
+      const float4 b0 = *reinterpret_cast<const float4*>(src + c * mn);
+      const float4 b1 = *reinterpret_cast<const float4*>(src + c * mn + 4);
+      a0.x += b0.x; a0.y += b0.y; a0.z += b0.z; a0.w += b0.w;
+      a1.x += b1.x; a1.y += b1.y; a1.z += b1.z; a1.w += b1.w;
+    }
+    uint4 v;
+    v.x = (uint32_t)f2bf(a0.x) | ((uint32_t)f2bf(a0.y) << 16);
+    v.y = (uint32_t)f2bf(a0.z) | ((uint32_t)f2bf(a0.w) << 16);
+    v.z = (uint32_t)f2bf(a1.x) | ((uint32_t)f2bf(a1.y) << 16);
+    v.w = (uint32_t)f2bf(a1.z) | ((uint32_t)f2bf(a1.w) << 16);
+    *reinterpret_cast<uint4*>(out + (long long)sl.x * mn + off) = v;
+  }
+}
+
+// Weight-gradient GEMM on the 256-tile kernel (C = M x N per expert, bf16):
+// plan, GEMM, then the sum of split experts' partials.
+hipError_t wgt_g4(const GemmDims& g, const int32_t* offsets, int M, int N, const Operand& a, const Operand& b,
+                  size_t a_bytes, size_t b_bytes, void* C, void* ws, hipStream_t st) {
+  const WgtPolicy pol = wgt_policy(g, M, N);
+  const WgtPlanLayout L = wgt_layout(g, pol, M, N);
+  char* w = static_cast<char*>(ws);
+  int* plan = reinterpret_cast<int*>(w);
+  int4* split_list = reinterpret_cast<int4*>(w + L.split_off);
+  PlanUnit* units = reinterpret_cast<PlanUnit*>(w + L.units_off);
+  float* partial = reinterpret_cast<float*>(w + L.partial_off);
+  hipLaunchKernelGGL(k_wgt_plan, dim3(1), dim3(1024), 0, st, offsets, g.E, pol.MT, pol.MU, pol.split, plan,
+                     split_list, units);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  GemmShape s{offsets, g.E, M, N, 0, N, 1};
+  s.plan = WgtPlan{plan, units, pol.MU};
+  using Epi = g4::G4StoreW;
+  typename Epi::Params ep{reinterpret_cast<bf16_t*>(C), N, partial};
+  err = run_gemm4<true, true, false, Epi>(s, a, b, a_bytes, b_bytes, ep, num_cus(), st);
+  if (err != hipSuccess || pol.split == 0) return err;
+  hipLaunchKernelGGL(k_wgt_reduce, dim3((unsigned)(2 * num_cus())), dim3(256), 0, st, plan, split_list, M, N,
+                     partial, reinterpret_cast<bf16_t*>(C));
+  return hipGetLastError();
+}
+
 template <typename T, int BMW, int BN>
 hipError_t dw1_t(const GemmDims& g, const void* x, const void* dH, const int32_t* row_token,
                  const int32_t* offsets, void* dW1, hipStream_t st) {
@@ -269,17 +493,13 @@ bool dw1_g4(const GemmDims& g) {
 }
 template <typename T>
 hipError_t dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* row_token, const int32_t* offsets,
-               void* dW1, hipStream_t st) {
+               void* dW1, void* ws, hipStream_t st) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (dw1_g4(g)) {
-      const int n = g.n, d = g.d, E = g.E;
-      using Epi = g4::G4Store;
-      GemmShape s{offsets, E, d, 2 * n, 0, 2 * n, 1};
+      const int n = g.n, d = g.d;
       Operand a{x, row_token, 0, d};
       Operand b{dH, nullptr, 0, 2 * n};
-      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dW1), 2 * n};
-      return run_gemm4<true, true, false, Epi>(s, a, b, (size_t)g.T * d * 2, g.cap * 2 * n * 2, ep,
-                                               (long long)E * (d / g4::BM) * (2 * n / g4::BN), st);
+      return wgt_g4(g, offsets, d, 2 * n, a, b, (size_t)g.T * d * 2, g.cap * 2 * n * 2, dW1, ws, st);
     }
     return dw1_t<T, 128, 128>(g, x, dH, row_token, offsets, dW1, st);
   } else {
@@ -304,17 +524,13 @@ bool dw2_g4(const GemmDims& g) {
 }
 template <typename T>
 hipError_t dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t* row_token, const int32_t* offsets,
-               void* dW2, hipStream_t st) {
+               void* dW2, void* ws, hipStream_t st) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (dw2_g4(g)) {
-      const int n = g.n, d = g.d, E = g.E;
-      using Epi = g4::G4Store;
-      GemmShape s{offsets, E, n, d, 0, d, 1};
+      const int n = g.n, d = g.d;
       Operand a{As, nullptr, 0, n};
       Operand b{d_o, row_token, 0, d};
-      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dW2), d};
-      return run_gemm4<true, true, false, Epi>(s, a, b, g.cap * n * 2, (size_t)g.T * d * 2, ep,
-                                               (long long)E * (n / g4::BM) * (d / g4::BN), st);
+      return wgt_g4(g, offsets, n, d, a, b, g.cap * n * 2, (size_t)g.T * d * 2, dW2, ws, st);
     }
     if (g.n % 128 == 0) return dw2_t<T, 128, 128>(g, As, d_o, row_token, offsets, dW2, st);
     return dw2_t<T, 64, 128>(g, As, d_o, row_token, offsets, dW2, st);
@@ -403,12 +619,18 @@ hipError_t launch_dxt(const GemmDims& g, const void* dH, const void* w1, const i
   return MOE_GDISPATCH(g, dxt, dH, w1, offsets, dXt, st);
 }
 hipError_t launch_dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* row_token,
-                      const int32_t* offsets, void* dW1, hipStream_t st) {
-  return MOE_GDISPATCH(g, dw1, x, dH, row_token, offsets, dW1, st);
+                      const int32_t* offsets, void* dW1, void* ws, hipStream_t st) {
+  return MOE_GDISPATCH(g, dw1, x, dH, row_token, offsets, dW1, ws, st);
 }
 hipError_t launch_dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t* row_token,
-                      const int32_t* offsets, void* dW2, hipStream_t st) {
-  return MOE_GDISPATCH(g, dw2, As, d_o, row_token, offsets, dW2, st);
+                      const int32_t* offsets, void* dW2, void* ws, hipStream_t st) {
+  return MOE_GDISPATCH(g, dw2, As, d_o, row_token, offsets, dW2, ws, st);
+}
+size_t wgt_ws_bytes(const GemmDims& g) {
+  size_t b = 0;
+  if (dw1_g4(g)) b = std::max(b, wgt_layout(g, wgt_policy(g, g.d, 2 * g.n), g.d, 2 * g.n).total);
+  if (dw2_g4(g)) b = std::max(b, wgt_layout(g, wgt_policy(g, g.n, g.d), g.n, g.d).total);
+  return b;
 }
 hipError_t launch_dwr(int dtype, const void* x, const void* dz_dense, int T, int d, int E, void* dWr,
                       float* partials, hipStream_t st) {

@@ -61,6 +61,24 @@ struct Operand {
   int ld;              // elements between rows
 };
 
+// Tile plan of a weight-gradient GEMM on the 256-tile kernel.  A unit is MU
+// consecutive m tiles times all n tiles of one (expert, row chunk) pair;
+// units are sorted by rows, largest first, and their tiles are dealt to the
+// workgroups round by round, reversing direction every round.
+struct PlanUnit {
+  int e;      // expert
+  int seg0;   // first routed row of the chunk
+  int segn;   // rows of the chunk
+  int slot;   // fp32 partial slot of the chunk, -1 when the expert is not split
+  int mt0;    // first m tile of the unit
+  int pad[3];
+};
+struct WgtPlan {
+  const int* nunits;      // [1] units in the plan
+  const PlanUnit* units;  // [nunits], sorted
+  int MU;
+};
+
 struct GemmShape {
   const int32_t* offsets;  // [E+1] row segments; null = one segment
   int E;                   // experts (1 when dense)
@@ -68,6 +86,7 @@ struct GemmShape {
   int n_valid;             // existing columns (<= N rounded up to BN)
   int ksplit;              // WGT: chunks each expert's reduction is split into
                            //   (output slice (e*ksplit + s) holds chunk s); 1 = none
+  WgtPlan plan{};          // WGT, 256-tile kernel: the tile plan
 };
 
 struct TileCtx {
@@ -75,6 +94,7 @@ struct TileCtx {
   int seg0, segn;      // segment of the tile's expert
   int m_valid;         // valid rows of this tile (ROW mode)
   long long out_row0;  // ROW: first routed row of the tile; WGT: slice*M + mt*BM
+  int slot;            // WGT with kchunk: partial slot of the tile's chunk, -1 = stored whole
   int n0;              // first column of the tile
   int tid, lane, wm, wn;
 };

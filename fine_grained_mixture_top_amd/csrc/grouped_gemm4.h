@@ -263,6 +263,36 @@ struct G4Store {
   }
 };
 
+// Weight-gradient store: tiles of an expert stored whole go to C as bf16
+// (G4Store); tiles of one chunk of a split expert write their fp32 partial
+// sums to slot c.slot of P ([slots][M][ldc]), summed later in chunk order.
+struct G4StoreW {
+  static constexpr bool WAVE = true;
+  struct Params {
+    bf16_t* C;
+    long long ldc;
+    float* P;
+  };
+  __device__ __forceinline__ static void run(const Params& p, const TileCtx& c, const f32x16_v (&acc)[2][4],
+                                             char* area) {
+    if (c.slot < 0) {
+      G4Store::run(G4Store::Params{p.C, p.ldc}, c, acc, area);
+      return;
+    }
+    const int cl = c.lane & 31, hl = c.lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float* row = p.P + (c.out_row0 + c.wm * 128 + 32 * j + cl) * p.ldc + c.n0 + c.wn * 64 + 4 * hl;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int eg = 0; eg < 4; ++eg)
+          *reinterpret_cast<float4*>(row + 32 * i + 8 * eg) =
+              make_float4(acc[i][j][4 * eg], acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2], acc[i][j][4 * eg + 3]);
+    }
+  }
+};
+
 // Up-projection: the B tile's columns are arranged so that wave wn holds the
 // gate columns j0 + 32 wn .. +31 in its first 32 columns and the matching up
 // columns in its last 32 (j0 = 128 * nt), so gate and up of one element sit in
@@ -341,6 +371,11 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
                      typename Epi::Params ep) {
   constexpr bool AMN = WGT;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
+  // ROW: tprefix[e] = row tiles of experts before e; workgroup v takes tiles
+  // v, v + G, v + 2G, ...  WGT: tiles of the plan's sorted units; in round r
+  // workgroup v takes tile r*G + v (r even) or r*G + G-1-v (r odd), which
+  // spreads the large units' tiles evenly over the workgroups.  v is the
+  // XCD-grouped id, so consecutive tiles share an XCD's L2 either way.
   __shared__ int tprefix[WGT ? 1 : MAX_E + 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -348,6 +383,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   const int wm = w >> 2, wn = w & 3;
 
   const int NT = s.N / BN;
+  const int UT = WGT ? s.plan.MU * NT : 1;  // tiles per plan unit
   int total;
   if constexpr (!WGT) {
     __shared__ int wsum[8];
@@ -375,8 +411,17 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     __syncthreads();
     total = tprefix[s.E] * NT;
   } else {
-    total = s.E * (s.M / BM) * NT;
+    total = __builtin_amdgcn_readfirstlane(s.plan.nunits[0]) * UT;
   }
+  const int G = gridDim.x;
+  const int vid = xcd_virtual_id(blockIdx.x, G);
+  // tile of round r, -1 past the end
+  auto tile_of = [&](int r) -> int {
+    int t;
+    if constexpr (WGT) t = r * G + ((r & 1) ? G - 1 - vid : vid);
+    else t = r * G + vid;
+    return t < total ? t : -1;
+  };
 
   float* Cs = reinterpret_cast<float*>(smem + CS_OFF);
   const char* abase = reinterpret_cast<const char*>(A.ptr);
@@ -394,16 +439,19 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       c.segn = s.offsets[c.e + 1] - c.seg0;
       c.m_valid = min(BM, c.segn - c.mt * BM);
       c.out_row0 = (long long)c.seg0 + (long long)c.mt * BM;
+      c.slot = -1;
     } else {
-      const int MT = s.M / BM;
-      c.e = t / (MT * NT);
-      const int rem = t % (MT * NT);
-      c.mt = rem / NT;
-      c.nt = rem % NT;
-      c.seg0 = s.offsets[c.e];
-      c.segn = s.offsets[c.e + 1] - c.seg0;
+      const int4* u = reinterpret_cast<const int4*>(s.plan.units + t / UT);
+      const int4 u0 = u[0], u1 = u[1];
+      const int ti = t % UT;
+      c.e = u0.x;
+      c.seg0 = u0.y;
+      c.segn = u0.z;
+      c.slot = u0.w;
+      c.mt = u1.x + ti / NT;
+      c.nt = ti % NT;
       c.m_valid = BM;
-      c.out_row0 = (long long)c.e * s.M + (long long)c.mt * BM;
+      c.out_row0 = (long long)(c.slot >= 0 ? c.slot : c.e) * s.M + (long long)c.mt * BM;
     }
     c.n0 = c.nt * BN;
   };
@@ -463,14 +511,15 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     for (int k = 0; k < NS - 1 && k < nk; ++k) issue(k);
   };
 
-  int t = xcd_virtual_id(blockIdx.x, gridDim.x);
+  int r = 0;
+  int t = tile_of(0);
   TileCtx c;
-  if (t < total) {
+  if (t >= 0) {
     decode(t, c);
     setup(c);
     prime(c);
   }
-  while (t < total) {
+  while (t >= 0) {
     const int nk = ksteps(c);
     f32x16_v acc[2][4];
 #pragma unroll
@@ -522,13 +571,13 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       int k = 0;
       for (; k + NS - 1 < nk; ++k) body(k, std::true_type());
       for (; k < nk; ++k) body(k, std::false_type());
-      __syncthreads();  // every wave is done reading the stages
     }
+    __syncthreads();  // every wave is done reading the stages
 
     // ---- next tile's first stages, then this tile's epilogue ----
-    const int tn = t + gridDim.x;
+    const int tn = tile_of(r + 1);
     TileCtx cn = c;
-    if (tn < total) {
+    if (tn >= 0) {
       decode(tn, cn);
       setup(cn);
       prime(cn);
@@ -567,6 +616,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     }
     c = cn;
     t = tn;
+    ++r;
   }
 }
 

@@ -38,10 +38,14 @@ hipError_t launch_dh(const GemmDims& g, const void* d_o, const void* w2, const v
                      void* As, float* dS_part, hipStream_t st);
 hipError_t launch_dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t* offsets, void* dXt,
                       hipStream_t st);
+// dW1 / dW2: `ws` (wgt_ws_bytes(g) bytes, 256-byte aligned; may be null when
+// that is 0) holds the tile plan and the fp32 partial sums of experts whose
+// reduction is split.
 hipError_t launch_dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* row_token,
-                      const int32_t* offsets, void* dW1, hipStream_t st);
+                      const int32_t* offsets, void* dW1, void* ws, hipStream_t st);
 hipError_t launch_dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t* row_token,
-                      const int32_t* offsets, void* dW2, hipStream_t st);
+                      const int32_t* offsets, void* dW2, void* ws, hipStream_t st);
+size_t wgt_ws_bytes(const GemmDims& g);
 // dW_r = x^T dz_dense, reduction split in dwr_splits() chunks whose fp32
 // partials ([splits][d][E]) go to `partials` and are then summed in order.
 int dwr_splits(int T, int d, int E);

@@ -42,7 +42,7 @@ size_t capacity(const moe_desc* d) {
 
 // Workspace items, in order, for each phase.
 struct Layout {
-  size_t off[9];
+  size_t off[10];
   size_t total;
 };
 
@@ -88,6 +88,7 @@ Layout bwd_layout(const moe_desc* d) {
   L.off[6] = o; o = up(o + (size_t)d->E * d->d * es);     // W_r^T [E][d]
   L.off[7] = o; o = up(o + cap * d->d * es);              // dXt
   L.off[8] = o; o = up(o + (size_t)dwr_splits(d->T, d->d, d->E) * d->d * d->E * 4);  // dW_r partials
+  L.off[9] = o; o = up(o + wgt_ws_bytes(gemm_dims(d)));                               // dW1 / dW2 plan + partials
   L.total = o;
   return L;
 }
@@ -249,8 +250,9 @@ int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1
   MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, dXt, dz_row, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T, D.d, dx,
                               st));
   // weight gradients
-  MOE_TRY(MOE_K_DW1, launch_dw1(g, x, dH, R.row_token, R.offsets, dw1, st));
-  MOE_TRY(MOE_K_DW2, launch_dw2(g, As, d_o, R.row_token, R.offsets, dw2, st));
+  void* wws = wgt_ws_bytes(g) ? (void*)(w + L.off[9]) : nullptr;
+  MOE_TRY(MOE_K_DW1, launch_dw1(g, x, dH, R.row_token, R.offsets, dw1, wws, st));
+  MOE_TRY(MOE_K_DW2, launch_dw2(g, As, d_o, R.row_token, R.offsets, dw2, wws, st));
   if (db) MOE_TRY(MOE_K_DB, launch_bias_grad(dz_row, R.offsets, D.E, db, st));
   return MOE_OK;
 }

@@ -146,3 +146,31 @@ def test_layer_is_deterministic():
         outs.append(layer_outputs(L, w))
     for k in outs[0]:
         assert np.array_equal(outs[0][k], outs[1][k]), k
+
+
+def test_weight_gradients_of_saturated_experts():
+    """Strongly skewed routing: the busiest experts hold nearly every token, so
+    their weight-gradient reduction (thousands of rows) is split into chunks
+    whose fp32 partials are summed afterwards.  Every expert's dW1 / dW2 must
+    match the oracle on its own, and two runs must agree bit for bit."""
+    w = W("bf16_wgt_skew", 6000, 256, 16, 256, 2, "bf16", seed=18, zipf=2.0)
+    a = I.draw_all(w)
+    o = oracle_layer(w, a["x"], a["w_r"], a["w1"], a["w2"], a["d_o"], a["bias"])
+    assert o["counts"].max() >= 4096  # at least two chunks of 2048 rows
+    outs = []
+    for _ in range(2):
+        L, _ = run_gpu(w, a["x"], a["w_r"], a["w1"], a["w2"], a["d_o"], a["bias"])
+        assert_routing_equal(routing_host(L, w), o)
+        outs.append(layer_outputs(L, w))
+    g = outs[0]
+    compare_layer(g, o, w.dtype)
+    from gpu_util import relF, tol
+    for e in range(w.E):
+        if o["counts"][e] == 0:
+            assert np.all(g["dW1"][e] == 0) and np.all(g["dW2"][e] == 0)
+            continue
+        for k in ("dW1", "dW2"):
+            err = relF(g[k][e], o[k][e])
+            assert err <= tol(w.dtype), (e, int(o["counts"][e]), k, err)
+    for k in ("dW1", "dW2"):
+        assert np.array_equal(outs[0][k], outs[1][k]), k
