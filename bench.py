@@ -6,7 +6,9 @@ routed rows) and its fraction of the bf16 MFMA peak, the roofline position of
 the dominant kernel (per-launch durations from HIP events the library records
 on its stream during the timed steps), every kernel's time and roofline
 fraction, and the fp64 CPU oracle timed on a bounded sample of the same
-workload as a reported baseline.
+workload as a reported baseline.  Also reported: single steps timed after a
+1 GiB write that evicts the caches ("flushed"), the bytes kept between forward
+and backward ("memory") and the realised expert loads ("routing").
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload fg7b_bf16]
 """
@@ -33,9 +35,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fg7b_bf16")
     ap.add_argument("--round-mode", type=int, default=0)
+    ap.add_argument("--tile", type=int, default=128,
+                    help="token-rounding tile (128 or 256; 256 matches the bf16 GEMMs' row tile)")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the oracle's CPU baseline sample (0 = skip, -1 = as many as "
                          "fit a 4 TFLOP budget, about 20 s of fp64 work, capped at the workload's T)")
+    ap.add_argument("--flushed-steps", type=int, default=5,
+                    help="after the timed steps, time this many single steps one by one, each "
+                         "after writing a 1 GiB buffer so that no input or weight is still in the "
+                         "L2 / MALL caches (reported as 'flushed'; 0 = skip)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many bytes "
                          "(calibration dispatch for HBM counter passes)")
@@ -95,6 +103,18 @@ def memory_report(w, L, es):
     }
 
 
+def routing_report(L, tile=128):
+    """Realised expert loads of the last routed batch: rows before / after
+    token rounding, max / min / median load, experts below one tile and
+    experts whose last tile is partial."""
+    import numpy as np
+    raw = L.routing.counts_raw.cpu().numpy().astype(np.int64)
+    cnt = L.routing.counts.cpu().numpy().astype(np.int64)
+    return {"rows_raw": int(raw.sum()), "rows": int(cnt.sum()), "max": int(raw.max()), "min": int(raw.min()),
+            "median": float(np.median(raw)), "below_tile": int((raw < tile).sum()),
+            "partial_tile": int((raw % tile != 0).sum()), "tile": tile}
+
+
 def cpu_baseline(w, a, tokens):
     """fp64 oracle (as it stands) on the first `tokens` tokens of the workload."""
     import numpy as np
@@ -142,7 +162,7 @@ def main():
 
     x, wr, w1, w2, do = (dev(a[k]) for k in ("x", "w_r", "w1", "w2", "d_o"))
     bias = None if a["bias"] is None else torch.from_numpy(a["bias"]).cuda()
-    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=args.round_mode)
+    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=args.round_mode, tile=args.tile)
     L = B.Layer(desc)
 
     def step():
@@ -171,6 +191,23 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    flushed = None
+    if args.flushed_steps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(args.flushed_steps):
+            flush.zero_()
+            e0.record()
+            step()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del flush
+        times.sort()
+        flushed = {"steps": args.flushed_steps, "flush_bytes": 1 << 30,
+                   "ms_per_step_median": round(times[len(times) // 2], 4), "ms_per_step_min": round(times[0], 4)}
 
     P = int(L.routing.offsets[-1].item())
     es = 2 if w.dtype == "bf16" else 4
@@ -211,14 +248,18 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "n": w.n, "K": w.K,
-                   "round_mode": args.round_mode, "rows": P, "parallelism": "single GPU"},
+                   "round_mode": args.round_mode, "tile": args.tile, "rows": P, "parallelism": "single GPU"},
         "mfma_peak_frac": round(tflops / peak_mfma, 4),
         "tokens_per_s": round(w.T / (ms_step * 1e-3), 1),
         "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
                      "unit": dk["unit"], "frac": dk["frac"], "traffic": measured_traffic(w.name, dom)},
         "kernels": {k: {kk: v for kk, v in d.items() if kk != "work"} for k, d in kernels.items()},
         "memory": memory_report(w, L, es),
+        "routing": routing_report(L, args.tile),
     }
+    if flushed is not None:
+        flushed["tflops_median"] = round(useful / (flushed["ms_per_step_median"] * 1e-3) / 1e12, 2)
+        out["flushed"] = flushed
     cpu_tokens = args.cpu_tokens
     if cpu_tokens < 0:
         cpu_tokens = max(1, min(w.T, int(CPU_FLOP_BUDGET // (18.0 * w.K * w.d * w.n))))

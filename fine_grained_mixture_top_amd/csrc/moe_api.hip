@@ -23,7 +23,7 @@ int validate_desc(const moe_desc* d) {
   if (d->T < 1 || d->d < 1 || d->E < 1 || d->n < 1 || d->K < 1 || d->K > d->E) return MOE_EINVAL;
   if (d->round_mode < MOE_ROUND_OFF || d->round_mode > MOE_ROUND_STOCHASTIC) return MOE_EINVAL;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_EDTYPE;
-  if (d->tile != 128) return MOE_ESHAPE;
+  if (d->tile != 128 && d->tile != 256) return MOE_ESHAPE;
   if (d->E % 8 != 0 || d->E > 1024) return MOE_ESHAPE;
   if (d->d % 128 != 0 || d->n % 64 != 0) return MOE_ESHAPE;
   if ((int64_t)d->T * d->E > INT32_MAX - 1) return MOE_ESHAPE;  // rows are int32

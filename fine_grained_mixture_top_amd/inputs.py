@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import dataclasses
+import json
 import math
 import os
 from typing import Optional
@@ -44,6 +45,7 @@ class Workload:
     dtype: str  # "f32" or "bf16"
     zipf_s: Optional[float] = None  # skewed per-expert bias when set
     seed: int = 0
+    bias_file: Optional[str] = None  # fitted bias stored beside this module (overrides the closed form)
 
     @property
     def P(self) -> int:
@@ -65,7 +67,7 @@ WORKLOADS = {
     "sweep_e128": Workload("sweep_e128", T=16384, d=2048, E=128, n=256, K=8, dtype="bf16"),
     "sweep_e256": Workload("sweep_e256", T=16384, d=2048, E=256, n=128, K=16, dtype="bf16"),
     "zipf_e256": Workload("zipf_e256", T=32768, d=2048, E=256, n=256, K=8, dtype="bf16",
-                          zipf_s=1.1),
+                          zipf_s=1.1, bias_file="zipf_e256_bias.json"),
     "prod_e256": Workload("prod_e256", T=16384, d=7168, E=256, n=2048, K=8, dtype="bf16"),
     # the OLMoE-shaped layer the pages break down per kernel
     "olmoe_bf16": Workload("olmoe_bf16", T=32768, d=2048, E=64, n=1024, K=8, dtype="bf16"),
@@ -143,9 +145,12 @@ def draw_do(w: Workload) -> np.ndarray:
 
 
 def draw_bias(w: Workload) -> Optional[np.ndarray]:
-    """Per-expert router bias (fp32) for the skewed workload, else None.
+    """Per-expert router bias (fp32) for the skewed workloads, else None.
 
-    The expected load of expert e is meant to follow Zipf(s): p_e proportional
+    A workload with a ``bias_file`` reads its bias from that JSON file: for
+    zipf_e256 it was fitted so that the realised loads follow a capped
+    Zipf(1.1) law on the workload's own tokens (see oracle/zipf_bias.py, which
+    wrote it).  Otherwise the expected load of expert e is meant to follow Zipf(s): p_e proportional
     to (e+1)^-s.  The bias is set in closed form, with no routing involved:
     treating each logit's data part x.W_r[:, e] as noise of standard deviation
     sigma = 0.02*sqrt(d) and approximating that Gaussian noise by a Gumbel law
@@ -155,6 +160,9 @@ def draw_bias(w: Workload) -> Optional[np.ndarray]:
     A random permutation (drawn from the bias child stream) decides which
     expert takes which Zipf rank, so heavy experts are not all at low ids.
     """
+    if w.bias_file is not None:
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), w.bias_file)) as f:
+            return np.asarray(json.load(f)["bias"], dtype=np.float32)
     if w.zipf_s is None:
         return None
     sigma = W_STD * math.sqrt(w.d)

@@ -111,10 +111,14 @@ extern "C" {
  *   T, d, E, n, K: tokens, hidden size, experts, expert intermediate size,
  *     experts per token ([A] "实验结果" uses these names).
  *   Supported by the kernels: T >= 1, 1 <= K <= E, E % 8 == 0, E <= 1024,
- *     d % 128 == 0, n % 64 == 0, tile == 128 (else MOE_ESHAPE).
+ *     d % 128 == 0, n % 64 == 0, tile 128 or 256 (else MOE_ESHAPE).
  *   dtype: MOE_F32 or MOE_BF16.
  *   round_mode / tile / round_seed: token rounding ([B] scheduling
- *     paragraph); round_seed drives MOE_ROUND_STOCHASTIC only.
+ *     paragraph): counts become multiples of `tile`, the row tile of the
+ *     grouped GEMMs they feed (256 for bf16 layers whose d and n are
+ *     multiples of 256, 128 otherwise and with MOE_FLAG_GEMM_128); any
+ *     supported value is correct, the matching one removes the most padding.
+ *     round_seed drives MOE_ROUND_STOCHASTIC only.
  *   flags: MOE_FLAG_* bits.
  *   profile: NULL, or where to record per-kernel launch timing.
  */

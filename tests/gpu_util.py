@@ -42,11 +42,11 @@ def relF(gpu: np.ndarray, ref: np.ndarray) -> float:
 
 
 def run_gpu(w: I.Workload, x, w_r, w1, w2, d_o, bias=None, round_mode=0, round_seed=0,
-            scores=None, backward=True, flags=0):
+            scores=None, backward=True, flags=0, tile=128):
     """Route + forward (+ backward) on the GPU; returns the Layer and device inputs."""
     flags |= B.MOE_FLAG_SCORES_GIVEN if scores is not None else 0
     desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=round_mode,
-                       round_seed=round_seed, flags=flags)
+                       round_seed=round_seed, flags=flags, tile=tile)
     L = B.Layer(desc)
     X, WR, W1, W2, DO = (dev(a, w.dtype) for a in (x, w_r, w1, w2, d_o))
     bias_t = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).cuda()
@@ -102,8 +102,8 @@ def layer_outputs(L: B.Layer, w: I.Workload) -> dict:
 
 
 def oracle_layer(w: I.Workload, x, w_r, w1, w2, d_o, bias=None, round_mode=0, round_seed=0,
-                 scores=None):
-    return O.layer(x, w_r, w1, w2, d_o, w.dtype, w.K, bias=bias, tile=128, round_mode=round_mode,
+                 scores=None, tile=128):
+    return O.layer(x, w_r, w1, w2, d_o, w.dtype, w.K, bias=bias, tile=tile, round_mode=round_mode,
                    round_seed=round_seed, scores=scores)
 
 

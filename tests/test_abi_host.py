@@ -62,7 +62,7 @@ def test_capacity_and_workspace():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(T=0), B.MOE_EINVAL), (dict(K=0), B.MOE_EINVAL), (dict(K=9), B.MOE_EINVAL),
-    (dict(dtype=7), B.MOE_EDTYPE), (dict(round_mode=3), B.MOE_EINVAL), (dict(tile=64), B.MOE_ESHAPE),
+    (dict(dtype=7), B.MOE_EDTYPE), (dict(round_mode=3), B.MOE_EINVAL), (dict(tile=64), B.MOE_ESHAPE), (dict(tile=512), B.MOE_ESHAPE),
     (dict(d=100), B.MOE_ESHAPE), (dict(n=48), B.MOE_ESHAPE), (dict(E=12, K=2), B.MOE_ESHAPE),
     (dict(flags=4), B.MOE_EINVAL),
 ])

@@ -38,8 +38,9 @@ def inputs_of(name):
     return _CACHE[name]
 
 
-def run_layer(w, a, round_mode, round_seed):
-    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=round_mode, round_seed=round_seed)
+def run_layer(w, a, round_mode, round_seed, tile=128):
+    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=round_mode, round_seed=round_seed,
+                       tile=tile)
     L = B.Layer(desc)
     X, WR, W1, W2, DO = (dev(a[k], w.dtype) for k in ("x", "w_r", "w1", "w2", "d_o"))
     bias = None if a["bias"] is None else torch.from_numpy(a["bias"]).cuda()
@@ -130,22 +131,23 @@ def ws_rows(L, item, rows, width, dtype):
     return rows_host(L.ws_view(item, cap * width, dtype), rows, width)
 
 
-FULL = [("fg7b_bf16", 0), ("sweep_e32", 0), ("sweep_e64", 0), ("sweep_e128", 0), ("sweep_e256", 0),
-        ("zipf_e256", 0), ("zipf_e256", 1), ("zipf_e256", 2), ("olmoe_bf16", 0)]
+FULL = [("fg7b_bf16", 0, 128), ("sweep_e32", 0, 128), ("sweep_e64", 0, 128), ("sweep_e128", 0, 128),
+        ("sweep_e256", 0, 128), ("zipf_e256", 0, 128), ("zipf_e256", 1, 128), ("zipf_e256", 2, 128),
+        ("zipf_e256", 1, 256), ("zipf_e256", 2, 256), ("olmoe_bf16", 0, 128)]
 
 
-@pytest.mark.parametrize("name,mode", FULL, ids=[f"{n}-round{m}" for n, m in FULL])
-def test_full_size_token_sample(name, mode):
+@pytest.mark.parametrize("name,mode,tile", FULL, ids=[f"{n}-round{m}-tile{t}" for n, m, t in FULL])
+def test_full_size_token_sample(name, mode, tile):
     w = I.WORKLOADS[name]
     a = inputs_of(name)
-    L = run_layer(w, a, mode, 0)
+    L = run_layer(w, a, mode, 0, tile)
     x64, wr64 = O.to_f64(a["x"], w.dtype), O.to_f64(a["w_r"], w.dtype)
-    rt = O.route(x64, wr64, a["bias"], w.K, 128, mode, 0)
+    rt = O.route(x64, wr64, a["bias"], w.K, tile, mode, 0)
     bad_t, bad_e = check_routing(L, w, rt, x64, wr64, a["bias"])
     if mode:
         cnt = host_int(L.routing.counts)
-        assert np.all(cnt % 128 == 0)
-        assert np.all(np.abs(cnt - host_int(L.routing.counts_raw)) < 128)
+        assert np.all(cnt % tile == 0)
+        assert np.all(np.abs(cnt - host_int(L.routing.counts_raw)) < tile)
 
     rng = np.random.default_rng(1234)
     counts = rt["counts"]

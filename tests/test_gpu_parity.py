@@ -25,19 +25,21 @@ def W(name, T, d, E, n, K, dtype, seed=0, zipf=None):
 # ---------------------------------------------------------------------------
 
 ROUTE_CASES = [
-    (300, 16, 3, 0, 0), (1000, 64, 8, 0, 1), (4097, 256, 16, 0, 2), (513, 8, 8, 0, 3),
-    (4096, 16, 2, 1, 4), (4096, 16, 2, 2, 5), (3000, 24, 5, 1, 6), (3000, 24, 5, 2, 7),
-    (700, 32, 1, 1, 8), (1, 8, 2, 0, 9), (5000, 1024, 7, 2, 10),
+    (300, 16, 3, 0, 0, 128), (1000, 64, 8, 0, 1, 128), (4097, 256, 16, 0, 2, 128), (513, 8, 8, 0, 3, 128),
+    (4096, 16, 2, 1, 4, 128), (4096, 16, 2, 2, 5, 128), (3000, 24, 5, 1, 6, 128), (3000, 24, 5, 2, 7, 128),
+    (700, 32, 1, 1, 8, 128), (1, 8, 2, 0, 9, 128), (5000, 1024, 7, 2, 10, 128),
+    # rounding to 256-row tiles
+    (4096, 16, 2, 1, 11, 256), (4096, 16, 2, 2, 12, 256), (3000, 24, 5, 2, 13, 256), (700, 8, 3, 1, 14, 256),
 ]
 
 
-@pytest.mark.parametrize("T,E,K,mode,seed", ROUTE_CASES)
+@pytest.mark.parametrize("T,E,K,mode,seed,tile", ROUTE_CASES)
 @pytest.mark.parametrize("ties", [True, False])
-def test_routing_bit_exact_on_given_scores(T, E, K, mode, seed, ties):
+def test_routing_bit_exact_on_given_scores(T, E, K, mode, seed, tile, ties):
     w = W("route", T, 128, E, 64, K, "f32", seed=seed)
     z = I.draw_logits(T, E, seed, ties=ties)
     desc = B.make_desc(T, 128, E, 64, K, "f32", round_mode=mode, round_seed=seed + 100,
-                       flags=B.MOE_FLAG_SCORES_GIVEN)
+                       flags=B.MOE_FLAG_SCORES_GIVEN, tile=tile)
     R = B.Routing(desc)
     R.logits.copy_(torch.from_numpy(z).view(-1))
     ws = B.workspace(desc, B.MOE_WS_ROUTE)
@@ -47,7 +49,7 @@ def test_routing_bit_exact_on_given_scores(T, E, K, mode, seed, ties):
     class _L:  # adapter for routing_host
         routing = R
     g = routing_host(_L, w)
-    o = O.route_scores(z, K, tile=128, round_mode=mode, round_seed=seed + 100)
+    o = O.route_scores(z, K, tile=tile, round_mode=mode, round_seed=seed + 100)
     assert_routing_equal(g, o)
     assert np.array_equal(g["counts"], o["counts"])
     np.testing.assert_allclose(g["topk_gate"], o["topk_gate"], rtol=2e-6, atol=1e-7)
@@ -108,13 +110,17 @@ def test_layer_token_rounding_matches_oracle(mode):
     compare_layer(g, o, w.dtype)
 
 
-def test_layer_token_rounding_big_tiles():
+@pytest.mark.parametrize("tile", [128, 256])
+def test_layer_token_rounding_big_tiles(tile):
+    """Token rounding to the 128-row tile and to the 256-row tile of the bf16
+    GEMMs (every count a multiple of 256)."""
     w = W("bf16_tr_big", 1800, 256, 16, 256, 2, "bf16", seed=16)
     a = I.draw_all(w)
-    L, _ = run_gpu(w, a["x"], a["w_r"], a["w1"], a["w2"], a["d_o"], round_mode=2, round_seed=9)
+    L, _ = run_gpu(w, a["x"], a["w_r"], a["w1"], a["w2"], a["d_o"], round_mode=2, round_seed=9, tile=tile)
     g_rt = routing_host(L, w)
-    o = oracle_layer(w, a["x"], a["w_r"], a["w1"], a["w2"], a["d_o"], round_mode=2, round_seed=9)
+    o = oracle_layer(w, a["x"], a["w_r"], a["w1"], a["w2"], a["d_o"], round_mode=2, round_seed=9, tile=tile)
     assert_routing_equal(g_rt, o)
+    assert np.all(g_rt["counts"] % tile == 0)
     g = layer_outputs(L, w)
     compare_layer(g, o, w.dtype)
 

@@ -76,7 +76,7 @@ def test_splitmix64_known_answers():
 def _round_cases():
     out = []
     for T, E, K, M, seed in [(300, 8, 2, 16, 0), (1000, 32, 4, 32, 1), (517, 16, 3, 8, 2),
-                             (2048, 64, 8, 128, 3)]:
+                             (2048, 64, 8, 128, 3), (4096, 32, 4, 256, 4)]:
         out.append((T, E, K, M, seed))
     return out
 
