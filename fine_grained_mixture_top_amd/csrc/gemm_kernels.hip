@@ -6,6 +6,7 @@
 
 #include "epilogues.h"
 #include "grouped_gemm4.h"
+#include "grouped_gemm5.h"
 #include "launch.h"
 
 namespace moe {
@@ -55,6 +56,33 @@ hipError_t run_gemm4(const GemmShape& s, const Operand& A, const Operand& B, siz
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(g4::NTH), g4::SMEM, st, s, A, B, (uint32_t)a_bytes,
                      (uint32_t)b_bytes, ep);
   return hipGetLastError();
+}
+
+// Row-mode 256 x 256 tile kernel with k = 64 per stage (one workgroup per CU).
+template <bool BMN, bool PAIRED, class Epi>
+hipError_t run_gemm5(const GemmShape& s, const Operand& A, const Operand& B, size_t a_bytes, size_t b_bytes,
+                     const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
+  auto kern = g5::grouped_gemm5_kernel<BMN, PAIRED, Epi>;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, g5::SMEM);
+  if (attr != hipSuccess) return attr;
+  long long grid = std::min<long long>(max_tiles, num_cus());
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(g5::NTH), g5::SMEM, st, s, A, B, (uint32_t)a_bytes,
+                     (uint32_t)b_bytes, ep);
+  return hipGetLastError();
+}
+
+// Row-mode GEMMs of the 256 x 256 tile family: k = 64 stages for
+// reductions of at least 512 (measured faster there: up, dH, dXt), k = 32
+// stages for short ones (the down-projection at n = 256, where the deeper
+// pipeline of the k = 32 kernel wins).
+template <bool BMN, bool PAIRED, class Epi>
+hipError_t run_row256(const GemmShape& s, const Operand& A, const Operand& B, size_t a_bytes, size_t b_bytes,
+                      const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
+  if (s.K % g5::BK == 0 && s.K >= 512)
+    return run_gemm5<BMN, PAIRED, Epi>(s, A, B, a_bytes, b_bytes, ep, max_tiles, st);
+  return run_gemm4<false, BMN, PAIRED, Epi>(s, A, B, a_bytes, b_bytes, ep, max_tiles, st);
 }
 
 // Buffer-addressed operands use 32-bit byte offsets with the top half of the
@@ -118,8 +146,8 @@ hipError_t up_swiglu_g4(const GemmDims& g, const void* x, const void* w1, const 
   Operand a{x, row_token, 0, d};
   Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
   typename Epi::Params ep{reinterpret_cast<bf16_t*>(H), reinterpret_cast<bf16_t*>(A), n};
-  return run_gemm4<false, true, true, Epi>(s, a, b, (size_t)g.T * d * 2, (size_t)d * 2 * n * 2, ep,
-                                           row_tiles_bound(g.cap, E, g4::BM) * (2 * n / g4::BN), st);
+  return run_row256<true, true, Epi>(s, a, b, (size_t)g.T * d * 2, (size_t)d * 2 * n * 2, ep,
+                                     row_tiles_bound(g.cap, E, g4::BM) * (2 * n / g4::BN), st);
 }
 bool up_g4(const GemmDims& g) {
   return g.dtype == DT_BF16 && !g.small_tiles && (2 * g.n) % 256 == 0 && g.d % 32 == 0 &&
@@ -162,8 +190,8 @@ hipError_t down(const GemmDims& g, const void* A, const void* w2, const int32_t*
       Operand a{A, nullptr, 0, n};
       Operand b{w2, nullptr, (long long)n * d, d};
       typename Epi::Params ep{reinterpret_cast<bf16_t*>(Y), d};
-      return run_gemm4<false, true, false, Epi>(s, a, b, g.cap * n * 2, (size_t)n * d * 2, ep,
-                                                row_tiles_bound(g.cap, E, g4::BM) * (d / g4::BN), st);
+      return run_row256<true, false, Epi>(s, a, b, g.cap * n * 2, (size_t)n * d * 2, ep,
+                                          row_tiles_bound(g.cap, E, g4::BM) * (d / g4::BN), st);
     }
   }
   if (g.d % Cfg<T>::BIG == 0) return down_t<T, Cfg<T>::BIG>(g, A, w2, offsets, Y, st);
@@ -207,8 +235,8 @@ hipError_t dh(const GemmDims& g, const void* d_o, const void* w2, const void* H,
       Operand b{w2, nullptr, (long long)n * d, d};
       typename Epi::Params ep{reinterpret_cast<const bf16_t*>(H), row_gate, reinterpret_cast<bf16_t*>(dH),
                               reinterpret_cast<bf16_t*>(As), dS_part, n, n / g4::BN};
-      return run_gemm4<false, false, false, Epi>(s, a, b, (size_t)g.T * d * 2, (size_t)n * d * 2, ep,
-                                                 row_tiles_bound(g.cap, E, g4::BM) * (n / g4::BN), st);
+      return run_row256<false, false, Epi>(s, a, b, (size_t)g.T * d * 2, (size_t)n * d * 2, ep,
+                                           row_tiles_bound(g.cap, E, g4::BM) * (n / g4::BN), st);
     }
     if (bn == 128) return dh_t<T, 128>(g, d_o, w2, H, row_token, row_gate, offsets, dH, As, dS_part, st);
     return dh_t<T, 64>(g, d_o, w2, H, row_token, row_gate, offsets, dH, As, dS_part, st);
@@ -244,8 +272,8 @@ hipError_t dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t*
       Operand a{dH, nullptr, 0, 2 * n};
       Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
       typename Epi::Params ep{reinterpret_cast<bf16_t*>(dXt), d};
-      return run_gemm4<false, false, false, Epi>(s, a, b, g.cap * 2 * n * 2, (size_t)d * 2 * n * 2, ep,
-                                                 row_tiles_bound(g.cap, E, g4::BM) * (d / g4::BN), st);
+      return run_row256<false, false, Epi>(s, a, b, g.cap * 2 * n * 2, (size_t)d * 2 * n * 2, ep,
+                                           row_tiles_bound(g.cap, E, g4::BM) * (d / g4::BN), st);
     }
   }
   if (g.d % Cfg<T>::BIG == 0) return dxt_t<T, Cfg<T>::BIG>(g, dH, w1, offsets, dXt, st);

@@ -1,0 +1,315 @@
+// Row-mode grouped GEMM for bf16 on gfx950 with k = 64 per stage: the
+// up-projection, down-projection, dH and dXt GEMMs (every row of A is one
+// routed row, gathered or contiguous; B is an expert's weight matrix).
+//
+// Same tile and wave layout as the 256 x 256 kernel of grouped_gemm4.h
+// (8 waves in 2 (m) x 4 (n), 128 x 64 outputs each, v_mfma_f32_32x32x16_bf16,
+// N-side fragment as the MFMA's first operand) and the same epilogues.  What
+// differs is the k depth of a stage:
+//  * A CU's loads are limited by the number of cache lines it can request per
+//    clock, not by bytes: a load instruction that touches 64 bytes of each of
+//    16 rows costs as much as one that touches 128 bytes of each of 8 rows.
+//    With k = 64 per stage every row segment of a k-contiguous operand tile
+//    is 128 bytes (a whole line), half the lines per byte of k = 32.
+//  * Two stages of 64 KB (A 256 x 64 and B 64 x 256 or 256 x 64): one is
+//    computed while the other loads, with one workgroup barrier per stage.
+//  * Layouts: k-contiguous operands [256 rows][64 k] with 128-byte rows,
+//    16-byte chunk c of row r in slot c ^ ((r >> 1) & 7), which keeps the
+//    fragment reads (32 rows x 2 chunks per wave) conflict-free; weight tiles
+//    stored [k][n] are [64 k-rows][256 cols] with the 512-byte-row layout and
+//    transpose reads of the 256 x 256 kernel.
+//  * The epilogue areas lie over stage 1: the next tile's stage 0 is loaded
+//    before the epilogue, its stage 1 once every wave has finished it.
+#pragma once
+
+#include "grouped_gemm4.h"
+
+namespace moe {
+namespace g5 {
+
+using g4::dma16;
+using g4::f32x16_v;
+using g4::make_rsrc;
+using g4::OOB;
+using g4::wait_vm;
+
+constexpr int BM = 256, BN = 256, BK = 64, NS = 2, NTH = 512;
+constexpr int OPB = 256 * BK * 2;  // bytes of one operand tile per stage (32 KB)
+constexpr int STAGE = 2 * OPB;     // 64 KB
+constexpr int LPS = 8;             // 16-byte loads per thread per stage (4 per operand)
+constexpr int EROWS = g4::EROWS;
+constexpr int LDC = g4::LDC;
+constexpr int CS_OFF = STAGE;      // fp32 staging of the pass epilogue: over stage 1
+constexpr int WE_OFF = STAGE;      // wave-local epilogue areas: over stage 1
+constexpr int SMEM = NS * STAGE;
+static_assert(CS_OFF + g4::STAGE_C <= SMEM, "pass staging fits over stage 1");
+static_assert(WE_OFF + 8 * g4::WAVE_LDS <= SMEM, "wave areas fit over stage 1");
+
+__device__ __forceinline__ int swz_kc(int r) { return (r >> 1) & 7; }
+
+// k-contiguous rows, 128 bytes per row and stage.  Instruction i (0..3) of
+// wave w covers tile rows (4w + i) * 8 .. +7; lane l takes row rb + l/8 and
+// LDS slot l%8, which holds chunk (l%8) ^ swz(row) of that row.
+struct KCLoad5 {
+  uint32_t off[4];  // byte offset of this lane's chunk at k = 0
+  template <class F>
+  __device__ __forceinline__ void setup(int w, int lane, F rowoff) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (4 * w + i) * 8 + (lane >> 3);
+      const uint32_t ro = rowoff(r);
+      off[i] = ro == OOB ? OOB : ro + (uint32_t)(((lane & 7) ^ swz_kc(r)) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* op, int w, int k0) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rs, op + (4 * w + i) * 1024, off[i] + (uint32_t)k0 * 2u);
+  }
+};
+
+// Weights stored [k][n]: k-rows of 256 columns.  Instruction i of wave w
+// covers k-rows (4w + i) * 2 and +1 (lanes 0..31 and 32..63), slot l % 32.
+struct MNLoad5 {
+  uint32_t coff[4];  // column byte offset of this lane's chunk (OOB if absent)
+  int kr[4];         // k-row of each instruction within the stage
+  uint32_t ldb;      // row pitch in bytes
+  template <class F>
+  __device__ __forceinline__ void setup_cols(int w, int lane, F colmap) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = (4 * w + i) * 2 + (lane >> 5);
+      const int chunk = (lane & 31) ^ g4::swz_mn(kr[i]);
+      const int col = colmap(chunk * 8);
+      coff[i] = col < 0 ? OOB : (uint32_t)col * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* op, int w, int k0) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = coff[i] == OOB ? OOB : coff[i] + (uint32_t)(k0 + kr[i]) * ldb;
+      dma16(rs, op + (4 * w + i) * 1024, o);
+    }
+  }
+};
+
+// k-contiguous tile: row rb + lane%32, k = 16s + 8*(lane/32) .. +7 (s = 0..3)
+__device__ __forceinline__ bf16x8_v frag_kc(const char* op, int rb, int s, int lane) {
+  const int r = rb + (lane & 31);
+  const int c = 2 * s + (lane >> 5);
+  return *reinterpret_cast<const bf16x8_v*>(op + r * 128 + ((c ^ swz_kc(r)) & 7) * 16);
+}
+
+template <bool BMN>
+struct Frags {
+  bf16x8_v m[4], n[2];
+  __device__ __forceinline__ void read(const char* st, int s, int lane, int wm, int wn) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = frag_kc(st, wm * 128 + 32 * j, s, lane);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if constexpr (BMN) n[i] = g4::frag_mn(st + OPB, wn * 64 + 32 * i, s, lane);
+      else n[i] = frag_kc(st + OPB, wn * 64 + 32 * i, s, lane);
+    }
+  }
+};
+
+template <bool BMN>
+__device__ __forceinline__ void mma(f32x16_v (&acc)[2][4], const Frags<BMN>& f) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.n[i], f.m[j], acc[i][j], 0, 0, 0);
+}
+
+// A: routed rows (A.idx gathers them), k-contiguous, K = s.K.  B: the
+// expert's weights, [N][K] (BMN = false) or [K][N] (BMN = true; PAIRED
+// arranges the columns for G4SwiGLU).  Workgroup v takes tiles v, v + G, ...
+// of the expert-major tile list (v the XCD-grouped id).
+template <bool BMN, bool PAIRED, class Epi>
+__global__ void __launch_bounds__(NTH, 1)
+grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32_t b_bytes,
+                     typename Epi::Params ep) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  __shared__ int tprefix[MAX_E + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 2, wn = w & 3;
+  const int NT = s.N / BN;
+  {
+    __shared__ int wsum[8];
+    int carry = 0;
+    for (int e0 = 0; e0 < s.E; e0 += NTH) {
+      const int e = e0 + tid;
+      const int tiles = e < s.E ? (s.offsets[e + 1] - s.offsets[e] + BM - 1) / BM : 0;
+      int incl = tiles;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      if (lane == 63) wsum[w] = incl;
+      __syncthreads();
+      int base = carry, tot = 0;
+      for (int x = 0; x < NTH / 64; ++x) {
+        if (x < w) base += wsum[x];
+        tot += wsum[x];
+      }
+      if (e < s.E) tprefix[e] = base + incl - tiles;
+      carry += tot;
+      __syncthreads();
+    }
+    if (tid == 0) tprefix[s.E] = carry;
+    __syncthreads();
+  }
+  const int total = tprefix[s.E] * NT;
+  const int G = gridDim.x;
+  const int vid = xcd_virtual_id(blockIdx.x, G);
+  auto tile_of = [&](int r) -> int {
+    const int t = r * G + vid;
+    return t < total ? t : -1;
+  };
+  const int nk = s.K / BK;
+  const char* abase = reinterpret_cast<const char*>(A.ptr);
+  const char* bbase = reinterpret_cast<const char*>(B.ptr);
+  float* Cs = reinterpret_cast<float*>(smem + CS_OFF);
+
+  auto decode = [&](int t, TileCtx& c) {
+    c.tid = tid; c.lane = lane; c.wm = wm; c.wn = wn;
+    const int mg = t / NT;
+    c.nt = t % NT;
+    c.e = upper_index(tprefix, s.E + 1, mg);
+    c.mt = mg - tprefix[c.e];
+    c.seg0 = s.offsets[c.e];
+    c.segn = s.offsets[c.e + 1] - c.seg0;
+    c.m_valid = min(BM, c.segn - c.mt * BM);
+    c.out_row0 = (long long)c.seg0 + (long long)c.mt * BM;
+    c.slot = -1;
+    c.n0 = c.nt * BN;
+  };
+
+  __amdgpu_buffer_rsrc_t ra, rb;
+  KCLoad5 la, lb_kc;
+  MNLoad5 lb_mn;
+  auto setup = [&](const TileCtx& c) {
+    ra = make_rsrc(abase, a_bytes);
+    la.setup(w, lane, [&](int r) -> uint32_t {
+      const int m = c.mt * BM + r;
+      const int row = c.seg0 + (m < c.segn ? m : c.segn - 1);  // rows past the end repeat the last one
+      const uint32_t src = A.idx ? (uint32_t)A.idx[row] : (uint32_t)row;
+      return src * (uint32_t)A.ld * 2u;
+    });
+    rb = make_rsrc(bbase + (long long)c.e * B.estride * 2, b_bytes);
+    if constexpr (!BMN) {
+      lb_kc.setup(w, lane, [&](int r) -> uint32_t { return (uint32_t)(c.n0 + r) * (uint32_t)B.ld * 2u; });
+    } else {
+      lb_mn.setup_cols(w, lane, [&](int cc) {
+        if constexpr (PAIRED) return g4::G4SwiGLU::col(cc, c.nt, s.N / 2);
+        return c.n0 + cc;
+      });
+      lb_mn.ldb = (uint32_t)B.ld * 2u;
+    }
+  };
+  auto issue = [&](int k) {
+    char* st = smem + (k & 1) * STAGE;
+    const int k0 = k * BK;
+    la.issue(ra, st, w, k0);
+    if constexpr (!BMN) lb_kc.issue(rb, st + OPB, w, k0);
+    else lb_mn.issue(rb, st + OPB, w, k0);
+  };
+
+  int r = 0;
+  int t = tile_of(0);
+  TileCtx c;
+  if (t >= 0) {
+    decode(t, c);
+    setup(c);
+    issue(0);
+  }
+  while (t >= 0) {
+    f32x16_v acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // stage 1 overwrites the previous tile's epilogue areas: every wave must
+    // be done with them
+    __syncthreads();
+    if (nk > 1) issue(1);
+    // stage 0 complete: only stage 1's loads came after it (and, for tiles
+    // after the first, the previous epilogue's stores before those)
+    if (nk > 1) wait_vm<LPS>();
+    else wait_vm<0>();
+    __syncthreads();
+    Frags<BMN> f0, f1;
+    f0.read(smem, 0, lane, wm, wn);
+    for (int k = 0; k < nk; ++k) {
+      const char* cur = smem + (k & 1) * STAGE;
+      f1.read(cur, 1, lane, wm, wn);
+      mma(acc, f0);
+      f0.read(cur, 2, lane, wm, wn);
+      mma(acc, f1);
+      f1.read(cur, 3, lane, wm, wn);
+      mma(acc, f0);
+      if (k + 1 < nk) {
+        // stage k+1 complete (nothing was issued after it); the barrier also
+        // frees stage k's buffer for stage k+2
+        wait_vm<0>();
+        __syncthreads();
+        if (k + 2 < nk) issue(k + 2);
+        f0.read(smem + ((k + 1) & 1) * STAGE, 0, lane, wm, wn);
+      }
+      mma(acc, f1);
+    }
+    __syncthreads();  // every wave is done reading the stages
+
+    // ---- next tile's stage 0, then this tile's epilogue ----
+    const int tn = tile_of(r + 1);
+    TileCtx cn = c;
+    if (tn >= 0) {
+      decode(tn, cn);
+      setup(cn);
+      issue(0);
+    }
+    if constexpr (g4::is_wave_epi<Epi>::value) {
+      Epi::run(ep, c, acc, smem + WE_OFF + w * g4::WAVE_LDS);
+    } else {
+      // eight passes of 32 rows: pass p holds block j = p % 4 of the waves
+      // of m half p / 4
+#pragma unroll 1
+      for (int p = 0; p < BM / EROWS; ++p) {
+        TileCtx cp = c;
+        cp.out_row0 = c.out_row0 + p * EROWS;
+        cp.m_valid = min(EROWS, c.m_valid - p * EROWS);
+        if (cp.m_valid <= 0) break;  // uniform over the workgroup
+        if (wm == (p >> 2)) {
+          const int jp = p & 3;
+          const int cl = lane & 31, hl = lane >> 5;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (j != jp) continue;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int eg = 0; eg < 4; ++eg) {
+                const float4 v = make_float4(acc[i][j][4 * eg], acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2],
+                                             acc[i][j][4 * eg + 3]);
+                *reinterpret_cast<float4*>(Cs + cl * LDC + wn * 64 + 32 * i + 8 * eg + 4 * hl) = v;
+              }
+          }
+        }
+        __syncthreads();
+        Epi::run(ep, s, cp, Cs, nullptr);
+        __syncthreads();
+      }
+    }
+    c = cn;
+    t = tn;
+    ++r;
+  }
+}
+
+}  // namespace g5
+}  // namespace moe

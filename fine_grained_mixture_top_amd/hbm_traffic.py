@@ -50,6 +50,16 @@ def classify(name: str, wgt_seen: dict) -> str:
             wgt_seen["n"] += 1
             return "dw1" if k == 0 else "dw2"
         return "down" if bmn else "dxt"
+    if "grouped_gemm5_kernel" in name:
+        m = re.search(r"grouped_gemm5_kernel<(true|false), (true|false), moe::(?:g4::)?(\w+)", name)
+        if not m:
+            return None
+        bmn, epi = m.group(1) == "true", m.group(3)
+        if epi in ("EpiSwiGLU", "G4SwiGLU"):
+            return "up"
+        if epi in ("EpiDH", "G4DH"):
+            return "dh"
+        return "down" if bmn else "dxt"
     if "grouped_gemm_kernel" in name:
         m = re.search(r"grouped_gemm_kernel<([^,]+), (\d+), (\d+), (true|false), (\d), (true|false), moe::(\w+)<([^>]*)>", name)
         if not m:

@@ -75,6 +75,10 @@ LAYER_CASES = [
     W("bf16_big_tiles", 1500, 512, 16, 256, 4, "bf16", seed=13),
     W("bf16_big_tiles_sparse", 90, 256, 64, 256, 2, "bf16", seed=14),
     W("bf16_big_tiles_skewed", 3000, 256, 32, 512, 3, "bf16", seed=15, zipf=1.2),
+    # d and n of 512 and more: the row-mode GEMMs (up, down, dH, dXt) take the
+    # k = 64 stage kernel; d = 256 above keeps the k = 32 one in use
+    W("bf16_k64_stages", 1200, 512, 16, 512, 2, "bf16", seed=19),
+    W("bf16_k64_stages_ragged", 700, 768, 8, 512, 3, "bf16", seed=20),
 ]
 
 
