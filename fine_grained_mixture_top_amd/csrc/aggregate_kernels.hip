@@ -39,6 +39,8 @@ __device__ __forceinline__ void store_vec(T* p, const float (&v)[16 / sizeof(T)]
   if constexpr (sizeof(T) == 2) {
     uint32_t w[4];
 #pragma unroll
+    // (one conversion per value here: the paired form made the compiler keep
+    // the dX kernel's whole accumulator set live twice)
     for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
     u = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
@@ -48,7 +50,10 @@ __device__ __forceinline__ void store_vec(T* p, const float (&v)[16 / sizeof(T)]
 }
 
 constexpr int UNR = 4;  // rows in flight per lane
-constexpr int CPL = 4;  // 16-byte column chunks per lane per pass
+// Column chunks per lane per pass (CPL) are a template parameter: the
+// launcher picks the smallest CPL (at most 4) that covers a row's 16-byte
+// chunks in as few passes as CPL = 4 would, so no chunk slot idles (d = 1536
+// bf16: 192 chunks = 64 lanes x 3) and fewer registers stay live.
 
 // Streaming 16-byte load (read once: keep it out of the caches' way).
 typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
@@ -75,7 +80,7 @@ __device__ __forceinline__ void unpack(const uint4 u, float (&v)[16 / sizeof(T)]
 // O[t] = sum over token t's rows (ascending) of gate_r * Y[r].  One wave per
 // token; each lane owns up to CPL 16-byte column chunks per pass and keeps
 // UNR rows x CPL chunks of loads in flight.
-template <typename T>
+template <typename T, int CPL>
 __global__ void __launch_bounds__(256)
 k_aggregate_o(const T* __restrict__ Y, const float* __restrict__ row_gate,
               const int32_t* __restrict__ tok_ptr, const int32_t* __restrict__ tok_row, int Tn, int d,
@@ -125,7 +130,7 @@ k_aggregate_o(const T* __restrict__ Y, const float* __restrict__ row_gate,
 }
 
 // dX[t] = sum over token t's rows (ascending) of dXt[r] + dz_r * W_r^T[e_r]
-template <typename T>
+template <typename T, int CPL>
 __global__ void __launch_bounds__(256)
 k_aggregate_dx(const T* __restrict__ dXt, const float* __restrict__ dz_row,
                const int32_t* __restrict__ row_expert, const T* __restrict__ w_rT,
@@ -264,28 +269,60 @@ __global__ void k_transpose(const T* __restrict__ src, int rows, int cols, T* __
 
 }  // namespace
 
+// chunks per lane: fewest passes of 64 x 4 chunks, then the smallest CPL
+// that keeps that number of passes
+int agg_cpl(int nch) {
+  const int passes = (nch + 255) / 256;
+  const int per = (nch + 64 * passes - 1) / (64 * passes);
+  return per < 1 ? 1 : (per > 4 ? 4 : per);
+}
+
+template <typename TE, int CPL>
+void agg_o_launch(const void* Y, const float* row_gate, const int32_t* tok_ptr, const int32_t* tok_row, int T,
+                  int d, void* O, hipStream_t st) {
+  hipLaunchKernelGGL((k_aggregate_o<TE, CPL>), dim3((T + 3) / 4), dim3(256), 0, st, (const TE*)Y, row_gate, tok_ptr,
+                     tok_row, T, d, (TE*)O);
+}
+template <typename TE>
+void agg_o_t(const void* Y, const float* row_gate, const int32_t* tok_ptr, const int32_t* tok_row, int T, int d,
+             void* O, hipStream_t st) {
+  switch (agg_cpl(d / (16 / (int)sizeof(TE)))) {
+    case 1: agg_o_launch<TE, 1>(Y, row_gate, tok_ptr, tok_row, T, d, O, st); break;
+    case 2: agg_o_launch<TE, 2>(Y, row_gate, tok_ptr, tok_row, T, d, O, st); break;
+    case 3: agg_o_launch<TE, 3>(Y, row_gate, tok_ptr, tok_row, T, d, O, st); break;
+    default: agg_o_launch<TE, 4>(Y, row_gate, tok_ptr, tok_row, T, d, O, st); break;
+  }
+}
+
 hipError_t launch_aggregate_o(int dtype, const void* Y, const float* row_gate, const int32_t* tok_ptr,
                               const int32_t* tok_row, int T, int d, void* O, hipStream_t st) {
-  dim3 grid((T + 3) / 4), block(256);
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(k_aggregate_o<bf16_t>, grid, block, 0, st, (const bf16_t*)Y, row_gate, tok_ptr,
-                       tok_row, T, d, (bf16_t*)O);
-  else
-    hipLaunchKernelGGL(k_aggregate_o<float>, grid, block, 0, st, (const float*)Y, row_gate, tok_ptr,
-                       tok_row, T, d, (float*)O);
+  if (dtype == DT_BF16) agg_o_t<bf16_t>(Y, row_gate, tok_ptr, tok_row, T, d, O, st);
+  else agg_o_t<float>(Y, row_gate, tok_ptr, tok_row, T, d, O, st);
   return hipGetLastError();
+}
+
+template <typename TE, int CPL>
+void agg_dx_launch(const void* dXt, const float* dz_row, const int32_t* row_expert, const void* w_rT,
+                   const int32_t* tok_ptr, const int32_t* tok_row, int T, int d, void* dX, hipStream_t st) {
+  hipLaunchKernelGGL((k_aggregate_dx<TE, CPL>), dim3((T + 3) / 4), dim3(256), 0, st, (const TE*)dXt, dz_row,
+                     row_expert, (const TE*)w_rT, tok_ptr, tok_row, T, d, (TE*)dX);
+}
+template <typename TE>
+void agg_dx_t(const void* dXt, const float* dz_row, const int32_t* row_expert, const void* w_rT,
+              const int32_t* tok_ptr, const int32_t* tok_row, int T, int d, void* dX, hipStream_t st) {
+  switch (agg_cpl(d / (16 / (int)sizeof(TE)))) {
+    case 1: agg_dx_launch<TE, 1>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st); break;
+    case 2: agg_dx_launch<TE, 2>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st); break;
+    case 3: agg_dx_launch<TE, 3>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st); break;
+    default: agg_dx_launch<TE, 4>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st); break;
+  }
 }
 
 hipError_t launch_aggregate_dx(int dtype, const void* dXt, const float* dz_row, const int32_t* row_expert,
                                const void* w_rT, const int32_t* tok_ptr, const int32_t* tok_row, int T,
                                int d, void* dX, hipStream_t st) {
-  dim3 grid((T + 3) / 4), block(256);
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(k_aggregate_dx<bf16_t>, grid, block, 0, st, (const bf16_t*)dXt, dz_row, row_expert,
-                       (const bf16_t*)w_rT, tok_ptr, tok_row, T, d, (bf16_t*)dX);
-  else
-    hipLaunchKernelGGL(k_aggregate_dx<float>, grid, block, 0, st, (const float*)dXt, dz_row, row_expert,
-                       (const float*)w_rT, tok_ptr, tok_row, T, d, (float*)dX);
+  if (dtype == DT_BF16) agg_dx_t<bf16_t>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st);
+  else agg_dx_t<float>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st);
   return hipGetLastError();
 }
 

@@ -14,12 +14,16 @@ constexpr int WAVE = 64;
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet): gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32, two values per instruction).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+// two values -> one packed word (a in the low half)
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  const bf16x2_v v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct Elem;
@@ -41,7 +45,9 @@ template <typename T> __device__ __forceinline__ float through(float v) {
   return Elem<T>::to_f(Elem<T>::from_f(v));
 }
 
-__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// logistic sigmoid with the hardware exponential and reciprocal (about one
+// ulp each; the forward and the backward's recomputation share this code)
+__device__ __forceinline__ float sigmoidf_(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // Largest i in [0, n) with a[i] <= v (a non-decreasing, a[0] <= v).
 __device__ __forceinline__ int upper_index(const int32_t* a, int n, int v) {

@@ -470,10 +470,10 @@ k_wgt_reduce(const int* __restrict__ plan, const int4* __restrict__ split_list, 
       a1.x += b1.x; a1.y += b1.y; a1.z += b1.z; a1.w += b1.w;
     }
     uint4 v;
-    v.x = (uint32_t)f2bf(a0.x) | ((uint32_t)f2bf(a0.y) << 16);
-    v.y = (uint32_t)f2bf(a0.z) | ((uint32_t)f2bf(a0.w) << 16);
-    v.z = (uint32_t)f2bf(a1.x) | ((uint32_t)f2bf(a1.y) << 16);
-    v.w = (uint32_t)f2bf(a1.z) | ((uint32_t)f2bf(a1.w) << 16);
+    v.x = f2bf2(a0.x, a0.y);
+    v.y = f2bf2(a0.z, a0.w);
+    v.z = f2bf2(a1.x, a1.y);
+    v.w = f2bf2(a1.z, a1.w);
     *reinterpret_cast<uint4*>(out + (long long)sl.x * mn + off) = v;
   }
 }

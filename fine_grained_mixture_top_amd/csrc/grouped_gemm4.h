@@ -227,7 +227,7 @@ template <class E, class = void> struct is_wave_epi : std::false_type {};
 template <class E> struct is_wave_epi<E, std::void_t<decltype(E::WAVE)>> : std::bool_constant<E::WAVE> {};
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  return make_uint2((uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16), (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16));
+  return make_uint2(f2bf2(a, b), f2bf2(c, d));
 }
 
 // C[row, n0 + col] = acc as bf16.
@@ -325,16 +325,19 @@ struct G4SwiGLU {
       if (rb >= c.m_valid) break;
 #pragma unroll
       for (int eg = 0; eg < 4; ++eg) {
-        float g[4], u[4], a[4];
+        // H rounded to bf16 once (packed pairs); A from the rounded values
+        const uint2 hg = pack4(acc[0][j][4 * eg], acc[0][j][4 * eg + 1], acc[0][j][4 * eg + 2], acc[0][j][4 * eg + 3]);
+        const uint2 hu = pack4(acc[1][j][4 * eg], acc[1][j][4 * eg + 1], acc[1][j][4 * eg + 2], acc[1][j][4 * eg + 3]);
+        const float g[4] = {__uint_as_float(hg.x << 16), __uint_as_float(hg.x & 0xffff0000u),
+                            __uint_as_float(hg.y << 16), __uint_as_float(hg.y & 0xffff0000u)};
+        const float u[4] = {__uint_as_float(hu.x << 16), __uint_as_float(hu.x & 0xffff0000u),
+                            __uint_as_float(hu.y << 16), __uint_as_float(hu.y & 0xffff0000u)};
+        float a[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          g[e] = through<bf16_t>(acc[0][j][4 * eg + e]);
-          u[e] = through<bf16_t>(acc[1][j][4 * eg + e]);
-          a[e] = g[e] * sigmoidf_(g[e]) * u[e];
-        }
+        for (int e = 0; e < 4; ++e) a[e] = g[e] * sigmoidf_(g[e]) * u[e];
         const int cc = 8 * eg + 4 * hl;
-        *reinterpret_cast<uint2*>(Lh + cl * LH + cc) = pack4(g[0], g[1], g[2], g[3]);
-        *reinterpret_cast<uint2*>(Lh + cl * LH + 32 + cc) = pack4(u[0], u[1], u[2], u[3]);
+        *reinterpret_cast<uint2*>(Lh + cl * LH + cc) = hg;
+        *reinterpret_cast<uint2*>(Lh + cl * LH + 32 + cc) = hu;
         *reinterpret_cast<uint2*>(La + cl * LA + cc) = pack4(a[0], a[1], a[2], a[3]);
       }
 #pragma unroll
