@@ -82,8 +82,8 @@ __device__ __forceinline__ int block_scan1024(int v, int* lds /* >= 16 ints */, 
   return base + incl - v;
 }
 
-// G lanes per token (G = 16 or 64): K rounds of an arg-max over the token's
-// scores held E/G per lane.  Writes the slot-ordered experts, their softmax
+// G lanes per token (G = 4 .. 32, the smallest with E <= 32 G): K rounds of
+// an arg-max over the token's scores held E/G per lane.  Writes the slot-ordered experts, their softmax
 // gates and the membership bytes; with fixed_ptr also tok_ptr[t] = t*K (every
 // token keeps exactly K rows when there is no token rounding).  Slot k's score
 // is kept by lane k % G of the group.
@@ -91,7 +91,7 @@ template <int G>
 __global__ void __launch_bounds__(256)
 k_topk(const float* __restrict__ scores, int T, int E, int K, int mpitch, int32_t* __restrict__ topk_idx,
        float* __restrict__ topk_gate, uint8_t* __restrict__ mask, int32_t* __restrict__ tok_ptr) {
-  constexpr int MAXV = 16;  // E <= 16 * G
+  constexpr int MAXV = 32;  // E <= 32 * G
   const int lane = threadIdx.x & (G - 1);
   const int t = (blockIdx.x * 256 + threadIdx.x) / G;
   const bool live = t < T;  // groups never straddle a wave, so shuffles stay inside live groups
@@ -405,7 +405,9 @@ k_compact(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restric
 }
 
 // Plain top-K: each token's rows are its K slots sorted by expert id; the
-// row gate is the slot's top-K gate.
+// row gate is the slot's top-K gate.  For K <= 16 the slots sit in registers
+// and each lands at its rank (the number of slots with a smaller expert id;
+// ids are distinct); larger K takes a selection pass per position.
 __global__ void __launch_bounds__(256)
 k_tok_fill_topk(const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_gate,
                 const int32_t* __restrict__ rowmap, int mpitch, int T, int K,
@@ -415,7 +417,22 @@ k_tok_fill_topk(const int32_t* __restrict__ topk_idx, const float* __restrict__ 
   const int32_t* idx = topk_idx + (size_t)t * K;
   const float* g = topk_gate + (size_t)t * K;
   int32_t* out = tok_row + (size_t)t * K;
-  // selection sort by expert id; K is small (<= E) and ids are distinct
+  if (K <= 16) {
+    int ids[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ids[k] = k < K ? idx[k] : 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= K) break;
+      int pos = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) pos += ids[k] < ids[j] ? 1 : 0;
+      const int row = rowmap[(size_t)ids[j] * mpitch + t];
+      out[pos] = row;
+      row_gate[row] = g[j];
+    }
+    return;
+  }
   int prev = -1;
   for (int j = 0; j < K; ++j) {
     int best = 0x7fffffff, bk = 0;
@@ -554,15 +571,15 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
   const int mp = mask_pitch(T);
   if ((err = hipMemsetAsync(sc.mask, 0, (size_t)E * mp, st)) != hipSuccess) return err;
   int32_t* fixed_ptr = round_mode == 0 ? rb.tok_ptr : nullptr;
-  if (E <= 256) {
-    const long long threads = (long long)T * 16;
-    hipLaunchKernelGGL(k_topk<16>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, rb.logits, T, E,
-                       K, mp, rb.topk_idx, rb.topk_gate, sc.mask, fixed_ptr);
-  } else {
-    const long long threads = (long long)T * 64;
-    hipLaunchKernelGGL(k_topk<64>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, rb.logits, T, E,
-                       K, mp, rb.topk_idx, rb.topk_gate, sc.mask, fixed_ptr);
-  }
+  auto topk = [&](auto kern, int G) {
+    const long long threads = (long long)T * G;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, rb.logits, T, E, K, mp,
+                       rb.topk_idx, rb.topk_gate, sc.mask, fixed_ptr);
+  };
+  if (E <= 128) topk(k_topk<4>, 4);
+  else if (E <= 256) topk(k_topk<8>, 8);
+  else if (E <= 512) topk(k_topk<16>, 16);
+  else topk(k_topk<32>, 32);
   if (round_mode == 0) {
     hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.counts_raw, rb.counts);
   } else {
