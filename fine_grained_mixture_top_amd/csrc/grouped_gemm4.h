@@ -226,6 +226,14 @@ __device__ __forceinline__ void mma(f32x16_v (&acc)[2][4], const Frags<AMN, BMN>
 template <class E, class = void> struct is_wave_epi : std::false_type {};
 template <class E> struct is_wave_epi<E, std::void_t<decltype(E::WAVE)>> : std::bool_constant<E::WAVE> {};
 
+// 16-byte store of an output that is read again only by a later kernel:
+// non-temporal, so it does not push operand lines out of the L2
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_out(void* p, uint4 x) {
+  const u32x4_t v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   return make_uint2(f2bf2(a, b), f2bf2(c, d));
 }
@@ -257,7 +265,7 @@ struct G4Store {
         const int v = c.lane + 64 * q, r = v >> 3, ch = v & 7;
         const uint4 x = *reinterpret_cast<const uint4*>(L + r * LD + ch * 8);
         if (rb + r < c.m_valid)
-          *reinterpret_cast<uint4*>(p.C + (c.out_row0 + rb + r) * p.ldc + c.n0 + c.wn * 64 + ch * 8) = x;
+          st_out(p.C + (c.out_row0 + rb + r) * p.ldc + c.n0 + c.wn * 64 + ch * 8, x);
       }
     }
   }
@@ -345,14 +353,14 @@ struct G4SwiGLU {
         const int v = c.lane + 64 * q, r = v >> 3, ch = v & 7;
         const uint4 x = *reinterpret_cast<const uint4*>(Lh + r * LH + ch * 8);
         const int gc = ch < 4 ? j0 + ch * 8 : p.n + j0 + (ch - 4) * 8;
-        if (rb + r < c.m_valid) *reinterpret_cast<uint4*>(p.H + (c.out_row0 + rb + r) * ldh + gc) = x;
+        if (rb + r < c.m_valid) st_out(p.H + (c.out_row0 + rb + r) * ldh + gc, x);
       }
 #pragma unroll
       for (int q = 0; q < 2; ++q) {  // A: 32 rows x 4 chunks
         const int v = c.lane + 64 * q, r = v >> 2, ch = v & 3;
         const uint4 x = *reinterpret_cast<const uint4*>(La + r * LA + ch * 8);
         if (rb + r < c.m_valid)
-          *reinterpret_cast<uint4*>(p.A + (c.out_row0 + rb + r) * (long long)p.n + j0 + ch * 8) = x;
+          *reinterpret_cast<uint4*>(p.A + (c.out_row0 + rb + r) * (long long)p.n + j0 + ch * 8) = x;  // read next by K2
       }
     }
   }
