@@ -235,8 +235,10 @@ hipError_t dh(const GemmDims& g, const void* d_o, const void* w2, const void* H,
       Operand b{w2, nullptr, (long long)n * d, d};
       typename Epi::Params ep{reinterpret_cast<const bf16_t*>(H), row_gate, reinterpret_cast<bf16_t*>(dH),
                               reinterpret_cast<bf16_t*>(As), dS_part, n, n / g4::BN};
-      return run_row256<false, false, Epi>(s, a, b, (size_t)g.T * d * 2, (size_t)n * d * 2, ep,
-                                           row_tiles_bound(g.cap, E, g4::BM) * (n / g4::BN), st);
+      const long long tiles = row_tiles_bound(g.cap, E, g4::BM) * (n / g4::BN);
+      if (d % g5::BK == 0 && d >= 512)  // k = 64 stages, H loads of the epilogue one pass ahead
+        return run_gemm5<false, false, g5::G5DH>(s, a, b, (size_t)g.T * d * 2, (size_t)n * d * 2, ep, tiles, st);
+      return run_gemm4<false, false, false, Epi>(s, a, b, (size_t)g.T * d * 2, (size_t)n * d * 2, ep, tiles, st);
     }
     if (bn == 128) return dh_t<T, 128>(g, d_o, w2, H, row_token, row_gate, offsets, dH, As, dS_part, st);
     return dh_t<T, 64>(g, d_o, w2, H, row_token, row_gate, offsets, dH, As, dS_part, st);

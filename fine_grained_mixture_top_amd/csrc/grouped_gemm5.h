@@ -121,6 +121,88 @@ __device__ __forceinline__ void mma(f32x16_v (&acc)[2][4], const Frags<BMN>& f) 
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.n[i], f.m[j], acc[i][j], 0, 0, 0);
 }
 
+// dH epilogue with its cached-H loads issued one pass ahead.  Same
+// arithmetic as EpiDH (recompute A from H, dS partial, dSwiGLU, A_s = gate A)
+// on the 256-column tile; each pass covers 32 rows, and every thread owns
+// chunk tid % 32 of rows tid / 32 and tid / 32 + 16.  The H values, gates of
+// pass p + 1 are loaded before pass p is computed, so their latency is not
+// paid once per pass.
+struct G5DH {
+  using Params = typename EpiDH<bf16_t, EROWS, BN, NTH>::Params;
+  static constexpr bool PREFETCH = true;
+  struct Pre {
+    uint4 g[2], u[2];
+    float gate[2];
+  };
+  __device__ __forceinline__ static long long row_of(const TileCtx& c, int pass, int it) {
+    const int r = pass * EROWS + (c.tid >> 5) + 16 * it;
+    return c.out_row0 + (r < c.m_valid ? r : c.m_valid - 1);
+  }
+  __device__ __forceinline__ static void load(const Params& p, const TileCtx& c, int pass, Pre& x) {
+    const long long ldh = 2LL * p.n;
+    const int col = c.n0 + (c.tid & 31) * 8;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const long long grow = row_of(c, pass, it);
+      x.g[it] = *reinterpret_cast<const uint4*>(p.H + grow * ldh + col);
+      x.u[it] = *reinterpret_cast<const uint4*>(p.H + grow * ldh + p.n + col);
+      x.gate[it] = p.gate[grow];
+    }
+  }
+  __device__ __forceinline__ static void unpack8(const uint4 w, float (&v)[8]) {
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void run(const Params& p, const TileCtx& c, int pass, const float* Cs,
+                                             const Pre& x) {
+    const long long ldh = 2LL * p.n;
+    const int ch = c.tid & 31;
+    const int col = c.n0 + ch * 8;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int r = (c.tid >> 5) + 16 * it;
+      const bool valid = pass * EROWS + r < c.m_valid;
+      const long long grow = row_of(c, pass, it);
+      float dap[8], g[8], u[8];
+      const float4 d0 = *reinterpret_cast<const float4*>(Cs + r * LDC + ch * 8);
+      const float4 d1 = *reinterpret_cast<const float4*>(Cs + r * LDC + ch * 8 + 4);
+      dap[0] = d0.x; dap[1] = d0.y; dap[2] = d0.z; dap[3] = d0.w;
+      dap[4] = d1.x; dap[5] = d1.y; dap[6] = d1.z; dap[7] = d1.w;
+      unpack8(x.g[it], g);
+      unpack8(x.u[it], u);
+      const float gt = x.gate[it];
+      float dg[8], du[8], as[8];
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float sg = sigmoidf_(g[i]);
+        const float sl = g[i] * sg;
+        const float a = sl * u[i];
+        ps += dap[i] * a;
+        const float da = gt * dap[i];
+        dg[i] = da * u[i] * sg * (1.f + g[i] * (1.f - sg));
+        du[i] = da * sl;
+        as[i] = gt * a;
+      }
+      if (valid) {
+        st8<bf16_t>(p.dH + grow * ldh + col, dg);
+        st8<bf16_t>(p.dH + grow * ldh + p.n + col, du);
+        st8<bf16_t>(p.As + grow * (long long)p.n + col, as);
+      }
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) ps += __shfl_xor(ps, o, 64);
+      if (valid && ch == 0) p.dS_part[grow * p.NT + c.nt] = ps;
+    }
+  }
+};
+
+template <class E, class = void> struct has_prefetch : std::false_type {};
+template <class E> struct has_prefetch<E, std::void_t<decltype(E::PREFETCH)>> : std::bool_constant<E::PREFETCH> {};
+
 // A: routed rows (A.idx gathers them), k-contiguous, K = s.K.  B: the
 // expert's weights, [N][K] (BMN = false) or [K][N] (BMN = true; PAIRED
 // arranges the columns for G4SwiGLU).  Workgroup v takes tiles v, v + G, ...
@@ -275,6 +357,35 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     }
     if constexpr (g4::is_wave_epi<Epi>::value) {
       Epi::run(ep, c, acc, smem + WE_OFF + w * g4::WAVE_LDS);
+    } else if constexpr (has_prefetch<Epi>::value) {
+      // eight passes of 32 rows, each pass's global operands loaded one ahead
+      typename Epi::Pre cur, nxt;
+      Epi::load(ep, c, 0, cur);
+#pragma unroll 1
+      for (int p = 0; p < BM / EROWS; ++p) {
+        if (c.m_valid - p * EROWS <= 0) break;  // uniform over the workgroup
+        if (wm == (p >> 2)) {
+          const int jp = p & 3;
+          const int cl = lane & 31, hl = lane >> 5;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (j != jp) continue;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int eg = 0; eg < 4; ++eg) {
+                const float4 v = make_float4(acc[i][j][4 * eg], acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2],
+                                             acc[i][j][4 * eg + 3]);
+                *reinterpret_cast<float4*>(Cs + cl * LDC + wn * 64 + 32 * i + 8 * eg + 4 * hl) = v;
+              }
+          }
+        }
+        __syncthreads();
+        if (p + 1 < BM / EROWS) Epi::load(ep, c, p + 1, nxt);
+        Epi::run(ep, c, p, Cs, cur);
+        cur = nxt;
+        __syncthreads();
+      }
     } else {
       // eight passes of 32 rows: pass p holds block j = p % 4 of the waves
       // of m half p / 4
