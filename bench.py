@@ -77,7 +77,10 @@ def kernel_work(name, w, P, es):
     # bandwidth-bound kernels: bytes that must cross HBM once
     bytes_ = {
         "agg_o": P * d * es + T * d * es + P * 8 + (T + 1) * 4,
-        "agg_dx": P * d * es + T * d * es + P * 12 + (T + 1) * 4 + E * d * es,
+        # dXt rows, dX out, tok_row / row_expert, W_r^T, and the folded router
+        # backward: dS partials and gates in, dS / dz per row and dense dz out
+        "agg_dx": P * d * es + T * d * es + P * 8 + (T + 1) * 4 + E * d * es
+                  + P * (4 + 4 + 4 + 4) + T * E * es,
         "route_select": T * E * 4 + T * w.K * 8 + P * 16 + T * E * (1 + 1 + 4),
         "router_grad": P * (8 + 4 + 4 + 4) + T * E * es,
         "wr_t": 2 * E * d * es, "db": P * 4,

@@ -9,7 +9,8 @@
 // Router backward ([B] algorithm paragraph: the router gradient comes from
 // the reordered contraction, no cached Y): dS per row is the sum of the dH
 // kernel's per-column-tile partials; dz = gate * (dS - sum over the token's
-// set of gate * dS) is the softmax-over-set backward.
+// set of gate * dS) is the softmax-over-set backward.  It is computed per
+// token inside the dX aggregation, which walks the token's rows anyway.
 #include "device_common.h"
 #include "launch.h"
 
@@ -129,18 +130,72 @@ k_aggregate_o(const T* __restrict__ Y, const float* __restrict__ row_gate,
   }
 }
 
-// dX[t] = sum over token t's rows (ascending) of dXt[r] + dz_r * W_r^T[e_r]
+// dX[t] = sum over token t's rows (ascending) of dXt[r] + dz_r * W_r^T[e_r],
+// with the router backward of the token folded in: dS_r = sum of the row's
+// dH-epilogue partials (fixed order), dz_r = g_r (dS_r - sum_j g_j dS_j) over
+// the token's set; dS_r and dz_r are written per row and dz as the token's
+// dense row (zeros outside its set) for the router weight gradient.  One wave
+// per token; its dense dz row lives in LDS (E floats per wave).
 template <typename T, int CPL>
 __global__ void __launch_bounds__(256)
-k_aggregate_dx(const T* __restrict__ dXt, const float* __restrict__ dz_row,
-               const int32_t* __restrict__ row_expert, const T* __restrict__ w_rT,
-               const int32_t* __restrict__ tok_ptr, const int32_t* __restrict__ tok_row, int Tn, int d,
-               T* __restrict__ dX) {
+k_aggregate_dx(const T* __restrict__ dXt, const float* __restrict__ dS_part, int nparts,
+               const float* __restrict__ row_gate, const int32_t* __restrict__ row_expert,
+               const T* __restrict__ w_rT, const int32_t* __restrict__ tok_ptr, const int32_t* __restrict__ tok_row,
+               int Tn, int d, int E, float* __restrict__ dS_row, float* __restrict__ dz_row,
+               T* __restrict__ dz_dense, T* __restrict__ dX) {
+  extern __shared__ float dzs[];  // [4][E]
   constexpr int V = 16 / sizeof(T);
-  const int lane = threadIdx.x & 63;
-  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  if (t >= Tn) return;
-  const int j0 = tok_ptr[t], j1 = tok_ptr[t + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
+  const bool live = t < Tn;
+  float* dense = dzs + wave * E;
+  for (int e = lane; e < E; e += 64) dense[e] = 0.f;
+  __syncthreads();
+  int j0 = 0, j1 = 0;
+  if (live) {
+    j0 = tok_ptr[t];
+    j1 = tok_ptr[t + 1];
+  }
+  if (live && j1 - j0 <= 64) {
+    // one row per lane, kept in registers
+    const bool mine = j0 + lane < j1;
+    const int r = mine ? tok_row[j0 + lane] : 0;
+    float sv = 0.f, gv = 0.f;
+    int ev = 0;
+    if (mine) {
+      for (int q = 0; q < nparts; ++q) sv += dS_part[(size_t)r * nparts + q];
+      gv = row_gate[r];
+      ev = row_expert[r];
+    }
+    const float tot = wave_sum(gv * sv);
+    if (mine) {
+      const float dz = gv * (sv - tot);
+      dS_row[r] = sv;
+      dz_row[r] = dz;
+      dense[ev] = dz;
+    }
+  } else if (live) {
+    float part = 0.f;
+    for (int j = j0 + lane; j < j1; j += 64) {
+      const int r = tok_row[j];
+      float sv = 0.f;
+      for (int q = 0; q < nparts; ++q) sv += dS_part[(size_t)r * nparts + q];
+      part += row_gate[r] * sv;
+    }
+    const float tot = wave_sum(part);
+    for (int j = j0 + lane; j < j1; j += 64) {
+      const int r = tok_row[j];
+      float sv = 0.f;
+      for (int q = 0; q < nparts; ++q) sv += dS_part[(size_t)r * nparts + q];
+      const float dz = row_gate[r] * (sv - tot);
+      dS_row[r] = sv;
+      dz_row[r] = dz;
+      dense[row_expert[r]] = dz;
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  for (int e = lane; e < E; e += 64) dz_dense[(size_t)t * E + e] = Elem<T>::from_f(dense[e]);
   const int nch = d / V;
   for (int cb = 0; cb < nch; cb += 64 * CPL) {
     float acc[CPL][V];
@@ -155,8 +210,8 @@ k_aggregate_dx(const T* __restrict__ dXt, const float* __restrict__ dz_row,
       for (int u = 0; u < UNR; ++u) {
         const bool ok = j + u < j1;
         const int r = ok ? tok_row[j + u] : 0;
-        g[u] = ok ? dz_row[r] : 0.f;
         const int e = ok ? row_expert[r] : 0;
+        g[u] = ok ? dense[e] : 0.f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const int ch = cb + lane + 64 * c;
@@ -182,46 +237,6 @@ k_aggregate_dx(const T* __restrict__ dXt, const float* __restrict__ dz_row,
       if (ch < nch) store_vec<T>(dX + (size_t)t * d + ch * V, acc[c]);
     }
   }
-}
-
-// One wave per token.  dS_r = sum of the row's partials (fixed order);
-// dz_r = g_r (dS_r - sum_j g_j dS_j).  Also writes the token's dense row of dz
-// (zeros outside its set) for the router weight-gradient GEMM.
-template <typename T>
-__global__ void __launch_bounds__(256)
-k_router_grad(const float* __restrict__ dS_part, int nparts, const float* __restrict__ row_gate,
-              const int32_t* __restrict__ row_expert, const int32_t* __restrict__ tok_ptr,
-              const int32_t* __restrict__ tok_row, int Tn, int E, float* __restrict__ dS_row,
-              float* __restrict__ dz_row, T* __restrict__ dz_dense) {
-  __shared__ float dense[4][1024];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  const bool live = t < Tn;
-  for (int e = lane; e < E; e += 64) dense[wave][e] = 0.f;
-  __syncthreads();
-  if (live) {
-    const int j0 = tok_ptr[t], j1 = tok_ptr[t + 1];
-    float part = 0.f;
-    for (int j = j0 + lane; j < j1; j += 64) {
-      const int r = tok_row[j];
-      float s = 0.f;
-      for (int p = 0; p < nparts; ++p) s += dS_part[(size_t)r * nparts + p];
-      part += row_gate[r] * s;
-    }
-    const float mean = wave_sum(part);
-    for (int j = j0 + lane; j < j1; j += 64) {
-      const int r = tok_row[j];
-      float s = 0.f;
-      for (int p = 0; p < nparts; ++p) s += dS_part[(size_t)r * nparts + p];
-      const float dz = row_gate[r] * (s - mean);
-      dS_row[r] = s;
-      dz_row[r] = dz;
-      dense[wave][row_expert[r]] = dz;
-    }
-  }
-  __syncthreads();
-  if (live)
-    for (int e = lane; e < E; e += 64) dz_dense[(size_t)t * E + e] = Elem<T>::from_f(dense[wave][e]);
 }
 
 // db[e] = sum of dz over expert e's rows (fixed per-thread split and tree).
@@ -302,42 +317,27 @@ hipError_t launch_aggregate_o(int dtype, const void* Y, const float* row_gate, c
 }
 
 template <typename TE, int CPL>
-void agg_dx_launch(const void* dXt, const float* dz_row, const int32_t* row_expert, const void* w_rT,
-                   const int32_t* tok_ptr, const int32_t* tok_row, int T, int d, void* dX, hipStream_t st) {
-  hipLaunchKernelGGL((k_aggregate_dx<TE, CPL>), dim3((T + 3) / 4), dim3(256), 0, st, (const TE*)dXt, dz_row,
-                     row_expert, (const TE*)w_rT, tok_ptr, tok_row, T, d, (TE*)dX);
+void agg_dx_launch(const AggDxArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_aggregate_dx<TE, CPL>), dim3((a.T + 3) / 4), dim3(256), (size_t)4 * a.E * sizeof(float), st,
+                     (const TE*)a.dXt, a.dS_part, a.nparts, a.row_gate, a.row_expert, (const TE*)a.w_rT, a.tok_ptr,
+                     a.tok_row, a.T, a.d, a.E, a.dS_row, a.dz_row, (TE*)a.dz_dense, (TE*)a.dX);
 }
 template <typename TE>
-void agg_dx_t(const void* dXt, const float* dz_row, const int32_t* row_expert, const void* w_rT,
-              const int32_t* tok_ptr, const int32_t* tok_row, int T, int d, void* dX, hipStream_t st) {
-  switch (agg_cpl(d / (16 / (int)sizeof(TE)))) {
-    case 1: agg_dx_launch<TE, 1>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st); break;
-    case 2: agg_dx_launch<TE, 2>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st); break;
-    case 3: agg_dx_launch<TE, 3>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st); break;
-    default: agg_dx_launch<TE, 4>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st); break;
+void agg_dx_t(const AggDxArgs& a, hipStream_t st) {
+  switch (agg_cpl(a.d / (16 / (int)sizeof(TE)))) {
+    case 1: agg_dx_launch<TE, 1>(a, st); break;
+    case 2: agg_dx_launch<TE, 2>(a, st); break;
+    case 3: agg_dx_launch<TE, 3>(a, st); break;
+    default: agg_dx_launch<TE, 4>(a, st); break;
   }
 }
 
-hipError_t launch_aggregate_dx(int dtype, const void* dXt, const float* dz_row, const int32_t* row_expert,
-                               const void* w_rT, const int32_t* tok_ptr, const int32_t* tok_row, int T,
-                               int d, void* dX, hipStream_t st) {
-  if (dtype == DT_BF16) agg_dx_t<bf16_t>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st);
-  else agg_dx_t<float>(dXt, dz_row, row_expert, w_rT, tok_ptr, tok_row, T, d, dX, st);
+hipError_t launch_aggregate_dx(int dtype, const AggDxArgs& a, hipStream_t st) {
+  if (dtype == DT_BF16) agg_dx_t<bf16_t>(a, st);
+  else agg_dx_t<float>(a, st);
   return hipGetLastError();
 }
 
-hipError_t launch_router_grad(int dtype, const float* dS_part, int nparts, const float* row_gate,
-                              const int32_t* row_expert, const int32_t* tok_ptr, const int32_t* tok_row,
-                              int T, int E, float* dS_row, float* dz_row, void* dz_dense, hipStream_t st) {
-  dim3 grid((T + 3) / 4), block(256);
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(k_router_grad<bf16_t>, grid, block, 0, st, dS_part, nparts, row_gate, row_expert,
-                       tok_ptr, tok_row, T, E, dS_row, dz_row, (bf16_t*)dz_dense);
-  else
-    hipLaunchKernelGGL(k_router_grad<float>, grid, block, 0, st, dS_part, nparts, row_gate, row_expert,
-                       tok_ptr, tok_row, T, E, dS_row, dz_row, (float*)dz_dense);
-  return hipGetLastError();
-}
 
 hipError_t launch_bias_grad(const float* dz_row, const int32_t* offsets, int E, float* db, hipStream_t st) {
   hipLaunchKernelGGL(k_bias_grad, dim3(E), dim3(1024), 0, st, dz_row, offsets, db);

@@ -83,17 +83,25 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
 hipError_t launch_aggregate_o(int dtype, const void* Y, const float* row_gate,
                               const int32_t* tok_ptr, const int32_t* tok_row, int T, int d,
                               void* O, hipStream_t st);
-hipError_t launch_router_grad(int dtype, const float* dS_part, int nparts, const float* row_gate,
-                              const int32_t* row_expert, const int32_t* tok_ptr,
-                              const int32_t* tok_row, int T, int E, float* dS_row, float* dz_row,
-                              void* dz_dense, hipStream_t st);
 hipError_t launch_bias_grad(const float* dz_row, const int32_t* offsets, int E, float* db,
                             hipStream_t st);
 hipError_t launch_transpose(int dtype, const void* src, int rows, int cols, void* dst,
                             hipStream_t st);
-hipError_t launch_aggregate_dx(int dtype, const void* dXt, const float* dz_row,
-                               const int32_t* row_expert, const void* w_rT,
-                               const int32_t* tok_ptr, const int32_t* tok_row, int T, int d,
-                               void* dX, hipStream_t st);
-
+// dX aggregation with the router backward folded in (see aggregate_kernels.hip)
+struct AggDxArgs {
+  const void* dXt;         // [cap][d]
+  const float* dS_part;    // [cap][nparts] dH-epilogue partials of dS
+  int nparts;
+  const float* row_gate;   // [cap]
+  const int32_t* row_expert;
+  const void* w_rT;        // [E][d]
+  const int32_t* tok_ptr;  // [T+1]
+  const int32_t* tok_row;  // [cap]
+  int T, d, E;
+  float* dS_row;           // [cap] out
+  float* dz_row;           // [cap] out
+  void* dz_dense;          // [T][E] out (dtype)
+  void* dX;                // [T][d] out
+};
+hipError_t launch_aggregate_dx(int dtype, const AggDxArgs& a, hipStream_t st);
 }  // namespace moe

@@ -240,15 +240,15 @@ int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1
   // dH kernel: dA' = dO W2^T with the recompute-A epilogue (dH, A_s, dS parts)
   const GemmDims g = gemm_dims(desc);
   MOE_TRY(MOE_K_DH, launch_dh(g, d_o, w2, h_cache, R.row_token, R.row_gate, R.offsets, dH, As, dS_part, st));
-  // router gradient: dS -> dz (per row and dense), dW_r = X^T dz
-  MOE_TRY(MOE_K_ROUTER_GRAD, launch_router_grad(D.dtype, dS_part, dh_partials(g), R.row_gate, R.row_expert, R.tok_ptr,
-                             R.tok_row, D.T, D.E, dS_row, dz_row, dz_dense, st));
-  MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, (float*)(w + L.off[8]), st));
-  // activation gradient: dXt = dH W1^T, then dX = sum of dXt + dz W_r^T
+  // activation gradient: dXt = dH W1^T, then dX = sum of dXt + dz W_r^T, with
+  // the router backward (dS -> dz per row and dense) folded into the
+  // aggregation; then dW_r = X^T dz
   MOE_TRY(MOE_K_WR_T, launch_transpose(D.dtype, w_r, D.d, D.E, w_rT, st));
   MOE_TRY(MOE_K_DXT, launch_dxt(g, dH, w1, R.offsets, dXt, st));
-  MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, dXt, dz_row, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T, D.d, dx,
-                              st));
+  const AggDxArgs ax{dXt,    dS_part, dh_partials(g), R.row_gate, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T,
+                     D.d,    D.E,     dS_row,         dz_row,     dz_dense,     dx};
+  MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, ax, st));
+  MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, (float*)(w + L.off[8]), st));
   // weight gradients
   void* wws = wgt_ws_bytes(g) ? (void*)(w + L.off[9]) : nullptr;
   MOE_TRY(MOE_K_DW1, launch_dw1(g, x, dH, R.row_token, R.offsets, dw1, wws, st));

@@ -82,11 +82,11 @@ extern "C" {
 #define MOE_K_DOWN          3   /* K2: A w2 -> Y                                   */
 #define MOE_K_AGG_O         4   /* K3: O = sum of gate * Y                         */
 #define MOE_K_DH            5   /* K4: dO w2^T with the dH epilogue -> dH, A_s, dS */
-#define MOE_K_ROUTER_GRAD   6   /* dS -> dz (softmax over the token's set)         */
+#define MOE_K_ROUTER_GRAD   6   /* reserved: dS -> dz now runs inside MOE_K_AGG_DX */
 #define MOE_K_DWR           7   /* dw_r = x^T dz                                   */
 #define MOE_K_WR_T          8   /* w_r transposed for the dX aggregation           */
 #define MOE_K_DXT           9   /* K5: dH w1^T -> dXt                              */
-#define MOE_K_AGG_DX       10   /* K6: dX = sum of dXt + dz w_r^T                  */
+#define MOE_K_AGG_DX       10   /* K6: dS -> dz, dX = sum of dXt + dz w_r^T        */
 #define MOE_K_DW1          11   /* K7: dw1 = x_g^T dH                              */
 #define MOE_K_DW2          12   /* K8: dw2 = A_s^T dO_g                            */
 #define MOE_K_DB           13   /* db = per-expert sum of dz                       */

@@ -79,6 +79,9 @@ LAYER_CASES = [
     # k = 64 stage kernel; d = 256 above keeps the k = 32 one in use
     W("bf16_k64_stages", 1200, 512, 16, 512, 2, "bf16", seed=19),
     W("bf16_k64_stages_ragged", 700, 768, 8, 512, 3, "bf16", seed=20),
+    # more than 64 rows per token: the dX aggregation's router backward takes
+    # its multi-pass branch
+    W("bf16_many_slots", 300, 256, 80, 64, 72, "bf16", seed=21),
 ]
 
 
