@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--round-mode", type=int, default=0)
     ap.add_argument("--tile", type=int, default=128,
                     help="token-rounding tile (128 or 256; 256 matches the bf16 GEMMs' row tile)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the unfused layer (separate gather / SwiGLU kernels, X_g H A Y cached, "
+                         "dS = <dO_g, Y>) instead of the fused one, for comparison")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the oracle's CPU baseline sample (0 = skip, -1 = as many as "
                          "fit a 4 TFLOP budget, about 20 s of fp64 work, capped at the workload's T)")
@@ -70,7 +73,7 @@ def kernel_work(name, w, P, es):
     flops = {
         "router_logits": 2.0 * T * d * E, "up": 4.0 * P * d * n, "down": 2.0 * P * n * d,
         "dh": 2.0 * P * d * n, "dxt": 4.0 * P * d * n, "dw1": 4.0 * P * d * n,
-        "dw2": 2.0 * P * n * d, "dwr": 2.0 * T * d * E,
+        "dw2": 2.0 * P * n * d, "dwr": 2.0 * T * d * E, "da": 2.0 * P * d * n,
     }
     if name in flops:
         return flops[name], "flop"
@@ -84,6 +87,9 @@ def kernel_work(name, w, P, es):
         "route_select": T * E * 4 + T * w.K * 8 + P * 16 + T * E * (1 + 1 + 4),
         "router_grad": P * (8 + 4 + 4 + 4) + T * E * es,
         "wr_t": 2 * E * d * es, "db": P * 4,
+        # unfused layer: row gather (read + write), SwiGLU, dS = <dO_g, Y>, SwiGLU backward
+        "gather": 2 * P * d * es + P * 4, "swiglu": 3 * P * n * es, "row_dot": 2 * P * d * es + P * 4,
+        "swiglu_bwd": P * (n + 2 * n + n) * es + P * 4 + P * (2 * n + n) * es,
     }
     return float(bytes_.get(name, 0)), "byte"
 
@@ -97,6 +103,10 @@ def memory_report(w, L, es):
     P = w.P
     cap = int(L.routing.cap)
     routing = sum(t.numel() * t.element_size() for t in L.routing.tensors())
+    if L.unfused:
+        cache = B.moe_unfused_cache_bytes(L.desc)
+        return {"cached_bytes": cache + routing, "activation_cache_bytes": cache, "workspace_fwd_bytes": 0,
+                "workspace_bwd_bytes": B.moe_workspace_bytes(L.desc, B.MOE_WS_BWD_UNFUSED)}
     return {
         "cached_bytes": cap * 2 * w.n * es + routing,
         "h_cache_bytes": cap * 2 * w.n * es,
@@ -166,7 +176,7 @@ def main():
     x, wr, w1, w2, do = (dev(a[k]) for k in ("x", "w_r", "w1", "w2", "d_o"))
     bias = None if a["bias"] is None else torch.from_numpy(a["bias"]).cuda()
     desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=args.round_mode, tile=args.tile)
-    L = B.Layer(desc)
+    L = B.Layer(desc, unfused=args.unfused)
 
     def step():
         L.route(x, wr, bias)
@@ -251,11 +261,12 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "n": w.n, "K": w.K,
-                   "round_mode": args.round_mode, "tile": args.tile, "rows": P, "parallelism": "single GPU"},
+                   "round_mode": args.round_mode, "tile": args.tile, "rows": P, "parallelism": "single GPU",
+                   "layer": "unfused" if args.unfused else "fused"},
         "mfma_peak_frac": round(tflops / peak_mfma, 4),
         "tokens_per_s": round(w.T / (ms_step * 1e-3), 1),
         "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
-                     "unit": dk["unit"], "frac": dk["frac"], "traffic": measured_traffic(w.name, dom)},
+                     "unit": dk["unit"], "frac": dk["frac"], "traffic": None if args.unfused else measured_traffic(w.name, dom)},
         "kernels": {k: {kk: v for kk, v in d.items() if kk != "work"} for k, d in kernels.items()},
         "memory": memory_report(w, L, es),
         "routing": routing_report(L, args.tile),

@@ -25,14 +25,15 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUND_OFF, MOE_ROUND_NEAREST, MOE_ROUND_STOCHASTIC = 0, 1, 2
 MOE_FLAG_SCORES_GIVEN = 1
 MOE_FLAG_GEMM_128 = 2
-MOE_WS_ROUTE, MOE_WS_FWD, MOE_WS_BWD = 0, 1, 2
+MOE_WS_ROUTE, MOE_WS_FWD, MOE_WS_BWD, MOE_WS_BWD_UNFUSED = 0, 1, 2, 3
 MOE_ITEM_Y, MOE_ITEM_A, MOE_ITEM_DH, MOE_ITEM_AS, MOE_ITEM_DXT, MOE_ITEM_DS, MOE_ITEM_DZ = range(7)
 KERNEL_NAMES = ["router_logits", "route_select", "up", "down", "agg_o", "dh", "router_grad", "dwr",
-                "wr_t", "dxt", "agg_dx", "dw1", "dw2", "db"]
+                "wr_t", "dxt", "agg_dx", "dw1", "dw2", "db",
+                "gather", "swiglu", "row_dot", "da", "swiglu_bwd"]
 (MOE_K_ROUTER_LOGITS, MOE_K_ROUTE_SELECT, MOE_K_UP, MOE_K_DOWN, MOE_K_AGG_O, MOE_K_DH,
  MOE_K_ROUTER_GRAD, MOE_K_DWR, MOE_K_WR_T, MOE_K_DXT, MOE_K_AGG_DX, MOE_K_DW1, MOE_K_DW2,
- MOE_K_DB) = range(14)
-MOE_K_COUNT = 14
+ MOE_K_DB, MOE_K_GATHER, MOE_K_SWIGLU, MOE_K_ROW_DOT, MOE_K_DA, MOE_K_SWIGLU_BWD) = range(19)
+MOE_K_COUNT = 19
 
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16}
@@ -88,6 +89,11 @@ def lib() -> ctypes.CDLL:
         L.moe_fwd.restype = i32
         L.moe_bwd.argtypes = [pdesc, vp, vp, vp, vp, prout, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_bwd.restype = i32
+        L.moe_unfused_cache_bytes.argtypes, L.moe_unfused_cache_bytes.restype = [pdesc], sz
+        L.moe_fwd_unfused.argtypes = [pdesc, vp, vp, vp, prout, vp, vp, sz, vp]
+        L.moe_fwd_unfused.restype = i32
+        L.moe_bwd_unfused.argtypes = [pdesc, vp, vp, vp, vp, prout, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_bwd_unfused.restype = i32
         L.moe_strerror.argtypes, L.moe_strerror.restype = [i32], ctypes.c_char_p
         _lib = L
     return _lib
@@ -244,19 +250,44 @@ def moe_bwd(desc, x, w_r, w1, w2, routing: Routing, h_cache, d_o, dx, dw_r, dw1,
                                     _stream(stream)))
 
 
+def moe_unfused_cache_bytes(desc: MoeDesc) -> int:
+    return lib().moe_unfused_cache_bytes(ctypes.byref(desc))
+
+
+def moe_fwd_unfused(desc, x, w1, w2, routing: Routing, o, cache, stream=None):
+    _check("moe_fwd_unfused", lib().moe_fwd_unfused(ctypes.byref(desc), _p(x), _p(w1), _p(w2),
+                                                    ctypes.byref(routing.c), _p(o), _p(cache), cache.numel(),
+                                                    _stream(stream)))
+
+
+def moe_bwd_unfused(desc, x, w_r, w1, w2, routing: Routing, cache, d_o, dx, dw_r, dw1, dw2, ds, db, ws,
+                    stream=None):
+    _check("moe_bwd_unfused", lib().moe_bwd_unfused(ctypes.byref(desc), _p(x), _p(w_r), _p(w1), _p(w2),
+                                                    ctypes.byref(routing.c), _p(cache), _p(d_o), _p(dx),
+                                                    _p(dw_r), _p(dw1), _p(dw2), _p(ds), _p(db), _p(ws),
+                                                    ws.numel(), _stream(stream)))
+
+
 class Layer:
     """One MoE layer's buffers plus route / forward / backward calls.
 
     Inputs are device tensors of the layer dtype: x [T,d], w_r [d,E],
-    w1 [E,d,2n], w2 [E,n,d], optional fp32 bias [E]."""
+    w1 [E,d,2n], w2 [E,n,d], optional fp32 bias [E].  unfused=True runs the
+    unfused layer (moe_fwd_unfused / moe_bwd_unfused) with its activation
+    cache in place of h_cache."""
 
-    def __init__(self, desc: MoeDesc, device="cuda"):
+    def __init__(self, desc: MoeDesc, device="cuda", unfused: bool = False):
         self.desc = desc
+        self.unfused = unfused
         dt = TORCH_DTYPE[desc.dtype]
         T, d, E, n = desc.T, desc.d, desc.E, desc.n
         self.routing = Routing(desc, device)
         cap = self.routing.cap
-        self.h_cache = torch.empty((cap, 2 * n), dtype=dt, device=device)
+        if unfused:
+            self.cache = torch.empty(max(moe_unfused_cache_bytes(desc), 256), dtype=torch.uint8, device=device)
+            self.h_cache = None
+        else:
+            self.h_cache = torch.empty((cap, 2 * n), dtype=dt, device=device)
         self.o = torch.empty((T, d), dtype=dt, device=device)
         self.dx = torch.empty((T, d), dtype=dt, device=device)
         self.dw_r = torch.empty((d, E), dtype=dt, device=device)
@@ -265,19 +296,30 @@ class Layer:
         self.ds = torch.empty(max(cap, 1), dtype=torch.float32, device=device)
         self.db = torch.empty(E, dtype=torch.float32, device=device)
         self.ws_route = workspace(desc, MOE_WS_ROUTE, device)
-        self.ws_fwd = workspace(desc, MOE_WS_FWD, device)
-        self.ws_bwd = workspace(desc, MOE_WS_BWD, device)
+        if unfused:
+            self.ws_fwd = None
+            self.ws_bwd = workspace(desc, MOE_WS_BWD_UNFUSED, device)
+        else:
+            self.ws_fwd = workspace(desc, MOE_WS_FWD, device)
+            self.ws_bwd = workspace(desc, MOE_WS_BWD, device)
 
     def route(self, x, w_r, bias=None, stream=None):
         moe_route(self.desc, x, w_r, bias, self.routing, self.ws_route, stream)
 
     def forward(self, x, w1, w2, stream=None):
-        moe_fwd(self.desc, x, w1, w2, self.routing, self.o, self.h_cache, self.ws_fwd, stream)
+        if self.unfused:
+            moe_fwd_unfused(self.desc, x, w1, w2, self.routing, self.o, self.cache, stream)
+        else:
+            moe_fwd(self.desc, x, w1, w2, self.routing, self.o, self.h_cache, self.ws_fwd, stream)
         return self.o
 
     def backward(self, x, w_r, w1, w2, d_o, stream=None):
-        moe_bwd(self.desc, x, w_r, w1, w2, self.routing, self.h_cache, d_o, self.dx, self.dw_r,
-                self.dw1, self.dw2, self.ds, self.db, self.ws_bwd, stream)
+        if self.unfused:
+            moe_bwd_unfused(self.desc, x, w_r, w1, w2, self.routing, self.cache, d_o, self.dx, self.dw_r,
+                            self.dw1, self.dw2, self.ds, self.db, self.ws_bwd, stream)
+        else:
+            moe_bwd(self.desc, x, w_r, w1, w2, self.routing, self.h_cache, d_o, self.dx, self.dw_r,
+                    self.dw1, self.dw2, self.ds, self.db, self.ws_bwd, stream)
         return self.dx
 
     def ws_view(self, item: int, count: int, dtype) -> torch.Tensor:

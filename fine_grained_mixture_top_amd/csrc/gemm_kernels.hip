@@ -519,7 +519,7 @@ hipError_t dw1_t(const GemmDims& g, const void* x, const void* dH, const int32_t
 }
 bool dw1_g4(const GemmDims& g) {
   return g.dtype == DT_BF16 && !g.small_tiles && g.d % 256 == 0 && (2 * g.n) % 256 == 0 &&
-         fits_g4((size_t)g.T * g.d * 2) && fits_g4(g.cap * 2 * g.n * 2);
+         fits_g4(std::max<size_t>(g.T, g.cap) * g.d * 2) && fits_g4(g.cap * 2 * g.n * 2);
 }
 template <typename T>
 hipError_t dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* row_token, const int32_t* offsets,
@@ -529,7 +529,8 @@ hipError_t dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* 
       const int n = g.n, d = g.d;
       Operand a{x, row_token, 0, d};
       Operand b{dH, nullptr, 0, 2 * n};
-      return wgt_g4(g, offsets, d, 2 * n, a, b, (size_t)g.T * d * 2, g.cap * 2 * n * 2, dW1, ws, st);
+      const size_t xrows = row_token ? (size_t)g.T : g.cap;  // null: x already gathered per row
+      return wgt_g4(g, offsets, d, 2 * n, a, b, xrows * d * 2, g.cap * 2 * n * 2, dW1, ws, st);
     }
     return dw1_t<T, 128, 128>(g, x, dH, row_token, offsets, dW1, st);
   } else {
@@ -550,7 +551,7 @@ hipError_t dw2_t(const GemmDims& g, const void* As, const void* d_o, const int32
 }
 bool dw2_g4(const GemmDims& g) {
   return g.dtype == DT_BF16 && !g.small_tiles && g.n % 256 == 0 && g.d % 256 == 0 &&
-         fits_g4(g.cap * g.n * 2) && fits_g4((size_t)g.T * g.d * 2);
+         fits_g4(g.cap * g.n * 2) && fits_g4(std::max<size_t>(g.T, g.cap) * g.d * 2);
 }
 template <typename T>
 hipError_t dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t* row_token, const int32_t* offsets,
@@ -560,7 +561,8 @@ hipError_t dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t
       const int n = g.n, d = g.d;
       Operand a{As, nullptr, 0, n};
       Operand b{d_o, row_token, 0, d};
-      return wgt_g4(g, offsets, n, d, a, b, g.cap * n * 2, (size_t)g.T * d * 2, dW2, ws, st);
+      const size_t orows = row_token ? (size_t)g.T : g.cap;  // null: dO already gathered per row
+      return wgt_g4(g, offsets, n, d, a, b, g.cap * n * 2, orows * d * 2, dW2, ws, st);
     }
     if (g.n % 128 == 0) return dw2_t<T, 128, 128>(g, As, d_o, row_token, offsets, dW2, st);
     return dw2_t<T, 64, 128>(g, As, d_o, row_token, offsets, dW2, st);
@@ -568,6 +570,41 @@ hipError_t dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t
     if (g.n % 128 == 0) return dw2_t<T, 128, 64>(g, As, d_o, row_token, offsets, dW2, st);
     return dw2_t<T, 64, 64>(g, As, d_o, row_token, offsets, dW2, st);
   }
+}
+
+// C[r] = A[r] W[e_r] for every routed row r (segment rows, no gather): W[e]
+// is [K][N] (w_kn) or [N][K].  Used by the unfused layer.
+template <typename T, int BL, int BN>
+hipError_t rows_gemm_t(const GemmDims& g, const void* A, int K, const void* W, int N, const int32_t* offsets,
+                       void* C, hipStream_t st) {
+  constexpr int BM = ROWS<T>;
+  using Epi = EpiStore<T, T, BM, BN>;
+  GemmShape s{offsets, g.E, 0, (N + BN - 1) / BN * BN, K, N, 1};
+  Operand a{A, nullptr, 0, K};
+  Operand b{W, nullptr, (long long)K * N, BL == B_KN ? N : K};
+  typename Epi::Params ep{reinterpret_cast<T*>(C), N, nullptr};
+  return run_gemm<T, BM, BN, false, BL, false, Epi>(s, a, b, ep, row_tiles_bound(g.cap, g.E, BM) * ((N + BN - 1) / BN),
+                                                    st);
+}
+template <typename T>
+hipError_t rows_gemm(const GemmDims& g, const void* A, int K, const void* W, int N, bool w_kn,
+                     const int32_t* offsets, void* C, hipStream_t st) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (!g.small_tiles && N % 256 == 0 && K % 32 == 0 && fits_g4(g.cap * (size_t)K * 2) &&
+        fits_g4((size_t)K * N * 2)) {
+      using Epi = g4::G4Store;
+      GemmShape s{offsets, g.E, 0, N, K, N, 1};
+      Operand a{A, nullptr, 0, K};
+      Operand b{W, nullptr, (long long)K * N, w_kn ? N : K};
+      typename Epi::Params ep{reinterpret_cast<bf16_t*>(C), N};
+      const long long tiles = row_tiles_bound(g.cap, g.E, g4::BM) * (N / g4::BN);
+      if (w_kn) return run_row256<true, false, Epi>(s, a, b, g.cap * (size_t)K * 2, (size_t)K * N * 2, ep, tiles, st);
+      return run_row256<false, false, Epi>(s, a, b, g.cap * (size_t)K * 2, (size_t)K * N * 2, ep, tiles, st);
+    }
+  }
+  constexpr int BN = Cfg<T>::BIG;
+  if (w_kn) return rows_gemm_t<T, B_KN, BN>(g, A, K, W, N, offsets, C, st);
+  return rows_gemm_t<T, B_NK, BN>(g, A, K, W, N, offsets, C, st);
 }
 
 // Router weight gradient dW_r = X^T dz: one dense reduction over all T
@@ -661,6 +698,10 @@ size_t wgt_ws_bytes(const GemmDims& g) {
   if (dw1_g4(g)) b = std::max(b, wgt_layout(g, wgt_policy(g, g.d, 2 * g.n), g.d, 2 * g.n).total);
   if (dw2_g4(g)) b = std::max(b, wgt_layout(g, wgt_policy(g, g.n, g.d), g.n, g.d).total);
   return b;
+}
+hipError_t launch_rows_gemm(const GemmDims& g, const void* A, int K, const void* W, int N, bool w_kn,
+                            const int32_t* offsets, void* C, hipStream_t st) {
+  return MOE_GDISPATCH(g, rows_gemm, A, K, W, N, w_kn, offsets, C, st);
 }
 hipError_t launch_dwr(int dtype, const void* x, const void* dz_dense, int T, int d, int E, void* dWr,
                       float* partials, hipStream_t st) {

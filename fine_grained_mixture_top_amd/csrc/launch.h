@@ -46,6 +46,23 @@ hipError_t launch_dw1(const GemmDims& g, const void* x, const void* dH, const in
 hipError_t launch_dw2(const GemmDims& g, const void* As, const void* d_o, const int32_t* row_token,
                       const int32_t* offsets, void* dW2, void* ws, hipStream_t st);
 size_t wgt_ws_bytes(const GemmDims& g);
+// dW1 / dW2 also take row_token = null: x (dO) is then already gathered per
+// row ([cap][d]).
+
+// C[r] = A[r] W[e_r] over the routed rows (no gather); W[e] is [K][N] when
+// w_kn, else [N][K]; A [cap][K], C [cap][N] (dtype).  Unfused layer.
+hipError_t launch_rows_gemm(const GemmDims& g, const void* A, int K, const void* W, int N, bool w_kn,
+                            const int32_t* offsets, void* C, hipStream_t st);
+
+// ---- unfused layer (unfused_kernels.hip); rows 0 .. *nrows-1 of cap ----
+hipError_t launch_gather_rows(int dtype, const void* src, int width, const int32_t* idx, const int32_t* nrows,
+                              size_t cap, void* dst, hipStream_t st);
+hipError_t launch_swiglu_fwd(int dtype, const void* H, int n, const int32_t* nrows, size_t cap, void* A,
+                             hipStream_t st);
+hipError_t launch_row_dot(int dtype, const void* a, const void* b, int width, const int32_t* nrows, size_t cap,
+                          float* out, hipStream_t st);
+hipError_t launch_swiglu_bwd(int dtype, const void* dAp, const void* H, const void* A, const float* gate, int n,
+                             const int32_t* nrows, size_t cap, void* dH, void* As, hipStream_t st);
 // dW_r = x^T dz_dense, reduction split in dwr_splits() chunks whose fp32
 // partials ([splits][d][E]) go to `partials` and are then summed in order.
 int dwr_splits(int T, int d, int E);

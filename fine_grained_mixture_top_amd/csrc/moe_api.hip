@@ -93,6 +93,38 @@ Layout bwd_layout(const moe_desc* d) {
   return L;
 }
 
+// Unfused layer: the activation cache kept from forward to backward holds the
+// gathered inputs X_g, H, A and Y of every routed row.
+Layout unfused_cache_layout(const moe_desc* d) {
+  Layout L{};
+  const size_t cap = capacity(d), es = elem_size(d->dtype);
+  size_t o = 0;
+  L.off[0] = o; o = up(o + cap * d->d * es);       // X_g
+  L.off[1] = o; o = up(o + cap * 2 * d->n * es);   // H
+  L.off[2] = o; o = up(o + cap * d->n * es);       // A
+  L.off[3] = o; o = up(o + cap * d->d * es);       // Y
+  L.total = o;
+  return L;
+}
+
+Layout unfused_bwd_layout(const moe_desc* d) {
+  Layout L{};
+  const size_t cap = capacity(d), es = elem_size(d->dtype);
+  size_t o = 0;
+  L.off[0] = o; o = up(o + cap * d->d * es);              // dO_g
+  L.off[1] = o; o = up(o + cap * d->n * es);              // dA' = dO_g W2^T
+  L.off[2] = o; o = up(o + cap * 2 * d->n * es);          // dH
+  L.off[3] = o; o = up(o + cap * d->n * es);              // A_s
+  L.off[4] = o; o = up(o + cap * 4 * 3);                  // dS = <dO_g, Y>, dS per row, dz per row
+  L.off[5] = o; o = up(o + (size_t)d->T * d->E * es);     // dz dense [T][E]
+  L.off[6] = o; o = up(o + (size_t)d->E * d->d * es);     // W_r^T [E][d]
+  L.off[7] = o; o = up(o + cap * d->d * es);              // dXt
+  L.off[8] = o; o = up(o + (size_t)dwr_splits(d->T, d->d, d->E) * d->d * d->E * 4);  // dW_r partials
+  L.off[9] = o; o = up(o + wgt_ws_bytes(gemm_dims(d)));                               // dW1 / dW2 plan + partials
+  L.total = o;
+  return L;
+}
+
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return MOE_OK;
   if (!ws) return MOE_EINVAL;
@@ -147,6 +179,7 @@ size_t moe_workspace_bytes(const moe_desc* desc, int which) {
     case MOE_WS_ROUTE: return route_layout(desc).total;
     case MOE_WS_FWD: return fwd_layout(desc).total;
     case MOE_WS_BWD: return bwd_layout(desc).total;
+    case MOE_WS_BWD_UNFUSED: return unfused_bwd_layout(desc).total;
     default: return 0;
   }
 }
@@ -253,6 +286,94 @@ int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1
   void* wws = wgt_ws_bytes(g) ? (void*)(w + L.off[9]) : nullptr;
   MOE_TRY(MOE_K_DW1, launch_dw1(g, x, dH, R.row_token, R.offsets, dw1, wws, st));
   MOE_TRY(MOE_K_DW2, launch_dw2(g, As, d_o, R.row_token, R.offsets, dw2, wws, st));
+  if (db) MOE_TRY(MOE_K_DB, launch_bias_grad(dz_row, R.offsets, D.E, db, st));
+  return MOE_OK;
+}
+
+size_t moe_unfused_cache_bytes(const moe_desc* desc) {
+  if (validate_desc(desc) != MOE_OK) return 0;
+  return unfused_cache_layout(desc).total;
+}
+
+int moe_fwd_unfused(const moe_desc* desc, const void* x, const void* w1, const void* w2,
+                    const moe_routing* routing, void* o, void* cache, size_t cache_bytes, void* stream) {
+  int s = validate_desc(desc);
+  if (s != MOE_OK) return s;
+  if (!x || !w1 || !w2 || !o || !routing_ok(routing)) return MOE_EINVAL;
+  const Layout C = unfused_cache_layout(desc);
+  if ((s = check_ws(cache, cache_bytes, C.total)) != MOE_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* c = (char*)cache;
+  void* Xg = c + C.off[0];
+  void* H = c + C.off[1];
+  void* A = c + C.off[2];
+  void* Y = c + C.off[3];
+  const size_t cap = capacity(desc);
+  const moe_desc& D = *desc;
+  const GemmDims g = gemm_dims(desc);
+  const moe_routing& R = *routing;
+  const int32_t* P = R.offsets + D.E;
+  MOE_TRY(MOE_K_GATHER, launch_gather_rows(D.dtype, x, D.d, R.row_token, P, cap, Xg, st));
+  MOE_TRY(MOE_K_UP, launch_rows_gemm(g, Xg, D.d, w1, 2 * D.n, true, R.offsets, H, st));
+  MOE_TRY(MOE_K_SWIGLU, launch_swiglu_fwd(D.dtype, H, D.n, P, cap, A, st));
+  MOE_TRY(MOE_K_DOWN, launch_down(g, A, w2, R.offsets, Y, st));
+  MOE_TRY(MOE_K_AGG_O, launch_aggregate_o(D.dtype, Y, R.row_gate, R.tok_ptr, R.tok_row, D.T, D.d, o, st));
+  return MOE_OK;
+}
+
+int moe_bwd_unfused(const moe_desc* desc, const void* x, const void* w_r, const void* w1, const void* w2,
+                    const moe_routing* routing, const void* cache, const void* d_o, void* dx, void* dw_r,
+                    void* dw1, void* dw2, float* ds, float* db, void* ws, size_t ws_bytes, void* stream) {
+  int s = validate_desc(desc);
+  if (s != MOE_OK) return s;
+  if (!x || !w_r || !w1 || !w2 || !cache || !d_o || !dx || !dw_r || !dw1 || !dw2 || !routing_ok(routing))
+    return MOE_EINVAL;
+  if (((uintptr_t)cache & (ALIGN - 1)) != 0) return MOE_EINVAL;
+  const Layout L = unfused_bwd_layout(desc);
+  if ((s = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  const Layout C = unfused_cache_layout(desc);
+  const char* c = (const char*)cache;
+  const void* Xg = c + C.off[0];
+  const void* H = c + C.off[1];
+  const void* A = c + C.off[2];
+  const void* Y = c + C.off[3];
+  char* w = (char*)ws;
+  const moe_desc& D = *desc;
+  const size_t cap = capacity(desc);
+  void* dOg = w + L.off[0];
+  void* dAp = w + L.off[1];
+  void* dH = w + L.off[2];
+  void* As = w + L.off[3];
+  float* dS_dot = (float*)(w + L.off[4]);
+  float* dS_row = ds ? ds : dS_dot + cap;
+  float* dz_row = dS_dot + 2 * cap;
+  void* dz_dense = w + L.off[5];
+  void* w_rT = w + L.off[6];
+  void* dXt = w + L.off[7];
+  const moe_routing& R = *routing;
+  const int32_t* P = R.offsets + D.E;
+  const GemmDims g = gemm_dims(desc);
+
+  // dO gathered per row; dS = <dO_g, Y> from the cached Y
+  MOE_TRY(MOE_K_GATHER, launch_gather_rows(D.dtype, d_o, D.d, R.row_token, P, cap, dOg, st));
+  MOE_TRY(MOE_K_ROW_DOT, launch_row_dot(D.dtype, dOg, Y, D.d, P, cap, dS_dot, st));
+  // dA' = dO_g W2^T, then the SwiGLU backward as a kernel of its own
+  MOE_TRY(MOE_K_DA, launch_rows_gemm(g, dOg, D.d, w2, D.n, false, R.offsets, dAp, st));
+  MOE_TRY(MOE_K_SWIGLU_BWD, launch_swiglu_bwd(D.dtype, dAp, H, A, R.row_gate, D.n, P, cap, dH, As, st));
+  // input and router gradients as in the fused layer, from the one dS part
+  MOE_TRY(MOE_K_WR_T, launch_transpose(D.dtype, w_r, D.d, D.E, w_rT, st));
+  MOE_TRY(MOE_K_DXT, launch_dxt(g, dH, w1, R.offsets, dXt, st));
+  const AggDxArgs ax{dXt, dS_dot, 1, R.row_gate, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T,
+                     D.d, D.E,    dS_row, dz_row, dz_dense,   dx};
+  MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, ax, st));
+  MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, (float*)(w + L.off[8]), st));
+  // weight gradients from the cached, already gathered rows
+  void* wws = wgt_ws_bytes(g) ? (void*)(w + L.off[9]) : nullptr;
+  MOE_TRY(MOE_K_DW1, launch_dw1(g, Xg, dH, nullptr, R.offsets, dw1, wws, st));
+  MOE_TRY(MOE_K_DW2, launch_dw2(g, As, dOg, nullptr, R.offsets, dw2, wws, st));
   if (db) MOE_TRY(MOE_K_DB, launch_bias_grad(dz_row, R.offsets, D.E, db, st));
   return MOE_OK;
 }

@@ -90,12 +90,19 @@ extern "C" {
 #define MOE_K_DW1          11   /* K7: dw1 = x_g^T dH                              */
 #define MOE_K_DW2          12   /* K8: dw2 = A_s^T dO_g                            */
 #define MOE_K_DB           13   /* db = per-expert sum of dz                       */
-#define MOE_K_COUNT        14
+/* launched by the unfused layer only (moe_fwd_unfused / moe_bwd_unfused) */
+#define MOE_K_GATHER       14   /* rows of x (fwd) or d_o (bwd) gathered per row   */
+#define MOE_K_SWIGLU       15   /* A = SwiGLU(H), element-wise                     */
+#define MOE_K_ROW_DOT      16   /* dS = <dO_g, Y> per row                          */
+#define MOE_K_DA           17   /* dA' = dO_g w2^T                                 */
+#define MOE_K_SWIGLU_BWD   18   /* dH, A_s from dA', H, A and the gates            */
+#define MOE_K_COUNT        19
 
 /* workspace phases */
 #define MOE_WS_ROUTE 0
 #define MOE_WS_FWD   1
 #define MOE_WS_BWD   2
+#define MOE_WS_BWD_UNFUSED 3  /* moe_bwd_unfused */
 
 /* internal workspace items exposed for inspection (moe_workspace_offset) */
 #define MOE_ITEM_Y        0  /* fwd: down-proj output Y [cap, d] (dtype)          */
@@ -238,6 +245,35 @@ int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1
             const void* w2, const moe_routing* routing, const void* h_cache, const void* d_o,
             void* dx, void* dw_r, void* dw1, void* dw2, float* ds, float* db, void* ws,
             size_t ws_bytes, void* stream);
+
+/*
+ * The unfused layer: the standard MoE workflow that SonicMoE is set against
+ * ([A] "MoE 与它的隐患": forward and backward workflow figures; [B] algorithm
+ * paragraph), for comparison with moe_fwd / moe_bwd.  Same inputs, outputs,
+ * conventions and results (to rounding) as the fused calls; what differs is
+ * the work: x and d_o are gathered into per-row buffers by kernels of their
+ * own, SwiGLU and its backward run as element-wise kernels between the GEMMs,
+ * the per-row activations X_g, H, A and Y are kept from forward to backward,
+ * and the score gradient is the row dot product dS_r = <dO_t, Y_r>.
+ *
+ * moe_unfused_cache_bytes: bytes of that activation cache: the blocks
+ *   X_g [cap,d], H [cap,2n], A [cap,n] and Y [cap,d] (dtype, rows in routed
+ *   order), in that order, each starting at a 256-byte boundary; 0 for an
+ *   invalid descriptor.  Host only.
+ * moe_fwd_unfused: as moe_fwd, with `cache` (256-byte aligned, at least
+ *   moe_unfused_cache_bytes) in place of h_cache and the forward workspace.
+ * moe_bwd_unfused: as moe_bwd, reading `cache` as the forward left it;
+ *   ws: MOE_WS_BWD_UNFUSED workspace.
+ */
+size_t moe_unfused_cache_bytes(const moe_desc* desc);
+
+int moe_fwd_unfused(const moe_desc* desc, const void* x, const void* w1, const void* w2,
+                    const moe_routing* routing, void* o, void* cache, size_t cache_bytes, void* stream);
+
+int moe_bwd_unfused(const moe_desc* desc, const void* x, const void* w_r, const void* w1,
+                    const void* w2, const moe_routing* routing, const void* cache, const void* d_o,
+                    void* dx, void* dw_r, void* dw1, void* dw2, float* ds, float* db, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /* Static text for a status code.  Host only. */
 const char* moe_strerror(int status);

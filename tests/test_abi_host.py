@@ -29,7 +29,8 @@ def lib():
 def test_header_functions_exported(lib):
     names = declared_functions()
     assert set(names) == {"moe_row_capacity", "moe_workspace_bytes", "moe_workspace_offset",
-                          "moe_route", "moe_fwd", "moe_bwd", "moe_strerror"}
+                          "moe_route", "moe_fwd", "moe_bwd", "moe_strerror",
+                          "moe_unfused_cache_bytes", "moe_fwd_unfused", "moe_bwd_unfused"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -50,7 +51,7 @@ def test_capacity_and_workspace():
     assert B.moe_row_capacity(ds) == 2000 + 16 * 127
     dcap = B.make_desc(10, 128, 16, 64, 2, "bf16", round_mode=2)
     assert B.moe_row_capacity(dcap) == 10 * 16
-    for which in (0, 1, 2):
+    for which in (0, 1, 2, 3):
         assert B.moe_workspace_bytes(d, which) > 0
         assert B.moe_workspace_bytes(d, which) % 256 == 0
     assert B.moe_workspace_bytes(d, 7) == 0
@@ -97,6 +98,32 @@ def test_null_pointers_and_workspace_rejected_before_launch(lib):
     need_b = B.moe_workspace_bytes(d, B.MOE_WS_BWD)
     assert lib.moe_bwd(ctypes.byref(d), *([4096] * 4), ctypes.byref(r), *([4096] * 6), None, None,
                        4096, need_b - 256, None) == B.MOE_EWORKSPACE
+
+
+def test_unfused_cache_and_validation(lib):
+    d = B.make_desc(256, 128, 8, 64, 2, "bf16")
+    cap = B.moe_row_capacity(d)
+    up = lambda v: (v + 255) // 256 * 256
+    # rows of X_g [d], H [2n], A [n], Y [d], each block 256-byte aligned
+    assert B.moe_unfused_cache_bytes(d) == up(cap * 128 * 2) + up(cap * 128 * 2) + up(cap * 64 * 2) + \
+        up(cap * 128 * 2)
+    bad = B.make_desc(256, 100, 8, 64, 2, "bf16")
+    assert B.moe_unfused_cache_bytes(bad) == 0
+    assert lib.moe_fwd_unfused(ctypes.byref(bad), None, None, None, None, None, None, 0, None) == B.MOE_ESHAPE
+    r = B.MoeRouting(*([4096] * len(B.ROUTING_FIELDS)))
+    need_c = B.moe_unfused_cache_bytes(d)
+    assert lib.moe_fwd_unfused(ctypes.byref(d), 4096, 4096, 4096, ctypes.byref(r), 4096, 4096, need_c - 1,
+                               None) == B.MOE_EWORKSPACE
+    assert lib.moe_fwd_unfused(ctypes.byref(d), 4096, 4096, 4096, ctypes.byref(r), 4096, 4097, need_c,
+                               None) == B.MOE_EINVAL  # misaligned cache
+    assert lib.moe_fwd_unfused(ctypes.byref(d), 4096, None, 4096, ctypes.byref(r), 4096, 4096, need_c,
+                               None) == B.MOE_EINVAL
+    need_b = B.moe_workspace_bytes(d, B.MOE_WS_BWD_UNFUSED)
+    assert need_b > 0
+    assert lib.moe_bwd_unfused(ctypes.byref(d), *([4096] * 4), ctypes.byref(r), *([4096] * 6), None, None,
+                               4096, need_b - 256, None) == B.MOE_EWORKSPACE
+    assert lib.moe_bwd_unfused(ctypes.byref(d), *([4096] * 4), ctypes.byref(r), None, *([4096] * 5), None,
+                               None, 4096, need_b, None) == B.MOE_EINVAL  # no cache
 
 
 def test_strerror():
