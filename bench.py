@@ -24,6 +24,7 @@ if ROOT not in sys.path:
 
 MFMA_PEAK_BF16 = 2500.0   # TFLOP/s, MI355X dense bf16
 MFMA_PEAK_F32 = 157.3     # TFLOP/s, MI355X fp32 (MFMA fp32 reuses this figure)
+MFMA_PEAK_FP8 = 5000.0    # TFLOP/s, MI355X dense fp8 (the MXFP8 forward GEMMs)
 HBM_PEAK = 8000.0         # GB/s
 CPU_FLOP_BUDGET = 4.0e12  # useful FLOPs of the default CPU oracle sample
 
@@ -40,6 +41,8 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="run the unfused layer (separate gather / SwiGLU kernels, X_g H A Y cached, "
                          "dS = <dO_g, Y>) instead of the fused one, for comparison")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="run the forward with MXFP8 grouped GEMMs (moe_fwd_mxfp8); the backward stays bf16")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the oracle's CPU baseline sample (0 = skip, -1 = as many as "
                          "fit a 4 TFLOP budget, about 20 s of fp64 work, capped at the workload's T)")
@@ -74,6 +77,7 @@ def kernel_work(name, w, P, es):
         "router_logits": 2.0 * T * d * E, "up": 4.0 * P * d * n, "down": 2.0 * P * n * d,
         "dh": 2.0 * P * d * n, "dxt": 4.0 * P * d * n, "dw1": 4.0 * P * d * n,
         "dw2": 2.0 * P * n * d, "dwr": 2.0 * T * d * E, "da": 2.0 * P * d * n,
+        "up_mx": 4.0 * P * d * n, "down_mx": 2.0 * P * n * d,
     }
     if name in flops:
         return flops[name], "flop"
@@ -90,6 +94,10 @@ def kernel_work(name, w, P, es):
         # unfused layer: row gather (read + write), SwiGLU, dS = <dO_g, Y>, SwiGLU backward
         "gather": 2 * P * d * es + P * 4, "swiglu": 3 * P * n * es, "row_dot": 2 * P * d * es + P * 4,
         "swiglu_bwd": P * (n + 2 * n + n) * es + P * 4 + P * (2 * n + n) * es,
+        # MXFP8 quantizers (bf16 in, codes + 1/32 scale bytes out), averaged
+        # over their two launches per step: x and A rows, w1 and w2
+        "mx_quant_rows": (T * d + P * n) * (es + 1 + 1 / 32) / 2,
+        "mx_quant_w": 3 * E * d * n * (es + 1 + 1 / 32) / 2,
     }
     return float(bytes_.get(name, 0)), "byte"
 
@@ -158,6 +166,10 @@ def main():
               "(the layer is built and measured on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 
+    if args.unfused and args.mxfp8:
+        print("--unfused and --mxfp8 are separate comparisons; pick one", file=sys.stderr)
+        sys.exit(2)
+
     import numpy as np
     import torch
 
@@ -180,7 +192,10 @@ def main():
 
     def step():
         L.route(x, wr, bias)
-        L.forward(x, w1, w2)
+        if args.mxfp8:
+            L.forward_mxfp8(x, w1, w2)
+        else:
+            L.forward(x, w1, w2)
         L.backward(x, wr, w1, w2, do)
 
     for _ in range(args.warmup):
@@ -235,8 +250,9 @@ def main():
         work, kind = kernel_work(name, w, P, es)
         if kind == "flop":
             ach = work / (avg * 1e-3) / 1e12
+            pk = MFMA_PEAK_FP8 if name.endswith("_mx") else peak_mfma
             kernels[name] = {"ms": round(avg, 4), "bound": "mfma", "achieved": round(ach, 1),
-                             "peak": peak_mfma, "unit": "TFLOP/s", "frac": round(ach / peak_mfma, 4),
+                             "peak": pk, "unit": "TFLOP/s", "frac": round(ach / pk, 4),
                              "work": work}
         else:
             ach = work / (avg * 1e-3) / 1e9
@@ -258,15 +274,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "mxfp8 fwd + bf16 bwd" if args.mxfp8 else w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "n": w.n, "K": w.K,
                    "round_mode": args.round_mode, "tile": args.tile, "rows": P, "parallelism": "single GPU",
-                   "layer": "unfused" if args.unfused else "fused"},
+                   "layer": "unfused" if args.unfused else "fused",
+                   "forward_gemms": "mxfp8" if args.mxfp8 else w.dtype},
         "mfma_peak_frac": round(tflops / peak_mfma, 4),
         "tokens_per_s": round(w.T / (ms_step * 1e-3), 1),
         "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
-                     "unit": dk["unit"], "frac": dk["frac"], "traffic": None if args.unfused else measured_traffic(w.name, dom)},
+                     "unit": dk["unit"], "frac": dk["frac"], "traffic": None if (args.unfused or args.mxfp8) else measured_traffic(w.name, dom)},
         "kernels": {k: {kk: v for kk, v in d.items() if kk != "work"} for k, d in kernels.items()},
         "memory": memory_report(w, L, es),
         "routing": routing_report(L, args.tile),

@@ -1,0 +1,303 @@
+// Row-mode grouped GEMM with MXFP8 operands on gfx950: the forward
+// up-projection (SwiGLU epilogue) and down-projection with both operands in
+// the OCP MX format -- E4M3 elements, one E8M0 power-of-two scale per 32
+// consecutive k -- multiplied by v_mfma_scale_f32_32x32x64_f8f6f4, which
+// applies the block scales inside the matrix core and accumulates in fp32.
+//
+// Tile, wave and scheduling layout as the bf16 row-mode kernels
+// (grouped_gemm5.h): 256 x 256 tiles, 8 waves in 2 (m) x 4 (n), 128 x 64
+// outputs per wave, the N-side operand first in the MFMA (so each lane's
+// accumulators are four consecutive columns of one row and the bf16 kernels'
+// wave-local epilogues apply unchanged), persistent XCD-grouped walk over the
+// expert-major tile list, the next tile's first stage loaded before the
+// epilogue.  What is specific to MXFP8:
+//  * Both operands are k-contiguous bytes: A = routed rows [rows][K]
+//    (gathered through idx or direct), B = an expert's transposed weights
+//    [N][K].  A stage is k = 128, one 128-byte line per row and operand
+//    (32 KB each), loaded straight into LDS; two stages.
+//  * LDS rows are 128 bytes with 16-byte chunk c of row r in slot c ^ (r & 7):
+//    the fragment reads (16 bytes per lane, 8 consecutive rows per LDS cycle
+//    group) hit 8 distinct slots.
+//  * Fragments: for the 64-k step s of a stage, lane l of a 32-row block
+//    holds row l % 32, bytes k = 64s + 16h .. +15 and 64s + 32 + 16h .. +15
+//    (h = l / 32); the block scale of (row, 32-k block b of the step) is
+//    taken from lane row + 32 b.  Both operands use this placement, so the
+//    contraction pairs equal k and each 32-k block meets its own scale.
+//  * Scales: A's (per routed row, K/32 bytes) for the whole tile are loaded
+//    into LDS with the tile's first stage; B's are stored blocked per stage,
+//    [E][K/128][N] dwords (the four block scales of one column and stage),
+//    and loaded with each stage.
+#pragma once
+
+#include "grouped_gemm4.h"
+
+namespace moe {
+namespace gmx {
+
+using g4::f32x16_v;
+using g4::make_rsrc;
+using g4::OOB;
+using g4::wait_vm;
+
+typedef int i32x8_v __attribute__((ext_vector_type(8)));
+
+constexpr int BM = 256, BN = 256, BK = 128, NS = 2, NTH = 512;
+constexpr int OPB = 256 * BK;             // bytes of one operand tile per stage (32 KB)
+constexpr int BSC = 256 * 4;              // B scales of a stage: one dword per column
+constexpr int STAGE = 2 * OPB + BSC;      // 65 KB
+constexpr int LPS = 8;                    // 16-byte data loads per thread per stage
+constexpr int MAX_PA = 64;                // A scale bytes per row: K <= 2048
+constexpr int ASC_OFF = NS * STAGE;       // A scales of the tile: [256 rows][K/32]
+constexpr int SMEM = ASC_OFF + 256 * MAX_PA;
+constexpr int WE_OFF = STAGE;             // wave-local epilogue areas: over stage 1
+static_assert(WE_OFF + 8 * g4::WAVE_LDS <= 2 * STAGE, "wave areas fit over stage 1");
+static_assert(STAGE % 1024 == 0, "stage alignment");
+
+// buffer -> LDS loads; soff (wave-uniform) is added to the per-lane voff
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (g4::lds_void_t*)lds, 4, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma16s(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (g4::lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ int swz(int r) { return r & 7; }
+
+// k-contiguous byte rows, 128 bytes per row and stage.  Instruction i (0..3)
+// of wave w covers tile rows (4w + i) * 8 .. +7; lane l takes row rb + l/8
+// and LDS slot l % 8, which holds chunk (l % 8) ^ swz(row) of that row.
+struct KCLoad {
+  uint32_t off[4];
+  template <class F>
+  __device__ __forceinline__ void setup(int w, int lane, F rowoff) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (4 * w + i) * 8 + (lane >> 3);
+      off[i] = rowoff(r) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* op, int w, int k0) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16s(rs, op + (4 * w + i) * 1024, off[i], (uint32_t)k0);
+  }
+};
+
+// 16 bytes of row rb + lane % 32 at chunk c of the current stage
+__device__ __forceinline__ uint4 chunk(const char* op, int r, int c) {
+  return *reinterpret_cast<const uint4*>(op + r * BK + ((c ^ swz(r)) & 7) * 16);
+}
+
+// operand fragment of 32 rows for the 64-k step s of a stage
+__device__ __forceinline__ i32x8_v frag(const char* op, int rb, int s, int lane) {
+  const int r = rb + (lane & 31), h = lane >> 5;
+  const uint4 lo = chunk(op, r, 4 * s + h), hi = chunk(op, r, 4 * s + 2 + h);
+  i32x8_v v;
+  v[0] = (int)lo.x; v[1] = (int)lo.y; v[2] = (int)lo.z; v[3] = (int)lo.w;
+  v[4] = (int)hi.x; v[5] = (int)hi.y; v[6] = (int)hi.z; v[7] = (int)hi.w;
+  return v;
+}
+
+// one 64-k step s of a stage: B fragments of the wave's two column blocks,
+// then per row block its A fragment and two MFMAs.  asc / bsc: the stage's
+// scale dwords (4 blocks of 32 k) of this lane's rows / columns.
+__device__ __forceinline__ void step(f32x16_v (&acc)[2][4], const char* st, int s, int lane, int wm, int wn,
+                                     const uint32_t (&asc)[4], const uint32_t (&bsc)[2]) {
+  const int sh = 8 * (2 * s + (lane >> 5));
+  i32x8_v n[2];
+  int sn[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    n[i] = frag(st + OPB, wn * 64 + 32 * i, s, lane);
+    sn[i] = (int)__builtin_amdgcn_ubfe(bsc[i], sh, 8);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const i32x8_v m = frag(st, wm * 128 + 32 * j, s, lane);
+    const int sm = (int)__builtin_amdgcn_ubfe(asc[j], sh, 8);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(n[i], m, acc[i][j], 0, 0, 0, sn[i], 0, sm);
+  }
+}
+
+// A: routed rows of fp8 codes (A.idx gathers them), A.ld = K bytes per row;
+// ascale: their E8M0 scales, K/32 bytes per row, same row numbering.
+// B: the expert's transposed fp8 weights [N][K] (B.estride bytes per expert);
+// bscale: [E][K/128][N] dwords.  PAIRED arranges B's columns for G4SwiGLU.
+template <bool PAIRED, class Epi>
+__global__ void __launch_bounds__(NTH, 1)
+grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restrict__ ascale,
+                       const uint32_t* __restrict__ bscale, uint32_t a_bytes, uint32_t b_bytes,
+                       uint32_t as_bytes, uint32_t bs_bytes, typename Epi::Params ep) {
+  static_assert(g4::is_wave_epi<Epi>::value, "wave-local epilogues only");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  __shared__ int tprefix[MAX_E + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 2, wn = w & 3;
+  const int NT = s.N / BN;
+  const int PA = s.K / 32;  // A scale bytes per row
+  {
+    __shared__ int wsum[8];
+    int carry = 0;
+    for (int e0 = 0; e0 < s.E; e0 += NTH) {
+      const int e = e0 + tid;
+      const int tiles = e < s.E ? (s.offsets[e + 1] - s.offsets[e] + BM - 1) / BM : 0;
+      int incl = tiles;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      if (lane == 63) wsum[w] = incl;
+      __syncthreads();
+      int base = carry, tot = 0;
+      for (int x = 0; x < NTH / 64; ++x) {
+        if (x < w) base += wsum[x];
+        tot += wsum[x];
+      }
+      if (e < s.E) tprefix[e] = base + incl - tiles;
+      carry += tot;
+      __syncthreads();
+    }
+    if (tid == 0) tprefix[s.E] = carry;
+    __syncthreads();
+  }
+  const int total = tprefix[s.E] * NT;
+  const int G = gridDim.x;
+  const int vid = xcd_virtual_id(blockIdx.x, G);
+  auto tile_of = [&](int r) -> int {
+    const int t = r * G + vid;
+    return t < total ? t : -1;
+  };
+  const int nk = s.K / BK;
+  const char* abase = reinterpret_cast<const char*>(A.ptr);
+  const char* bbase = reinterpret_cast<const char*>(B.ptr);
+
+  auto decode = [&](int t, TileCtx& c) {
+    c.tid = tid; c.lane = lane; c.wm = wm; c.wn = wn;
+    const int mg = t / NT;
+    c.nt = t % NT;
+    c.e = upper_index(tprefix, s.E + 1, mg);
+    c.mt = mg - tprefix[c.e];
+    c.seg0 = s.offsets[c.e];
+    c.segn = s.offsets[c.e + 1] - c.seg0;
+    c.m_valid = min(BM, c.segn - c.mt * BM);
+    c.out_row0 = (long long)c.seg0 + (long long)c.mt * BM;
+    c.slot = -1;
+    c.n0 = c.nt * BN;
+  };
+
+  __amdgpu_buffer_rsrc_t ra, rb, ras, rbs;
+  KCLoad la, lb;
+  uint32_t bso = 0;          // B-scale dword offset of this lane's column (waves 0..3)
+  auto src_row = [&](const TileCtx& c, int r) -> uint32_t {
+    const int m = c.mt * BM + r;
+    const int row = c.seg0 + (m < c.segn ? m : c.segn - 1);  // rows past the end repeat the last one
+    return A.idx ? (uint32_t)A.idx[row] : (uint32_t)row;
+  };
+  auto colmap = [&](const TileCtx& c, int cc) -> int {
+    if constexpr (PAIRED) return g4::G4SwiGLU::col(cc, c.nt, s.N / 2);
+    return c.n0 + cc;
+  };
+  auto setup = [&](const TileCtx& c) {
+    ra = make_rsrc(abase, a_bytes);
+    la.setup(w, lane, [&](int r) -> uint32_t { return src_row(c, r) * (uint32_t)A.ld; });
+    rb = make_rsrc(bbase + (long long)c.e * B.estride, b_bytes);
+    lb.setup(w, lane, [&](int r) -> uint32_t { return (uint32_t)colmap(c, r) * (uint32_t)B.ld; });
+    ras = make_rsrc(ascale, as_bytes);
+    rbs = make_rsrc(bscale + (long long)c.e * nk * s.N, bs_bytes);
+    bso = w < 4 ? (uint32_t)colmap(c, 64 * w + lane) * 4u : 0u;
+  };
+  // the tile's A scales: PA instructions of 64 dwords, wave w taking
+  // w, w + 8, ...; dword q of the block is byte 4 (q % (PA/4)) of row q / (PA/4)
+  auto issue_ascale = [&](const TileCtx& c) {
+    const int dpr = PA / 4;
+#pragma unroll 1
+    for (int i = w; i < PA; i += 8) {
+      const int q = i * 64 + lane;
+      dma4(ras, smem + ASC_OFF + i * 256, src_row(c, q / dpr) * (uint32_t)PA + (uint32_t)(q % dpr) * 4u);
+    }
+  };
+  auto issue = [&](int k) {
+    char* st = smem + (k & 1) * STAGE;
+    const int k0 = k * BK;
+    la.issue(ra, st, w, k0);
+    lb.issue(rb, st + OPB, w, k0);
+    if (w < 4) dma4(rbs, st + 2 * OPB + w * 256, bso, (uint32_t)(k * s.N) * 4u);
+  };
+  // scale dwords of stage k for this lane's 4 row blocks and 2 column blocks
+  auto read_scales = [&](int k, uint32_t (&asc)[4], uint32_t (&bsc)[2]) {
+    const char* st = smem + (k & 1) * STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      asc[j] = *reinterpret_cast<const uint32_t*>(smem + ASC_OFF + (wm * 128 + 32 * j + (lane & 31)) * PA + 4 * k);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      bsc[i] = *reinterpret_cast<const uint32_t*>(st + 2 * OPB + (wn * 64 + 32 * i + (lane & 31)) * 4);
+  };
+
+  int r = 0;
+  int t = tile_of(0);
+  TileCtx c;
+  if (t >= 0) {
+    decode(t, c);
+    setup(c);
+    issue_ascale(c);
+    issue(0);
+  }
+  while (t >= 0) {
+    f32x16_v acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // stage 1 overwrites the previous tile's epilogue areas
+    __syncthreads();
+    if (nk > 1) issue(1);
+    // the A scales and stage 0 are complete once only stage 1's loads remain
+    if (nk > 1) {
+      if (w < 4) wait_vm<LPS + 1>();
+      else wait_vm<LPS>();
+    } else {
+      wait_vm<0>();
+    }
+    __syncthreads();
+    uint32_t asc[4], bsc[2];
+    read_scales(0, asc, bsc);
+    // one 64-k step per iteration, two per stage; after a stage's second
+    // step: stage k+1 complete, the barrier frees stage k for stage k+2, and
+    // stage k+1's scales are read before the next loads are issued
+#pragma unroll 1
+    for (int it = 0; it < 2 * nk; ++it) {
+      const int k = it >> 1, sidx = it & 1;
+      step(acc, smem + (k & 1) * STAGE, sidx, lane, wm, wn, asc, bsc);
+      if (sidx == 1 && k + 1 < nk) {
+        wait_vm<0>();
+        __syncthreads();
+        read_scales(k + 1, asc, bsc);
+        if (k + 2 < nk) issue(k + 2);
+      }
+    }
+    __syncthreads();  // every wave is done reading the stages and the A scales
+
+    const int tn = tile_of(r + 1);
+    TileCtx cn = c;
+    if (tn >= 0) {
+      decode(tn, cn);
+      setup(cn);
+      issue_ascale(cn);
+      issue(0);
+    }
+    Epi::run(ep, c, acc, smem + WE_OFF + w * g4::WAVE_LDS);
+    c = cn;
+    t = tn;
+    ++r;
+  }
+}
+
+}  // namespace gmx
+}  // namespace moe

@@ -54,6 +54,21 @@ size_t wgt_ws_bytes(const GemmDims& g);
 hipError_t launch_rows_gemm(const GemmDims& g, const void* A, int K, const void* W, int N, bool w_kn,
                             const int32_t* offsets, void* C, hipStream_t st);
 
+// ---- MXFP8 forward (mx_kernels.hip) ----
+// Shapes the MX GEMMs take: bf16 layer, d and n multiples of 256, at most 2048.
+bool mx_shape_ok(const GemmDims& g);
+// rows [rows][K] bf16 -> E4M3 codes [rows][K] and E8M0 scales [rows][K/32];
+// nrows (device) bounds the rows when set.
+hipError_t launch_mx_quant_rows(const void* src, int K, long long rows, const int32_t* nrows, uint8_t* q,
+                                uint8_t* s, hipStream_t st);
+// W [E][K][N] bf16 -> codes [E][N][K] and scales [E][K/128][N] (4 bytes each)
+hipError_t launch_mx_quant_w(const void* W, int E, int K, int N, uint8_t* q, uint8_t* sblk, hipStream_t st);
+hipError_t launch_up_mx(const GemmDims& g, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q,
+                        const uint8_t* w1s, const int32_t* row_token, const int32_t* offsets, void* H, void* A,
+                        hipStream_t st);
+hipError_t launch_down_mx(const GemmDims& g, const uint8_t* aq, const uint8_t* as, const uint8_t* w2q,
+                          const uint8_t* w2s, const int32_t* offsets, void* Y, hipStream_t st);
+
 // ---- unfused layer (unfused_kernels.hip); rows 0 .. *nrows-1 of cap ----
 hipError_t launch_gather_rows(int dtype, const void* src, int width, const int32_t* idx, const int32_t* nrows,
                               size_t cap, void* dst, hipStream_t st);

@@ -125,6 +125,25 @@ Layout unfused_bwd_layout(const moe_desc* d) {
   return L;
 }
 
+// MXFP8 forward workspace: quantized operands, A (bf16 and quantized), Y.
+Layout mx_fwd_layout(const moe_desc* d) {
+  Layout L{};
+  const size_t cap = capacity(d), T = d->T, D = d->d, n = d->n, E = d->E;
+  size_t o = 0;
+  L.off[0] = o; o = up(o + T * D);                       // x codes [T][d]
+  L.off[1] = o; o = up(o + T * (D / 32));                // x scales [T][d/32]
+  L.off[2] = o; o = up(o + E * 2 * n * D);               // W1^T codes [E][2n][d]
+  L.off[3] = o; o = up(o + E * (D / 128) * 2 * n * 4);   // W1 scales [E][d/128][2n][4]
+  L.off[4] = o; o = up(o + E * D * n);                   // W2^T codes [E][d][n]
+  L.off[5] = o; o = up(o + E * (n / 128) * D * 4);       // W2 scales [E][n/128][d][4]
+  L.off[6] = o; o = up(o + cap * n * 2);                 // A (bf16)
+  L.off[7] = o; o = up(o + cap * n);                     // A codes [cap][n]
+  L.off[8] = o; o = up(o + cap * (n / 32));              // A scales [cap][n/32]
+  L.off[9] = o; o = up(o + cap * D * 2);                 // Y (bf16)
+  L.total = o;
+  return L;
+}
+
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return MOE_OK;
   if (!ws) return MOE_EINVAL;
@@ -180,6 +199,7 @@ size_t moe_workspace_bytes(const moe_desc* desc, int which) {
     case MOE_WS_FWD: return fwd_layout(desc).total;
     case MOE_WS_BWD: return bwd_layout(desc).total;
     case MOE_WS_BWD_UNFUSED: return unfused_bwd_layout(desc).total;
+    case MOE_WS_FWD_MXFP8: return mx_shape_ok(gemm_dims(desc)) ? mx_fwd_layout(desc).total : 0;
     default: return 0;
   }
 }
@@ -194,8 +214,13 @@ size_t moe_workspace_offset(const moe_desc* desc, int item) {
     case MOE_ITEM_DS: return bwd_layout(desc).off[3];
     case MOE_ITEM_DZ: return bwd_layout(desc).off[4];
     case MOE_ITEM_DXT: return bwd_layout(desc).off[7];
-    default: return (size_t)-1;
+    default: break;
   }
+  if (item >= MOE_ITEM_MX_XQ && item <= MOE_ITEM_MX_Y) {
+    if (!mx_shape_ok(gemm_dims(desc))) return (size_t)-1;
+    return mx_fwd_layout(desc).off[item - MOE_ITEM_MX_XQ];
+  }
+  return (size_t)-1;
 }
 
 int moe_route(const moe_desc* desc, const void* x, const void* w_r, const float* bias,
@@ -287,6 +312,38 @@ int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1
   MOE_TRY(MOE_K_DW1, launch_dw1(g, x, dH, R.row_token, R.offsets, dw1, wws, st));
   MOE_TRY(MOE_K_DW2, launch_dw2(g, As, d_o, R.row_token, R.offsets, dw2, wws, st));
   if (db) MOE_TRY(MOE_K_DB, launch_bias_grad(dz_row, R.offsets, D.E, db, st));
+  return MOE_OK;
+}
+
+int moe_fwd_mxfp8(const moe_desc* desc, const void* x, const void* w1, const void* w2,
+                  const moe_routing* routing, void* o, void* h_cache, void* ws, size_t ws_bytes, void* stream) {
+  int s = validate_desc(desc);
+  if (s != MOE_OK) return s;
+  if (desc->dtype != MOE_BF16) return MOE_EDTYPE;
+  const GemmDims g = gemm_dims(desc);
+  if (!mx_shape_ok(g)) return MOE_ESHAPE;
+  if (!x || !w1 || !w2 || !o || !h_cache || !routing_ok(routing)) return MOE_EINVAL;
+  const Layout L = mx_fwd_layout(desc);
+  if ((s = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  const moe_desc& D = *desc;
+  const moe_routing& R = *routing;
+  const size_t cap = capacity(desc);
+  uint8_t *xq = w + L.off[0], *xs = w + L.off[1], *w1q = w + L.off[2], *w1s = w + L.off[3];
+  uint8_t *w2q = w + L.off[4], *w2s = w + L.off[5], *aq = w + L.off[7], *as = w + L.off[8];
+  void* A = w + L.off[6];
+  void* Y = w + L.off[9];
+  // operands quantized along each GEMM's reduction: x and W1 along d, W2 along n
+  MOE_TRY(MOE_K_MX_QUANT_ROWS, launch_mx_quant_rows(x, D.d, D.T, nullptr, xq, xs, st));
+  MOE_TRY(MOE_K_MX_QUANT_W, launch_mx_quant_w(w1, D.E, D.d, 2 * D.n, w1q, w1s, st));
+  MOE_TRY(MOE_K_MX_QUANT_W, launch_mx_quant_w(w2, D.E, D.n, D.d, w2q, w2s, st));
+  MOE_TRY(MOE_K_UP_MX, launch_up_mx(g, xq, xs, w1q, w1s, R.row_token, R.offsets, h_cache, A, st));
+  // A along n, from the bf16 values the up-projection stored
+  MOE_TRY(MOE_K_MX_QUANT_ROWS, launch_mx_quant_rows(A, D.n, (long long)cap, R.offsets + D.E, aq, as, st));
+  MOE_TRY(MOE_K_DOWN_MX, launch_down_mx(g, aq, as, w2q, w2s, R.offsets, Y, st));
+  MOE_TRY(MOE_K_AGG_O, launch_aggregate_o(D.dtype, Y, R.row_gate, R.tok_ptr, R.tok_row, D.T, D.d, o, st));
   return MOE_OK;
 }
 

@@ -1,0 +1,193 @@
+// MXFP8 forward: quantization of the GEMM operands to the OCP MX format
+// (E4M3 elements, one E8M0 scale per 32 consecutive values along the
+// reduction) and the two forward grouped GEMMs on the MX-scaled MFMA
+// (grouped_gemm_mx.h).  The pages name MXFP8 as the method's next precision
+// step ([A] closing "未来展望" paragraph); the format is the OCP MX
+// specification's (section 5: blocks and scales; section 6.3: the shared
+// exponent floor(log2(amax)) - emax of the element type, 8 for E4M3).
+//
+// Rounding: elements round to nearest, ties to even, after an exact
+// power-of-two division by the block scale; magnitudes beyond 448 saturate
+// to 448 (the block's largest value lands in [256, 512) before rounding, so
+// only the top of that range saturates).  An all-zero block gets scale code
+// 0 and zero elements.
+#include <algorithm>
+
+#include "grouped_gemm_mx.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+// E4M3 code of x (finite, any magnitude: saturates at 448), ties to even.
+// With e = max(floor(log2 |x|), -6), |x| / 2^(e-3) rounded to an integer m
+// gives the code (e + 6) * 8 + m: for normals m is 8..16 (16 carries into
+// the next exponent by itself), for subnormals (e = -6) m is the count of
+// 2^-9 steps, 8 being the smallest normal.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  const int e = max((int)(__float_as_uint(a) >> 23) - 127, -6);
+  const int m = (int)rintf(a * __uint_as_float((uint32_t)(130 - e) << 23));  // a * 2^(3-e)
+  return sign | (uint32_t)(((e + 6) << 3) + m);
+}
+
+// E8M0 scale code of a block whose largest magnitude is amax (> 0)
+__device__ __forceinline__ int scale_code(float amax) {
+  const int c = (int)(__float_as_uint(amax) >> 23) - 8;  // floor(log2 amax) - 8 + 127
+  return c < 0 ? 0 : (c > 254 ? 254 : c);
+}
+
+// quantize 32 values (fp32) to codes packed 4 per word; returns the scale code
+__device__ __forceinline__ int quant32(const float (&v)[32], uint32_t (&q)[8]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  if (amax == 0.f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = 0u;
+    return 0;
+  }
+  const int sc = scale_code(amax);
+  const float inv = __uint_as_float((uint32_t)(254 - sc) << 23);  // 2^(127 - sc)
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    q[i] = e4m3_code(v[4 * i] * inv) | (e4m3_code(v[4 * i + 1] * inv) << 8) |
+           (e4m3_code(v[4 * i + 2] * inv) << 16) | (e4m3_code(v[4 * i + 3] * inv) << 24);
+  return sc;
+}
+
+// rows [rows][K] bf16 -> codes [rows][K], scales [rows][K/32]; one thread per
+// block of 32.  rows = *nrows when nrows is set (launched over the capacity).
+__global__ void __launch_bounds__(256)
+k_mx_quant_rows(const bf16_t* __restrict__ src, int K, long long rows, const int32_t* __restrict__ nrows,
+                uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int nb = K / 32;
+  const long long row = t / nb;
+  const int kb = (int)(t % nb);
+  const long long nr = nrows ? (long long)*nrows : rows;
+  if (row >= nr) return;
+  const uint4* p = reinterpret_cast<const uint4*>(src + row * K + kb * 32);
+  float v[32];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 u = p[c];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * c + 2 * i] = __uint_as_float(w[i] << 16);
+      v[8 * c + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  uint32_t qw[8];
+  const int sc = quant32(v, qw);
+  uint4* o = reinterpret_cast<uint4*>(q + row * K + kb * 32);
+  o[0] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+  o[1] = make_uint4(qw[4], qw[5], qw[6], qw[7]);
+  s[row * nb + kb] = (uint8_t)sc;
+}
+
+// weights W [E][K][N] bf16 -> transposed codes [E][N][K] and stage-blocked
+// scales [E][K/128][N] (dword per column and 128-k group, byte b = k-block b
+// of the group); one thread per (expert, 32-k block, column)
+__global__ void __launch_bounds__(256)
+k_mx_quant_w(const bf16_t* __restrict__ W, int E, int K, int N, uint8_t* __restrict__ q,
+             uint8_t* __restrict__ sblk) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int nb = K / 32;
+  const long long total = (long long)E * nb * N;
+  if (t >= total) return;
+  const int col = (int)(t % N);
+  const long long rest = t / N;
+  const int kb = (int)(rest % nb);
+  const int e = (int)(rest / nb);
+  const bf16_t* p = W + ((long long)e * K + (long long)kb * 32) * N + col;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, p[(long long)i * N]) << 16);
+  uint32_t qw[8];
+  const int sc = quant32(v, qw);
+  uint4* o = reinterpret_cast<uint4*>(q + ((long long)e * N + col) * K + kb * 32);
+  o[0] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+  o[1] = make_uint4(qw[4], qw[5], qw[6], qw[7]);
+  sblk[(((long long)e * (K / 128) + kb / 4) * N + col) * 4 + (kb & 3)] = (uint8_t)sc;
+}
+
+int cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+template <bool PAIRED, class Epi>
+hipError_t run_gemm_mx(const GemmShape& s, const Operand& A, const Operand& B, const uint8_t* ascale,
+                       const uint32_t* bscale, size_t a_bytes, size_t b_bytes, size_t as_bytes, size_t bs_bytes,
+                       const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
+  auto kern = gmx::grouped_gemm_mx_kernel<PAIRED, Epi>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, gmx::SMEM);
+  if (attr != hipSuccess) return attr;
+  long long grid = std::min<long long>(max_tiles, cu_count());
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(gmx::NTH), gmx::SMEM, st, s, A, B, ascale, bscale,
+                     (uint32_t)a_bytes, (uint32_t)b_bytes, (uint32_t)as_bytes, (uint32_t)bs_bytes, ep);
+  return hipGetLastError();
+}
+
+long long tiles_bound(size_t cap, int E) { return (long long)(cap + gmx::BM - 1) / gmx::BM + E; }
+
+}  // namespace
+
+bool mx_shape_ok(const GemmDims& g) {
+  return g.dtype == DT_BF16 && g.d % 256 == 0 && g.n % 256 == 0 && g.d / 32 <= gmx::MAX_PA &&
+         g.n / 32 <= gmx::MAX_PA && (size_t)g.T * g.d < (size_t)g4::OOB && g.cap * (size_t)g.d < (size_t)g4::OOB;
+}
+
+hipError_t launch_mx_quant_rows(const void* src, int K, long long rows, const int32_t* nrows, uint8_t* q,
+                                uint8_t* s, hipStream_t st) {
+  const long long threads = rows * (K / 32);
+  if (threads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_mx_quant_rows, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     (const bf16_t*)src, K, rows, nrows, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_w(const void* W, int E, int K, int N, uint8_t* q, uint8_t* sblk, hipStream_t st) {
+  const long long threads = (long long)E * (K / 32) * N;
+  hipLaunchKernelGGL(k_mx_quant_w, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, (const bf16_t*)W,
+                     E, K, N, q, sblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_up_mx(const GemmDims& g, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q,
+                        const uint8_t* w1s, const int32_t* row_token, const int32_t* offsets, void* H, void* A,
+                        hipStream_t st) {
+  const int n = g.n, d = g.d, E = g.E;
+  using Epi = g4::G4SwiGLU;
+  GemmShape s{offsets, E, 0, 2 * n, d, 2 * n, 1};
+  Operand a{xq, row_token, 0, d};
+  Operand b{w1q, nullptr, (long long)2 * n * d, d};
+  typename Epi::Params ep{reinterpret_cast<bf16_t*>(H), reinterpret_cast<bf16_t*>(A), n};
+  return run_gemm_mx<true, Epi>(s, a, b, xs, reinterpret_cast<const uint32_t*>(w1s), (size_t)g.T * d,
+                                (size_t)2 * n * d, (size_t)g.T * (d / 32), (size_t)(d / 128) * 2 * n * 4, ep,
+                                tiles_bound(g.cap, E) * (2 * n / gmx::BN), st);
+}
+
+hipError_t launch_down_mx(const GemmDims& g, const uint8_t* aq, const uint8_t* as, const uint8_t* w2q,
+                          const uint8_t* w2s, const int32_t* offsets, void* Y, hipStream_t st) {
+  const int n = g.n, d = g.d, E = g.E;
+  using Epi = g4::G4Store;
+  GemmShape s{offsets, E, 0, d, n, d, 1};
+  Operand a{aq, nullptr, 0, n};
+  Operand b{w2q, nullptr, (long long)d * n, n};
+  typename Epi::Params ep{reinterpret_cast<bf16_t*>(Y), d};
+  return run_gemm_mx<false, Epi>(s, a, b, as, reinterpret_cast<const uint32_t*>(w2s), g.cap * n, (size_t)d * n,
+                                 g.cap * (n / 32), (size_t)(n / 128) * d * 4, ep,
+                                 tiles_bound(g.cap, E) * (d / gmx::BN), st);
+}
+
+}  // namespace moe

@@ -96,13 +96,19 @@ extern "C" {
 #define MOE_K_ROW_DOT      16   /* dS = <dO_g, Y> per row                          */
 #define MOE_K_DA           17   /* dA' = dO_g w2^T                                 */
 #define MOE_K_SWIGLU_BWD   18   /* dH, A_s from dA', H, A and the gates            */
-#define MOE_K_COUNT        19
+/* launched by the MXFP8 forward only (moe_fwd_mxfp8) */
+#define MOE_K_MX_QUANT_ROWS 19  /* x or A rows -> E4M3 codes + E8M0 scales         */
+#define MOE_K_MX_QUANT_W   20   /* w1 or w2 -> transposed codes + scales           */
+#define MOE_K_UP_MX        21   /* K1 on MXFP8 operands (SwiGLU epilogue) -> H, A  */
+#define MOE_K_DOWN_MX      22   /* K2 on MXFP8 operands -> Y                       */
+#define MOE_K_COUNT        23
 
 /* workspace phases */
 #define MOE_WS_ROUTE 0
 #define MOE_WS_FWD   1
 #define MOE_WS_BWD   2
 #define MOE_WS_BWD_UNFUSED 3  /* moe_bwd_unfused */
+#define MOE_WS_FWD_MXFP8   4  /* moe_fwd_mxfp8 (0 when the shape is unsupported) */
 
 /* internal workspace items exposed for inspection (moe_workspace_offset) */
 #define MOE_ITEM_Y        0  /* fwd: down-proj output Y [cap, d] (dtype)          */
@@ -112,6 +118,18 @@ extern "C" {
 #define MOE_ITEM_DXT      4  /* bwd: per-row input gradient dXt [cap, d] (dtype)  */
 #define MOE_ITEM_DS       5  /* bwd: per-row score gradient dS [cap] (fp32)       */
 #define MOE_ITEM_DZ       6  /* bwd: per-row router-logit gradient dz [cap] (fp32) */
+/* MXFP8 forward workspace (E4M3 codes and E8M0 scale codes are uint8) */
+#define MOE_ITEM_MX_XQ    7  /* x codes [T, d]                                    */
+#define MOE_ITEM_MX_XS    8  /* x scales [T, d/32]                                */
+#define MOE_ITEM_MX_W1Q   9  /* w1 codes, transposed: [E, 2n, d]                  */
+#define MOE_ITEM_MX_W1S  10  /* w1 scales [E, d/128, 2n, 4]: byte b of a column's
+                                word = block 4g + b along d                       */
+#define MOE_ITEM_MX_W2Q  11  /* w2 codes, transposed: [E, d, n]                   */
+#define MOE_ITEM_MX_W2S  12  /* w2 scales [E, n/128, d, 4]                        */
+#define MOE_ITEM_MX_A    13  /* SwiGLU output A [cap, n] (bf16)                   */
+#define MOE_ITEM_MX_AQ   14  /* A codes [cap, n]                                  */
+#define MOE_ITEM_MX_AS   15  /* A scales [cap, n/32]                              */
+#define MOE_ITEM_MX_Y    16  /* down-proj output Y [cap, d] (bf16)                */
 
 /*
  * Layer description (host struct).
@@ -274,6 +292,25 @@ int moe_bwd_unfused(const moe_desc* desc, const void* x, const void* w_r, const 
                     const void* w2, const moe_routing* routing, const void* cache, const void* d_o,
                     void* dx, void* dw_r, void* dw1, void* dw2, float* ds, float* db, void* ws,
                     size_t ws_bytes, void* stream);
+
+/*
+ * Forward with MXFP8 grouped GEMMs (the pages' next precision step, [A]
+ * closing "未来展望" paragraph; format: OCP Microscaling (MX) specification
+ * v1.0, E4M3 elements, one E8M0 power-of-two scale per 32 values along each
+ * GEMM's reduction).  Same arguments and outputs as moe_fwd for a bf16 layer:
+ * x, w1 and w2 are quantized inside the call (x and w1 along d, w2 along n;
+ * each element rounded to nearest, ties to even, after division by its
+ * block scale 2^(floor(log2 amax) - 8); beyond 448 it saturates), the
+ * up-projection and down-projection run on the MX-scaled matrix cores with
+ * fp32 accumulation, A is quantized along n from its bf16 value, and o and
+ * h_cache are written in bf16 as by moe_fwd, so moe_bwd can follow.
+ *   Shapes: dtype MOE_BF16 (else MOE_EDTYPE); d and n multiples of 256 and
+ *   at most 2048 (else MOE_ESHAPE).
+ *   ws: MOE_WS_FWD_MXFP8 workspace.
+ */
+int moe_fwd_mxfp8(const moe_desc* desc, const void* x, const void* w1, const void* w2,
+                  const moe_routing* routing, void* o, void* h_cache, void* ws, size_t ws_bytes,
+                  void* stream);
 
 /* Static text for a status code.  Host only. */
 const char* moe_strerror(int status);

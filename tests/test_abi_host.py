@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +30,7 @@ def test_header_functions_exported(lib):
     names = declared_functions()
     assert set(names) == {"moe_row_capacity", "moe_workspace_bytes", "moe_workspace_offset",
                           "moe_route", "moe_fwd", "moe_bwd", "moe_strerror",
-                          "moe_unfused_cache_bytes", "moe_fwd_unfused", "moe_bwd_unfused"}
+                          "moe_unfused_cache_bytes", "moe_fwd_unfused", "moe_bwd_unfused", "moe_fwd_mxfp8"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -124,6 +124,27 @@ def test_unfused_cache_and_validation(lib):
                                4096, need_b - 256, None) == B.MOE_EWORKSPACE
     assert lib.moe_bwd_unfused(ctypes.byref(d), *([4096] * 4), ctypes.byref(r), None, *([4096] * 5), None,
                                None, 4096, need_b, None) == B.MOE_EINVAL  # no cache
+
+
+def test_mxfp8_shapes_and_validation(lib):
+    ok = B.make_desc(256, 512, 8, 256, 2, "bf16")
+    assert B.moe_workspace_bytes(ok, B.MOE_WS_FWD_MXFP8) > 0
+    assert B.moe_workspace_offset(ok, B.MOE_ITEM_MX_Y) % 256 == 0
+    r = B.MoeRouting(*([4096] * len(B.ROUTING_FIELDS)))
+    for kw, code in ((dict(n=128), B.MOE_ESHAPE), (dict(d=2304), B.MOE_ESHAPE), (dict(n=2304), B.MOE_ESHAPE),
+                     (dict(dtype="f32"), B.MOE_EDTYPE)):
+        a = dict(T=256, d=512, E=8, n=256, K=2, dtype="bf16")
+        a.update(kw)
+        d = B.make_desc(**a)
+        assert B.moe_workspace_bytes(d, B.MOE_WS_FWD_MXFP8) == 0
+        assert B.moe_workspace_offset(d, B.MOE_ITEM_MX_XQ) == -1
+        assert lib.moe_fwd_mxfp8(ctypes.byref(d), 4096, 4096, 4096, ctypes.byref(r), 4096, 4096, 4096, 1 << 40,
+                                 None) == code
+    need = B.moe_workspace_bytes(ok, B.MOE_WS_FWD_MXFP8)
+    assert lib.moe_fwd_mxfp8(ctypes.byref(ok), 4096, 4096, 4096, ctypes.byref(r), 4096, 4096, 4096, need - 1,
+                             None) == B.MOE_EWORKSPACE
+    assert lib.moe_fwd_mxfp8(ctypes.byref(ok), 4096, None, 4096, ctypes.byref(r), 4096, 4096, 4096, need,
+                             None) == B.MOE_EINVAL
 
 
 def test_strerror():
