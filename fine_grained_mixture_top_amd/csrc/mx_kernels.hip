@@ -91,28 +91,48 @@ k_mx_quant_rows(const bf16_t* __restrict__ src, int K, long long rows, const int
 
 // weights W [E][K][N] bf16 -> transposed codes [E][N][K] and stage-blocked
 // scales [E][K/128][N] (dword per column and 128-k group, byte b = k-block b
-// of the group); one thread per (expert, 32-k block, column)
+// of the group).  One workgroup per (expert, 128-k group, 64 columns): the
+// 128 x 64 tile is read in whole rows, each thread quantizes one
+// (column, 32-k block) from LDS, and the codes leave as 128-byte rows of the
+// transposed matrix.
 __global__ void __launch_bounds__(256)
-k_mx_quant_w(const bf16_t* __restrict__ W, int E, int K, int N, uint8_t* __restrict__ q,
-             uint8_t* __restrict__ sblk) {
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const int nb = K / 32;
-  const long long total = (long long)E * nb * N;
-  if (t >= total) return;
-  const int col = (int)(t % N);
-  const long long rest = t / N;
-  const int kb = (int)(rest % nb);
-  const int e = (int)(rest / nb);
-  const bf16_t* p = W + ((long long)e * K + (long long)kb * 32) * N + col;
+k_mx_quant_w(const bf16_t* __restrict__ W, int K, int N, uint8_t* __restrict__ q, uint32_t* __restrict__ sblk) {
+  __shared__ bf16_t tin[128][64 + 2];
+  __shared__ uint32_t tout[64][32 + 1];  // codes of 64 columns x 128 k, 4 per word
+  const int tid = threadIdx.x;
+  const int cg = blockIdx.x, kg = blockIdx.y, e = blockIdx.z;
+  const int c0 = cg * 64, k0 = kg * 128;
+  const bf16_t* src = W + ((long long)e * K + k0) * N + c0;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {  // 128 rows x 64 columns, 4 columns (8 bytes) per thread
+    const int v = it * 256 + tid, r = v >> 4, c4 = (v & 15) * 4;
+    const uint2 x = *reinterpret_cast<const uint2*>(src + (long long)r * N + c4);
+    tin[r][c4] = (bf16_t)(x.x & 0xffffu);
+    tin[r][c4 + 1] = (bf16_t)(x.x >> 16);
+    tin[r][c4 + 2] = (bf16_t)(x.y & 0xffffu);
+    tin[r][c4 + 3] = (bf16_t)(x.y >> 16);
+  }
+  __syncthreads();
+  const int col = tid & 63, b = tid >> 6;  // 32-k block b of the group
   float v[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, p[(long long)i * N]) << 16);
+  for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)tin[32 * b + i][col] << 16);
   uint32_t qw[8];
   const int sc = quant32(v, qw);
-  uint4* o = reinterpret_cast<uint4*>(q + ((long long)e * N + col) * K + kb * 32);
-  o[0] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
-  o[1] = make_uint4(qw[4], qw[5], qw[6], qw[7]);
-  sblk[(((long long)e * (K / 128) + kb / 4) * N + col) * 4 + (kb & 3)] = (uint8_t)sc;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tout[col][8 * b + i] = qw[i];
+  // the group's four block scales of this column, one byte each
+  __shared__ uint32_t ts[4][64];
+  ts[b][col] = (uint32_t)sc;
+  __syncthreads();
+  if (tid < 64) sblk[((long long)e * (K / 128) + kg) * N + c0 + tid] =
+      ts[0][tid] | (ts[1][tid] << 8) | (ts[2][tid] << 16) | (ts[3][tid] << 24);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {  // 64 rows of 128 bytes, 16 bytes per thread
+    const int v2 = it * 256 + tid, r = v2 >> 3, ch = v2 & 7;
+    *reinterpret_cast<uint4*>(q + ((long long)e * N + c0 + r) * K + k0 + ch * 16) =
+        make_uint4(tout[r][4 * ch], tout[r][4 * ch + 1], tout[r][4 * ch + 2], tout[r][4 * ch + 3]);
+  }
 }
 
 int cu_count() {
@@ -157,9 +177,9 @@ hipError_t launch_mx_quant_rows(const void* src, int K, long long rows, const in
 }
 
 hipError_t launch_mx_quant_w(const void* W, int E, int K, int N, uint8_t* q, uint8_t* sblk, hipStream_t st) {
-  const long long threads = (long long)E * (K / 32) * N;
-  hipLaunchKernelGGL(k_mx_quant_w, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, (const bf16_t*)W,
-                     E, K, N, q, sblk);
+  // K a multiple of 128, N a multiple of 64 (the MX shapes)
+  hipLaunchKernelGGL(k_mx_quant_w, dim3((unsigned)(N / 64), (unsigned)(K / 128), (unsigned)E), dim3(256), 0, st,
+                     (const bf16_t*)W, K, N, q, reinterpret_cast<uint32_t*>(sblk));
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ from fine_grained_mixture_top_amd import inputs as I
 from oracle import moe_oracle as O
 from oracle import mx_oracle as M
 
-from gpu_util import assert_routing_equal, dev, host64, relF, routing_host
+from gpu_util import assert_routing_equal, dev, host64, host_int, relF, routing_host
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +123,47 @@ def test_mxfp8_is_deterministic():
     L1, _ = run_mx(w, a)
     L2, _ = run_mx(w, a)
     assert torch.equal(L1.o, L2.o) and torch.equal(L1.h_cache, L2.h_cache)
+
+
+@pytest.mark.parametrize("name", ["fg7b_bf16", "olmoe_bf16"])
+def test_mxfp8_full_size_expert_sample(name):
+    """Full workload size, the benchmark's launch configuration: two sampled
+    experts over all their rows (the GPU's routing; routing parity is tested
+    elsewhere): codes and scales of their tokens' x rows and of their w1 / w2
+    bit-exact, H and A against the oracle, Y against the oracle's
+    down-projection of the GPU's A codes."""
+    w = I.WORKLOADS[name]
+    a = I.draw_all(w)
+    L, _ = run_mx(w, a)
+    T, d, E, n = w.T, w.d, w.E, w.n
+    off = host_int(L.routing.offsets)
+    P = int(off[-1])
+    rng = np.random.default_rng(5)
+    for e in rng.choice(E, 2, replace=False):
+        s0, s1 = int(off[e]), int(off[e + 1])
+        rows = np.arange(s0, s1)
+        tok = host_int(L.routing.row_token[s0:s1])
+        x64 = O.to_f64(a["x"][tok], "bf16")
+        xq, xs = M.quantize_rows(x64)
+        gx = u8(L, B.MOE_ITEM_MX_XQ, T * d).reshape(T, d)[tok]
+        gs = u8(L, B.MOE_ITEM_MX_XS, T * d // 32).reshape(T, d // 32)[tok]
+        assert np.array_equal(gx, xq) and np.array_equal(gs, xs)
+        w1q, w1s = M.quantize_weights(O.to_f64(a["w1"][e:e + 1], "bf16"))
+        w2q, w2s = M.quantize_weights(O.to_f64(a["w2"][e:e + 1], "bf16"))
+        g1q = u8(L, B.MOE_ITEM_MX_W1Q, E * 2 * n * d).reshape(E, 2 * n, d)[e:e + 1]
+        g1s = blocked_to_rows(u8(L, B.MOE_ITEM_MX_W1S, E * d // 32 * 2 * n), E, d, 2 * n)[e:e + 1]
+        g2q = u8(L, B.MOE_ITEM_MX_W2Q, E * d * n).reshape(E, d, n)[e:e + 1]
+        g2s = blocked_to_rows(u8(L, B.MOE_ITEM_MX_W2S, E * n // 32 * d), E, n, d)[e:e + 1]
+        assert np.array_equal(g1q, w1q) and np.array_equal(g1s, w1s)
+        assert np.array_equal(g2q, w2q) and np.array_equal(g2s, w2s)
+        H = M.dequantize(xq, xs) @ np.swapaxes(M.dequantize(w1q, w1s), 1, 2)[0]
+        A = O.silu(H[:, :n]) * H[:, n:]
+        Hg = host64(L.h_cache[s0:s1])
+        Ag = host64(L.ws_view(B.MOE_ITEM_MX_A, P * n, torch.bfloat16)).reshape(P, n)[rows]
+        aq, as_ = M.quantize(Ag)
+        assert np.array_equal(u8(L, B.MOE_ITEM_MX_AQ, P * n).reshape(P, n)[rows], aq)
+        Y = M.dequantize(aq, as_) @ np.swapaxes(M.dequantize(w2q, w2s), 1, 2)[0]
+        Yg = host64(L.ws_view(B.MOE_ITEM_MX_Y, P * d, torch.bfloat16)).reshape(P, d)[rows]
+        errs = dict(H=relF(Hg, H), A=relF(Ag, A), Y=relF(Yg, Y))
+        print(name, int(e), s1 - s0, {k: f"{v:.2e}" for k, v in errs.items()})
+        assert all(v <= TOL for v in errs.values()), errs
