@@ -25,19 +25,20 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUND_OFF, MOE_ROUND_NEAREST, MOE_ROUND_STOCHASTIC = 0, 1, 2
 MOE_FLAG_SCORES_GIVEN = 1
 MOE_FLAG_GEMM_128 = 2
-MOE_WS_ROUTE, MOE_WS_FWD, MOE_WS_BWD, MOE_WS_BWD_UNFUSED, MOE_WS_FWD_MXFP8 = 0, 1, 2, 3, 4
+MOE_WS_ROUTE, MOE_WS_FWD, MOE_WS_BWD, MOE_WS_BWD_UNFUSED, MOE_WS_FWD_MXFP8, MOE_WS_BWD_MXFP8 = range(6)
 MOE_ITEM_Y, MOE_ITEM_A, MOE_ITEM_DH, MOE_ITEM_AS, MOE_ITEM_DXT, MOE_ITEM_DS, MOE_ITEM_DZ = range(7)
 (MOE_ITEM_MX_XQ, MOE_ITEM_MX_XS, MOE_ITEM_MX_W1Q, MOE_ITEM_MX_W1S, MOE_ITEM_MX_W2Q, MOE_ITEM_MX_W2S,
  MOE_ITEM_MX_A, MOE_ITEM_MX_AQ, MOE_ITEM_MX_AS, MOE_ITEM_MX_Y) = range(7, 17)
+MOE_ITEM_MX_DHQ, MOE_ITEM_MX_DHS, MOE_ITEM_MX_W1RQ, MOE_ITEM_MX_W1RS = range(17, 21)
 KERNEL_NAMES = ["router_logits", "route_select", "up", "down", "agg_o", "dh", "router_grad", "dwr",
                 "wr_t", "dxt", "agg_dx", "dw1", "dw2", "db",
                 "gather", "swiglu", "row_dot", "da", "swiglu_bwd",
-                "mx_quant_rows", "mx_quant_w", "up_mx", "down_mx"]
+                "mx_quant_rows", "mx_quant_w", "up_mx", "down_mx", "dxt_mx"]
 (MOE_K_ROUTER_LOGITS, MOE_K_ROUTE_SELECT, MOE_K_UP, MOE_K_DOWN, MOE_K_AGG_O, MOE_K_DH,
  MOE_K_ROUTER_GRAD, MOE_K_DWR, MOE_K_WR_T, MOE_K_DXT, MOE_K_AGG_DX, MOE_K_DW1, MOE_K_DW2,
  MOE_K_DB, MOE_K_GATHER, MOE_K_SWIGLU, MOE_K_ROW_DOT, MOE_K_DA, MOE_K_SWIGLU_BWD,
- MOE_K_MX_QUANT_ROWS, MOE_K_MX_QUANT_W, MOE_K_UP_MX, MOE_K_DOWN_MX) = range(23)
-MOE_K_COUNT = 23
+ MOE_K_MX_QUANT_ROWS, MOE_K_MX_QUANT_W, MOE_K_UP_MX, MOE_K_DOWN_MX, MOE_K_DXT_MX) = range(24)
+MOE_K_COUNT = 24
 
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16}
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.moe_bwd.restype = i32
         L.moe_fwd_mxfp8.argtypes = [pdesc, vp, vp, vp, prout, vp, vp, vp, sz, vp]
         L.moe_fwd_mxfp8.restype = i32
+        L.moe_bwd_mxfp8.argtypes = [pdesc, vp, vp, vp, vp, prout, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_bwd_mxfp8.restype = i32
         L.moe_unfused_cache_bytes.argtypes, L.moe_unfused_cache_bytes.restype = [pdesc], sz
         L.moe_fwd_unfused.argtypes = [pdesc, vp, vp, vp, prout, vp, vp, sz, vp]
         L.moe_fwd_unfused.restype = i32
@@ -262,6 +265,14 @@ def moe_fwd_mxfp8(desc, x, w1, w2, routing: Routing, o, h_cache, ws, stream=None
                                                 _stream(stream)))
 
 
+def moe_bwd_mxfp8(desc, x, w_r, w1, w2, routing: Routing, h_cache, d_o, dx, dw_r, dw1, dw2, ds, db, ws,
+                  stream=None):
+    _check("moe_bwd_mxfp8", lib().moe_bwd_mxfp8(ctypes.byref(desc), _p(x), _p(w_r), _p(w1), _p(w2),
+                                                ctypes.byref(routing.c), _p(h_cache), _p(d_o), _p(dx), _p(dw_r),
+                                                _p(dw1), _p(dw2), _p(ds), _p(db), _p(ws), ws.numel(),
+                                                _stream(stream)))
+
+
 def moe_unfused_cache_bytes(desc: MoeDesc) -> int:
     return lib().moe_unfused_cache_bytes(ctypes.byref(desc))
 
@@ -344,10 +355,24 @@ class Layer:
         moe_fwd_mxfp8(self.desc, x, w1, w2, self.routing, self.o, self.h_cache, self.ws_fwd_mx, stream)
         return self.o
 
-    def ws_view(self, item: int, count: int, dtype) -> torch.Tensor:
-        """View of an internal workspace item (MOE_ITEM_*) of ``count`` elements."""
+    def backward_mxfp8(self, x, w_r, w1, w2, d_o, stream=None):
+        """Backward with the dXt GEMM in MXFP8 (bf16 layers); same outputs as backward."""
+        if getattr(self, "ws_bwd_mx", None) is None:
+            n = moe_workspace_bytes(self.desc, MOE_WS_BWD_MXFP8)
+            if n == 0:
+                raise MoEError("moe_bwd_mxfp8", MOE_ESHAPE)
+            self.ws_bwd_mx = torch.empty(n, dtype=torch.uint8, device=self.o.device)
+        moe_bwd_mxfp8(self.desc, x, w_r, w1, w2, self.routing, self.h_cache, d_o, self.dx, self.dw_r,
+                      self.dw1, self.dw2, self.ds, self.db, self.ws_bwd_mx, stream)
+        return self.dx
+
+    def ws_view(self, item: int, count: int, dtype, mx_bwd: bool = False) -> torch.Tensor:
+        """View of an internal workspace item (MOE_ITEM_*) of ``count`` elements;
+        mx_bwd: the backward items of the MXFP8 backward's workspace."""
         off = moe_workspace_offset(self.desc, item)
-        if item >= MOE_ITEM_MX_XQ:
+        if item >= MOE_ITEM_MX_DHQ or (mx_bwd and item not in (MOE_ITEM_Y, MOE_ITEM_A)):
+            ws = self.ws_bwd_mx
+        elif item >= MOE_ITEM_MX_XQ:
             ws = self.ws_fwd_mx
         else:
             ws = self.ws_fwd if item in (MOE_ITEM_Y, MOE_ITEM_A) else self.ws_bwd

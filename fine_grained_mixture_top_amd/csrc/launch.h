@@ -60,7 +60,13 @@ bool mx_shape_ok(const GemmDims& g);
 // rows [rows][K] bf16 -> E4M3 codes [rows][K] and E8M0 scales [rows][K/32];
 // nrows (device) bounds the rows when set.
 hipError_t launch_mx_quant_rows(const void* src, int K, long long rows, const int32_t* nrows, uint8_t* q,
-                                uint8_t* s, hipStream_t st);
+                                uint8_t* s, hipStream_t st, int bN = 0);
+// the MXFP8 activation-gradient GEMM also takes 2n (<= 2048) as a reduction
+bool mx_bwd_shape_ok(const GemmDims& g);
+// dXt = dH W1^T on MXFP8 operands: dH codes [cap][2n] and scales [cap][2n/32],
+// W1 codes [E][d][2n] (rows along 2n) and scales [E][2n/128][d][4]
+hipError_t launch_dxt_mx(const GemmDims& g, const uint8_t* dhq, const uint8_t* dhs, const uint8_t* w1q,
+                         const uint8_t* w1s, const int32_t* offsets, void* dXt, hipStream_t st);
 // W [E][K][N] bf16 -> codes [E][N][K] and scales [E][K/128][N] (4 bytes each)
 hipError_t launch_mx_quant_w(const void* W, int E, int K, int N, uint8_t* q, uint8_t* sblk, hipStream_t st);
 hipError_t launch_up_mx(const GemmDims& g, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q,

@@ -42,7 +42,7 @@ size_t capacity(const moe_desc* d) {
 
 // Workspace items, in order, for each phase.
 struct Layout {
-  size_t off[10];
+  size_t off[16];
   size_t total;
 };
 
@@ -144,6 +144,20 @@ Layout mx_fwd_layout(const moe_desc* d) {
   return L;
 }
 
+// MXFP8 backward workspace: the bf16 backward's items, then the quantized
+// operands of the activation-gradient GEMM.
+Layout mx_bwd_layout(const moe_desc* d) {
+  Layout L = bwd_layout(d);
+  const size_t cap = capacity(d), D = d->d, n = d->n, E = d->E;
+  size_t o = L.total;
+  L.off[10] = o; o = up(o + cap * 2 * n);                 // dH codes [cap][2n]
+  L.off[11] = o; o = up(o + cap * (2 * n / 32));          // dH scales [cap][2n/32]
+  L.off[12] = o; o = up(o + E * D * 2 * n);               // W1 codes, rows along 2n [E][d][2n]
+  L.off[13] = o; o = up(o + E * (2 * n / 128) * D * 4);   // W1 scales [E][2n/128][d][4]
+  L.total = o;
+  return L;
+}
+
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return MOE_OK;
   if (!ws) return MOE_EINVAL;
@@ -200,6 +214,7 @@ size_t moe_workspace_bytes(const moe_desc* desc, int which) {
     case MOE_WS_BWD: return bwd_layout(desc).total;
     case MOE_WS_BWD_UNFUSED: return unfused_bwd_layout(desc).total;
     case MOE_WS_FWD_MXFP8: return mx_shape_ok(gemm_dims(desc)) ? mx_fwd_layout(desc).total : 0;
+    case MOE_WS_BWD_MXFP8: return mx_bwd_shape_ok(gemm_dims(desc)) ? mx_bwd_layout(desc).total : 0;
     default: return 0;
   }
 }
@@ -219,6 +234,10 @@ size_t moe_workspace_offset(const moe_desc* desc, int item) {
   if (item >= MOE_ITEM_MX_XQ && item <= MOE_ITEM_MX_Y) {
     if (!mx_shape_ok(gemm_dims(desc))) return (size_t)-1;
     return mx_fwd_layout(desc).off[item - MOE_ITEM_MX_XQ];
+  }
+  if (item >= MOE_ITEM_MX_DHQ && item <= MOE_ITEM_MX_W1RS) {
+    if (!mx_bwd_shape_ok(gemm_dims(desc))) return (size_t)-1;
+    return mx_bwd_layout(desc).off[10 + item - MOE_ITEM_MX_DHQ];
   }
   return (size_t)-1;
 }
@@ -271,14 +290,23 @@ int moe_fwd(const moe_desc* desc, const void* x, const void* w1, const void* w2,
   return MOE_OK;
 }
 
-int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1, const void* w2,
-            const moe_routing* routing, const void* h_cache, const void* d_o, void* dx, void* dw_r,
-            void* dw1, void* dw2, float* ds, float* db, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The backward's launch sequence; mx: the activation-gradient GEMM on MXFP8
+// operands (workspace laid out by mx_bwd_layout).
+int bwd_impl(const moe_desc* desc, const void* x, const void* w_r, const void* w1, const void* w2,
+             const moe_routing* routing, const void* h_cache, const void* d_o, void* dx, void* dw_r, void* dw1,
+             void* dw2, float* ds, float* db, void* ws, size_t ws_bytes, void* stream, bool mx) {
   int s = validate_desc(desc);
   if (s != MOE_OK) return s;
+  if (mx) {
+    if (desc->dtype != MOE_BF16) return MOE_EDTYPE;
+    if (!mx_bwd_shape_ok(gemm_dims(desc))) return MOE_ESHAPE;
+  }
   if (!x || !w_r || !w1 || !w2 || !h_cache || !d_o || !dx || !dw_r || !dw1 || !dw2 || !routing_ok(routing))
     return MOE_EINVAL;
-  const Layout L = bwd_layout(desc);
+  const Layout L = mx ? mx_bwd_layout(desc) : bwd_layout(desc);
   if ((s = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return s;
 
   hipStream_t st = (hipStream_t)stream;
@@ -302,7 +330,16 @@ int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1
   // the router backward (dS -> dz per row and dense) folded into the
   // aggregation; then dW_r = X^T dz
   MOE_TRY(MOE_K_WR_T, launch_transpose(D.dtype, w_r, D.d, D.E, w_rT, st));
-  MOE_TRY(MOE_K_DXT, launch_dxt(g, dH, w1, R.offsets, dXt, st));
+  if (mx) {
+    // dH and W1 quantized along 2n (dH from the bf16 values just written)
+    uint8_t *dhq = (uint8_t*)(w + L.off[10]), *dhs = (uint8_t*)(w + L.off[11]);
+    uint8_t *w1q = (uint8_t*)(w + L.off[12]), *w1s = (uint8_t*)(w + L.off[13]);
+    MOE_TRY(MOE_K_MX_QUANT_ROWS, launch_mx_quant_rows(dH, 2 * D.n, (long long)cap, R.offsets + D.E, dhq, dhs, st));
+    MOE_TRY(MOE_K_MX_QUANT_W, launch_mx_quant_rows(w1, 2 * D.n, (long long)D.E * D.d, nullptr, w1q, w1s, st, D.d));
+    MOE_TRY(MOE_K_DXT_MX, launch_dxt_mx(g, dhq, dhs, w1q, w1s, R.offsets, dXt, st));
+  } else {
+    MOE_TRY(MOE_K_DXT, launch_dxt(g, dH, w1, R.offsets, dXt, st));
+  }
   const AggDxArgs ax{dXt,    dS_part, dh_partials(g), R.row_gate, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T,
                      D.d,    D.E,     dS_row,         dz_row,     dz_dense,     dx};
   MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, ax, st));
@@ -313,6 +350,23 @@ int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1
   MOE_TRY(MOE_K_DW2, launch_dw2(g, As, d_o, R.row_token, R.offsets, dw2, wws, st));
   if (db) MOE_TRY(MOE_K_DB, launch_bias_grad(dz_row, R.offsets, D.E, db, st));
   return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_bwd(const moe_desc* desc, const void* x, const void* w_r, const void* w1, const void* w2,
+            const moe_routing* routing, const void* h_cache, const void* d_o, void* dx, void* dw_r,
+            void* dw1, void* dw2, float* ds, float* db, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_impl(desc, x, w_r, w1, w2, routing, h_cache, d_o, dx, dw_r, dw1, dw2, ds, db, ws, ws_bytes, stream,
+                  false);
+}
+
+int moe_bwd_mxfp8(const moe_desc* desc, const void* x, const void* w_r, const void* w1, const void* w2,
+                  const moe_routing* routing, const void* h_cache, const void* d_o, void* dx, void* dw_r,
+                  void* dw1, void* dw2, float* ds, float* db, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_impl(desc, x, w_r, w1, w2, routing, h_cache, d_o, dx, dw_r, dw1, dw2, ds, db, ws, ws_bytes, stream,
+                  true);
 }
 
 int moe_fwd_mxfp8(const moe_desc* desc, const void* x, const void* w1, const void* w2,

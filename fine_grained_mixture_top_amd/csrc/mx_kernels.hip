@@ -60,9 +60,11 @@ __device__ __forceinline__ int quant32(const float (&v)[32], uint32_t (&q)[8]) {
 
 // rows [rows][K] bf16 -> codes [rows][K], scales [rows][K/32]; one thread per
 // block of 32.  rows = *nrows when nrows is set (launched over the capacity).
+// bN > 0: the rows are E stacked [bN][K] weight matrices whose scales go to
+// the stage-blocked layout [E][K/128][bN] (4 bytes each) instead.
 __global__ void __launch_bounds__(256)
 k_mx_quant_rows(const bf16_t* __restrict__ src, int K, long long rows, const int32_t* __restrict__ nrows,
-                uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+                uint8_t* __restrict__ q, uint8_t* __restrict__ s, int bN) {
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   const int nb = K / 32;
   const long long row = t / nb;
@@ -86,7 +88,12 @@ k_mx_quant_rows(const bf16_t* __restrict__ src, int K, long long rows, const int
   uint4* o = reinterpret_cast<uint4*>(q + row * K + kb * 32);
   o[0] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
   o[1] = make_uint4(qw[4], qw[5], qw[6], qw[7]);
-  s[row * nb + kb] = (uint8_t)sc;
+  if (bN > 0) {
+    const long long e = row / bN, col = row % bN;
+    s[((e * (K / 128) + kb / 4) * bN + col) * 4 + (kb & 3)] = (uint8_t)sc;
+  } else {
+    s[row * nb + kb] = (uint8_t)sc;
+  }
 }
 
 // weights W [E][K][N] bf16 -> transposed codes [E][N][K] and stage-blocked
@@ -162,17 +169,21 @@ long long tiles_bound(size_t cap, int E) { return (long long)(cap + gmx::BM - 1)
 
 }  // namespace
 
+bool mx_bwd_shape_ok(const GemmDims& g) {
+  return mx_shape_ok(g) && 2 * g.n / 32 <= gmx::MAX_PA && g.cap * (size_t)2 * g.n < (size_t)g4::OOB;
+}
+
 bool mx_shape_ok(const GemmDims& g) {
   return g.dtype == DT_BF16 && g.d % 256 == 0 && g.n % 256 == 0 && g.d / 32 <= gmx::MAX_PA &&
          g.n / 32 <= gmx::MAX_PA && (size_t)g.T * g.d < (size_t)g4::OOB && g.cap * (size_t)g.d < (size_t)g4::OOB;
 }
 
 hipError_t launch_mx_quant_rows(const void* src, int K, long long rows, const int32_t* nrows, uint8_t* q,
-                                uint8_t* s, hipStream_t st) {
+                                uint8_t* s, hipStream_t st, int bN) {
   const long long threads = rows * (K / 32);
   if (threads <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_mx_quant_rows, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                     (const bf16_t*)src, K, rows, nrows, q, s);
+                     (const bf16_t*)src, K, rows, nrows, q, s, bN);
   return hipGetLastError();
 }
 
@@ -195,6 +206,19 @@ hipError_t launch_up_mx(const GemmDims& g, const uint8_t* xq, const uint8_t* xs,
   return run_gemm_mx<true, Epi>(s, a, b, xs, reinterpret_cast<const uint32_t*>(w1s), (size_t)g.T * d,
                                 (size_t)2 * n * d, (size_t)g.T * (d / 32), (size_t)(d / 128) * 2 * n * 4, ep,
                                 tiles_bound(g.cap, E) * (2 * n / gmx::BN), st);
+}
+
+hipError_t launch_dxt_mx(const GemmDims& g, const uint8_t* dhq, const uint8_t* dhs, const uint8_t* w1q,
+                         const uint8_t* w1s, const int32_t* offsets, void* dXt, hipStream_t st) {
+  const int n = g.n, d = g.d, E = g.E;
+  using Epi = g4::G4Store;
+  GemmShape s{offsets, E, 0, d, 2 * n, d, 1};
+  Operand a{dhq, nullptr, 0, 2 * n};
+  Operand b{w1q, nullptr, (long long)d * 2 * n, 2 * n};
+  typename Epi::Params ep{reinterpret_cast<bf16_t*>(dXt), d};
+  return run_gemm_mx<false, Epi>(s, a, b, dhs, reinterpret_cast<const uint32_t*>(w1s), g.cap * 2 * n,
+                                 (size_t)d * 2 * n, g.cap * (2 * n / 32), (size_t)(2 * n / 128) * d * 4, ep,
+                                 tiles_bound(g.cap, E) * (d / gmx::BN), st);
 }
 
 hipError_t launch_down_mx(const GemmDims& g, const uint8_t* aq, const uint8_t* as, const uint8_t* w2q,

@@ -101,7 +101,8 @@ extern "C" {
 #define MOE_K_MX_QUANT_W   20   /* w1 or w2 -> transposed codes + scales           */
 #define MOE_K_UP_MX        21   /* K1 on MXFP8 operands (SwiGLU epilogue) -> H, A  */
 #define MOE_K_DOWN_MX      22   /* K2 on MXFP8 operands -> Y                       */
-#define MOE_K_COUNT        23
+#define MOE_K_DXT_MX       23   /* K5 on MXFP8 operands -> dXt (moe_bwd_mxfp8)     */
+#define MOE_K_COUNT        24
 
 /* workspace phases */
 #define MOE_WS_ROUTE 0
@@ -109,6 +110,7 @@ extern "C" {
 #define MOE_WS_BWD   2
 #define MOE_WS_BWD_UNFUSED 3  /* moe_bwd_unfused */
 #define MOE_WS_FWD_MXFP8   4  /* moe_fwd_mxfp8 (0 when the shape is unsupported) */
+#define MOE_WS_BWD_MXFP8   5  /* moe_bwd_mxfp8 (0 when the shape is unsupported) */
 
 /* internal workspace items exposed for inspection (moe_workspace_offset) */
 #define MOE_ITEM_Y        0  /* fwd: down-proj output Y [cap, d] (dtype)          */
@@ -130,6 +132,11 @@ extern "C" {
 #define MOE_ITEM_MX_AQ   14  /* A codes [cap, n]                                  */
 #define MOE_ITEM_MX_AS   15  /* A scales [cap, n/32]                              */
 #define MOE_ITEM_MX_Y    16  /* down-proj output Y [cap, d] (bf16)                */
+/* MXFP8 backward workspace (its other items sit where MOE_WS_BWD has them) */
+#define MOE_ITEM_MX_DHQ  17  /* dH codes [cap, 2n]                                */
+#define MOE_ITEM_MX_DHS  18  /* dH scales [cap, 2n/32]                            */
+#define MOE_ITEM_MX_W1RQ 19  /* w1 codes along 2n: [E, d, 2n]                     */
+#define MOE_ITEM_MX_W1RS 20  /* w1 scales [E, 2n/128, d, 4]                       */
 
 /*
  * Layer description (host struct).
@@ -311,6 +318,20 @@ int moe_bwd_unfused(const moe_desc* desc, const void* x, const void* w_r, const 
 int moe_fwd_mxfp8(const moe_desc* desc, const void* x, const void* w1, const void* w2,
                   const moe_routing* routing, void* o, void* h_cache, void* ws, size_t ws_bytes,
                   void* stream);
+
+/*
+ * Backward with the activation-gradient GEMM dXt = dH w1^T on MXFP8 operands:
+ * dH (as the dH kernel wrote it, bf16) and each expert's w1 are quantized
+ * along 2n (E4M3, one E8M0 scale per 32 values, as in moe_fwd_mxfp8); every
+ * other step is moe_bwd's.  Same arguments and outputs as moe_bwd.
+ *   Shapes: those of moe_fwd_mxfp8 with n at most 1024 (else MOE_ESHAPE);
+ *   dtype MOE_BF16 (else MOE_EDTYPE).
+ *   ws: MOE_WS_BWD_MXFP8 workspace.
+ */
+int moe_bwd_mxfp8(const moe_desc* desc, const void* x, const void* w_r, const void* w1,
+                  const void* w2, const moe_routing* routing, const void* h_cache, const void* d_o,
+                  void* dx, void* dw_r, void* dw1, void* dw2, float* ds, float* db, void* ws,
+                  size_t ws_bytes, void* stream);
 
 /* Static text for a status code.  Host only. */
 const char* moe_strerror(int status);

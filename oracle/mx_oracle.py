@@ -25,7 +25,11 @@ specification leaves a choice (each listed in the design doc):
     output A rows along n, W2 along n;
   * A is quantized from its bf16 value, the precision the forward stores it
     in; H is returned in fp64 (the kernels store it in bf16 as in the plain
-    layer) and the backward runs in bf16 from it.
+    layer);
+  * in the backward, the activation-gradient GEMM dXt = dH W1^T takes dH
+    quantized along 2n from its bf16 value and W1 quantized along 2n (the
+    rows of each expert's [d, 2n] matrix); the other backward GEMMs stay in
+    the layer dtype.
 
 The forward itself is the plain layer forward (moe_oracle.forward) on the
 dequantized operands: H = deq(x_q)[tok] deq(W1_q), A = silu(G) * U,
@@ -177,6 +181,36 @@ def forward_mxfp8(x64, w1_64, w2_64, rt) -> dict:
     Out = np.zeros((T, d))
     np.add.at(Out, tok, rt["row_gate"][:, None] * Y)
     return dict(H=H, A=A, Y=Y, O=Out, xq=xq, xs=xs, w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, Aq=Aq, As=As)
+
+
+def backward_mxfp8(x64, wr64, w1_64, w2_64, rt, H, dO) -> dict:
+    """The backward with the activation-gradient GEMM dXt = dH W1^T on MXFP8
+    operands: dH quantized along 2n from its bf16 value, each expert's W1
+    quantized along 2n (rows of its [d, 2n] matrix, no transpose).  Every
+    other step is the plain backward (moe_oracle.backward) on the same H;
+    dX then sums the quantized-path dXt rows."""
+    b = O.backward(x64, wr64, w1_64, w2_64, rt, H, dO)
+    dHq, dHs = quantize(bf16_round(b["dH"]))
+    w1q, w1s = quantize(w1_64)                       # [E, d, 2n] along 2n
+    return dict(b, **dxt_from_codes(dHq, dHs, w1q, w1s, rt, b["dz"], wr64), dHq=dHq, dHs=dHs,
+                w1rq=w1q, w1rs=w1s)
+
+
+def dxt_from_codes(dHq, dHs, w1q, w1s, rt, dz, wr64) -> dict:
+    """dXt per row from the quantized dH rows and W1 rows, and the dX it
+    aggregates to (plus the router's dz W_r^T)."""
+    off, tok = rt["offsets"], rt["row_token"]
+    dHd = dequantize(dHq, dHs)
+    w1d = dequantize(w1q, w1s)                       # [E, d, 2n]
+    E, d = w1d.shape[0], w1d.shape[1]
+    dXt = np.zeros((dHd.shape[0], d))
+    for e in range(E):
+        s, t = off[e], off[e + 1]
+        if s < t:
+            dXt[s:t] = dHd[s:t] @ w1d[e].T
+    dX = dz @ wr64.T
+    np.add.at(dX, tok, dXt)
+    return dict(dXt=dXt, dX=dX)
 
 
 def layer_fwd_mxfp8(x, w_r, w1, w2, K, bias=None, tile=128, round_mode=0, round_seed=0) -> dict:

@@ -30,7 +30,8 @@ def test_header_functions_exported(lib):
     names = declared_functions()
     assert set(names) == {"moe_row_capacity", "moe_workspace_bytes", "moe_workspace_offset",
                           "moe_route", "moe_fwd", "moe_bwd", "moe_strerror",
-                          "moe_unfused_cache_bytes", "moe_fwd_unfused", "moe_bwd_unfused", "moe_fwd_mxfp8"}
+                          "moe_unfused_cache_bytes", "moe_fwd_unfused", "moe_bwd_unfused", "moe_fwd_mxfp8",
+                          "moe_bwd_mxfp8"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -140,6 +141,14 @@ def test_mxfp8_shapes_and_validation(lib):
         assert B.moe_workspace_offset(d, B.MOE_ITEM_MX_XQ) == -1
         assert lib.moe_fwd_mxfp8(ctypes.byref(d), 4096, 4096, 4096, ctypes.byref(r), 4096, 4096, 4096, 1 << 40,
                                  None) == code
+    assert B.moe_workspace_bytes(ok, B.MOE_WS_BWD_MXFP8) > B.moe_workspace_bytes(ok, B.MOE_WS_BWD)
+    big_n = B.make_desc(256, 512, 8, 1280, 2, "bf16")  # 2n = 2560 > 2048: backward only
+    assert B.moe_workspace_bytes(big_n, B.MOE_WS_BWD_MXFP8) == 0
+    assert lib.moe_bwd_mxfp8(ctypes.byref(big_n), *([4096] * 4), ctypes.byref(r), *([4096] * 6), None, None,
+                             4096, 1 << 40, None) == B.MOE_ESHAPE
+    nb = B.moe_workspace_bytes(ok, B.MOE_WS_BWD_MXFP8)
+    assert lib.moe_bwd_mxfp8(ctypes.byref(ok), *([4096] * 4), ctypes.byref(r), *([4096] * 6), None, None,
+                             4096, nb - 256, None) == B.MOE_EWORKSPACE
     need = B.moe_workspace_bytes(ok, B.MOE_WS_FWD_MXFP8)
     assert lib.moe_fwd_mxfp8(ctypes.byref(ok), 4096, 4096, 4096, ctypes.byref(r), 4096, 4096, 4096, need - 1,
                              None) == B.MOE_EWORKSPACE

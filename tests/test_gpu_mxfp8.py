@@ -167,3 +167,81 @@ def test_mxfp8_full_size_expert_sample(name):
         errs = dict(H=relF(Hg, H), A=relF(Ag, A), Y=relF(Yg, Y))
         print(name, int(e), s1 - s0, {k: f"{v:.2e}" for k, v in errs.items()})
         assert all(v <= TOL for v in errs.values()), errs
+
+
+BWD_CASES = [CASES[0], CASES[1], CASES[3]]
+
+
+@pytest.mark.parametrize("w,mode,tile", BWD_CASES, ids=[c[0].name for c in BWD_CASES])
+def test_mxfp8_backward_matches_oracle(w, mode, tile):
+    """moe_bwd_mxfp8 after the bf16 forward: dH and W1 codes bit-exact (dH
+    quantized from the GPU's own bf16 dH through the oracle's quantizer),
+    dXt / dX against the oracle on those codes, every other gradient against
+    the plain oracle backward, and dX end to end against the oracle's own
+    quantization."""
+    a = I.draw_all(w)
+    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, "bf16", round_mode=mode, round_seed=3, tile=tile)
+    L = B.Layer(desc)
+    X, WR, W1, W2, DO = (dev(a[k], "bf16") for k in ("x", "w_r", "w1", "w2", "d_o"))
+    L.route(X, WR)
+    L.forward(X, W1, W2)
+    L.backward_mxfp8(X, WR, W1, W2, DO)
+    torch.cuda.synchronize()
+    x64, wr64 = O.to_f64(a["x"], "bf16"), O.to_f64(a["w_r"], "bf16")
+    w1_64, w2_64 = O.to_f64(a["w1"], "bf16"), O.to_f64(a["w2"], "bf16")
+    rt = O.route(x64, wr64, None, w.K, tile, mode, 3)
+    assert_routing_equal(routing_host(L, w), rt)
+    fwd = O.forward(x64, w1_64, w2_64, rt)
+    dO = O.to_f64(a["d_o"], "bf16")
+    o = M.backward_mxfp8(x64, wr64, w1_64, w2_64, rt, M.bf16_round(fwd["H"]), dO)
+    d, E, n, P = w.d, w.E, w.n, rt["n_rows"]
+    dH_gpu = host64(L.ws_view(B.MOE_ITEM_DH, P * 2 * n, torch.bfloat16, mx_bwd=True)).reshape(P, 2 * n)
+    dhq, dhs = M.quantize(dH_gpu)
+    assert np.array_equal(u8(L, B.MOE_ITEM_MX_DHQ, P * 2 * n).reshape(P, 2 * n), dhq)
+    assert np.array_equal(u8(L, B.MOE_ITEM_MX_DHS, P * 2 * n // 32).reshape(P, 2 * n // 32), dhs)
+    assert np.array_equal(u8(L, B.MOE_ITEM_MX_W1RQ, E * d * 2 * n).reshape(E, d, 2 * n), o["w1rq"])
+    assert np.array_equal(blocked_to_rows(u8(L, B.MOE_ITEM_MX_W1RS, E * 2 * n // 32 * d), E, 2 * n, d), o["w1rs"])
+    ref = M.dxt_from_codes(dhq, dhs, o["w1rq"], o["w1rs"], rt, o["dz"], wr64)
+    dXt_gpu = host64(L.ws_view(B.MOE_ITEM_DXT, P * d, torch.bfloat16, mx_bwd=True)).reshape(P, d)
+    errs = dict(dH=relF(dH_gpu, o["dH"]), dXt=relF(dXt_gpu, ref["dXt"]), dX=relF(host64(L.dx), ref["dX"]),
+                dW1=relF(host64(L.dw1), o["dW1"]), dW2=relF(host64(L.dw2), o["dW2"]),
+                dWr=relF(host64(L.dw_r), o["dWr"]), dS=relF(host64(L.ds[:P]), o["dS"]))
+    e2e = relF(host64(L.dx), o["dX"])
+    print(w.name, {k: f"{v:.2e}" for k, v in errs.items()}, f"dX vs independent oracle {e2e:.2e}")
+    bad = {k: v for k, v in errs.items() if not v <= TOL}
+    assert not bad, bad
+    assert e2e <= E2E_TOL
+
+
+@pytest.mark.parametrize("name", ["fg7b_bf16", "olmoe_bf16"])
+def test_mxfp8_backward_full_size_expert_sample(name):
+    """Full size: for two sampled experts, dH and W1 codes bit-exact and their
+    dXt rows against the oracle on those codes."""
+    w = I.WORKLOADS[name]
+    a = I.draw_all(w)
+    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, "bf16")
+    L = B.Layer(desc)
+    X, WR, W1, W2, DO = (dev(a[k], "bf16") for k in ("x", "w_r", "w1", "w2", "d_o"))
+    L.route(X, WR)
+    L.forward(X, W1, W2)
+    L.backward_mxfp8(X, WR, W1, W2, DO)
+    torch.cuda.synchronize()
+    d, E, n = w.d, w.E, w.n
+    off = host_int(L.routing.offsets)
+    P = int(off[-1])
+    dH_all = L.ws_view(B.MOE_ITEM_DH, P * 2 * n, torch.bfloat16, mx_bwd=True).view(P, 2 * n)
+    dhq_all = L.ws_view(B.MOE_ITEM_MX_DHQ, P * 2 * n, torch.uint8).view(P, 2 * n)
+    w1q_all = L.ws_view(B.MOE_ITEM_MX_W1RQ, E * d * 2 * n, torch.uint8).view(E, d, 2 * n)
+    w1s_all = blocked_to_rows(u8(L, B.MOE_ITEM_MX_W1RS, E * 2 * n // 32 * d), E, 2 * n, d)
+    dXt_all = L.ws_view(B.MOE_ITEM_DXT, P * d, torch.bfloat16, mx_bwd=True).view(P, d)
+    for e in np.random.default_rng(7).choice(E, 2, replace=False):
+        s0, s1 = int(off[e]), int(off[e + 1])
+        dH = host64(dH_all[s0:s1])
+        dhq, dhs = M.quantize(dH)
+        assert np.array_equal(dhq_all[s0:s1].cpu().numpy(), dhq)
+        w1q, w1s = M.quantize(O.to_f64(a["w1"][e], "bf16"))
+        assert np.array_equal(w1q_all[e].cpu().numpy(), w1q) and np.array_equal(w1s_all[e], w1s)
+        ref = M.dequantize(dhq, dhs) @ M.dequantize(w1q, w1s).T
+        err = relF(host64(dXt_all[s0:s1]), ref)
+        print(name, int(e), s1 - s0, f"dXt {err:.2e}")
+        assert err <= TOL

@@ -106,3 +106,23 @@ def test_unfused_is_deterministic():
     L2, _ = run(w, a, True)
     for k in ("o", "dx", "dw_r", "dw1", "dw2"):
         assert torch.equal(getattr(L1, k), getattr(L2, k)), k
+
+
+@pytest.mark.parametrize("name", ["fg7b_bf16", "olmoe_bf16"])
+def test_unfused_full_size_agrees_with_fused(name):
+    """Full workload size, the benchmark's configuration: the unfused layer
+    against the fused one on the same inputs (the fused layer's full-size
+    parity with the oracle is tested in test_gpu_fullsize.py); the gathered
+    rows are exact copies."""
+    w = I.WORKLOADS[name]
+    a = I.draw_all(w)
+    Lf, _ = run(w, a, False)
+    Lu, X = run(w, a, True)
+    assert torch.equal(Lf.routing.row_token, Lu.routing.row_token)
+    P = int(host_int(Lf.routing.offsets)[-1])
+    c = cache_views(Lu, w, P)
+    assert torch.equal(c["Xg"], X[Lu.routing.row_token[:P].long()])
+    for k in ("o", "dx", "dw_r", "dw1", "dw2"):
+        e = relF(host64(getattr(Lu, k)), host64(getattr(Lf, k)))
+        assert e <= tol(w.dtype), (k, e)
+    assert relF(host64(c["H"]), host64(Lf.h_cache[:P])) <= tol(w.dtype)

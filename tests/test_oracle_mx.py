@@ -188,3 +188,30 @@ def test_forward_on_random_inputs_is_close_to_plain():
     for k in ("H", "Y", "O"):
         rel = np.linalg.norm(o[k] - p[k]) / np.linalg.norm(p[k])
         assert 1e-3 < rel < 0.08, (k, rel)
+
+
+def test_backward_dxt_on_exact_inputs_equals_plain():
+    """With dH's quantization the only rounding (integer W1 with a large
+    element in every 32-block along 2n), dXt is the plain dXt of the
+    dequantized dH, and the other gradients are the plain ones."""
+    T, d, E, n, K = 40, 64, 4, 64, 2
+    x, w1, w2 = exact_inputs(T, d, E, n, K, 3)
+    w1 = np.round(w1 * 64.0)
+    w1[:, :, ::32] = 11.0
+    w1 /= 64.0
+    wr = np.random.default_rng(13).standard_normal((d, E))
+    dO = np.random.default_rng(14).standard_normal((T, d))
+    rt = O.route(x, wr, None, K)
+    H = O.forward(x, w1, w2, rt)["H"]
+    b = M.backward_mxfp8(x, wr, w1, w2, rt, H, dO)
+    p = O.backward(x, wr, w1, w2, rt, H, dO)
+    _, w1s = M.quantize(w1)
+    assert np.array_equal(M.dequantize(M.quantize(w1)[0], w1s), w1)
+    dHd = M.dequantize(b["dHq"], b["dHs"])
+    for e in range(E):
+        s0, s1 = rt["offsets"][e], rt["offsets"][e + 1]
+        assert np.allclose(b["dXt"][s0:s1], dHd[s0:s1] @ w1[e].T, rtol=0, atol=1e-12)
+    for k in ("dH", "dS", "dW1", "dW2", "dWr", "dz"):
+        assert np.array_equal(b[k], p[k]), k
+    rel = np.linalg.norm(b["dX"] - p["dX"]) / np.linalg.norm(p["dX"])
+    assert 0 < rel < 0.05
