@@ -26,10 +26,11 @@ specification leaves a choice (each listed in the design doc):
   * A is quantized from its bf16 value, the precision the forward stores it
     in; H is returned in fp64 (the kernels store it in bf16 as in the plain
     layer);
-  * in the backward, the activation-gradient GEMM dXt = dH W1^T takes dH
-    quantized along 2n from its bf16 value and W1 quantized along 2n (the
-    rows of each expert's [d, 2n] matrix); the other backward GEMMs stay in
-    the layer dtype.
+  * in the backward, the activation-gradient GEMMs take MXFP8 operands:
+    dA' = dO W2^T with dO and W2 quantized along d (W2 by the rows of each
+    expert's [n, d] matrix), dXt = dH W1^T with dH quantized along 2n from
+    its bf16 value and W1 along 2n (rows of each expert's [d, 2n] matrix);
+    the weight-gradient GEMMs stay in the layer dtype.
 
 The forward itself is the plain layer forward (moe_oracle.forward) on the
 dequantized operands: H = deq(x_q)[tok] deq(W1_q), A = silu(G) * U,
@@ -184,16 +185,53 @@ def forward_mxfp8(x64, w1_64, w2_64, rt) -> dict:
 
 
 def backward_mxfp8(x64, wr64, w1_64, w2_64, rt, H, dO) -> dict:
-    """The backward with the activation-gradient GEMM dXt = dH W1^T on MXFP8
-    operands: dH quantized along 2n from its bf16 value, each expert's W1
-    quantized along 2n (rows of its [d, 2n] matrix, no transpose).  Every
-    other step is the plain backward (moe_oracle.backward) on the same H;
-    dX then sums the quantized-path dXt rows."""
-    b = O.backward(x64, wr64, w1_64, w2_64, rt, H, dO)
-    dHq, dHs = quantize(bf16_round(b["dH"]))
+    """The backward with both activation-gradient GEMMs on MXFP8 operands:
+    dA' = dO W2^T with dO quantized along d and each expert's W2 quantized
+    along d (rows of its [n, d] matrix), and dXt = dH W1^T with dH quantized
+    along 2n from its bf16 value and W1 along 2n.  The dH epilogue (A
+    recomputed from H, dS, the SwiGLU backward, A_s) and the weight and router
+    gradients follow the plain backward (moe_oracle.backward) from that dA':
+    dW1 = X_g^T dH, dW2 = A^T (gate dO_g) with the unquantized dO."""
+    T, d = x64.shape
+    E = w1_64.shape[0]
+    n = w1_64.shape[2] // 2
+    P = rt["n_rows"]
+    off, tok, rg = rt["offsets"], rt["row_token"], rt["row_gate"]
+    dOq, dOs = quantize(dO)                          # [T, d] along d
+    w2q, w2s = quantize(w2_64)                       # [E, n, d] along d
+    dOd = dequantize(dOq, dOs)
+    w2d = dequantize(w2q, w2s)
+    dAp = np.zeros((P, n))
+    dS = np.zeros(P)
+    dH = np.zeros((P, 2 * n))
+    dW1 = np.zeros_like(w1_64)
+    dW2 = np.zeros_like(w2_64)
+    for e in range(E):
+        s, t = off[e], off[e + 1]
+        if s == t:
+            continue
+        G, U = H[s:t, :n], H[s:t, n:]
+        sg = O.sigmoid(G)
+        A = G * sg * U
+        dAp[s:t] = dOd[tok[s:t]] @ w2d[e].T
+        dS[s:t] = np.sum(dAp[s:t] * A, axis=1)
+        dA = rg[s:t, None] * dAp[s:t]
+        dH[s:t, :n] = dA * U * sg * (1.0 + G * (1.0 - sg))
+        dH[s:t, n:] = dA * G * sg
+        dW1[e] = x64[tok[s:t]].T @ dH[s:t]
+        dW2[e] = A.T @ (rg[s:t, None] * dO[tok[s:t]])
+    # router: softmax-over-set backward per token, as in the plain backward
+    dSte = np.zeros((T, E))
+    dSte[tok, rt["row_expert"]] = dS
+    Gt = rt["gate"]
+    mean = np.sum(Gt * dSte, axis=1, keepdims=True)
+    dz = np.where(rt["member"], Gt * (dSte - mean), 0.0)
+    dHq, dHs = quantize(bf16_round(dH))
     w1q, w1s = quantize(w1_64)                       # [E, d, 2n] along 2n
-    return dict(b, **dxt_from_codes(dHq, dHs, w1q, w1s, rt, b["dz"], wr64), dHq=dHq, dHs=dHs,
-                w1rq=w1q, w1rs=w1s)
+    out = dict(dAp=dAp, dS=dS, dH=dH, dW1=dW1, dW2=dW2, dz=dz, dWr=x64.T @ dz, db=dz.sum(axis=0),
+               dOq=dOq, dOs=dOs, w2rq=w2q, w2rs=w2s, dHq=dHq, dHs=dHs, w1rq=w1q, w1rs=w1s)
+    out.update(dxt_from_codes(dHq, dHs, w1q, w1s, rt, dz, wr64))
+    return out
 
 
 def dxt_from_codes(dHq, dHs, w1q, w1s, rt, dz, wr64) -> dict:

@@ -190,28 +190,51 @@ def test_forward_on_random_inputs_is_close_to_plain():
         assert 1e-3 < rel < 0.08, (k, rel)
 
 
-def test_backward_dxt_on_exact_inputs_equals_plain():
-    """With dH's quantization the only rounding (integer W1 with a large
-    element in every 32-block along 2n), dXt is the plain dXt of the
-    dequantized dH, and the other gradients are the plain ones."""
+def test_backward_on_exact_inputs_equals_plain():
+    """dO, W1 and W2 that MXFP8 represents exactly (integer-valued, a large
+    element in every 32-block along d and along 2n): dA', dS, dH and every
+    weight and router gradient equal the plain backward's, and dXt is the
+    plain product of the dequantized dH (whose quantization is then the only
+    rounding)."""
     T, d, E, n, K = 40, 64, 4, 64, 2
     x, w1, w2 = exact_inputs(T, d, E, n, K, 3)
     w1 = np.round(w1 * 64.0)
     w1[:, :, ::32] = 11.0
     w1 /= 64.0
+    w2 = np.round(w2 * 64.0)
+    w2[:, :, ::32] = -12.0          # along d (rows of W2[e]) too
+    w2 /= 64.0
+    rng = np.random.default_rng(14)
+    dO = rng.integers(-7, 8, (T, d)).astype(np.float64)
+    dO[:, ::32] = 9.0
     wr = np.random.default_rng(13).standard_normal((d, E))
-    dO = np.random.default_rng(14).standard_normal((T, d))
     rt = O.route(x, wr, None, K)
     H = O.forward(x, w1, w2, rt)["H"]
     b = M.backward_mxfp8(x, wr, w1, w2, rt, H, dO)
     p = O.backward(x, wr, w1, w2, rt, H, dO)
-    _, w1s = M.quantize(w1)
-    assert np.array_equal(M.dequantize(M.quantize(w1)[0], w1s), w1)
+    assert np.array_equal(M.dequantize(b["dOq"], b["dOs"]), dO)
+    assert np.array_equal(M.dequantize(b["w2rq"], b["w2rs"]), w2)
+    assert np.array_equal(M.dequantize(b["w1rq"], b["w1rs"]), w1)
+    for k in ("dAp", "dS", "dH", "dW1", "dW2", "dWr", "dz", "db"):
+        assert np.allclose(b[k], p[k], rtol=0, atol=1e-12 * max(1.0, np.abs(p[k]).max())), k
     dHd = M.dequantize(b["dHq"], b["dHs"])
     for e in range(E):
         s0, s1 = rt["offsets"][e], rt["offsets"][e + 1]
         assert np.allclose(b["dXt"][s0:s1], dHd[s0:s1] @ w1[e].T, rtol=0, atol=1e-12)
-    for k in ("dH", "dS", "dW1", "dW2", "dWr", "dz"):
-        assert np.array_equal(b[k], p[k]), k
     rel = np.linalg.norm(b["dX"] - p["dX"]) / np.linalg.norm(p["dX"])
     assert 0 < rel < 0.05
+
+
+def test_backward_on_random_inputs_is_close_to_plain():
+    w = I.Workload("mx_small", T=64, d=128, E=8, n=64, K=2, dtype="bf16", seed=5)
+    a = I.draw_all(w)
+    x64, wr64 = O.to_f64(a["x"], "bf16"), O.to_f64(a["w_r"], "bf16")
+    w1, w2, dO = (O.to_f64(a[k], "bf16") for k in ("w1", "w2", "d_o"))
+    rt = O.route(x64, wr64, None, w.K)
+    H = O.forward(x64, w1, w2, rt)["H"]
+    b = M.backward_mxfp8(x64, wr64, w1, w2, rt, H, dO)
+    p = O.backward(x64, wr64, w1, w2, rt, H, dO)
+    for k in ("dAp", "dH", "dXt", "dX", "dW1", "dWr"):
+        rel = np.linalg.norm(b[k] - p[k]) / np.linalg.norm(p[k])
+        assert 1e-3 < rel < 0.08, (k, rel)
+    assert np.array_equal(b["dW2"], p["dW2"])  # A and the unquantized dO only
