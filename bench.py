@@ -42,8 +42,8 @@ def parse():
                     help="run the unfused layer (separate gather / SwiGLU kernels, X_g H A Y cached, "
                          "dS = <dO_g, Y>) instead of the fused one, for comparison")
     ap.add_argument("--mxfp8", action="store_true",
-                    help="run the forward GEMMs and the dXt GEMM in MXFP8 (moe_fwd_mxfp8, moe_bwd_mxfp8); "
-                         "the other backward GEMMs stay bf16")
+                    help="run the forward GEMMs and the dH and dXt GEMMs in MXFP8 (moe_fwd_mxfp8, "
+                         "moe_bwd_mxfp8); the weight-gradient GEMMs stay bf16")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the oracle's CPU baseline sample (0 = skip, -1 = as many as "
                          "fit a 4 TFLOP budget, about 20 s of fp64 work, capped at the workload's T)")
@@ -78,7 +78,7 @@ def kernel_work(name, w, P, es, mx=False):
         "router_logits": 2.0 * T * d * E, "up": 4.0 * P * d * n, "down": 2.0 * P * n * d,
         "dh": 2.0 * P * d * n, "dxt": 4.0 * P * d * n, "dw1": 4.0 * P * d * n,
         "dw2": 2.0 * P * n * d, "dwr": 2.0 * T * d * E, "da": 2.0 * P * d * n,
-        "up_mx": 4.0 * P * d * n, "down_mx": 2.0 * P * n * d, "dxt_mx": 4.0 * P * d * n,
+        "up_mx": 4.0 * P * d * n, "down_mx": 2.0 * P * n * d, "dxt_mx": 4.0 * P * d * n, "dh_mx": 2.0 * P * d * n,
     }
     if name in flops:
         return flops[name], "flop"
@@ -96,10 +96,10 @@ def kernel_work(name, w, P, es, mx=False):
         "gather": 2 * P * d * es + P * 4, "swiglu": 3 * P * n * es, "row_dot": 2 * P * d * es + P * 4,
         "swiglu_bwd": P * (n + 2 * n + n) * es + P * 4 + P * (2 * n + n) * es,
         # MXFP8 quantizers (bf16 in, codes + 1/32 scale bytes out), averaged
-        # over their three launches per step: x, A and dH rows; w1 and w2
-        # along their forward reductions, w1 along 2n for dXt
-        "mx_quant_rows": (T * d + P * n + P * 2 * n) * (es + 1 + 1 / 32) / 3,
-        "mx_quant_w": 5 * E * d * n * (es + 1 + 1 / 32) / 3,
+        # over their four launches per step: x, A, dO and dH rows; w1 and w2
+        # along their forward reductions, w2 along d for dH, w1 along 2n for dXt
+        "mx_quant_rows": (T * d + P * n + T * d + P * 2 * n) * (es + 1 + 1 / 32) / 4,
+        "mx_quant_w": 6 * E * d * n * (es + 1 + 1 / 32) / 4,
     }
     return float(bytes_.get(name, 0)), "byte"
 
@@ -277,7 +277,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8 (fwd GEMMs, dXt) + bf16" if args.mxfp8 else w.dtype,
+        "dtype": "mxfp8 (fwd, dH, dXt GEMMs) + bf16" if args.mxfp8 else w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "n": w.n, "K": w.K,
                    "round_mode": args.round_mode, "tile": args.tile, "rows": P, "parallelism": "single GPU",

@@ -30,6 +30,7 @@
 #pragma once
 
 #include "grouped_gemm4.h"
+#include "grouped_gemm5.h"
 
 namespace moe {
 namespace gmx {
@@ -50,6 +51,8 @@ constexpr int MAX_PA = 64;                // A scale bytes per row: K <= 2048
 constexpr int ASC_OFF = NS * STAGE;       // A scales of the tile: [256 rows][K/32]
 constexpr int SMEM = ASC_OFF + 256 * MAX_PA;
 constexpr int WE_OFF = STAGE;             // wave-local epilogue areas: over stage 1
+constexpr int CS_OFF = STAGE;             // fp32 staging of the pass epilogue: over stage 1
+static_assert(CS_OFF + g4::STAGE_C <= 2 * STAGE, "pass staging fits over stage 1");
 static_assert(WE_OFF + 8 * g4::WAVE_LDS <= 2 * STAGE, "wave areas fit over stage 1");
 static_assert(STAGE % 1024 == 0, "stage alignment");
 
@@ -129,7 +132,8 @@ __global__ void __launch_bounds__(NTH, 1)
 grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restrict__ ascale,
                        const uint32_t* __restrict__ bscale, uint32_t a_bytes, uint32_t b_bytes,
                        uint32_t as_bytes, uint32_t bs_bytes, typename Epi::Params ep) {
-  static_assert(g4::is_wave_epi<Epi>::value, "wave-local epilogues only");
+  static_assert(g4::is_wave_epi<Epi>::value || g5::has_prefetch<Epi>::value,
+                "wave-local epilogues or the pass epilogue with prefetched operands");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int tprefix[MAX_E + 1];
 
@@ -292,7 +296,40 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
       issue_ascale(cn);
       issue(0);
     }
-    Epi::run(ep, c, acc, smem + WE_OFF + w * g4::WAVE_LDS);
+    if constexpr (g4::is_wave_epi<Epi>::value) {
+      Epi::run(ep, c, acc, smem + WE_OFF + w * g4::WAVE_LDS);
+    } else {
+      // eight passes of 32 rows (pass p holds block j = p % 4 of the waves of
+      // m half p / 4), each pass's global operands loaded one pass ahead
+      float* Cs = reinterpret_cast<float*>(smem + CS_OFF);
+      typename Epi::Pre pcur, pnxt;
+      Epi::load(ep, c, 0, pcur);
+#pragma unroll 1
+      for (int p = 0; p < BM / g4::EROWS; ++p) {
+        if (c.m_valid - p * g4::EROWS <= 0) break;  // uniform over the workgroup
+        if (wm == (p >> 2)) {
+          const int jp = p & 3;
+          const int cl = lane & 31, hl = lane >> 5;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (j != jp) continue;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int eg = 0; eg < 4; ++eg) {
+                const float4 v = make_float4(acc[i][j][4 * eg], acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2],
+                                             acc[i][j][4 * eg + 3]);
+                *reinterpret_cast<float4*>(Cs + cl * g4::LDC + wn * 64 + 32 * i + 8 * eg + 4 * hl) = v;
+              }
+          }
+        }
+        __syncthreads();
+        if (p + 1 < BM / g4::EROWS) Epi::load(ep, c, p + 1, pnxt);
+        Epi::run(ep, c, p, Cs, pcur);
+        pcur = pnxt;
+        __syncthreads();
+      }
+    }
     c = cn;
     t = tn;
     ++r;

@@ -67,6 +67,12 @@ bool mx_bwd_shape_ok(const GemmDims& g);
 // W1 codes [E][d][2n] (rows along 2n) and scales [E][2n/128][d][4]
 hipError_t launch_dxt_mx(const GemmDims& g, const uint8_t* dhq, const uint8_t* dhs, const uint8_t* w1q,
                          const uint8_t* w1s, const int32_t* offsets, void* dXt, hipStream_t st);
+// dA' = dO W2^T on MXFP8 operands with the dH epilogue (as launch_dh): dO
+// codes [T][d] and scales [T][d/32] gathered per row, W2 codes [E][n][d]
+// (rows along d) and scales [E][d/128][n][4]; dS partials: n / 256 per row
+hipError_t launch_dh_mx(const GemmDims& g, const uint8_t* doq, const uint8_t* dos, const uint8_t* w2q,
+                        const uint8_t* w2s, const int32_t* row_token, const float* row_gate, const int32_t* offsets,
+                        const void* H, void* dH, void* As, float* dS_part, hipStream_t st);
 // W [E][K][N] bf16 -> codes [E][N][K] and scales [E][K/128][N] (4 bytes each)
 hipError_t launch_mx_quant_w(const void* W, int E, int K, int N, uint8_t* q, uint8_t* sblk, hipStream_t st);
 hipError_t launch_up_mx(const GemmDims& g, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q,

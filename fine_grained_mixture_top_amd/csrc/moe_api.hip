@@ -42,7 +42,7 @@ size_t capacity(const moe_desc* d) {
 
 // Workspace items, in order, for each phase.
 struct Layout {
-  size_t off[16];
+  size_t off[20];
   size_t total;
 };
 
@@ -145,7 +145,7 @@ Layout mx_fwd_layout(const moe_desc* d) {
 }
 
 // MXFP8 backward workspace: the bf16 backward's items, then the quantized
-// operands of the activation-gradient GEMM.
+// operands of the two activation-gradient GEMMs.
 Layout mx_bwd_layout(const moe_desc* d) {
   Layout L = bwd_layout(d);
   const size_t cap = capacity(d), D = d->d, n = d->n, E = d->E;
@@ -154,6 +154,10 @@ Layout mx_bwd_layout(const moe_desc* d) {
   L.off[11] = o; o = up(o + cap * (2 * n / 32));          // dH scales [cap][2n/32]
   L.off[12] = o; o = up(o + E * D * 2 * n);               // W1 codes, rows along 2n [E][d][2n]
   L.off[13] = o; o = up(o + E * (2 * n / 128) * D * 4);   // W1 scales [E][2n/128][d][4]
+  L.off[14] = o; o = up(o + (size_t)d->T * D);            // dO codes [T][d]
+  L.off[15] = o; o = up(o + (size_t)d->T * (D / 32));     // dO scales [T][d/32]
+  L.off[16] = o; o = up(o + E * n * D);                   // W2 codes, rows along d [E][n][d]
+  L.off[17] = o; o = up(o + E * (D / 128) * n * 4);       // W2 scales [E][d/128][n][4]
   L.total = o;
   return L;
 }
@@ -235,7 +239,7 @@ size_t moe_workspace_offset(const moe_desc* desc, int item) {
     if (!mx_shape_ok(gemm_dims(desc))) return (size_t)-1;
     return mx_fwd_layout(desc).off[item - MOE_ITEM_MX_XQ];
   }
-  if (item >= MOE_ITEM_MX_DHQ && item <= MOE_ITEM_MX_W1RS) {
+  if (item >= MOE_ITEM_MX_DHQ && item <= MOE_ITEM_MX_W2RS) {
     if (!mx_bwd_shape_ok(gemm_dims(desc))) return (size_t)-1;
     return mx_bwd_layout(desc).off[10 + item - MOE_ITEM_MX_DHQ];
   }
@@ -293,8 +297,8 @@ int moe_fwd(const moe_desc* desc, const void* x, const void* w1, const void* w2,
 }  // extern "C"
 
 namespace {
-// The backward's launch sequence; mx: the activation-gradient GEMM on MXFP8
-// operands (workspace laid out by mx_bwd_layout).
+// The backward's launch sequence; mx: the two activation-gradient GEMMs on
+// MXFP8 operands (workspace laid out by mx_bwd_layout).
 int bwd_impl(const moe_desc* desc, const void* x, const void* w_r, const void* w1, const void* w2,
              const moe_routing* routing, const void* h_cache, const void* d_o, void* dx, void* dw_r, void* dw1,
              void* dw2, float* ds, float* db, void* ws, size_t ws_bytes, void* stream, bool mx) {
@@ -325,7 +329,17 @@ int bwd_impl(const moe_desc* desc, const void* x, const void* w_r, const void* w
 
   // dH kernel: dA' = dO W2^T with the recompute-A epilogue (dH, A_s, dS parts)
   const GemmDims g = gemm_dims(desc);
-  MOE_TRY(MOE_K_DH, launch_dh(g, d_o, w2, h_cache, R.row_token, R.row_gate, R.offsets, dH, As, dS_part, st));
+  if (mx) {
+    // dO and W2 quantized along d (W2 by the rows of each expert's [n][d])
+    uint8_t *doq = (uint8_t*)(w + L.off[14]), *dos = (uint8_t*)(w + L.off[15]);
+    uint8_t *w2q = (uint8_t*)(w + L.off[16]), *w2s = (uint8_t*)(w + L.off[17]);
+    MOE_TRY(MOE_K_MX_QUANT_ROWS, launch_mx_quant_rows(d_o, D.d, D.T, nullptr, doq, dos, st));
+    MOE_TRY(MOE_K_MX_QUANT_W, launch_mx_quant_rows(w2, D.d, (long long)D.E * D.n, nullptr, w2q, w2s, st, D.n));
+    MOE_TRY(MOE_K_DH_MX, launch_dh_mx(g, doq, dos, w2q, w2s, R.row_token, R.row_gate, R.offsets, h_cache, dH, As,
+                                      dS_part, st));
+  } else {
+    MOE_TRY(MOE_K_DH, launch_dh(g, d_o, w2, h_cache, R.row_token, R.row_gate, R.offsets, dH, As, dS_part, st));
+  }
   // activation gradient: dXt = dH W1^T, then dX = sum of dXt + dz W_r^T, with
   // the router backward (dS -> dz per row and dense) folded into the
   // aggregation; then dW_r = X^T dz

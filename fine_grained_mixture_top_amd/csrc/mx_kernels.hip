@@ -221,6 +221,21 @@ hipError_t launch_dxt_mx(const GemmDims& g, const uint8_t* dhq, const uint8_t* d
                                  tiles_bound(g.cap, E) * (d / gmx::BN), st);
 }
 
+hipError_t launch_dh_mx(const GemmDims& g, const uint8_t* doq, const uint8_t* dos, const uint8_t* w2q,
+                        const uint8_t* w2s, const int32_t* row_token, const float* row_gate, const int32_t* offsets,
+                        const void* H, void* dH, void* As, float* dS_part, hipStream_t st) {
+  const int n = g.n, d = g.d, E = g.E;
+  using Epi = g5::G5DH;
+  GemmShape s{offsets, E, 0, n, d, n, 1};
+  Operand a{doq, row_token, 0, d};
+  Operand b{w2q, nullptr, (long long)n * d, d};
+  typename Epi::Params ep{reinterpret_cast<const bf16_t*>(H), row_gate, reinterpret_cast<bf16_t*>(dH),
+                          reinterpret_cast<bf16_t*>(As), dS_part, n, n / gmx::BN};
+  return run_gemm_mx<false, Epi>(s, a, b, dos, reinterpret_cast<const uint32_t*>(w2s), (size_t)g.T * d,
+                                 (size_t)n * d, (size_t)g.T * (d / 32), (size_t)(d / 128) * n * 4, ep,
+                                 tiles_bound(g.cap, E) * (n / gmx::BN), st);
+}
+
 hipError_t launch_down_mx(const GemmDims& g, const uint8_t* aq, const uint8_t* as, const uint8_t* w2q,
                           const uint8_t* w2s, const int32_t* offsets, void* Y, hipStream_t st) {
   const int n = g.n, d = g.d, E = g.E;

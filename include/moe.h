@@ -102,7 +102,8 @@ extern "C" {
 #define MOE_K_UP_MX        21   /* K1 on MXFP8 operands (SwiGLU epilogue) -> H, A  */
 #define MOE_K_DOWN_MX      22   /* K2 on MXFP8 operands -> Y                       */
 #define MOE_K_DXT_MX       23   /* K5 on MXFP8 operands -> dXt (moe_bwd_mxfp8)     */
-#define MOE_K_COUNT        24
+#define MOE_K_DH_MX        24   /* K4 on MXFP8 operands -> dH, A_s, dS             */
+#define MOE_K_COUNT        25
 
 /* workspace phases */
 #define MOE_WS_ROUTE 0
@@ -137,6 +138,10 @@ extern "C" {
 #define MOE_ITEM_MX_DHS  18  /* dH scales [cap, 2n/32]                            */
 #define MOE_ITEM_MX_W1RQ 19  /* w1 codes along 2n: [E, d, 2n]                     */
 #define MOE_ITEM_MX_W1RS 20  /* w1 scales [E, 2n/128, d, 4]                       */
+#define MOE_ITEM_MX_DOQ  21  /* d_o codes [T, d]                                  */
+#define MOE_ITEM_MX_DOS  22  /* d_o scales [T, d/32]                              */
+#define MOE_ITEM_MX_W2RQ 23  /* w2 codes along d: [E, n, d]                       */
+#define MOE_ITEM_MX_W2RS 24  /* w2 scales [E, d/128, n, 4]                        */
 
 /*
  * Layer description (host struct).
@@ -320,10 +325,12 @@ int moe_fwd_mxfp8(const moe_desc* desc, const void* x, const void* w1, const voi
                   void* stream);
 
 /*
- * Backward with the activation-gradient GEMM dXt = dH w1^T on MXFP8 operands:
- * dH (as the dH kernel wrote it, bf16) and each expert's w1 are quantized
- * along 2n (E4M3, one E8M0 scale per 32 values, as in moe_fwd_mxfp8); every
- * other step is moe_bwd's.  Same arguments and outputs as moe_bwd.
+ * Backward with the two activation-gradient GEMMs on MXFP8 operands (E4M3,
+ * one E8M0 scale per 32 values, as in moe_fwd_mxfp8): dA' = d_o w2^T with
+ * d_o and each expert's w2 quantized along d, feeding the dH epilogue; and
+ * dXt = dH w1^T with dH (as that epilogue wrote it, bf16) and each expert's
+ * w1 quantized along 2n.  The weight-gradient GEMMs, the aggregation and the
+ * router backward are moe_bwd's.  Same arguments and outputs as moe_bwd.
  *   Shapes: those of moe_fwd_mxfp8 with n at most 1024 (else MOE_ESHAPE);
  *   dtype MOE_BF16 (else MOE_EDTYPE).
  *   ws: MOE_WS_BWD_MXFP8 workspace.

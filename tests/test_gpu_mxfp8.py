@@ -174,11 +174,11 @@ BWD_CASES = [CASES[0], CASES[1], CASES[3]]
 
 @pytest.mark.parametrize("w,mode,tile", BWD_CASES, ids=[c[0].name for c in BWD_CASES])
 def test_mxfp8_backward_matches_oracle(w, mode, tile):
-    """moe_bwd_mxfp8 after the bf16 forward: dH and W1 codes bit-exact (dH
-    quantized from the GPU's own bf16 dH through the oracle's quantizer),
-    dXt / dX against the oracle on those codes, every other gradient against
-    the plain oracle backward, and dX end to end against the oracle's own
-    quantization."""
+    """moe_bwd_mxfp8 after the bf16 forward: dO, W2, dH and W1 codes
+    bit-exact (dH quantized from the GPU's own bf16 dH through the oracle's
+    quantizer), dH / A_s / dS and the weight and router gradients against the
+    oracle's MXFP8 backward, dXt / dX against the oracle on the GPU's dH
+    codes, and dX end to end against the oracle's own quantization."""
     a = I.draw_all(w)
     desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, "bf16", round_mode=mode, round_seed=3, tile=tile)
     L = B.Layer(desc)
@@ -195,6 +195,11 @@ def test_mxfp8_backward_matches_oracle(w, mode, tile):
     dO = O.to_f64(a["d_o"], "bf16")
     o = M.backward_mxfp8(x64, wr64, w1_64, w2_64, rt, M.bf16_round(fwd["H"]), dO)
     d, E, n, P = w.d, w.E, w.n, rt["n_rows"]
+    T = w.T
+    assert np.array_equal(u8(L, B.MOE_ITEM_MX_DOQ, T * d).reshape(T, d), o["dOq"])
+    assert np.array_equal(u8(L, B.MOE_ITEM_MX_DOS, T * d // 32).reshape(T, d // 32), o["dOs"])
+    assert np.array_equal(u8(L, B.MOE_ITEM_MX_W2RQ, E * n * d).reshape(E, n, d), o["w2rq"])
+    assert np.array_equal(blocked_to_rows(u8(L, B.MOE_ITEM_MX_W2RS, E * d // 32 * n), E, d, n), o["w2rs"])
     dH_gpu = host64(L.ws_view(B.MOE_ITEM_DH, P * 2 * n, torch.bfloat16, mx_bwd=True)).reshape(P, 2 * n)
     dhq, dhs = M.quantize(dH_gpu)
     assert np.array_equal(u8(L, B.MOE_ITEM_MX_DHQ, P * 2 * n).reshape(P, 2 * n), dhq)
