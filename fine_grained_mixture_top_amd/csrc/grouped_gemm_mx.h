@@ -1,8 +1,9 @@
-// Row-mode grouped GEMM with MXFP8 operands on gfx950: the forward
-// up-projection (SwiGLU epilogue) and down-projection with both operands in
-// the OCP MX format -- E4M3 elements, one E8M0 power-of-two scale per 32
-// consecutive k -- multiplied by v_mfma_scale_f32_32x32x64_f8f6f4, which
-// applies the block scales inside the matrix core and accumulates in fp32.
+// Row-mode grouped GEMM with MXFP8 operands on gfx950: the up-projection
+// (SwiGLU epilogue), the down-projection, and the two activation-gradient
+// GEMMs (dH with its pass epilogue, dXt) with both operands in the OCP MX
+// format -- E4M3 elements, one E8M0 power-of-two scale per 32 consecutive k
+// -- multiplied by v_mfma_scale_f32_32x32x64_f8f6f4, which applies the block
+// scales inside the matrix core and accumulates in fp32.
 //
 // Tile, wave and scheduling layout as the bf16 row-mode kernels
 // (grouped_gemm5.h): 256 x 256 tiles, 8 waves in 2 (m) x 4 (n), 128 x 64

@@ -1,7 +1,7 @@
-// MXFP8 forward: quantization of the GEMM operands to the OCP MX format
-// (E4M3 elements, one E8M0 scale per 32 consecutive values along the
-// reduction) and the two forward grouped GEMMs on the MX-scaled MFMA
-// (grouped_gemm_mx.h).  The pages name MXFP8 as the method's next precision
+// MXFP8 grouped GEMMs: quantization of the GEMM operands to the OCP MX
+// format (E4M3 elements, one E8M0 scale per 32 consecutive values along the
+// reduction) and the two forward GEMMs and two activation-gradient GEMMs on
+// the MX-scaled MFMA (grouped_gemm_mx.h).  The pages name MXFP8 as the method's next precision
 // step ([A] closing "未来展望" paragraph); the format is the OCP MX
 // specification's (section 5: blocks and scales; section 6.3: the shared
 // exponent floor(log2(amax)) - emax of the element type, 8 for E4M3).
