@@ -37,7 +37,7 @@ def source_hash() -> str:
 def classify(name: str, wgt_seen: dict) -> str:
     """Bench kernel name of one dispatch (None for kernels that are not tracked)."""
     if "grouped_gemm4_kernel" in name:
-        m = re.search(r"grouped_gemm4_kernel<(true|false), (true|false), (true|false), moe::(?:g4::)?(\w+)", name)
+        m = re.search(r"grouped_gemm4_kernel<(true|false), (true|false), (true|false), moe::(?:g\d::)?(\w+)", name)
         if not m:
             return None
         wgt, bmn, epi = m.group(1) == "true", m.group(2) == "true", m.group(4)
@@ -51,13 +51,13 @@ def classify(name: str, wgt_seen: dict) -> str:
             return "dw1" if k == 0 else "dw2"
         return "down" if bmn else "dxt"
     if "grouped_gemm5_kernel" in name:
-        m = re.search(r"grouped_gemm5_kernel<(true|false), (true|false), moe::(?:g4::)?(\w+)", name)
+        m = re.search(r"grouped_gemm5_kernel<(true|false), (true|false), moe::(?:g\d::)?(\w+)", name)
         if not m:
             return None
         bmn, epi = m.group(1) == "true", m.group(3)
         if epi in ("EpiSwiGLU", "G4SwiGLU"):
             return "up"
-        if epi in ("EpiDH", "G4DH"):
+        if epi in ("EpiDH", "G4DH", "G5DH"):
             return "dh"
         return "down" if bmn else "dxt"
     if "grouped_gemm_kernel" in name:
