@@ -50,7 +50,11 @@ __device__ __forceinline__ void store_vec(T* p, const float (&v)[16 / sizeof(T)]
   *reinterpret_cast<uint4*>(p) = u;
 }
 
-constexpr int UNR = 4;  // rows in flight per lane
+constexpr int UNR = 4;  // rows in flight per lane (output aggregation)
+// The dX aggregation also loads a router-weight row per token row, so it keeps
+// two rows in flight per lane: fewer registers, more waves per SIMD (measured
+// 0.195 -> 0.191 ms at T = 32768, d = 1536, K = 8 against four rows).
+constexpr int UNR_DX = 2;
 // Column chunks per lane per pass (CPL) are a template parameter: the
 // launcher picks the smallest CPL (at most 4) that covers a row's 16-byte
 // chunks in as few passes as CPL = 4 would, so no chunk slot idles (d = 1536
@@ -203,11 +207,11 @@ k_aggregate_dx(const T* __restrict__ dXt, const float* __restrict__ dS_part, int
     for (int c = 0; c < CPL; ++c)
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[c][i] = 0.f;
-    for (int j = j0; j < j1; j += UNR) {
-      uint4 raw[UNR][CPL], wr[UNR][CPL];
-      float g[UNR];
+    for (int j = j0; j < j1; j += UNR_DX) {
+      uint4 raw[UNR_DX][CPL], wr[UNR_DX][CPL];
+      float g[UNR_DX];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
+      for (int u = 0; u < UNR_DX; ++u) {
         const bool ok = j + u < j1;
         const int r = ok ? tok_row[j + u] : 0;
         const int e = ok ? row_expert[r] : 0;
@@ -221,7 +225,7 @@ k_aggregate_dx(const T* __restrict__ dXt, const float* __restrict__ dS_part, int
         }
       }
 #pragma unroll
-      for (int u = 0; u < UNR; ++u)
+      for (int u = 0; u < UNR_DX; ++u)
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           float v[V], ww[V];

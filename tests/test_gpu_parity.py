@@ -82,6 +82,8 @@ LAYER_CASES = [
     # more than 64 rows per token: the dX aggregation's router backward takes
     # its multi-pass branch
     W("bf16_many_slots", 300, 256, 80, 64, 72, "bf16", seed=21),
+    # exactly 64 rows per token: the last one-row-per-lane case
+    W("bf16_64_slots", 200, 256, 64, 64, 64, "bf16", seed=22),
 ]
 
 
