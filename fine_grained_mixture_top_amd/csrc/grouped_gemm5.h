@@ -213,6 +213,7 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
                      typename Epi::Params ep) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int tprefix[MAX_E + 1];
+  __shared__ __attribute__((aligned(256))) char touch_sink[256];  // written by the B-line touches, never read
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -272,6 +273,46 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   __amdgpu_buffer_rsrc_t ra, rb;
   KCLoad5 la, lb_kc;
   MNLoad5 lb_mn;
+  // B-line touch (weights stored [k][n]).  The tiles that share an expert's
+  // weight tile run side by side on one XCD (an XCD takes 32 consecutive
+  // tiles of the list per round, so about 32 / NT blocks of an expert), and
+  // each stage of the weight tile is a fresh set of 256 lines that misses L2
+  // for all of them at once.  When wave 7 issues stage k it also reads 4
+  // bytes of 256 / S of the lines of stage k + 2 into a scratch LDS area,
+  // S = 32 / NT clamped to 4..8 and the share chosen by the block index
+  // mod S, so that the tiles of one weight tile touch different lines and
+  // bring them into L2 a stage ahead of their loads.  Past the last stage the
+  // touch reads nothing (out-of-range offset) but is still issued, so that
+  // wave 7's load counts stay fixed.  Measured at T = 32768, d = 1536,
+  // E = 128, n = 256: up-projection 0.540 -> 0.511 ms; for the k-contiguous
+  // weights of dH and dXt, and in the k = 32 kernel's down-projection, it
+  // cost 1-2%, so those do not touch.
+  constexpr bool TOUCH = BMN;
+  const int tshare = NT >= 8 ? 4 : 8;  // S (NT = 1, 2, 4 give 8; 8 and more give 4)
+  uint32_t tch_col = OOB;  // byte offset of this lane's line at k = 0 (column part for [k][n] weights)
+  int tch_row = 0;         // k-row of this lane's line within a stage ([k][n] weights)
+  auto setup_touch = [&](const TileCtx& c) {
+    if constexpr (!TOUCH) return;
+    const int per = 256 / tshare;  // lines per tile and stage: 32 or 64
+    const int q = (c.mt % tshare) * per + lane;
+    if (lane >= per) {
+      tch_col = OOB;
+    } else {
+      // four lines per k-row, 64 k-rows per stage
+      tch_row = q >> 2;
+      const int which = q & 3;
+      int col;
+      if constexpr (PAIRED) col = c.nt * 128 + ((which & 1) ? 64 : 0) + ((which >> 1) ? s.N / 2 : 0);
+      else col = c.n0 + 64 * which;
+      tch_col = (uint32_t)col * 2u;
+    }
+  };
+  auto touch = [&](int k) {
+    const int kt = k + 2;
+    uint32_t o = OOB;
+    if (kt < nk && tch_col != OOB) o = tch_col + (uint32_t)(kt * BK + tch_row) * ((uint32_t)B.ld * 2u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (g4::lds_void_t*)touch_sink, 4, o, 0, 0, 0);
+  };
   auto setup = [&](const TileCtx& c) {
     ra = make_rsrc(abase, a_bytes);
     la.setup(w, lane, [&](int r) -> uint32_t {
@@ -290,6 +331,7 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       });
       lb_mn.ldb = (uint32_t)B.ld * 2u;
     }
+    if (TOUCH && w == 7) setup_touch(c);
   };
   auto issue = [&](int k) {
     char* st = smem + (k & 1) * STAGE;
@@ -297,6 +339,7 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     la.issue(ra, st, w, k0);
     if constexpr (!BMN) lb_kc.issue(rb, st + OPB, w, k0);
     else lb_mn.issue(rb, st + OPB, w, k0);
+    if (TOUCH && w == 7) touch(k);
   };
 
   int r = 0;
@@ -322,8 +365,14 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     if (nk > 1) issue(1);
     // stage 0 complete: only stage 1's loads came after it (and, for tiles
     // after the first, the previous epilogue's stores before those)
-    if (nk > 1) wait_vm<LPS>();
-    else wait_vm<0>();
+    // (wave 7: also the touches issued with stages 0 and 1)
+    if (TOUCH && w == 7) {
+      if (nk > 1) wait_vm<LPS + 2>();
+      else wait_vm<1>();
+    } else {
+      if (nk > 1) wait_vm<LPS>();
+      else wait_vm<0>();
+    }
     __syncthreads();
     Frags<BMN> f0, f1;
     f0.read(smem, 0, lane, wm, wn);
@@ -338,7 +387,9 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       if (k + 1 < nk) {
         // stage k+1 complete (nothing was issued after it); the barrier also
         // frees stage k's buffer for stage k+2
-        wait_vm<0>();
+        // (wave 7: its touch issued with stage k+1 may still be out)
+        if (TOUCH && w == 7) wait_vm<1>();
+        else wait_vm<0>();
         __syncthreads();
         if (k + 2 < nk) issue(k + 2);
         f0.read(smem + ((k + 1) & 1) * STAGE, 0, lane, wm, wn);
