@@ -114,7 +114,9 @@ template <typename T> constexpr int ROWS = ROWS_TILE;
 template <typename T>
 hipError_t router_logits(const void* x, const void* w_r, const float* bias, float* logits, int T_,
                          int d, int E, hipStream_t st) {
-  constexpr int BM = ROWS<T>, BN = std::is_same<T, bf16_t>::value ? 128 : 64;
+  // bf16: 64-row tiles, so that T = 32768 tokens give 512 tiles (two per
+  // CU) for this bandwidth-bound GEMM (N = E is small)
+  constexpr int BM = std::is_same<T, bf16_t>::value ? 64 : ROWS<T>, BN = std::is_same<T, bf16_t>::value ? 128 : 64;
   using Epi = EpiStore<T, float, BM, BN>;
   GemmShape s{nullptr, 1, T_, (E + BN - 1) / BN * BN, d, E, 1};
   Operand A{x, nullptr, 0, d};

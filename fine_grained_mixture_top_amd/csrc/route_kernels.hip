@@ -82,16 +82,19 @@ __device__ __forceinline__ int block_scan1024(int v, int* lds /* >= 16 ints */, 
   return base + incl - v;
 }
 
-// G lanes per token (G = 4 .. 32, the smallest with E <= 32 G): K rounds of
-// an arg-max over the token's scores held E/G per lane.  Writes the slot-ordered experts, their softmax
+// G lanes per token, MAXV >= E / G scores per lane: K rounds of an arg-max
+// over the token's scores.  Many lanes per token keep the dependent
+// compare chain of a round short and put more waves on each SIMD (T = 32768,
+// E = 128, K = 8: the whole route selection 0.063 -> 0.060 ms with 16 lanes
+// x 8 scores against 4 x 32).  Writes the slot-ordered experts, their softmax
 // gates and the membership bytes; with fixed_ptr also tok_ptr[t] = t*K (every
 // token keeps exactly K rows when there is no token rounding).  Slot k's score
 // is kept by lane k % G of the group.
-template <int G>
+template <int G, int MAXV>
 __global__ void __launch_bounds__(256)
 k_topk(const float* __restrict__ scores, int T, int E, int K, int mpitch, int32_t* __restrict__ topk_idx,
        float* __restrict__ topk_gate, uint8_t* __restrict__ mask, int32_t* __restrict__ tok_ptr) {
-  constexpr int MAXV = 32;  // E <= 32 * G
+  static_assert(MAXV <= 32, "one taken bit per score slot");
   const int lane = threadIdx.x & (G - 1);
   const int t = (blockIdx.x * 256 + threadIdx.x) / G;
   const bool live = t < T;  // groups never straddle a wave, so shuffles stay inside live groups
@@ -576,10 +579,10 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
     hipLaunchKernelGGL(kern, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, rb.logits, T, E, K, mp,
                        rb.topk_idx, rb.topk_gate, sc.mask, fixed_ptr);
   };
-  if (E <= 128) topk(k_topk<4>, 4);
-  else if (E <= 256) topk(k_topk<8>, 8);
-  else if (E <= 512) topk(k_topk<16>, 16);
-  else topk(k_topk<32>, 32);
+  if (E <= 128) topk(k_topk<16, 8>, 16);
+  else if (E <= 256) topk(k_topk<16, 16>, 16);
+  else if (E <= 512) topk(k_topk<32, 16>, 32);
+  else topk(k_topk<32, 32>, 32);
   if (round_mode == 0) {
     hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.counts_raw, rb.counts);
   } else {
