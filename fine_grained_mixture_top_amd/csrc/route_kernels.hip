@@ -34,11 +34,6 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// a beats b: larger score, equal scores -> smaller expert id.
-__device__ __forceinline__ bool beats(float av, int ae, float bv, int be) {
-  return av > bv || (av == bv && ae < be);
-}
-
 // Exclusive scan of one int per thread over a 256-thread block, in thread
 // order; returns the prefix and writes the block total to *total.
 __device__ __forceinline__ int block_scan256(int v, int* lds /* >= 4 ints */, int* total) {
@@ -82,50 +77,69 @@ __device__ __forceinline__ int block_scan1024(int v, int* lds /* >= 16 ints */, 
   return base + incl - v;
 }
 
-// G lanes per token, MAXV >= E / G scores per lane: K rounds of an arg-max
-// over the token's scores.  Many lanes per token keep the dependent
-// compare chain of a round short and put more waves on each SIMD (T = 32768,
-// E = 128, K = 8: the whole route selection 0.063 -> 0.060 ms with 16 lanes
-// x 8 scores against 4 x 32).  Writes the slot-ordered experts, their softmax
-// gates and the membership bytes; with fixed_ptr also tok_ptr[t] = t*K (every
-// token keeps exactly K rows when there is no token rounding).  Slot k's score
-// is kept by lane k % G of the group.
+// Inverse of score_key (-0 comes back as +0).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// 64-bit max over the 16 lanes of a DPP row: rotations by 8, 4, 2, 1.
+__device__ __forceinline__ uint64_t row_max16(uint64_t b) {
+#define MOE_ROR_MAX(o)                                                                                  \
+  {                                                                                                     \
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, 0x120 + (o), 0xF, 0xF, false); \
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), 0x120 + (o), 0xF, 0xF, false); \
+    const uint64_t ob = ((uint64_t)hi << 32) | lo;                                                      \
+    b = ob > b ? ob : b;                                                                                \
+  }
+  MOE_ROR_MAX(8) MOE_ROR_MAX(4) MOE_ROR_MAX(2) MOE_ROR_MAX(1)
+#undef MOE_ROR_MAX
+  return b;
+}
+
+// G lanes per token (16 or 32), MAXV >= E / G scores per lane: K rounds of
+// an arg-max over the token's scores.  Each score is held as one 64-bit key,
+// (order-preserving score bits, ~expert id), so the larger key is the larger
+// score and, among equal scores, the smaller expert; a round is a max over
+// the lane's keys, a max over the group (DPP rotations inside a 16-lane row,
+// one lane exchange between rows for G = 32), and clearing the winner's key.
+// Slot k's score is kept by lane k % G of the group.  Writes the slot-ordered
+// experts, their softmax gates and the membership bytes; with tok_ptr also
+// tok_ptr[t] = t*K (every token keeps exactly K rows when there is no token
+// rounding).  (T = 32768, E = 128, K = 8: 23 -> 16 us against a compare-and-
+// branch version with the same lane layout.)
 template <int G, int MAXV>
 __global__ void __launch_bounds__(256)
 k_topk(const float* __restrict__ scores, int T, int E, int K, int mpitch, int32_t* __restrict__ topk_idx,
        float* __restrict__ topk_gate, uint8_t* __restrict__ mask, int32_t* __restrict__ tok_ptr) {
-  static_assert(MAXV <= 32, "one taken bit per score slot");
+  static_assert(G == 16 || G == 32, "DPP rows of 16 lanes");
   const int lane = threadIdx.x & (G - 1);
   const int t = (blockIdx.x * 256 + threadIdx.x) / G;
-  const bool live = t < T;  // groups never straddle a wave, so shuffles stay inside live groups
+  const bool live = t < T;  // groups never straddle a wave, so exchanges stay inside live groups
   const float* z = scores + (size_t)(live ? t : 0) * E;
-  float v[MAXV], zs[MAXV];
-  uint32_t taken = 0;
+  uint64_t key[MAXV];
+  float zs[MAXV];
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int e = lane + G * i;
     const bool ok = live && e < E;
-    v[i] = ok ? z[e] : 0.f;
+    key[i] = ok ? ((uint64_t)score_key(z[e]) << 32) | (0xffffffffu - (uint32_t)e) : 0ull;  // 0: no score
     zs[i] = 0.f;
-    if (!ok) taken |= 1u << i;
   }
   for (int k = 0; k < K; ++k) {
-    float bv = 0.f;
-    int be = 0x7fffffff;
+    uint64_t b = key[0];
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      if (!(taken & (1u << i))) {
-        const int e = lane + G * i;
-        if (be == 0x7fffffff || beats(v[i], e, bv, be)) { bv = v[i]; be = e; }
-      }
+    for (int i = 1; i < MAXV; ++i) b = key[i] > b ? key[i] : b;
+    if constexpr (G == 32) {
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)b, 16, 64);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(b >> 32), 16, 64);
+      const uint64_t ob = ((uint64_t)hi << 32) | lo;
+      b = ob > b ? ob : b;
     }
+    b = row_max16(b);
 #pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (oe != 0x7fffffff && (be == 0x7fffffff || beats(ov, oe, bv, be))) { bv = ov; be = oe; }
-    }
-    if (live && (be & (G - 1)) == lane) taken |= 1u << (be / G);
+    for (int i = 0; i < MAXV; ++i) key[i] = key[i] == b ? 0ull : key[i];  // keys are distinct
+    const int be = (int)(0xffffffffu - (uint32_t)b);
+    const float bv = key_score((uint32_t)(b >> 32));
     if ((k & (G - 1)) == lane) {
 #pragma unroll
       for (int i = 0; i < MAXV; ++i)
