@@ -422,9 +422,30 @@ k_compact(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restric
 }
 
 // Plain top-K: each token's rows are its K slots sorted by expert id; the
-// row gate is the slot's top-K gate.  For K <= 16 the slots sit in registers
-// and each lands at its rank (the number of slots with a smaller expert id;
-// ids are distinct); larger K takes a selection pass per position.
+// row gate is the slot's top-K gate.  For K <= 16 one thread per (token,
+// slot): the slot lands at its rank among the token's slots (the number of
+// slots with a smaller expert id; ids are distinct).  (One thread per token
+// left only two waves per CU for this latency-bound lookup: 12 us at
+// T = 32768, K = 8.)
+__global__ void __launch_bounds__(256)
+k_tok_fill_slots(const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_gate,
+                 const int32_t* __restrict__ rowmap, int mpitch, int T, int K,
+                 int32_t* __restrict__ tok_row, float* __restrict__ row_gate) {
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (long long)T * K) return;
+  const int t = (int)(q / K), j = (int)(q % K);
+  const int32_t* idx = topk_idx + (size_t)t * K;
+  const int e = idx[j];
+  int pos = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    if (k < K) pos += idx[k] < e ? 1 : 0;
+  const int row = rowmap[(size_t)e * mpitch + t];
+  tok_row[(size_t)t * K + pos] = row;
+  row_gate[row] = topk_gate[q];
+}
+
+// Same for K > 16: one thread per token, a selection pass per position.
 __global__ void __launch_bounds__(256)
 k_tok_fill_topk(const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_gate,
                 const int32_t* __restrict__ rowmap, int mpitch, int T, int K,
@@ -434,22 +455,6 @@ k_tok_fill_topk(const int32_t* __restrict__ topk_idx, const float* __restrict__ 
   const int32_t* idx = topk_idx + (size_t)t * K;
   const float* g = topk_gate + (size_t)t * K;
   int32_t* out = tok_row + (size_t)t * K;
-  if (K <= 16) {
-    int ids[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) ids[k] = k < K ? idx[k] : 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j >= K) break;
-      int pos = 0;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) pos += ids[k] < ids[j] ? 1 : 0;
-      const int row = rowmap[(size_t)ids[j] * mpitch + t];
-      out[pos] = row;
-      row_gate[row] = g[j];
-    }
-    return;
-  }
   int prev = -1;
   for (int j = 0; j < K; ++j) {
     int best = 0x7fffffff, bk = 0;
@@ -614,8 +619,12 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
   hipLaunchKernelGGL(k_compact, dim3(E), dim3(1024), 0, st, sc.mask, mp, rb.offsets, rb.row_token,
                      rb.row_expert, sc.rowmap);
   if (round_mode == 0) {
-    hipLaunchKernelGGL(k_tok_fill_topk, dim3((T + 255) / 256), dim3(256), 0, st, rb.topk_idx, rb.topk_gate,
-                       sc.rowmap, mp, T, K, rb.tok_row, rb.row_gate);
+    if (K <= 16)
+      hipLaunchKernelGGL(k_tok_fill_slots, dim3((unsigned)(((long long)T * K + 255) / 256)), dim3(256), 0, st,
+                         rb.topk_idx, rb.topk_gate, sc.rowmap, mp, T, K, rb.tok_row, rb.row_gate);
+    else
+      hipLaunchKernelGGL(k_tok_fill_topk, dim3((T + 255) / 256), dim3(256), 0, st, rb.topk_idx, rb.topk_gate,
+                         sc.rowmap, mp, T, K, rb.tok_row, rb.row_gate);
   } else {
     const unsigned blocks = (unsigned)((T + 63) / 64);
     hipLaunchKernelGGL(k_tok_stats, dim3(blocks), dim3(256), 0, st, sc.mask, mp, sc.scoresT, T, E, sc.tokcnt,
