@@ -10,7 +10,7 @@ Formats specification v1.0 (section 5: MX block of 32 elements sharing one
 E8M0 scale; section 6.3: converting a block of higher-precision values) and
 the OCP 8-bit floating point specification (E4M3: bias 7, no infinities,
 S.1111.111 the only NaN, largest finite 448).  Readings taken where the
-specification leaves a choice (each listed in the design doc):
+specification leaves a choice:
 
   * element type E4M3 (the "MXFP8" the pages name; E5M2 is the other MX
     8-bit type and is not used);
