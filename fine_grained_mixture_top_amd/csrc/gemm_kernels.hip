@@ -44,10 +44,10 @@ hipError_t run_gemm(const GemmShape& s, const Operand& A, const Operand& B,
 }
 
 // 256 x 256 tile kernel: one 512-thread workgroup per CU (LDS-bound).
-template <bool WGT, bool BMN, bool PAIRED, class Epi>
+template <bool WGT, bool BMN, bool PAIRED, class Epi, bool TCH = false>
 hipError_t run_gemm4(const GemmShape& s, const Operand& A, const Operand& B, size_t a_bytes, size_t b_bytes,
                      const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
-  auto kern = g4::grouped_gemm4_kernel<WGT, BMN, PAIRED, Epi>;
+  auto kern = g4::grouped_gemm4_kernel<WGT, BMN, PAIRED, Epi, TCH>;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, g4::SMEM);
   if (attr != hipSuccess) return attr;
@@ -501,7 +501,12 @@ hipError_t wgt_g4(const GemmDims& g, const int32_t* offsets, int M, int N, const
   s.plan = WgtPlan{plan, units, pol.MU};
   using Epi = g4::G4StoreW;
   typename Epi::Params ep{reinterpret_cast<bf16_t*>(C), N, partial};
-  err = run_gemm4<true, true, false, Epi>(s, a, b, a_bytes, b_bytes, ep, num_cus(), st);
+  // the row-touch variant when a widely shared operand is read without an
+  // index (see the kernel): B when MU > NT, A when NT > MU
+  const int nt = N / g4::BN;
+  const bool tch = pol.MU != nt && (pol.MU > nt ? b.idx : a.idx) == nullptr;
+  if (tch) err = run_gemm4<true, true, false, Epi, true>(s, a, b, a_bytes, b_bytes, ep, num_cus(), st);
+  else err = run_gemm4<true, true, false, Epi>(s, a, b, a_bytes, b_bytes, ep, num_cus(), st);
   if (err != hipSuccess || pol.split == 0) return err;
   hipLaunchKernelGGL(k_wgt_reduce, dim3((unsigned)(2 * num_cus())), dim3(256), 0, st, plan, split_list, M, N,
                      partial, reinterpret_cast<bf16_t*>(C));
