@@ -59,10 +59,10 @@ hipError_t run_gemm4(const GemmShape& s, const Operand& A, const Operand& B, siz
 }
 
 // Row-mode 256 x 256 tile kernel with k = 64 per stage (one workgroup per CU).
-template <bool BMN, bool PAIRED, class Epi>
+template <bool BMN, bool PAIRED, class Epi, bool TCHA = false>
 hipError_t run_gemm5(const GemmShape& s, const Operand& A, const Operand& B, size_t a_bytes, size_t b_bytes,
                      const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
-  auto kern = g5::grouped_gemm5_kernel<BMN, PAIRED, Epi>;
+  auto kern = g5::grouped_gemm5_kernel<BMN, PAIRED, Epi, TCHA>;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, g5::SMEM);
   if (attr != hipSuccess) return attr;
@@ -80,8 +80,14 @@ hipError_t run_gemm5(const GemmShape& s, const Operand& A, const Operand& B, siz
 template <bool BMN, bool PAIRED, class Epi>
 hipError_t run_row256(const GemmShape& s, const Operand& A, const Operand& B, size_t a_bytes, size_t b_bytes,
                       const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
-  if (s.K % g5::BK == 0 && s.K >= 512)
+  if (s.K % g5::BK == 0 && s.K >= 512) {
+    // k-contiguous weights and A rows read without an index, shared by at
+    // least four column tiles: the A-row touch variant
+    if constexpr (!BMN)
+      if (A.idx == nullptr && s.N / g5::BN >= 4)
+        return run_gemm5<BMN, PAIRED, Epi, true>(s, A, B, a_bytes, b_bytes, ep, max_tiles, st);
     return run_gemm5<BMN, PAIRED, Epi>(s, A, B, a_bytes, b_bytes, ep, max_tiles, st);
+  }
   return run_gemm4<false, BMN, PAIRED, Epi>(s, A, B, a_bytes, b_bytes, ep, max_tiles, st);
 }
 

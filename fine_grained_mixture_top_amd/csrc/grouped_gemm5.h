@@ -207,7 +207,7 @@ template <class E> struct has_prefetch<E, std::void_t<decltype(E::PREFETCH)>> : 
 // expert's weights, [N][K] (BMN = false) or [K][N] (BMN = true; PAIRED
 // arranges the columns for G4SwiGLU).  Workgroup v takes tiles v, v + G, ...
 // of the expert-major tile list (v the XCD-grouped id).
-template <bool BMN, bool PAIRED, class Epi>
+template <bool BMN, bool PAIRED, class Epi, bool TCHA = false>
 __global__ void __launch_bounds__(NTH, 1)
 grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32_t b_bytes,
                      typename Epi::Params ep) {
@@ -287,12 +287,28 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   // E = 128, n = 256: up-projection 0.540 -> 0.511 ms; for the k-contiguous
   // weights of dH and dXt, and in the k = 32 kernel's down-projection, it
   // cost 1-2%, so those do not touch.
-  constexpr bool TOUCH = BMN;
-  const int tshare = NT >= 8 ? 4 : 8;  // S (NT = 1, 2, 4 give 8; 8 and more give 4)
+  //
+  // A-row touch (TCHA, chosen by the host for k-contiguous weights when A's
+  // rows are read without an index and NT >= 4, i.e. dXt): the NT tiles of
+  // one row block share its A rows; tile nt touches a 1/S share of the 256
+  // A lines of stage k + 2, S = NT clamped to 4..8, the same way.  dXt
+  // 0.516 -> 0.501 ms at d = 1536, n = 256 and 1.94 -> 1.88 ms at d = 2048,
+  // n = 1024.
+  static_assert(!(TCHA && BMN), "one touch kind per launch");
+  constexpr bool TOUCH = BMN || TCHA;
+  const int tshare = TCHA ? (NT < 4 ? 4 : (NT > 8 ? 8 : NT)) : (NT >= 8 ? 4 : 8);  // S
   uint32_t tch_col = OOB;  // byte offset of this lane's line at k = 0 (column part for [k][n] weights)
   int tch_row = 0;         // k-row of this lane's line within a stage ([k][n] weights)
   auto setup_touch = [&](const TileCtx& c) {
     if constexpr (!TOUCH) return;
+    if constexpr (TCHA) {
+      const int per = (256 + tshare - 1) / tshare;  // 32..64 lines per tile and stage
+      const int q = (c.nt % tshare) * per + lane;
+      const int m = c.mt * BM + q;
+      tch_row = 0;
+      tch_col = (lane < per && q < 256 && m < c.segn) ? (uint32_t)(c.seg0 + m) * (uint32_t)A.ld * 2u : OOB;
+      return;
+    }
     const int per = 256 / tshare;  // lines per tile and stage: 32 or 64
     const int q = (c.mt % tshare) * per + lane;
     if (lane >= per) {
@@ -310,8 +326,13 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   auto touch = [&](int k) {
     const int kt = k + 2;
     uint32_t o = OOB;
-    if (kt < nk && tch_col != OOB) o = tch_col + (uint32_t)(kt * BK + tch_row) * ((uint32_t)B.ld * 2u);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (g4::lds_void_t*)touch_sink, 4, o, 0, 0, 0);
+    if constexpr (TCHA) {
+      if (kt < nk && tch_col != OOB) o = tch_col + (uint32_t)(kt * BK) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (g4::lds_void_t*)touch_sink, 4, o, 0, 0, 0);
+    } else {
+      if (kt < nk && tch_col != OOB) o = tch_col + (uint32_t)(kt * BK + tch_row) * ((uint32_t)B.ld * 2u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (g4::lds_void_t*)touch_sink, 4, o, 0, 0, 0);
+    }
   };
   auto setup = [&](const TileCtx& c) {
     ra = make_rsrc(abase, a_bytes);
