@@ -84,6 +84,10 @@ LAYER_CASES = [
     W("bf16_many_slots", 300, 256, 80, 64, 72, "bf16", seed=21),
     # exactly 64 rows per token: the last one-row-per-lane case
     W("bf16_64_slots", 200, 256, 64, 64, 64, "bf16", seed=22),
+    # d = 1024, n = 256: every line-touch variant runs (dXt with four column
+    # tiles touches its A rows, dW1 with MU = 4 > NT = 2 its B rows, dW2 with
+    # NT = 4 > MU = 1 its A rows, the up-projection its [k][n] weights)
+    W("bf16_touch_variants", 600, 1024, 8, 256, 2, "bf16", seed=23),
 ]
 
 
