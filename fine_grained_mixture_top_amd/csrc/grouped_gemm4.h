@@ -28,6 +28,9 @@
 //    unchanged.  The staging area lies over the last stage only: before the
 //    epilogue of a tile, the first three stages of the workgroup's next tile
 //    are already being loaded, so that tile's start does not wait for memory.
+//  * Weight gradients, host-selected TCH variant: wave 7 touches a share of
+//    the lines of the operand the plan unit's tiles share most (read without
+//    an index) two stages ahead, and its waits count the touches.
 #pragma once
 
 #include <type_traits>

@@ -20,6 +20,10 @@
 //    transpose reads of the 256 x 256 kernel.
 //  * The epilogue areas lie over stage 1: the next tile's stage 0 is loaded
 //    before the epilogue, its stage 1 once every wave has finished it.
+//  * Line touches: the tiles that share an operand tile run side by side on
+//    one XCD, so wave 7 reads 4 bytes of a share of that operand's lines two
+//    stages ahead (the [k][n] weights always; A rows in the host-selected
+//    TCHA variant), and its waits count the touches.
 #pragma once
 
 #include "grouped_gemm4.h"
