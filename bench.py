@@ -2,9 +2,10 @@
 one MI355X through the C ABI.
 
 Prints one JSON line: whole-step TFLOPS (useful FLOPs 18*P*d*n per step, P =
-routed rows) and its fraction of the bf16 MFMA peak, the roofline position of
-the dominant kernel (per-launch durations from HIP events the library records
-on its stream during the timed steps), every kernel's time and roofline
+routed rows; the timed steps run with nothing recorded between launches) and
+its fraction of the bf16 MFMA peak, the roofline position of the dominant
+kernel (per-launch durations from HIP events the library records on its
+stream during a second pass of as many steps), every kernel's time and roofline
 fraction, and the fp64 CPU oracle timed on a bounded sample of the same
 workload as a reported baseline.  Also reported: single steps timed after a
 1 GiB write that evicts the caches ("flushed"), the bytes kept between forward
@@ -138,15 +139,42 @@ def routing_report(L, tile=128):
             "partial_tile": int((raw % tile != 0).sum()), "tile": tile}
 
 
-def cpu_baseline(w, a, tokens):
-    """fp64 oracle (as it stands) on the first `tokens` tokens of the workload."""
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(w, a, tokens, repeats=1):
+    """fp64 oracle (as it stands) on the first `tokens` tokens of the workload:
+    routing + forward and the backward timed separately; with repeats > 1 the
+    median of that many runs of each."""
     import numpy as np
     from oracle import moe_oracle as O
     tk = min(tokens, w.T)
-    t0 = time.perf_counter()
-    r = O.layer(a["x"][:tk], a["w_r"], a["w1"], a["w2"], a["d_o"][:tk], w.dtype, w.K, bias=a["bias"])
-    dt = time.perf_counter() - t0
-    rows = int(r["n_rows"])
+    x64, wr64 = O.to_f64(a["x"][:tk], w.dtype), O.to_f64(a["w_r"], w.dtype)
+    w1, w2 = O.to_f64(a["w1"], w.dtype), O.to_f64(a["w2"], w.dtype)
+    dO = O.to_f64(a["d_o"][:tk], w.dtype)
+    fwd_s, bwd_s = [], []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        rt = O.route(x64, wr64, a["bias"], w.K)
+        f = O.forward(x64, w1, w2, rt)
+        t1 = time.perf_counter()
+        O.backward(x64, wr64, w1, w2, rt, f["H"], dO)
+        t2 = time.perf_counter()
+        fwd_s.append(t1 - t0)
+        bwd_s.append(t2 - t1)
+    fwd, bwd = float(np.median(fwd_s)), float(np.median(bwd_s))
+    dt = fwd + bwd
+    rows = int(rt["n_rows"])
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -154,11 +182,13 @@ def cpu_baseline(w, a, tokens):
     omp = os.environ.get("OMP_NUM_THREADS")
     if omp and omp.isdigit():
         cores = min(cores, int(omp))
-    del np
+    med = f", median of {repeats} runs" if repeats > 1 else ""
     return {"value": 18.0 * rows * w.d * w.n / dt / 1e12, "unit": "TFLOPS", "cores": cores,
-            "kind": "oracle",
-            "sample": f"route+fwd+bwd of {tk} of {w.T} tokens ({rows} rows), same weights, "
-                      f"fp64 numpy, {dt:.1f} s"}
+            "kind": "oracle", "cpu": cpu_model(),
+            "fwd_s": round(fwd, 6), "bwd_s": round(bwd, 6),
+            "fwd_tflops": 6.0 * rows * w.d * w.n / fwd / 1e12, "bwd_tflops": 12.0 * rows * w.d * w.n / bwd / 1e12,
+            "sample": f"route+fwd ({fwd:.2f} s) and bwd ({bwd:.2f} s) of {tk} of {w.T} tokens ({rows} rows), "
+                      f"same weights, fp64 numpy{med}"}
 
 
 def main():
@@ -205,8 +235,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    prof = B.Profiler(capacity=(B.MOE_K_COUNT + 2) * args.steps)
-    prof.attach(L.desc)
+    # headline: the timed steps with nothing recorded between the launches
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
@@ -214,8 +243,20 @@ def main():
         step()
     t1.record()
     torch.cuda.synchronize()
-    B.Profiler.detach(L.desc)
     ms_step = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel times: the same number of steps again, with the library
+    # recording a HIP event pair around every launch on its stream
+    prof = B.Profiler(capacity=(B.MOE_K_COUNT + 2) * args.steps)
+    prof.attach(L.desc)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    B.Profiler.detach(L.desc)
+    ms_step_profiled = t0.elapsed_time(t1) / args.steps
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -284,6 +325,8 @@ def main():
                    "layer": "unfused" if args.unfused else "fused",
                    "forward_gemms": "mxfp8" if args.mxfp8 else w.dtype},
         "mfma_peak_frac": round(tflops / peak_mfma, 4),
+        # the per-kernel pass (event pair around every launch) timed on its own
+        "ms_per_step_profiled": round(ms_step_profiled, 4),
         "tokens_per_s": round(w.T / (ms_step * 1e-3), 1),
         "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
                      "unit": dk["unit"], "frac": dk["frac"], "traffic": None if (args.unfused or args.mxfp8) else measured_traffic(w.name, dom)},
@@ -298,7 +341,8 @@ def main():
     if cpu_tokens < 0:
         cpu_tokens = max(1, min(w.T, int(CPU_FLOP_BUDGET // (18.0 * w.K * w.d * w.n))))
     if cpu_tokens > 0:
-        out["cpu_baseline"] = cpu_baseline(w, a, cpu_tokens)
+        # the tiny workload runs in well under a second: median of 5
+        out["cpu_baseline"] = cpu_baseline(w, a, cpu_tokens, repeats=5 if w.T * w.d * w.n < (1 << 24) else 1)
     print(json.dumps(out), flush=True)
 
 

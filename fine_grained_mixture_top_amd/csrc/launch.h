@@ -63,6 +63,9 @@ hipError_t launch_mx_quant_rows(const void* src, int K, long long rows, const in
                                 uint8_t* s, hipStream_t st, int bN = 0);
 // the MXFP8 activation-gradient GEMM also takes 2n (<= 2048) as a reduction
 bool mx_bwd_shape_ok(const GemmDims& g);
+// score-gradient partials per row that launch_dh_mx writes (its column tile
+// is fixed, whatever dh_block(g) picks for the bf16 dH kernel)
+int dh_mx_partials(const GemmDims& g);
 // dXt = dH W1^T on MXFP8 operands: dH codes [cap][2n] and scales [cap][2n/32],
 // W1 codes [E][d][2n] (rows along 2n) and scales [E][2n/128][d][4]
 hipError_t launch_dxt_mx(const GemmDims& g, const uint8_t* dhq, const uint8_t* dhs, const uint8_t* w1q,

@@ -354,8 +354,10 @@ int bwd_impl(const moe_desc* desc, const void* x, const void* w_r, const void* w
   } else {
     MOE_TRY(MOE_K_DXT, launch_dxt(g, dH, w1, R.offsets, dXt, st));
   }
-  const AggDxArgs ax{dXt,    dS_part, dh_partials(g), R.row_gate, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T,
-                     D.d,    D.E,     dS_row,         dz_row,     dz_dense,     dx};
+  // the dS partial count is that of the dH kernel actually launched
+  const int nparts = mx ? dh_mx_partials(g) : dh_partials(g);
+  const AggDxArgs ax{dXt, dS_part, nparts, R.row_gate, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T,
+                     D.d, D.E,     dS_row, dz_row,     dz_dense,     dx};
   MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, ax, st));
   MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, (float*)(w + L.off[8]), st));
   // weight gradients

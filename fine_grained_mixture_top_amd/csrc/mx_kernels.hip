@@ -169,6 +169,8 @@ long long tiles_bound(size_t cap, int E) { return (long long)(cap + gmx::BM - 1)
 
 }  // namespace
 
+int dh_mx_partials(const GemmDims& g) { return g.n / gmx::BN; }
+
 bool mx_bwd_shape_ok(const GemmDims& g) {
   return mx_shape_ok(g) && 2 * g.n / 32 <= gmx::MAX_PA && g.cap * (size_t)2 * g.n < (size_t)g4::OOB;
 }

@@ -9,6 +9,8 @@
 // coalesced sweep; the GEMMs consume the compact segment form built from it.
 // Token rounding follows [B] (scheduling paragraph): counts become multiples
 // of the GEMM tile, at most one tile away from the plain count.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -585,13 +587,27 @@ k_tok_fill(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restri
 
 }  // namespace
 
+// Clears n16 16-byte words.  The membership bytes are cleared by a kernel
+// rather than a runtime memset, so that the routing launch sequence can be
+// captured into a HIP graph and replayed.
+static __global__ void k_zero16(uint4* __restrict__ p, long long n16) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 int mask_pitch(int T) { return (T + 15) / 16 * 16; }
 
 hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int T, int E, int K,
                                int tile, int round_mode, uint64_t round_seed, hipStream_t st) {
   hipError_t err;
   const int mp = mask_pitch(T);
-  if ((err = hipMemsetAsync(sc.mask, 0, (size_t)E * mp, st)) != hipSuccess) return err;
+  {
+    const long long n16 = (long long)E * mp / 16;  // mp is a multiple of 16
+    const long long blocks = std::min<long long>((n16 + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_zero16, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<uint4*>(sc.mask), n16);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   int32_t* fixed_ptr = round_mode == 0 ? rb.tok_ptr : nullptr;
   auto topk = [&](auto kern, int G) {
     const long long threads = (long long)T * G;

@@ -103,25 +103,96 @@ def layer_outputs(L: B.Layer, w: I.Workload) -> dict:
 
 def oracle_layer(w: I.Workload, x, w_r, w1, w2, d_o, bias=None, round_mode=0, round_seed=0,
                  scores=None, tile=128):
-    return O.layer(x, w_r, w1, w2, d_o, w.dtype, w.K, bias=bias, tile=tile, round_mode=round_mode,
-                   round_seed=round_seed, scores=scores)
+    o = O.layer(x, w_r, w1, w2, d_o, w.dtype, w.K, bias=bias, tile=tile, round_mode=round_mode,
+                round_seed=round_seed, scores=scores)
+    o["dWr_scale"] = router_column_scale(o, np.linalg.norm(O.to_f64(x, w.dtype), axis=1), w.E)
+    return o
+
+
+def router_column_scale(o: dict, x_norm: np.ndarray, E: int) -> np.ndarray:
+    """Per expert e, the size of the error that dW_r[:, e] = sum_t x_t dz[t,e]
+    picks up from a relative error in the per-row scores dS: dz[t,e] =
+    g_te (dS_te - sum_e' g_te' dS_te') moves by g_te (|dS_te| + sum_e' g_te'
+    |dS_te'|) per unit of relative dS error, whatever the (possibly
+    cancelling) value of dz itself, so the column's error scale is
+    sqrt(sum_t ||x_t||^2 u_te^2) with u that bound.  Zero for an expert
+    without rows."""
+    rt, re_, g, dS = o["row_token"], o["row_expert"], o["row_gate"], np.abs(o["dS"])
+    s_tok = np.zeros(x_norm.shape[0])
+    np.add.at(s_tok, rt, g * dS)
+    u = g * (dS + s_tok[rt])
+    sq = np.zeros(E)
+    np.add.at(sq, re_, (x_norm[rt] * u) ** 2)
+    return np.sqrt(sq)
+
+
+ROW_FACTOR = 3.0  # per-row / per-expert bound = ROW_FACTOR x the tensor tolerance
+
+
+def row_rel_max(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """Largest per-row relative error max_i ||gpu_i - ref_i|| / ||ref_i||.  A
+    reference row that is exactly zero must be exactly zero on the GPU too
+    (empty sets, empty experts)."""
+    g = gpu.reshape(gpu.shape[0], -1)
+    r = ref.reshape(ref.shape[0], -1)
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.linalg.norm(r, axis=1)
+    zero = den == 0
+    assert np.all(num[zero] == 0), f"{int((num[zero] != 0).sum())} zero rows are not zero"
+    return float((num[~zero] / den[~zero]).max()) if (~zero).any() else 0.0
+
+
+def scalar_rel_max(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """Largest error of a per-row scalar relative to the RMS of the reference
+    (a scalar near zero has no meaningful relative error of its own)."""
+    rms = float(np.sqrt(np.mean(np.square(ref)))) if ref.size else 0.0
+    err = np.abs(gpu - ref)
+    if rms == 0:
+        assert np.all(err == 0)
+        return 0.0
+    return float(err.max() / rms)
+
+
+PER_ROW = ("O", "H", "A", "Y", "dH", "dXt", "dX")
+
+
+def router_column_err_max(gpu: np.ndarray, ref: np.ndarray, scale: np.ndarray) -> float:
+    """Largest ||dW_r[:, e] error|| / scale_e over experts (router_column_scale);
+    an expert without rows must have an exactly zero column."""
+    num = np.linalg.norm(gpu - ref, axis=0)
+    zero = scale == 0
+    assert np.all(num[zero] == 0), "a router column of an expert without rows is not zero"
+    return float((num[~zero] / scale[~zero]).max()) if (~zero).any() else 0.0
 
 
 def compare_layer(g: dict, o: dict, dtype: str, skip=()):
-    """rel_F of every output; returns the dict of errors (asserts the tolerance)."""
+    """Every output within tolerance three ways: rel_F of the whole tensor
+    (<= tol), the largest per-row error of every per-row tensor and of the
+    per-row scores dS, and per expert rel_F of dW1 and dW2 (<= ROW_FACTOR x
+    tol), and the error of each dW_r column against the error its dz can
+    carry (router_column_scale; <= tol), so that one wrong row, chunk or
+    expert cannot hide in a large tensor.  Returns the errors (asserts)."""
     t = tol(dtype)
-    errs = {}
+    errs, rows = {}, {}
     pairs = dict(O="O", H="H", A="A", Y="Y", dH="dH", dXt="dXt", dS="dS", dX="dX", dWr="dWr",
-                 dW1="dW1", dW2="dW2")
+                 dW1="dW1", dW2="dW2", db="db")
     for gk, ok in pairs.items():
         if gk in skip:
             continue
         errs[gk] = relF(g[gk], o[ok])
-    if "db" not in skip:
-        # db sums per-row dz values that largely cancel (each token's dz sums to
-        # zero), so its error is measured against the size of its summands
-        scale = np.linalg.norm(np.abs(o["dz"]).sum(axis=0))
-        errs["db"] = float(np.linalg.norm(g["db"] - o["db"]) / scale) if scale > 0 else 0.0
+        if gk in PER_ROW:
+            rows[gk] = row_rel_max(g[gk], o[ok])
+        elif gk == "dS":
+            rows[gk] = scalar_rel_max(g[gk], o[ok])
+        elif gk in ("dW1", "dW2"):
+            rows[gk] = row_rel_max(g[gk], o[ok])  # one "row" per expert
+        elif gk == "dWr":
+            rows[gk] = router_column_err_max(g[gk], o[ok], o["dWr_scale"])
+    print("rel_F:", {k: f"{v:.2e}" for k, v in errs.items()},
+          "max per row/expert:", {k: f"{v:.2e}" for k, v in rows.items()})
     bad = {k: v for k, v in errs.items() if not v <= t}
-    assert not bad, f"outside tolerance {t}: {bad} (all: {errs})"
+    # a dW_r column's scale already bounds its summands (about twice the norm
+    # of a column whose dz do not cancel), so its bound is tol, not ROW_FACTOR tol
+    bad.update({f"{k}/row": v for k, v in rows.items() if not v <= (t if k == "dWr" else ROW_FACTOR * t)})
+    assert not bad, f"outside tolerance {t} (rows {ROW_FACTOR * t}): {bad} (all: {errs}, rows: {rows})"
     return errs

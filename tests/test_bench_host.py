@@ -59,3 +59,16 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_on():
         want = round(rec["kernels"][k]["bytes"]) if current else None
         assert bench.measured_traffic("fg7b_bf16", k) == want
     assert bench.measured_traffic("tiny_f32", "up") is None  # no counter passes for that workload
+
+
+def test_cpu_baseline_reports_forward_and_backward_apart():
+    """The oracle baseline names the CPU, times routing + forward and the
+    backward apart, and takes a median on the tiny workload."""
+    w = I.WORKLOADS["tiny_f32"]
+    a = I.draw_all(w)
+    r = bench.cpu_baseline(w, a, w.T, repeats=5)
+    assert r["kind"] == "oracle" and r["cores"] >= 1 and r["cpu"]
+    assert r["fwd_s"] > 0 and r["bwd_s"] > 0
+    assert "median of 5" in r["sample"]
+    rows = w.T * w.K
+    assert abs(r["value"] - 18.0 * rows * w.d * w.n / (r["fwd_s"] + r["bwd_s"]) / 1e12) <= 1e-2 * r["value"]

@@ -169,18 +169,23 @@ def test_mxfp8_full_size_expert_sample(name):
         assert all(v <= TOL for v in errs.values()), errs
 
 
-BWD_CASES = [CASES[0], CASES[1], CASES[3]]
+BWD_CASES = [CASES[0] + (0,), CASES[1] + (0,), CASES[3] + (0,),
+             # the bf16 kernels on 128-row tiles (their dH GEMM has another
+             # column tile than the MXFP8 dH GEMM, so the dS partial count
+             # the aggregation reads must follow the kernel launched)
+             CASES[0] + (B.MOE_FLAG_GEMM_128,)]
 
 
-@pytest.mark.parametrize("w,mode,tile", BWD_CASES, ids=[c[0].name for c in BWD_CASES])
-def test_mxfp8_backward_matches_oracle(w, mode, tile):
+@pytest.mark.parametrize("w,mode,tile,flags", BWD_CASES,
+                         ids=[c[0].name + ("-gemm128" if c[3] else "") for c in BWD_CASES])
+def test_mxfp8_backward_matches_oracle(w, mode, tile, flags):
     """moe_bwd_mxfp8 after the bf16 forward: dO, W2, dH and W1 codes
     bit-exact (dH quantized from the GPU's own bf16 dH through the oracle's
     quantizer), dH / A_s / dS and the weight and router gradients against the
     oracle's MXFP8 backward, dXt / dX against the oracle on the GPU's dH
     codes, and dX end to end against the oracle's own quantization."""
     a = I.draw_all(w)
-    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, "bf16", round_mode=mode, round_seed=3, tile=tile)
+    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, "bf16", round_mode=mode, round_seed=3, tile=tile, flags=flags)
     L = B.Layer(desc)
     X, WR, W1, W2, DO = (dev(a[k], "bf16") for k in ("x", "w_r", "w1", "w2", "d_o"))
     L.route(X, WR)
