@@ -20,7 +20,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_gfx950.so")
 
-MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EDTYPE, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EDTYPE, MOE_EWORKSPACE, MOE_EHIP, MOE_ENOSCRATCH = 0, -1, -2, -3, -4, -5, -6
+MOE_SCRATCH_BYTES = 64 << 20  # static scratch of moe_route_noalloc, per GPU
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUND_OFF, MOE_ROUND_NEAREST, MOE_ROUND_STOCHASTIC = 0, 1, 2
 MOE_FLAG_SCORES_GIVEN = 1
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_offset.argtypes, L.moe_workspace_offset.restype = [pdesc, i32], sz
         L.moe_route.argtypes = [pdesc, vp, vp, vp, prout, vp, sz, vp]
         L.moe_route.restype = i32
+        L.moe_route_noalloc.argtypes = [pdesc, vp, vp, vp, prout, vp]
+        L.moe_route_noalloc.restype = i32
         L.moe_fwd.argtypes = [pdesc, vp, vp, vp, prout, vp, vp, vp, sz, vp]
         L.moe_fwd.restype = i32
         L.moe_bwd.argtypes = [pdesc, vp, vp, vp, vp, prout, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -245,6 +248,11 @@ def workspace(desc: MoeDesc, which: int, device="cuda") -> torch.Tensor:
 def moe_route(desc, x, w_r, bias, routing: Routing, ws: torch.Tensor, stream=None):
     _check("moe_route", lib().moe_route(ctypes.byref(desc), _p(x), _p(w_r), _p(bias),
                                         ctypes.byref(routing.c), _p(ws), ws.numel(), _stream(stream)))
+
+
+def moe_route_noalloc(desc, x, w_r, bias, routing: Routing, stream=None):
+    _check("moe_route_noalloc", lib().moe_route_noalloc(ctypes.byref(desc), _p(x), _p(w_r), _p(bias),
+                                                        ctypes.byref(routing.c), _stream(stream)))
 
 
 def moe_fwd(desc, x, w1, w2, routing: Routing, o, h_cache, ws, stream=None):

@@ -4,8 +4,16 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "launch.h"
+
+// Routing scratch of moe_route_noalloc: one copy per GPU, alive until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MOE_SCRATCH_BYTES];
 
 namespace {
 
@@ -246,18 +254,45 @@ size_t moe_workspace_offset(const moe_desc* desc, int item) {
   return (size_t)-1;
 }
 
-int moe_route(const moe_desc* desc, const void* x, const void* w_r, const float* bias,
-              const moe_routing* routing, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Device address of this GPU's copy of `scratch`, resolved once per device
+// (with that device current) and kept; null if the runtime fails.
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[MAX_DEVICES] = {};
+
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_dev[dev] = p;
+  }
+  return scratch_dev[dev];
+}
+
+int route_checks(const moe_desc* desc, const void* x, const void* w_r, const moe_routing* routing) {
   int s = validate_desc(desc);
   if (s != MOE_OK) return s;
   const bool given = (desc->flags & MOE_FLAG_SCORES_GIVEN) != 0;
   if (!routing_ok(routing)) return MOE_EINVAL;
   if (!given && (!x || !w_r)) return MOE_EINVAL;
-  const Layout L = route_layout(desc);
-  if ((s = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return s;
+  return MOE_OK;
+}
 
+// The routing launch sequence on a validated descriptor; `ws` holds
+// route_layout(desc).total bytes.
+int route_impl(const moe_desc* desc, const void* x, const void* w_r, const float* bias,
+               const moe_routing* routing, char* ws, void* stream) {
+  const bool given = (desc->flags & MOE_FLAG_SCORES_GIVEN) != 0;
+  const Layout L = route_layout(desc);
   hipStream_t st = (hipStream_t)stream;
-  char* w = (char*)ws;
+  char* w = ws;
   if (!given)
     MOE_TRY(MOE_K_ROUTER_LOGITS,
             launch_router_logits(desc->dtype, x, w_r, bias, routing->logits, desc->T, desc->d, desc->E, st));
@@ -270,6 +305,28 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_r, const float*
   MOE_TRY(MOE_K_ROUTE_SELECT, launch_route_select(rb, sc, desc->T, desc->E, desc->K, desc->tile,
                                                   desc->round_mode, desc->round_seed, st));
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_route(const moe_desc* desc, const void* x, const void* w_r, const float* bias,
+              const moe_routing* routing, void* ws, size_t ws_bytes, void* stream) {
+  int s = route_checks(desc, x, w_r, routing);
+  if (s != MOE_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, route_layout(desc).total)) != MOE_OK) return s;
+  return route_impl(desc, x, w_r, bias, routing, (char*)ws, stream);
+}
+
+int moe_route_noalloc(const moe_desc* desc, const void* x, const void* w_r, const float* bias,
+                      const moe_routing* routing, void* stream) {
+  int s = route_checks(desc, x, w_r, routing);
+  if (s != MOE_OK) return s;
+  if (route_layout(desc).total > MOE_SCRATCH_BYTES) return MOE_ENOSCRATCH;
+  void* ws = scratch_for_current_device();
+  if (!ws) return MOE_EHIP;
+  return route_impl(desc, x, w_r, bias, routing, (char*)ws, stream);
 }
 
 int moe_fwd(const moe_desc* desc, const void* x, const void* w1, const void* w2,
@@ -513,6 +570,7 @@ const char* moe_strerror(int status) {
     case MOE_EDTYPE: return "unsupported dtype";
     case MOE_EWORKSPACE: return "workspace too small";
     case MOE_EHIP: return "HIP runtime error";
+    case MOE_ENOSCRATCH: return "routing needs more than the library's static scratch (MOE_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

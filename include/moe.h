@@ -28,7 +28,8 @@
  *     Router scores, gates, per-row score gradients and bias are fp32.
  *   - Every pointer except the host-side moe_desc is a device pointer owned
  *     by the caller.  The library never allocates or frees memory; scratch
- *     space comes from the caller's workspace (moe_workspace_bytes).
+ *     space comes from the caller's workspace (moe_workspace_bytes), except
+ *     for moe_route_noalloc, which uses one static device array per GPU.
  *   - Calls are stream-ordered and asynchronous on the hipStream_t passed in
  *     (NULL = the default stream); buffers must stay valid until the stream
  *     work completes.  No call synchronises the host.
@@ -56,6 +57,8 @@ extern "C" {
 #define MOE_EDTYPE     -3  /* unknown dtype */
 #define MOE_EWORKSPACE -4  /* workspace smaller than moe_workspace_bytes */
 #define MOE_EHIP       -5  /* the HIP runtime reported an error */
+#define MOE_ENOSCRATCH -6  /* moe_route_noalloc: the call needs more scratch
+                              than the library's static MOE_SCRATCH_BYTES */
 
 /* element types */
 #define MOE_F32  0
@@ -339,6 +342,29 @@ int moe_bwd_mxfp8(const moe_desc* desc, const void* x, const void* w_r, const vo
                   const void* w2, const moe_routing* routing, const void* h_cache, const void* d_o,
                   void* dx, void* dw_r, void* dw1, void* dw2, float* ds, float* db, void* ws,
                   size_t ws_bytes, void* stream);
+
+/*
+ * Routing without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results and errors as moe_route
+ * minus ws / ws_bytes: the routing scratch (membership bytes, row map, and
+ * with token rounding the transposed scores and per-token counters) lives in
+ * one static device array of MOE_SCRATCH_BYTES per GPU, which each GPU the
+ * library runs on holds until the process ends.  The call allocates nothing.
+ *   Limit: moe_workspace_bytes(desc, MOE_WS_ROUTE) <= MOE_SCRATCH_BYTES
+ *   (about 5 bytes per token and expert without token rounding, 9 with it:
+ *   e.g. T = 32768 with E = 256 and rounding off, or E = 128 with rounding),
+ *   else MOE_ENOSCRATCH before anything is enqueued.
+ *   The first call on a device resolves that device's copy of the array
+ *   (make it outside graph capture).  Every call on one GPU uses the same
+ *   array: calls that overlap on one GPU (other streams, other threads) race
+ *   and must be ordered by the caller.  What the scratch must start with is
+ *   cleared inside the call, by kernels (no runtime memset), so the call can
+ *   be captured and replayed.
+ */
+#define MOE_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_route_noalloc(const moe_desc* desc, const void* x, const void* w_r, const float* bias,
+                      const moe_routing* routing, void* stream);
 
 /* Static text for a status code.  Host only. */
 const char* moe_strerror(int status);

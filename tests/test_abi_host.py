@@ -29,7 +29,7 @@ def lib():
 def test_header_functions_exported(lib):
     names = declared_functions()
     assert set(names) == {"moe_row_capacity", "moe_workspace_bytes", "moe_workspace_offset",
-                          "moe_route", "moe_fwd", "moe_bwd", "moe_strerror",
+                          "moe_route", "moe_route_noalloc", "moe_fwd", "moe_bwd", "moe_strerror",
                           "moe_unfused_cache_bytes", "moe_fwd_unfused", "moe_bwd_unfused", "moe_fwd_mxfp8",
                           "moe_bwd_mxfp8"}
     for n in names:
