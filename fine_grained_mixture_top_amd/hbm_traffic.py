@@ -9,6 +9,11 @@ dispatches.
 
     python -m fine_grained_mixture_top_amd.hbm_traffic FETCH.csv WRITE.csv COPY_BYTES OUT.json
 
+(FETCH_SIZE and WRITE_SIZE count the L2's read and write traffic to the
+memory side of the chip -- the memory-attached last-level cache (MALL) and
+HBM alike; a MALL hit counts as traffic too.)  A second mode summarises any
+other counter passes per kernel (see counters_main).
+
 The result records a hash of the kernel sources; bench.py reports the traffic
 only while the sources still hash the same.
 """
@@ -51,11 +56,11 @@ def classify(name: str, wgt_seen: dict) -> str:
             return "dw1" if k == 0 else "dw2"
         return "down" if bmn else "dxt"
     if "grouped_gemm5_kernel" in name:
-        m = re.search(r"grouped_gemm5_kernel<(true|false), (true|false), moe::(?:g\d::)?(\w+)", name)
+        m = re.search(r"grouped_gemm5_kernel<(true|false), (true|false), moe::(?:\w+::)?(\w+)", name)
         if not m:
             return None
         bmn, epi = m.group(1) == "true", m.group(3)
-        if epi in ("EpiSwiGLU", "G4SwiGLU"):
+        if epi in ("EpiSwiGLU", "G4SwiGLU", "SplitSwiGLU"):
             return "up"
         if epi in ("EpiDH", "G4DH", "G5DH"):
             return "dh"
@@ -130,5 +135,76 @@ def main(fetch_csv, write_csv, copy_bytes, out_json):
     print(json.dumps(res))
 
 
+# ----------------------------------------------------------------------------
+# other counters: per-kernel means and the ratios the GEMM analysis uses
+#
+#     python -m fine_grained_mixture_top_amd.hbm_traffic counters OUT.json A.csv [B.csv ...]
+# ----------------------------------------------------------------------------
+
+CUS, SIMDS = 256, 1024  # MI355X: compute units and SIMDs of the whole chip
+
+
+def counter_means(paths):
+    """{kernel: {counter: mean over the kernel's dispatches}} from any number
+    of counter-collection CSVs.  A counter reported by several instances is
+    summed over them per dispatch, except GRBM_* (one per XCD, the same
+    clock), which takes their maximum."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        rows = list(csv.DictReader(open(path)))
+        vals = collections.defaultdict(list)
+        names = {}
+        for r in rows:
+            did = int(r["Dispatch_Id"])
+            vals[(did, r["Counter_Name"])].append(float(r["Counter_Value"]))
+            names[did] = r["Kernel_Name"]
+        seen = {"n": 0}
+        kernel_of = {did: classify(names[did], seen) for did in sorted(names)}
+        for (did, cname), v in vals.items():
+            k = kernel_of[did]
+            if k:
+                acc[k][cname].append(max(v) if cname.startswith("GRBM_") else sum(v))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+
+
+def derived(m: dict) -> dict:
+    """Ratios of one kernel's counter means (those whose counters are present)."""
+    out = {}
+    gui = m.get("GRBM_GUI_ACTIVE")
+    if gui:
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            out["mfma_busy_pct"] = 100.0 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS)
+        if "TCP_PENDING_STALL_CYCLES_sum" in m:
+            out["tcp_pending_stall_pct"] = 100.0 * m["TCP_PENDING_STALL_CYCLES_sum"] / (gui * CUS)
+        if "SQ_LDS_BANK_CONFLICT" in m:
+            out["lds_bank_conflict_pct"] = 100.0 * m["SQ_LDS_BANK_CONFLICT"] / (gui * CUS)
+        out["gui_active_cycles"] = gui
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in m:
+        out["mfma_bf16_flop"] = 512.0 * m["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+    h, x = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
+    if h is not None and x is not None and h + x > 0:
+        out["l2_hit_pct"] = 100.0 * h / (h + x)
+    rq = m.get("TCC_EA0_RDREQ_sum")
+    if rq:
+        for c, key in (("TCC_EA0_RDREQ_128B_sum", "rdreq_128b_pct"), ("TCC_EA0_RDREQ_64B_sum", "rdreq_64b_pct"),
+                       ("TCC_EA0_RDREQ_32B_sum", "rdreq_32b_pct"), ("TCC_BUBBLE_sum", "bubble_pct"),
+                       ("TCC_EA0_RDREQ_DRAM_sum", "rdreq_dram_pct")):
+            if c in m:
+                out[key] = 100.0 * m[c] / rq
+    return out
+
+
+def counters_main(out_json, *paths):
+    means = counter_means(paths)
+    res = {"source_hash": source_hash(), "kernels": {k: {"counters": v, "derived": derived(v)}
+                                                     for k, v in sorted(means.items())}}
+    with open(out_json, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps({k: v["derived"] for k, v in res["kernels"].items()}, indent=1))
+
+
 if __name__ == "__main__":
-    main(*sys.argv[1:5])
+    if sys.argv[1] == "counters":
+        counters_main(*sys.argv[2:])
+    else:
+        main(*sys.argv[1:5])
