@@ -30,7 +30,14 @@ specification leaves a choice:
     dA' = dO W2^T with dO and W2 quantized along d (W2 by the rows of each
     expert's [n, d] matrix), dXt = dH W1^T with dH quantized along 2n from
     its bf16 value and W1 along 2n (rows of each expert's [d, 2n] matrix);
-    the weight-gradient GEMMs stay in the layer dtype.
+  * the weight-gradient GEMMs reduce over an expert's rows, so their blocks
+    run along the rows of each expert's segment: block b of expert e holds
+    segment rows 32 b .. 32 b + 31 (counted from the segment's first row,
+    so no block holds rows of two experts), the last block of a segment
+    zero-padded (zeros change no block maximum and add nothing to a sum);
+    dW1[e] = X_g^T dH with X_g (the expert's gathered x rows) and dH (from
+    its bf16 value) quantized that way, dW2[e] = A_s^T dO_g with A_s (the
+    gate-scaled A, from its bf16 value) and dO_g likewise.
 
 The forward itself is the plain layer forward (moe_oracle.forward) on the
 dequantized operands: H = deq(x_q)[tok] deq(W1_q), A = silu(G) * U,
@@ -249,6 +256,50 @@ def dxt_from_codes(dHq, dHs, w1q, w1s, rt, dz, wr64) -> dict:
     dX = dz @ wr64.T
     np.add.at(dX, tok, dXt)
     return dict(dXt=dXt, dX=dX)
+
+
+# ----------------------------------------------------------------------------
+# weight gradients: operands quantized along each expert's segment of rows
+# ----------------------------------------------------------------------------
+
+def quantize_segment(rows64) -> tuple:
+    """One expert's rows [r, C] quantized along the rows: the matrix is
+    transposed to [C, r], zero-padded along the rows to a multiple of 32 and
+    quantized in blocks of 32 rows.  Returns (codes [C, r_pad], scales
+    [C, r_pad / 32])."""
+    v = np.asarray(rows64, dtype=np.float64)
+    r, C = v.shape
+    pad = (-r) % BLOCK
+    vt = np.concatenate([v.T, np.zeros((C, pad))], axis=1)
+    return quantize(vt)
+
+
+def weight_grads_mxfp8(x64, dO, rt, dH, As) -> dict:
+    """dW1[e] = X_g^T dH and dW2[e] = A_s^T dO_g with every operand quantized
+    along the expert's rows (quantize_segment): X_g = x[row_token] and dO_g =
+    dO[row_token] over the expert's segment, dH and A_s (per routed row, in
+    the expert-sorted order of rt) from their bf16 values.  Also returns each
+    expert's codes and scales (None for an expert without rows)."""
+    off, tok = rt["offsets"], rt["row_token"]
+    E = len(off) - 1
+    d, n2 = x64.shape[1], dH.shape[1]
+    n = As.shape[1]
+    dW1 = np.zeros((E, d, n2))
+    dW2 = np.zeros((E, n, d))
+    codes = []
+    for e in range(E):
+        s, t = off[e], off[e + 1]
+        if s == t:
+            codes.append(None)
+            continue
+        xq, xs = quantize_segment(x64[tok[s:t]])
+        hq, hs = quantize_segment(bf16_round(dH[s:t]))
+        aq, as_ = quantize_segment(bf16_round(As[s:t]))
+        oq, os_ = quantize_segment(dO[tok[s:t]])
+        dW1[e] = dequantize(xq, xs) @ dequantize(hq, hs).T
+        dW2[e] = dequantize(aq, as_) @ dequantize(oq, os_).T
+        codes.append(dict(xq=xq, xs=xs, hq=hq, hs=hs, aq=aq, as_=as_, oq=oq, os=os_))
+    return dict(dW1=dW1, dW2=dW2, codes=codes)
 
 
 def layer_fwd_mxfp8(x, w_r, w1, w2, K, bias=None, tile=128, round_mode=0, round_seed=0) -> dict:

@@ -238,3 +238,103 @@ def test_backward_on_random_inputs_is_close_to_plain():
         rel = np.linalg.norm(b[k] - p[k]) / np.linalg.norm(p[k])
         assert 1e-3 < rel < 0.08, (k, rel)
     assert np.array_equal(b["dW2"], p["dW2"])  # A and the unquantized dO only
+
+
+# ----------------------------------------------------------------------------
+# weight gradients on operands quantized along each expert's segment of rows
+# ----------------------------------------------------------------------------
+
+def exact_rows(rng, shape):
+    """Values MXFP8 represents exactly whatever block they fall in: every
+    magnitude in {256, 288, ..., 448} (1.0 .. 1.75 times 2^8), so every block
+    maximum is in [256, 448], the block scale is 2^0 and each value is its own
+    E4M3 code."""
+    mag = 256.0 + 32.0 * rng.integers(0, 7, shape)
+    return np.where(rng.random(shape) < 0.5, -mag, mag)
+
+
+def test_segment_quantization_layout_and_padding():
+    """A segment of r rows becomes [C, r rounded up to 32]: the first block
+    starts at the segment's first row, padding rows are zero codes, a block of
+    padding only has scale code 0, and quantizing rows 40.. of a longer array
+    as their own segment equals quantizing them alone."""
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal((100, 6))
+    q, s = M.quantize_segment(v[40:77])          # 37 rows -> 64
+    assert q.shape == (6, 64) and s.shape == (6, 2)
+    q2, s2 = M.quantize(np.concatenate([v[40:77].T, np.zeros((6, 27))], axis=1))
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    assert np.all(q[:, 37:] == 0)
+    # block 0 = rows 40..71 of v, block 1 = rows 72..76 plus zeros
+    assert np.array_equal(s[:, 0], M.shared_exponent(np.abs(v[40:72]).max(axis=0)))
+    assert np.array_equal(s[:, 1], M.shared_exponent(np.abs(v[72:77]).max(axis=0)))
+    qz, sz = M.quantize_segment(np.zeros((3, 4)))
+    assert np.all(qz == 0) and np.all(sz == 0)
+
+
+def test_segment_blocks_follow_the_segment_not_the_global_row_index():
+    """With segments [0, 40) and [40, 80) the second segment's blocks are rows
+    40..71 and 72..79, not the global blocks 32..63 and 64..95: its codes equal
+    those of the same rows quantized with no first segment in front."""
+    rng = np.random.default_rng(22)
+    T, d, E, n = 80, 64, 2, 32
+    x = rng.standard_normal((T, d))
+    x[45, 3] = 1000.0                      # a large value in global block 32..63, segment block 0
+    rt = dict(offsets=np.array([0, 40, 80]), row_token=np.arange(T))
+    dH = rng.standard_normal((T, 2 * n))
+    As = rng.standard_normal((T, n))
+    dO = rng.standard_normal((T, d))
+    w = M.weight_grads_mxfp8(x, dO, rt, dH, As)
+    alone = M.weight_grads_mxfp8(x[40:], dO[40:], dict(offsets=np.array([0, 40]), row_token=np.arange(40)),
+                                 dH[40:], As[40:])
+    for k in ("xq", "xs", "hq", "hs", "aq", "as_", "oq", "os"):
+        assert np.array_equal(w["codes"][1][k], alone["codes"][0][k]), k
+    assert np.array_equal(w["dW1"][1], alone["dW1"][0]) and np.array_equal(w["dW2"][1], alone["dW2"][0])
+    # the large value shares its scale with rows 40..71 of column 3 only
+    assert int(w["codes"][1]["xs"][3, 0]) == int(M.shared_exponent(np.array([1000.0]))[0])
+    assert int(w["codes"][0]["xs"][3, 1]) == int(M.shared_exponent(np.abs(x[32:40, 3]).max()[None])[0])
+
+
+def test_weight_grads_equal_plain_products_on_exact_inputs():
+    """Operands MXFP8 represents exactly (exact_rows), gathered and ragged
+    segments with partial last blocks and an empty expert: dW1 = X_g^T dH and
+    dW2 = A_s^T dO_g exactly, dH and A_s entering through their bf16 value
+    (exact here too)."""
+    rng = np.random.default_rng(23)
+    T, d, E, n, K = 70, 64, 5, 32, 2
+    x = exact_rows(rng, (T, d))
+    dO = exact_rows(rng, (T, d))
+    member = np.zeros((T, E), dtype=bool)
+    for t in range(T):
+        member[t, rng.choice(4, K, replace=False)] = True   # expert 4 stays empty
+    rt = O.segments(member, 128)
+    P = rt["n_rows"]
+    dH = exact_rows(rng, (P, 2 * n))
+    As = exact_rows(rng, (P, n))
+    w = M.weight_grads_mxfp8(x, dO, rt, dH, As)
+    off, tok = rt["offsets"], rt["row_token"]
+    assert off[4] == off[5] and w["codes"][4] is None
+    assert any((off[e + 1] - off[e]) % 32 for e in range(4))   # partial last blocks occur
+    for e in range(E):
+        s, t = off[e], off[e + 1]
+        assert np.array_equal(w["dW1"][e], x[tok[s:t]].T @ dH[s:t])
+        assert np.array_equal(w["dW2"][e], As[s:t].T @ dO[tok[s:t]])
+
+
+def test_weight_grads_on_random_inputs_are_close_to_plain():
+    rng = np.random.default_rng(24)
+    T, d, E, n, K = 200, 128, 4, 64, 2
+    x, dO = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    member = np.zeros((T, E), dtype=bool)
+    for t in range(T):
+        member[t, rng.choice(E, K, replace=False)] = True
+    rt = O.segments(member, 128)
+    P = rt["n_rows"]
+    dH, As = rng.standard_normal((P, 2 * n)), rng.standard_normal((P, n))
+    w = M.weight_grads_mxfp8(x, dO, rt, dH, As)
+    off, tok = rt["offsets"], rt["row_token"]
+    for e in range(E):
+        s, t = off[e], off[e + 1]
+        for k, ref in (("dW1", x[tok[s:t]].T @ dH[s:t]), ("dW2", As[s:t].T @ dO[tok[s:t]])):
+            rel = np.linalg.norm(w[k][e] - ref) / np.linalg.norm(ref)
+            assert 1e-3 < rel < 0.08, (k, e, rel)
