@@ -141,14 +141,16 @@ def main(fetch_csv, write_csv, copy_bytes, out_json):
 #     python -m fine_grained_mixture_top_amd.hbm_traffic counters OUT.json A.csv [B.csv ...]
 # ----------------------------------------------------------------------------
 
-CUS, SIMDS = 256, 1024  # MI355X: compute units and SIMDs of the whole chip
+CUS, SIMDS, XCDS = 256, 1024, 8  # MI355X: compute units, SIMDs, accelerator complex dies
 
 
 def counter_means(paths):
     """{kernel: {counter: mean over the kernel's dispatches}} from any number
-    of counter-collection CSVs.  A counter reported by several instances is
-    summed over them per dispatch, except GRBM_* (one per XCD, the same
-    clock), which takes their maximum."""
+    of counter-collection CSVs.  rocprofv3 reports one value per dispatch,
+    summed over the counter's instances: GRBM_GUI_ACTIVE is the sum of the 8
+    XCDs' busy clocks (it reads about 8 x the dispatch's duration times the
+    clock), so it is divided by 8 to give one XCD's cycles.  A counter still
+    reported by several instances is summed over them."""
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
     for path in paths:
         rows = list(csv.DictReader(open(path)))
@@ -163,7 +165,7 @@ def counter_means(paths):
         for (did, cname), v in vals.items():
             k = kernel_of[did]
             if k:
-                acc[k][cname].append(max(v) if cname.startswith("GRBM_") else sum(v))
+                acc[k][cname].append(sum(v) / XCDS if cname == "GRBM_GUI_ACTIVE" else sum(v))
     return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
 
 
