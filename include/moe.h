@@ -227,7 +227,11 @@ typedef struct moe_routing {
 } moe_routing;
 
 /* Upper bound on routed rows P: T*K without rounding, T*K + E*tile/2
- * (nearest) or T*K + E*(tile-1) (stochastic), never above T*E.
+ * (nearest) or T*K + E*(tile-1) (stochastic), never above T*E.  The
+ * rounding terms follow from [B] scheduling paragraph: each expert's count
+ * moves to a multiple of the tile by at most one tile (here by at most
+ * tile/2 when rounding to nearest and by at most tile-1 when rounding up at
+ * random), and never beyond the T tokens there are.
  * Returns 0 for an invalid descriptor.  Host only. */
 size_t moe_row_capacity(const moe_desc* desc);
 
