@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--mxfp8", action="store_true",
                     help="run the forward GEMMs and the dH and dXt GEMMs in MXFP8 (moe_fwd_mxfp8, "
                          "moe_bwd_mxfp8); the weight-gradient GEMMs stay bf16")
+    ap.add_argument("--mxfp8-wgrad", action="store_true",
+                    help="with --mxfp8: the two weight-gradient GEMMs in MXFP8 too, on operands "
+                         "quantized along each expert's rows (MOE_FLAG_MXFP8_WGRAD)")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the oracle's CPU baseline sample (0 = skip, -1 = as many as "
                          "fit a 4 TFLOP budget, about 20 s of fp64 work, capped at the workload's T)")
@@ -80,6 +83,7 @@ def kernel_work(name, w, P, es, mx=False):
         "dh": 2.0 * P * d * n, "dxt": 4.0 * P * d * n, "dw1": 4.0 * P * d * n,
         "dw2": 2.0 * P * n * d, "dwr": 2.0 * T * d * E, "da": 2.0 * P * d * n,
         "up_mx": 4.0 * P * d * n, "down_mx": 2.0 * P * n * d, "dxt_mx": 4.0 * P * d * n, "dh_mx": 2.0 * P * d * n,
+        "dw1_mx": 4.0 * P * d * n, "dw2_mx": 2.0 * P * n * d,
     }
     if name in flops:
         return flops[name], "flop"
@@ -101,6 +105,10 @@ def kernel_work(name, w, P, es, mx=False):
         # along their forward reductions, w2 along d for dH, w1 along 2n for dXt
         "mx_quant_rows": (T * d + P * n + T * d + P * 2 * n) * (es + 1 + 1 / 32) / 4,
         "mx_quant_w": 6 * E * d * n * (es + 1 + 1 / 32) / 4,
+        # weight-gradient operands along the segments, averaged over the four
+        # launches: x and dO rows gathered (d columns each), dH (2n), A_s (n)
+        "mx_quant_seg": (2 * d + 2 * n + n) * P * (es + 1 + 1 / 32) / 4,
+        "mx_pad_offsets": (E + 1) * 4 * 2,
     }
     return float(bytes_.get(name, 0)), "byte"
 
@@ -201,6 +209,9 @@ def main():
     if args.unfused and args.mxfp8:
         print("--unfused and --mxfp8 are separate comparisons; pick one", file=sys.stderr)
         sys.exit(2)
+    if args.mxfp8_wgrad and not args.mxfp8:
+        print("--mxfp8-wgrad goes with --mxfp8", file=sys.stderr)
+        sys.exit(2)
 
     import numpy as np
     import torch
@@ -219,7 +230,8 @@ def main():
 
     x, wr, w1, w2, do = (dev(a[k]) for k in ("x", "w_r", "w1", "w2", "d_o"))
     bias = None if a["bias"] is None else torch.from_numpy(a["bias"]).cuda()
-    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=args.round_mode, tile=args.tile)
+    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, w.dtype, round_mode=args.round_mode, tile=args.tile,
+                       flags=B.MOE_FLAG_MXFP8_WGRAD if args.mxfp8_wgrad else 0)
     L = B.Layer(desc, unfused=args.unfused)
 
     def step():
@@ -318,12 +330,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8 (fwd, dH, dXt GEMMs) + bf16" if args.mxfp8 else w.dtype,
+        "dtype": ("mxfp8 (all six GEMMs) + bf16" if args.mxfp8_wgrad else
+                  "mxfp8 (fwd, dH, dXt GEMMs) + bf16") if args.mxfp8 else w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "n": w.n, "K": w.K,
                    "round_mode": args.round_mode, "tile": args.tile, "rows": P, "parallelism": "single GPU",
                    "layer": "unfused" if args.unfused else "fused",
-                   "forward_gemms": "mxfp8" if args.mxfp8 else w.dtype},
+                   "forward_gemms": "mxfp8" if args.mxfp8 else w.dtype,
+                   "weight_grad_gemms": "mxfp8" if args.mxfp8_wgrad else w.dtype},
         "mfma_peak_frac": round(tflops / peak_mfma, 4),
         # the per-kernel pass (event pair around every launch) timed on its own
         "ms_per_step_profiled": round(ms_step_profiled, 4),

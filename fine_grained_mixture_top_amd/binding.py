@@ -26,21 +26,26 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUND_OFF, MOE_ROUND_NEAREST, MOE_ROUND_STOCHASTIC = 0, 1, 2
 MOE_FLAG_SCORES_GIVEN = 1
 MOE_FLAG_GEMM_128 = 2
+MOE_FLAG_MXFP8_WGRAD = 4
 MOE_WS_ROUTE, MOE_WS_FWD, MOE_WS_BWD, MOE_WS_BWD_UNFUSED, MOE_WS_FWD_MXFP8, MOE_WS_BWD_MXFP8 = range(6)
 MOE_ITEM_Y, MOE_ITEM_A, MOE_ITEM_DH, MOE_ITEM_AS, MOE_ITEM_DXT, MOE_ITEM_DS, MOE_ITEM_DZ = range(7)
 (MOE_ITEM_MX_XQ, MOE_ITEM_MX_XS, MOE_ITEM_MX_W1Q, MOE_ITEM_MX_W1S, MOE_ITEM_MX_W2Q, MOE_ITEM_MX_W2S,
  MOE_ITEM_MX_A, MOE_ITEM_MX_AQ, MOE_ITEM_MX_AS, MOE_ITEM_MX_Y) = range(7, 17)
 (MOE_ITEM_MX_DHQ, MOE_ITEM_MX_DHS, MOE_ITEM_MX_W1RQ, MOE_ITEM_MX_W1RS, MOE_ITEM_MX_DOQ, MOE_ITEM_MX_DOS,
  MOE_ITEM_MX_W2RQ, MOE_ITEM_MX_W2RS) = range(17, 25)
+(MOE_ITEM_MX_WG_PADOFF, MOE_ITEM_MX_WG_XQ, MOE_ITEM_MX_WG_XS, MOE_ITEM_MX_WG_HQ, MOE_ITEM_MX_WG_HS,
+ MOE_ITEM_MX_WG_AQ, MOE_ITEM_MX_WG_AS, MOE_ITEM_MX_WG_OQ, MOE_ITEM_MX_WG_OS) = range(25, 34)
 KERNEL_NAMES = ["router_logits", "route_select", "up", "down", "agg_o", "dh", "router_grad", "dwr",
                 "wr_t", "dxt", "agg_dx", "dw1", "dw2", "db",
                 "gather", "swiglu", "row_dot", "da", "swiglu_bwd",
-                "mx_quant_rows", "mx_quant_w", "up_mx", "down_mx", "dxt_mx", "dh_mx"]
+                "mx_quant_rows", "mx_quant_w", "up_mx", "down_mx", "dxt_mx", "dh_mx",
+                "mx_pad_offsets", "mx_quant_seg", "dw1_mx", "dw2_mx"]
 (MOE_K_ROUTER_LOGITS, MOE_K_ROUTE_SELECT, MOE_K_UP, MOE_K_DOWN, MOE_K_AGG_O, MOE_K_DH,
  MOE_K_ROUTER_GRAD, MOE_K_DWR, MOE_K_WR_T, MOE_K_DXT, MOE_K_AGG_DX, MOE_K_DW1, MOE_K_DW2,
  MOE_K_DB, MOE_K_GATHER, MOE_K_SWIGLU, MOE_K_ROW_DOT, MOE_K_DA, MOE_K_SWIGLU_BWD,
- MOE_K_MX_QUANT_ROWS, MOE_K_MX_QUANT_W, MOE_K_UP_MX, MOE_K_DOWN_MX, MOE_K_DXT_MX, MOE_K_DH_MX) = range(25)
-MOE_K_COUNT = 25
+ MOE_K_MX_QUANT_ROWS, MOE_K_MX_QUANT_W, MOE_K_UP_MX, MOE_K_DOWN_MX, MOE_K_DXT_MX, MOE_K_DH_MX,
+ MOE_K_MX_PAD_OFFSETS, MOE_K_MX_QUANT_SEG, MOE_K_DW1_MX, MOE_K_DW2_MX) = range(29)
+MOE_K_COUNT = 29
 
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16}

@@ -337,5 +337,145 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
   }
 }
 
+// Weight-gradient GEMM on MXFP8 operands: for each expert e,
+// C[e] (Ma x Nb) = A_e B_e^T, A_e = [Ma][Kp_e] and B_e = [Nb][Kp_e] codes
+// whose reduction runs along the expert's rows (padded to Kp_e, a multiple of
+// 128, by k_mx_quant_seg), at byte Ma * padoff[e] (Nb * padoff[e]) of qa
+// (qb); both operands' scales stage-blocked: dword (padoff[e] / 128 + k) *
+// Ma + m of sa holds row m's four block scales of stage k (likewise sb).
+// Tiles (e, m tile, n tile) in that order, each reducing over all of its
+// expert's stages (none for an expert without rows: its tiles store zeros).
+// Loads per wave and stage: 4 + 4 code instructions and one scale dword
+// (waves 0..3 the B scales of the tile's 256 columns, 4..7 the A scales of
+// its 256 rows).  Same fragments, MFMA step and wave-local epilogue as the
+// row-mode kernel.
+constexpr int WSC_OFF = 2 * OPB;               // B scales of a stage, then A scales
+constexpr int WSTAGE = 2 * OPB + 2 * BSC;      // 66 KB
+constexpr int WSMEM = NS * WSTAGE;
+constexpr int WLPS = 9;                        // loads per wave per stage
+static_assert(WSTAGE + 8 * g4::WAVE_LDS <= WSMEM, "wave areas fit over stage 1");
+static_assert(WSTAGE % 1024 == 0, "stage alignment");
+
+template <class Epi>
+__global__ void __launch_bounds__(NTH, 1)
+grouped_gemm_mxw_kernel(int E, int Ma, int Nb, const int32_t* __restrict__ padoff, const uint8_t* __restrict__ qa,
+                        const uint32_t* __restrict__ sa, const uint8_t* __restrict__ qb,
+                        const uint32_t* __restrict__ sb, uint32_t qa_bytes, uint32_t qb_bytes, uint32_t sa_bytes,
+                        uint32_t sb_bytes, typename Epi::Params ep) {
+  static_assert(g4::is_wave_epi<Epi>::value, "wave-local epilogues");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  __shared__ int poff[MAX_E + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 2, wn = w & 3;
+  for (int e = tid; e <= E; e += NTH) poff[e] = padoff[e];
+  __syncthreads();
+  const int MT = Ma / BM, NT = Nb / BN;
+  const int total = E * MT * NT;
+  const int G = gridDim.x;
+  const int vid = xcd_virtual_id(blockIdx.x, G);
+  auto tile_of = [&](int r) -> int {
+    const int t = r * G + vid;
+    return t < total ? t : -1;
+  };
+  int kp = 0, sbase = 0;  // the tile's padded rows and first stage
+  auto decode = [&](int t, TileCtx& c) {
+    c.tid = tid; c.lane = lane; c.wm = wm; c.wn = wn;
+    c.e = t / (MT * NT);
+    c.mt = (t / NT) % MT;
+    c.nt = t % NT;
+    c.seg0 = poff[c.e];
+    c.segn = poff[c.e + 1] - c.seg0;
+    c.m_valid = BM;
+    c.out_row0 = (long long)c.e * Ma + (long long)c.mt * BM;
+    c.slot = -1;
+    c.n0 = c.nt * BN;
+  };
+  __amdgpu_buffer_rsrc_t ra = make_rsrc(qa, qa_bytes), rb = make_rsrc(qb, qb_bytes);
+  __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa, sa_bytes), rsb = make_rsrc(sb, sb_bytes);
+  KCLoad la, lb;
+  uint32_t so = 0;  // scale dword offset of this lane's row (waves 4..7) or column (waves 0..3) at stage 0
+  auto setup = [&](const TileCtx& c) {
+    kp = c.segn;
+    sbase = c.seg0 / BK;
+    const uint32_t abase = (uint32_t)Ma * (uint32_t)c.seg0, bbase = (uint32_t)Nb * (uint32_t)c.seg0;
+    la.setup(w, lane, [&](int r) -> uint32_t { return abase + (uint32_t)(c.mt * BM + r) * (uint32_t)kp; });
+    lb.setup(w, lane, [&](int r) -> uint32_t { return bbase + (uint32_t)(c.n0 + r) * (uint32_t)kp; });
+    so = w < 4 ? ((uint32_t)sbase * (uint32_t)Nb + (uint32_t)(c.n0 + 64 * w + lane)) * 4u
+               : ((uint32_t)sbase * (uint32_t)Ma + (uint32_t)(c.mt * BM + 64 * (w - 4) + lane)) * 4u;
+  };
+  auto issue = [&](int k) {
+    char* st = smem + (k & 1) * WSTAGE;
+    const int k0 = k * BK;
+    la.issue(ra, st, w, k0);
+    lb.issue(rb, st + OPB, w, k0);
+    if (w < 4) dma4(rsb, st + WSC_OFF + w * 256, so, (uint32_t)(k * Nb) * 4u);
+    else dma4(rsa, st + WSC_OFF + BSC + (w - 4) * 256, so, (uint32_t)(k * Ma) * 4u);
+  };
+  auto read_scales = [&](int k, uint32_t (&asc)[4], uint32_t (&bsc)[2]) {
+    const char* st = smem + (k & 1) * WSTAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      asc[j] = *reinterpret_cast<const uint32_t*>(st + WSC_OFF + BSC + (wm * 128 + 32 * j + (lane & 31)) * 4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      bsc[i] = *reinterpret_cast<const uint32_t*>(st + WSC_OFF + (wn * 64 + 32 * i + (lane & 31)) * 4);
+  };
+
+  int r = 0;
+  int t = tile_of(0);
+  TileCtx c;
+  if (t >= 0) {
+    decode(t, c);
+    setup(c);
+    if (kp > 0) issue(0);
+  }
+  while (t >= 0) {
+    const int nk = kp / BK;
+    f32x16_v acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // stage 1 overwrites the previous tile's epilogue areas
+    __syncthreads();
+    if (nk > 0) {
+      if (nk > 1) issue(1);
+      if (nk > 1) wait_vm<WLPS>();
+      else wait_vm<0>();
+      __syncthreads();
+      uint32_t asc[4], bsc[2];
+      read_scales(0, asc, bsc);
+#pragma unroll 1
+      for (int it = 0; it < 2 * nk; ++it) {
+        const int k = it >> 1, sidx = it & 1;
+        step(acc, smem + (k & 1) * WSTAGE, sidx, lane, wm, wn, asc, bsc);
+        if (sidx == 1 && k + 1 < nk) {
+          wait_vm<0>();
+          __syncthreads();
+          read_scales(k + 1, asc, bsc);
+          if (k + 2 < nk) issue(k + 2);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done reading the stages
+
+    const int tn = tile_of(r + 1);
+    TileCtx cn = c;
+    if (tn >= 0) {
+      decode(tn, cn);
+      setup(cn);
+      if (kp > 0) issue(0);
+    }
+    Epi::run(ep, c, acc, smem + WSTAGE + w * g4::WAVE_LDS);
+    c = cn;
+    t = tn;
+    ++r;
+  }
+}
+
 }  // namespace gmx
 }  // namespace moe

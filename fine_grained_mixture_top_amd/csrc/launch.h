@@ -76,6 +76,23 @@ hipError_t launch_dxt_mx(const GemmDims& g, const uint8_t* dhq, const uint8_t* d
 hipError_t launch_dh_mx(const GemmDims& g, const uint8_t* doq, const uint8_t* dos, const uint8_t* w2q,
                         const uint8_t* w2s, const int32_t* row_token, const float* row_gate, const int32_t* offsets,
                         const void* H, void* dH, void* As, float* dS_part, hipStream_t st);
+// MXFP8 weight gradients.  Each expert's segment of routed rows, padded
+// with zero rows to a multiple of 128 (one GEMM stage), is quantized along
+// its rows.  padoff [E+1]: prefix of the padded lengths; stage_e: the expert
+// of each 128-row stage (mx_seg_rows_bound(g) / 128 entries at most).
+long long mx_seg_rows_bound(const GemmDims& g);
+bool mx_wgrad_shape_ok(const GemmDims& g);
+hipError_t launch_mx_pad_offsets(const int32_t* offsets, int E, int32_t* padoff, int32_t* stage_e, hipStream_t st);
+// src rows [*][C] bf16 (gathered through idx when set) -> codes, per expert
+// [C][Kp_e] at byte C * padoff[e], and stage-blocked scales (dword
+// (padoff[e]/128 + s) * C + c: column c's four block scales of stage s)
+hipError_t launch_mx_quant_seg(const void* src, int C, const int32_t* idx, const int32_t* offsets,
+                               const int32_t* padoff, const int32_t* stage_e, const GemmDims& g, uint8_t* q,
+                               uint32_t* sblk, hipStream_t st);
+// dW[e] (Ma x Nb, bf16) = A_e B_e^T from segment-quantized operands A (Ma
+// columns) and B (Nb columns)
+hipError_t launch_wgrad_mx(const GemmDims& g, int Ma, int Nb, const int32_t* padoff, const uint8_t* qa,
+                           const uint32_t* sa, const uint8_t* qb, const uint32_t* sb, void* dW, hipStream_t st);
 // W [E][K][N] bf16 -> codes [E][N][K] and scales [E][K/128][N] (4 bytes each)
 hipError_t launch_mx_quant_w(const void* W, int E, int K, int N, uint8_t* q, uint8_t* sblk, hipStream_t st);
 hipError_t launch_up_mx(const GemmDims& g, const uint8_t* xq, const uint8_t* xs, const uint8_t* w1q,

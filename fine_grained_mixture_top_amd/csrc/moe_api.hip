@@ -27,7 +27,7 @@ size_t elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 int validate_desc(const moe_desc* d) {
   if (!d) return MOE_EINVAL;
   if (d->reserved != 0) return MOE_EINVAL;
-  if ((d->flags & ~(MOE_FLAG_SCORES_GIVEN | MOE_FLAG_GEMM_128)) != 0) return MOE_EINVAL;
+  if ((d->flags & ~(MOE_FLAG_SCORES_GIVEN | MOE_FLAG_GEMM_128 | MOE_FLAG_MXFP8_WGRAD)) != 0) return MOE_EINVAL;
   if (d->T < 1 || d->d < 1 || d->E < 1 || d->n < 1 || d->K < 1 || d->K > d->E) return MOE_EINVAL;
   if (d->round_mode < MOE_ROUND_OFF || d->round_mode > MOE_ROUND_STOCHASTIC) return MOE_EINVAL;
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_EDTYPE;
@@ -50,7 +50,7 @@ size_t capacity(const moe_desc* d) {
 
 // Workspace items, in order, for each phase.
 struct Layout {
-  size_t off[20];
+  size_t off[32];
   size_t total;
 };
 
@@ -166,8 +166,26 @@ Layout mx_bwd_layout(const moe_desc* d) {
   L.off[15] = o; o = up(o + (size_t)d->T * (D / 32));     // dO scales [T][d/32]
   L.off[16] = o; o = up(o + E * n * D);                   // W2 codes, rows along d [E][n][d]
   L.off[17] = o; o = up(o + E * (D / 128) * n * 4);       // W2 scales [E][d/128][n][4]
+  if (d->flags & MOE_FLAG_MXFP8_WGRAD) {
+    // weight-gradient operands quantized along each expert's padded rows
+    const size_t rows = (size_t)mx_seg_rows_bound(gemm_dims(d));
+    L.off[18] = o; o = up(o + (E + 1) * 4);                 // padoff [E+1]
+    L.off[19] = o; o = up(o + rows / 128 * 4);              // expert of each 128-row stage
+    const size_t cols[4] = {D, 2 * n, n, D};                // x_g, dH, A_s, dO_g
+    for (int i = 0; i < 4; ++i) {
+      L.off[20 + 2 * i] = o; o = up(o + cols[i] * rows);    // codes
+      L.off[21 + 2 * i] = o; o = up(o + cols[i] * rows / 32);  // scales
+    }
+  }
   L.total = o;
   return L;
+}
+
+// shapes moe_bwd_mxfp8 takes (with the weight-gradient GEMMs too when flagged)
+bool mx_bwd_ok(const moe_desc* d) {
+  const GemmDims g = gemm_dims(d);
+  if (!mx_bwd_shape_ok(g)) return false;
+  return !(d->flags & MOE_FLAG_MXFP8_WGRAD) || mx_wgrad_shape_ok(g);
 }
 
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -226,7 +244,7 @@ size_t moe_workspace_bytes(const moe_desc* desc, int which) {
     case MOE_WS_BWD: return bwd_layout(desc).total;
     case MOE_WS_BWD_UNFUSED: return unfused_bwd_layout(desc).total;
     case MOE_WS_FWD_MXFP8: return mx_shape_ok(gemm_dims(desc)) ? mx_fwd_layout(desc).total : 0;
-    case MOE_WS_BWD_MXFP8: return mx_bwd_shape_ok(gemm_dims(desc)) ? mx_bwd_layout(desc).total : 0;
+    case MOE_WS_BWD_MXFP8: return mx_bwd_ok(desc) ? mx_bwd_layout(desc).total : 0;
     default: return 0;
   }
 }
@@ -248,8 +266,13 @@ size_t moe_workspace_offset(const moe_desc* desc, int item) {
     return mx_fwd_layout(desc).off[item - MOE_ITEM_MX_XQ];
   }
   if (item >= MOE_ITEM_MX_DHQ && item <= MOE_ITEM_MX_W2RS) {
-    if (!mx_bwd_shape_ok(gemm_dims(desc))) return (size_t)-1;
+    if (!mx_bwd_ok(desc)) return (size_t)-1;
     return mx_bwd_layout(desc).off[10 + item - MOE_ITEM_MX_DHQ];
+  }
+  if (item >= MOE_ITEM_MX_WG_PADOFF && item <= MOE_ITEM_MX_WG_OS) {
+    if (!mx_bwd_ok(desc) || !(desc->flags & MOE_FLAG_MXFP8_WGRAD)) return (size_t)-1;
+    const Layout L = mx_bwd_layout(desc);
+    return item == MOE_ITEM_MX_WG_PADOFF ? L.off[18] : L.off[20 + item - MOE_ITEM_MX_WG_XQ];
   }
   return (size_t)-1;
 }
@@ -363,7 +386,7 @@ int bwd_impl(const moe_desc* desc, const void* x, const void* w_r, const void* w
   if (s != MOE_OK) return s;
   if (mx) {
     if (desc->dtype != MOE_BF16) return MOE_EDTYPE;
-    if (!mx_bwd_shape_ok(gemm_dims(desc))) return MOE_ESHAPE;
+    if (!mx_bwd_ok(desc)) return MOE_ESHAPE;
   }
   if (!x || !w_r || !w1 || !w2 || !h_cache || !d_o || !dx || !dw_r || !dw1 || !dw2 || !routing_ok(routing))
     return MOE_EINVAL;
@@ -418,9 +441,29 @@ int bwd_impl(const moe_desc* desc, const void* x, const void* w_r, const void* w
   MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, ax, st));
   MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, (float*)(w + L.off[8]), st));
   // weight gradients
-  void* wws = wgt_ws_bytes(g) ? (void*)(w + L.off[9]) : nullptr;
-  MOE_TRY(MOE_K_DW1, launch_dw1(g, x, dH, R.row_token, R.offsets, dw1, wws, st));
-  MOE_TRY(MOE_K_DW2, launch_dw2(g, As, d_o, R.row_token, R.offsets, dw2, wws, st));
+  if (mx && (D.flags & MOE_FLAG_MXFP8_WGRAD)) {
+    // operands quantized along each expert's rows: x_g and dH for dW1, A_s and
+    // dO_g for dW2
+    int32_t* padoff = (int32_t*)(w + L.off[18]);
+    int32_t* stage_e = (int32_t*)(w + L.off[19]);
+    uint8_t* q[4];
+    uint32_t* sc[4];
+    for (int i = 0; i < 4; ++i) {
+      q[i] = (uint8_t*)(w + L.off[20 + 2 * i]);
+      sc[i] = (uint32_t*)(w + L.off[21 + 2 * i]);
+    }
+    MOE_TRY(MOE_K_MX_PAD_OFFSETS, launch_mx_pad_offsets(R.offsets, D.E, padoff, stage_e, st));
+    MOE_TRY(MOE_K_MX_QUANT_SEG, launch_mx_quant_seg(x, D.d, R.row_token, R.offsets, padoff, stage_e, g, q[0], sc[0], st));
+    MOE_TRY(MOE_K_MX_QUANT_SEG, launch_mx_quant_seg(dH, 2 * D.n, nullptr, R.offsets, padoff, stage_e, g, q[1], sc[1], st));
+    MOE_TRY(MOE_K_DW1_MX, launch_wgrad_mx(g, D.d, 2 * D.n, padoff, q[0], sc[0], q[1], sc[1], dw1, st));
+    MOE_TRY(MOE_K_MX_QUANT_SEG, launch_mx_quant_seg(As, D.n, nullptr, R.offsets, padoff, stage_e, g, q[2], sc[2], st));
+    MOE_TRY(MOE_K_MX_QUANT_SEG, launch_mx_quant_seg(d_o, D.d, R.row_token, R.offsets, padoff, stage_e, g, q[3], sc[3], st));
+    MOE_TRY(MOE_K_DW2_MX, launch_wgrad_mx(g, D.n, D.d, padoff, q[2], sc[2], q[3], sc[3], dw2, st));
+  } else {
+    void* wws = wgt_ws_bytes(g) ? (void*)(w + L.off[9]) : nullptr;
+    MOE_TRY(MOE_K_DW1, launch_dw1(g, x, dH, R.row_token, R.offsets, dw1, wws, st));
+    MOE_TRY(MOE_K_DW2, launch_dw2(g, As, d_o, R.row_token, R.offsets, dw2, wws, st));
+  }
   if (db) MOE_TRY(MOE_K_DB, launch_bias_grad(dz_row, R.offsets, D.E, db, st));
   return MOE_OK;
 }

@@ -142,6 +142,97 @@ k_mx_quant_w(const bf16_t* __restrict__ W, int K, int N, uint8_t* __restrict__ q
   }
 }
 
+// Weight-gradient operands: each expert's segment of routed rows is
+// quantized along its rows (the weight-gradient GEMMs' reduction), the
+// segment padded with zero rows to a multiple of 128 (one GEMM stage).
+// padoff[e] = sum over experts before e of the padded lengths; stage_e[g] =
+// the expert of global stage g (g < padoff[E] / 128).  One workgroup.
+__global__ void __launch_bounds__(1024)
+k_mx_pad_offsets(const int32_t* __restrict__ offsets, int E, int32_t* __restrict__ padoff,
+                 int32_t* __restrict__ stage_e) {
+  __shared__ int32_t ps[1025];
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int len = tid < E ? (offsets[tid + 1] - offsets[tid] + 127) / 128 * 128 : 0;
+  int incl = len;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int x = 0; x < w; ++x) base += wsum[x];
+  if (tid < E) ps[tid] = base + incl - len;
+  if (tid == E - 1) ps[E] = base + incl;
+  __syncthreads();
+  for (int e = tid; e <= E; e += 1024) padoff[e] = ps[e];
+  // stage map: expert e owns stages ps[e]/128 .. ps[e+1]/128 - 1
+  for (int e = 0; e < E; ++e) {
+    const int g0 = ps[e] / 128, g1 = ps[e + 1] / 128;
+    for (int g = g0 + tid; g < g1; g += 1024) stage_e[g] = e;
+  }
+}
+
+// src rows [*][C] bf16 (row r of expert e's segment is src[idx[seg0 + r]],
+// or src[seg0 + r] without idx) -> per expert, codes [C][Kp_e] at byte
+// C * padoff[e] (Kp_e = padded segment length) and stage-blocked scales: the
+// dword (padoff[e] / 128 + s) * C + c holds column c's four block scales of
+// stage s (byte b = rows 128 s + 32 b .. +31).  One workgroup per (64
+// columns, global stage): the 128 x 64 tile is read in whole rows (zeros
+// past the segment), each thread quantizes one (column, 32-row block) from
+// LDS, and the codes leave as 128-byte rows.  Workgroups past the last stage
+// return.
+__global__ void __launch_bounds__(256)
+k_mx_quant_seg(const bf16_t* __restrict__ src, int C, const int32_t* __restrict__ idx,
+               const int32_t* __restrict__ offsets, const int32_t* __restrict__ padoff,
+               const int32_t* __restrict__ stage_e, int E, uint8_t* __restrict__ q, uint32_t* __restrict__ sblk) {
+  __shared__ bf16_t tin[128][64 + 2];
+  __shared__ uint32_t tout[64][32 + 1];
+  __shared__ uint32_t ts[4][64];
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * 64, g = blockIdx.y;
+  if (g >= padoff[E] / 128) return;  // uniform over the workgroup
+  const int e = stage_e[g];
+  const int seg0 = offsets[e], segn = offsets[e + 1] - seg0;
+  const int pe = padoff[e], kp = padoff[e + 1] - pe;
+  const int s = g - pe / 128;  // stage of the segment
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {  // 128 rows x 64 columns, 4 columns (8 bytes) per thread
+    const int v = it * 256 + tid, r = v >> 4, c4 = (v & 15) * 4;
+    const int sr = 128 * s + r;
+    uint2 x = make_uint2(0u, 0u);
+    if (sr < segn) {
+      const long long row = idx ? (long long)idx[seg0 + sr] : (long long)(seg0 + sr);
+      x = *reinterpret_cast<const uint2*>(src + row * C + c0 + c4);
+    }
+    tin[r][c4] = (bf16_t)(x.x & 0xffffu);
+    tin[r][c4 + 1] = (bf16_t)(x.x >> 16);
+    tin[r][c4 + 2] = (bf16_t)(x.y & 0xffffu);
+    tin[r][c4 + 3] = (bf16_t)(x.y >> 16);
+  }
+  __syncthreads();
+  const int col = tid & 63, b = tid >> 6;  // 32-row block b of the stage
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = __uint_as_float((uint32_t)tin[32 * b + i][col] << 16);
+  uint32_t qw[8];
+  const int sc = quant32(v, qw);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tout[col][8 * b + i] = qw[i];
+  ts[b][col] = (uint32_t)sc;
+  __syncthreads();
+  if (tid < 64)
+    sblk[(long long)(pe / 128 + s) * C + c0 + tid] = ts[0][tid] | (ts[1][tid] << 8) | (ts[2][tid] << 16) | (ts[3][tid] << 24);
+  uint8_t* qe = q + (long long)C * pe;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {  // 64 rows of 128 bytes, 16 bytes per thread
+    const int v2 = it * 256 + tid, r = v2 >> 3, ch = v2 & 7;
+    *reinterpret_cast<uint4*>(qe + (long long)(c0 + r) * kp + 128 * s + ch * 16) =
+        make_uint4(tout[r][4 * ch], tout[r][4 * ch + 1], tout[r][4 * ch + 2], tout[r][4 * ch + 3]);
+  }
+}
+
 int cu_count() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -236,6 +327,46 @@ hipError_t launch_dh_mx(const GemmDims& g, const uint8_t* doq, const uint8_t* do
   return run_gemm_mx<false, Epi>(s, a, b, dos, reinterpret_cast<const uint32_t*>(w2s), (size_t)g.T * d,
                                  (size_t)n * d, (size_t)g.T * (d / 32), (size_t)(d / 128) * n * 4, ep,
                                  tiles_bound(g.cap, E) * (n / gmx::BN), st);
+}
+
+hipError_t launch_mx_pad_offsets(const int32_t* offsets, int E, int32_t* padoff, int32_t* stage_e, hipStream_t st) {
+  hipLaunchKernelGGL(k_mx_pad_offsets, dim3(1), dim3(1024), 0, st, offsets, E, padoff, stage_e);
+  return hipGetLastError();
+}
+
+long long mx_seg_rows_bound(const GemmDims& g) { return (long long)g.cap + 127LL * g.E; }
+
+hipError_t launch_mx_quant_seg(const void* src, int C, const int32_t* idx, const int32_t* offsets,
+                               const int32_t* padoff, const int32_t* stage_e, const GemmDims& g, uint8_t* q,
+                               uint32_t* sblk, hipStream_t st) {
+  const long long stages = (mx_seg_rows_bound(g) + 127) / 128;
+  hipLaunchKernelGGL(k_mx_quant_seg, dim3((unsigned)(C / 64), (unsigned)stages), dim3(256), 0, st,
+                     (const bf16_t*)src, C, idx, offsets, padoff, stage_e, g.E, q, sblk);
+  return hipGetLastError();
+}
+
+bool mx_wgrad_shape_ok(const GemmDims& g) {
+  const size_t rows = (size_t)mx_seg_rows_bound(g);
+  const size_t widest = (size_t)std::max(std::max(g.d, 2 * g.n), g.n);
+  return g.dtype == DT_BF16 && g.d % 256 == 0 && g.n % 256 == 0 && g.E <= MAX_E && widest * rows < (size_t)g4::OOB;
+}
+
+hipError_t launch_wgrad_mx(const GemmDims& g, int Ma, int Nb, const int32_t* padoff, const uint8_t* qa,
+                           const uint32_t* sa, const uint8_t* qb, const uint32_t* sb, void* dW, hipStream_t st) {
+  using Epi = g4::G4Store;
+  auto kern = gmx::grouped_gemm_mxw_kernel<Epi>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, gmx::WSMEM);
+  if (attr != hipSuccess) return attr;
+  const size_t rows = (size_t)mx_seg_rows_bound(g);
+  const long long tiles = (long long)g.E * (Ma / gmx::BM) * (Nb / gmx::BN);
+  long long grid = std::min<long long>(tiles, cu_count());
+  if (grid < 1) grid = 1;
+  typename Epi::Params ep{reinterpret_cast<bf16_t*>(dW), Nb};
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(gmx::NTH), gmx::WSMEM, st, g.E, Ma, Nb, padoff, qa, sa, qb,
+                     sb, (uint32_t)(rows * Ma), (uint32_t)(rows * Nb), (uint32_t)(rows / 128 * Ma * 4),
+                     (uint32_t)(rows / 128 * Nb * 4), ep);
+  return hipGetLastError();
 }
 
 hipError_t launch_down_mx(const GemmDims& g, const uint8_t* aq, const uint8_t* as, const uint8_t* w2q,

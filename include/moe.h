@@ -77,6 +77,9 @@ extern "C" {
                                      sizes are multiples of 256 use 256 x 256
                                      tiles); results agree to rounding, the
                                      workspace size may differ */
+#define MOE_FLAG_MXFP8_WGRAD  4u  /* moe_bwd_mxfp8 also runs the two weight-
+                                     gradient GEMMs on MXFP8 operands (see
+                                     moe_bwd_mxfp8); ignored by the other calls */
 
 /* kernel ids reported in moe_profile.kernel (one per launch, in order) */
 #define MOE_K_ROUTER_LOGITS 0   /* z = x w_r + b                                  */
@@ -106,7 +109,12 @@ extern "C" {
 #define MOE_K_DOWN_MX      22   /* K2 on MXFP8 operands -> Y                       */
 #define MOE_K_DXT_MX       23   /* K5 on MXFP8 operands -> dXt (moe_bwd_mxfp8)     */
 #define MOE_K_DH_MX        24   /* K4 on MXFP8 operands -> dH, A_s, dS             */
-#define MOE_K_COUNT        25
+/* launched by moe_bwd_mxfp8 with MOE_FLAG_MXFP8_WGRAD */
+#define MOE_K_MX_PAD_OFFSETS 25 /* padded segment offsets and stage -> expert map  */
+#define MOE_K_MX_QUANT_SEG 26   /* an expert segment's rows quantized along the rows */
+#define MOE_K_DW1_MX       27   /* K7 on MXFP8 operands                            */
+#define MOE_K_DW2_MX       28   /* K8 on MXFP8 operands                            */
+#define MOE_K_COUNT        29
 
 /* workspace phases */
 #define MOE_WS_ROUTE 0
@@ -145,6 +153,22 @@ extern "C" {
 #define MOE_ITEM_MX_DOS  22  /* d_o scales [T, d/32]                              */
 #define MOE_ITEM_MX_W2RQ 23  /* w2 codes along d: [E, n, d]                       */
 #define MOE_ITEM_MX_W2RS 24  /* w2 scales [E, d/128, n, 4]                        */
+/* MXFP8 weight gradients (MOE_WS_BWD_MXFP8 with MOE_FLAG_MXFP8_WGRAD).  Each
+ * expert's segment of c_e routed rows is padded with zero rows to
+ * Kp_e = c_e rounded up to 128 and quantized along its rows; padoff [E+1]
+ * int32 holds the prefix of Kp_e.  A segment operand of C columns is, per
+ * expert, codes [C][Kp_e] at byte C * padoff[e] and scales as dwords: dword
+ * (padoff[e]/128 + s) * C + c = column c's four block scales (bytes b = 0..3:
+ * segment rows 128 s + 32 b .. +31) */
+#define MOE_ITEM_MX_WG_PADOFF 25  /* padoff [E+1] int32                             */
+#define MOE_ITEM_MX_WG_XQ  26  /* x rows gathered per segment, C = d: codes        */
+#define MOE_ITEM_MX_WG_XS  27  /*   and scales                                    */
+#define MOE_ITEM_MX_WG_HQ  28  /* dH rows (bf16 as the dH kernel wrote them), C = 2n */
+#define MOE_ITEM_MX_WG_HS  29
+#define MOE_ITEM_MX_WG_AQ  30  /* A_s rows (bf16), C = n                            */
+#define MOE_ITEM_MX_WG_AS  31
+#define MOE_ITEM_MX_WG_OQ  32  /* d_o rows gathered per segment, C = d              */
+#define MOE_ITEM_MX_WG_OS  33
 
 /*
  * Layer description (host struct).
@@ -336,11 +360,19 @@ int moe_fwd_mxfp8(const moe_desc* desc, const void* x, const void* w1, const voi
  * one E8M0 scale per 32 values, as in moe_fwd_mxfp8): dA' = d_o w2^T with
  * d_o and each expert's w2 quantized along d, feeding the dH epilogue; and
  * dXt = dH w1^T with dH (as that epilogue wrote it, bf16) and each expert's
- * w1 quantized along 2n.  The weight-gradient GEMMs, the aggregation and the
- * router backward are moe_bwd's.  Same arguments and outputs as moe_bwd.
- *   Shapes: those of moe_fwd_mxfp8 with n at most 1024 (else MOE_ESHAPE);
- *   dtype MOE_BF16 (else MOE_EDTYPE).
- *   ws: MOE_WS_BWD_MXFP8 workspace.
+ * w1 quantized along 2n.  The aggregation and the router backward are
+ * moe_bwd's.  The weight-gradient GEMMs are moe_bwd's too, unless
+ * desc->flags has MOE_FLAG_MXFP8_WGRAD: then they also take MXFP8 operands,
+ * quantized along their reduction, each expert's rows (32-row blocks that
+ * start at the expert's first row, the last one zero-padded): dW1[e] =
+ * X_g^T dH from the gathered x rows and dH, dW2[e] = A_s^T dO_g from A_s
+ * (both as the dH kernel wrote them, bf16) and the gathered d_o rows.  Same
+ * arguments and outputs as moe_bwd.
+ *   Shapes: those of moe_fwd_mxfp8 with n at most 1024, and with
+ *   MOE_FLAG_MXFP8_WGRAD also (cap + 127 E) * max(d, 2n) below 2^31, the
+ *   padded segment operands' byte range (else MOE_ESHAPE); dtype MOE_BF16
+ *   (else MOE_EDTYPE).
+ *   ws: MOE_WS_BWD_MXFP8 workspace (larger with MOE_FLAG_MXFP8_WGRAD).
  */
 int moe_bwd_mxfp8(const moe_desc* desc, const void* x, const void* w_r, const void* w1,
                   const void* w2, const moe_routing* routing, const void* h_cache, const void* d_o,

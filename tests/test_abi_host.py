@@ -62,11 +62,34 @@ def test_capacity_and_workspace():
     assert B.moe_workspace_offset(d, 99) == -1
 
 
+def test_mx_weight_grad_workspace():
+    """MOE_FLAG_MXFP8_WGRAD grows the MXFP8 backward workspace by the padded
+    segment operands and gives their items offsets; without it they have none."""
+    T, d, E, n, K = 1000, 512, 16, 256, 2
+    plain = B.make_desc(T, d, E, n, K, "bf16")
+    flagged = B.make_desc(T, d, E, n, K, "bf16", flags=B.MOE_FLAG_MXFP8_WGRAD)
+    a = B.moe_workspace_bytes(plain, B.MOE_WS_BWD_MXFP8)
+    b = B.moe_workspace_bytes(flagged, B.MOE_WS_BWD_MXFP8)
+    rows = B.moe_row_capacity(plain) + 127 * E
+    assert a > 0 and b >= a + (d + 2 * n + n + d) * rows * (1 + 1 / 32)
+    assert B.moe_workspace_bytes(flagged, B.MOE_WS_BWD) == B.moe_workspace_bytes(plain, B.MOE_WS_BWD)
+    offs = [B.moe_workspace_offset(flagged, i)
+            for i in range(B.MOE_ITEM_MX_WG_PADOFF, B.MOE_ITEM_MX_WG_OS + 1)]
+    assert all(o >= a and o % 256 == 0 for o in offs) and offs == sorted(offs) and offs[-1] < b
+    assert all(B.moe_workspace_offset(plain, i) == -1
+               for i in range(B.MOE_ITEM_MX_WG_PADOFF, B.MOE_ITEM_MX_WG_OS + 1))
+    # the flag asks nothing of the other workspaces' shapes, but its own
+    # byte-range limit: (cap + 127 E) * max(d, 2n) below 2^31
+    big = B.make_desc(125000, 2048, 1024, 256, 8, "bf16", flags=B.MOE_FLAG_MXFP8_WGRAD)
+    assert B.moe_workspace_bytes(big, B.MOE_WS_BWD_MXFP8) == 0
+    assert B.moe_workspace_bytes(big, B.MOE_WS_FWD_MXFP8) > 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(T=0), B.MOE_EINVAL), (dict(K=0), B.MOE_EINVAL), (dict(K=9), B.MOE_EINVAL),
     (dict(dtype=7), B.MOE_EDTYPE), (dict(round_mode=3), B.MOE_EINVAL), (dict(tile=64), B.MOE_ESHAPE), (dict(tile=512), B.MOE_ESHAPE),
     (dict(d=100), B.MOE_ESHAPE), (dict(n=48), B.MOE_ESHAPE), (dict(E=12, K=2), B.MOE_ESHAPE),
-    (dict(flags=4), B.MOE_EINVAL),
+    (dict(flags=8), B.MOE_EINVAL),
 ])
 def test_invalid_descriptors_rejected(lib, kw, code):
     a = dict(T=256, d=128, E=8, n=64, K=2, dtype="f32")

@@ -255,3 +255,151 @@ def test_mxfp8_backward_full_size_expert_sample(name):
         err = relF(host64(dXt_all[s0:s1]), ref)
         print(name, int(e), s1 - s0, f"dXt {err:.2e}")
         assert err <= TOL
+
+
+WG_CASES = [CASES[0], CASES[1], CASES[3]]
+WG_E2E = 0.08      # MX dW against the plain bf16-operand product (E4M3 on both operands)
+
+
+def seg_scales(sblk_u8, pe, kp, C):
+    """stage-blocked segment scales -> [C, kp / 32] for the expert at padded row pe"""
+    s = sblk_u8.reshape(-1, C, 4)[pe // 128:(pe + kp) // 128]
+    return s.transpose(1, 0, 2).reshape(C, kp // 32)
+
+
+def pad128(rows):
+    r = rows.shape[0]
+    return np.concatenate([rows, np.zeros(((-r) % 128, rows.shape[1]))], axis=0)
+
+
+def mx_wgrad_layer(w, mode=0, tile=128):
+    a = I.draw_all(w)
+    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, "bf16", round_mode=mode, round_seed=3, tile=tile,
+                       flags=B.MOE_FLAG_MXFP8_WGRAD)
+    L = B.Layer(desc)
+    X, WR, W1, W2, DO = (dev(a[k], "bf16") for k in ("x", "w_r", "w1", "w2", "d_o"))
+    L.route(X, WR)
+    L.forward(X, W1, W2)
+    L.backward_mxfp8(X, WR, W1, W2, DO)
+    torch.cuda.synchronize()
+    return a, L
+
+
+def check_expert_wgrad(L, w, a, e, off, padoff, dH_all, As_all, wsq, x_rows=None):
+    """One expert: its four segment operands' codes and scales bit-exact
+    against the oracle's quantization of the same rows (x and dO gathered,
+    dH and A_s as the GPU's dH kernel wrote them), and dW1[e], dW2[e] against
+    the oracle's product of those codes.  Returns the relative errors."""
+    d, n = w.d, w.n
+    s0, s1 = int(off[e]), int(off[e + 1])
+    pe, kp = int(padoff[e]), int(padoff[e + 1]) - int(padoff[e])
+    assert kp == (s1 - s0 + 127) // 128 * 128
+    tok = host_int(L.routing.row_token[s0:s1])
+    x64 = O.to_f64(a["x"][tok], "bf16")
+    dO = O.to_f64(a["d_o"][tok], "bf16")
+    dH = host64(dH_all[s0:s1])
+    As = host64(As_all[s0:s1])
+    got = {}
+    for key, rows, C in (("x", x64, d), ("h", dH, 2 * n), ("a", As, n), ("o", dO, d)):
+        q_ref, s_ref = M.quantize_segment(pad128(rows))
+        q_all, s_all = wsq[key]
+        gq = q_all[C * pe:C * (pe + kp)].cpu().numpy().reshape(C, kp)
+        gs = seg_scales(s_all, pe, kp, C)
+        assert np.array_equal(gq, q_ref), (key, e)
+        assert np.array_equal(gs, s_ref), (key, e)
+        got[key] = M.dequantize(q_ref, s_ref)
+    ref1 = got["x"] @ got["h"].T
+    ref2 = got["a"] @ got["o"].T
+    g1, g2 = host64(L.dw1[e]), host64(L.dw2[e])
+    if s1 == s0:
+        assert not g1.any() and not g2.any()
+        return dict(dW1=0.0, dW2=0.0), None
+    plain = (x64.T @ dH, As.T @ dO)
+    return (dict(dW1=relF(g1, ref1), dW2=relF(g2, ref2)),
+            dict(dW1=relF(g1, plain[0]), dW2=relF(g2, plain[1])))
+
+
+def wgrad_views(L, w):
+    d, n = w.d, w.n
+    off = host_int(L.routing.offsets)
+    P = int(off[-1])
+    padoff = L.ws_view(B.MOE_ITEM_MX_WG_PADOFF, w.E + 1, torch.int32).cpu().numpy()
+    rows = int(padoff[-1])
+    wsq = {}
+    for key, qi, si, C in (("x", B.MOE_ITEM_MX_WG_XQ, B.MOE_ITEM_MX_WG_XS, d),
+                           ("h", B.MOE_ITEM_MX_WG_HQ, B.MOE_ITEM_MX_WG_HS, 2 * n),
+                           ("a", B.MOE_ITEM_MX_WG_AQ, B.MOE_ITEM_MX_WG_AS, n),
+                           ("o", B.MOE_ITEM_MX_WG_OQ, B.MOE_ITEM_MX_WG_OS, d)):
+        wsq[key] = (L.ws_view(qi, C * rows, torch.uint8), u8(L, si, C * rows // 32))
+    dH_all = L.ws_view(B.MOE_ITEM_DH, P * 2 * n, torch.bfloat16, mx_bwd=True).view(P, 2 * n)
+    As_all = L.ws_view(B.MOE_ITEM_AS, P * n, torch.bfloat16, mx_bwd=True).view(P, n)
+    return off, padoff, dH_all, As_all, wsq
+
+
+@pytest.mark.parametrize("w,mode,tile", WG_CASES, ids=[c[0].name for c in WG_CASES])
+def test_mxfp8_weight_grads_match_oracle(w, mode, tile):
+    """moe_bwd_mxfp8 with MOE_FLAG_MXFP8_WGRAD, every expert: padded segment
+    offsets exact, the segment operands' codes and scales bit-exact, dW1 / dW2
+    against the oracle on those codes (empty experts exactly zero), the whole
+    dW1 / dW2 against the oracle's weight_grads_mxfp8 on the GPU's dH and A_s,
+    the rest of the backward as without the flag, and every dW against the
+    plain product within the MX quantization bound."""
+    a, L = mx_wgrad_layer(w, mode, tile)
+    off, padoff, dH_all, As_all, wsq = wgrad_views(L, w)
+    cnt = np.diff(off)
+    assert np.array_equal(padoff, np.concatenate([[0], np.cumsum((cnt + 127) // 128 * 128)]))
+    worst, worst_e2e = {}, {}
+    for e in range(w.E):
+        errs, e2e = check_expert_wgrad(L, w, a, e, off, padoff, dH_all, As_all, wsq)
+        for k, v in errs.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+        for k, v in (e2e or {}).items():
+            worst_e2e[k] = max(worst_e2e.get(k, 0.0), v)
+    # whole tensors against the oracle's own weight-gradient routine
+    x64 = O.to_f64(a["x"], "bf16")
+    dO = O.to_f64(a["d_o"], "bf16")
+    rt = dict(offsets=off, row_token=host_int(L.routing.row_token[:int(off[-1])]))
+    o = M.weight_grads_mxfp8(x64, dO, rt, host64(dH_all), host64(As_all))
+    whole = dict(dW1=relF(host64(L.dw1), o["dW1"]), dW2=relF(host64(L.dw2), o["dW2"]))
+    print(w.name, "per expert", {k: f"{v:.2e}" for k, v in worst.items()},
+          "whole", {k: f"{v:.2e}" for k, v in whole.items()},
+          "vs plain", {k: f"{v:.2e}" for k, v in worst_e2e.items()})
+    assert all(v <= TOL for v in worst.values()), worst
+    assert all(v <= TOL for v in whole.values()), whole
+    assert all(v <= WG_E2E for v in worst_e2e.values()), worst_e2e
+
+
+def test_mxfp8_weight_grad_flag_leaves_the_rest_unchanged():
+    """The flag changes dW1 / dW2 only: dX, dW_r, dS, db bit-identical to
+    moe_bwd_mxfp8 without it on the same inputs."""
+    w = CASES[0][0]
+    a, L1 = mx_wgrad_layer(w)
+    desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, "bf16", round_seed=3)
+    L2 = B.Layer(desc)
+    X, WR, W1, W2, DO = (dev(a[k], "bf16") for k in ("x", "w_r", "w1", "w2", "d_o"))
+    L2.route(X, WR)
+    L2.forward(X, W1, W2)
+    L2.backward_mxfp8(X, WR, W1, W2, DO)
+    torch.cuda.synchronize()
+    P = int(host_int(L1.routing.offsets)[-1])
+    assert torch.equal(L1.dx, L2.dx) and torch.equal(L1.dw_r, L2.dw_r)
+    assert torch.equal(L1.ds[:P], L2.ds[:P]) and torch.equal(L1.db, L2.db)
+
+
+@pytest.mark.parametrize("name", ["fg7b_bf16", "olmoe_bf16"])
+def test_mxfp8_weight_grads_full_size_expert_sample(name):
+    """Full size, the benchmark's launch configuration with the flag: padded
+    offsets exact and, for three sampled experts, every segment operand's
+    codes and scales bit-exact and dW1[e] / dW2[e] against the oracle on
+    those codes."""
+    w = I.WORKLOADS[name]
+    a, L = mx_wgrad_layer(w)
+    off, padoff, dH_all, As_all, wsq = wgrad_views(L, w)
+    cnt = np.diff(off)
+    assert np.array_equal(padoff, np.concatenate([[0], np.cumsum((cnt + 127) // 128 * 128)]))
+    for e in np.random.default_rng(11).choice(w.E, 3, replace=False):
+        errs, e2e = check_expert_wgrad(L, w, a, int(e), off, padoff, dH_all, As_all, wsq)
+        print(name, int(e), int(cnt[e]), {k: f"{v:.2e}" for k, v in errs.items()},
+              "vs plain", {k: f"{v:.2e}" for k, v in (e2e or {}).items()})
+        assert all(v <= TOL for v in errs.values()), errs
+        assert all(v <= WG_E2E for v in (e2e or {}).values()), e2e
