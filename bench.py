@@ -90,12 +90,12 @@ def kernel_work(name, w, P, es, mx=False):
     # bandwidth-bound kernels: bytes that must cross HBM once
     bytes_ = {
         "agg_o": P * d * es + T * d * es + P * 8 + (T + 1) * 4,
-        # dXt rows, dX out, tok_row / row_expert, W_r^T, and the folded router
-        # backward: dS partials and gates in, dS / dz per row and dense dz out
-        "agg_dx": P * d * es + T * d * es + P * 8 + (T + 1) * 4 + E * d * es
-                  + P * (4 + 4 + 4 + 4) + T * E * es,
+        # dXt rows (each with its router term) in, dX out, the token CSR
+        "agg_dx": P * d * es + T * d * es + P * 4 + (T + 1) * 4,
         "route_select": T * E * 4 + T * w.K * 8 + P * 16 + T * E * (1 + 1 + 4),
-        "router_grad": P * (8 + 4 + 4 + 4) + T * E * es,
+        # router backward: dS (one partial per row counted), gate, expert and
+        # the token CSR in; dS and dz per row and the dense dz rows out
+        "router_grad": P * (4 + 4 + 4 + 4) + (T + 1) * 4 + P * (4 + 4) + T * E * es,
         "wr_t": 2 * E * d * es, "db": P * 4,
         # unfused layer: row gather (read + write), SwiGLU, dS = <dO_g, Y>, SwiGLU backward
         "gather": 2 * P * d * es + P * 4, "swiglu": 3 * P * n * es, "row_dot": 2 * P * d * es + P * 4,

@@ -9,8 +9,11 @@
 // Router backward ([B] algorithm paragraph: the router gradient comes from
 // the reordered contraction, no cached Y): dS per row is the sum of the dH
 // kernel's per-column-tile partials; dz = gate * (dS - sum over the token's
-// set of gate * dS) is the softmax-over-set backward.  It is computed per
-// token inside the dX aggregation, which walks the token's rows anyway.
+// set of gate * dS) is the softmax-over-set backward.  It runs per token
+// between the dH and dXt GEMMs (k_router_dz), so the dXt GEMM's epilogue
+// adds each row's router term dz_r W_r^T[e_r] to its output row, and dX is
+// then a plain gather-sum of those rows: the router-weight rows are read once
+// per output tile instead of once per routed row.
 #include "device_common.h"
 #include "launch.h"
 
@@ -50,11 +53,7 @@ __device__ __forceinline__ void store_vec(T* p, const float (&v)[16 / sizeof(T)]
   *reinterpret_cast<uint4*>(p) = u;
 }
 
-constexpr int UNR = 4;  // rows in flight per lane (output aggregation)
-// The dX aggregation also loads a router-weight row per token row, so it keeps
-// two rows in flight per lane: fewer registers, more waves per SIMD (measured
-// 0.195 -> 0.191 ms at T = 32768, d = 1536, K = 8 against four rows).
-constexpr int UNR_DX = 2;
+constexpr int UNR = 4;  // rows in flight per lane
 // Column chunks per lane per pass (CPL) are a template parameter: the
 // launcher picks the smallest CPL (at most 4) that covers a row's 16-byte
 // chunks in as few passes as CPL = 4 would, so no chunk slot idles (d = 1536
@@ -82,9 +81,10 @@ __device__ __forceinline__ void unpack(const uint4 u, float (&v)[16 / sizeof(T)]
   }
 }
 
-// O[t] = sum over token t's rows (ascending) of gate_r * Y[r].  One wave per
-// token; each lane owns up to CPL 16-byte column chunks per pass and keeps
-// UNR rows x CPL chunks of loads in flight.
+// O[t] = sum over token t's rows (ascending) of gate_r * Y[r] (gate 1 when
+// row_gate is null: the dX aggregation).  One wave per token; each lane owns
+// up to CPL 16-byte column chunks per pass and keeps UNR rows x CPL chunks of
+// loads in flight.
 template <typename T, int CPL>
 __global__ void __launch_bounds__(256)
 k_aggregate_o(const T* __restrict__ Y, const float* __restrict__ row_gate,
@@ -109,7 +109,7 @@ k_aggregate_o(const T* __restrict__ Y, const float* __restrict__ row_gate,
       for (int u = 0; u < UNR; ++u) {
         const bool ok = j + u < j1;
         const int r = ok ? tok_row[j + u] : 0;
-        g[u] = ok ? row_gate[r] : 0.f;
+        g[u] = ok ? (row_gate ? row_gate[r] : 1.f) : 0.f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const int ch = cb + lane + 64 * c;
@@ -134,113 +134,73 @@ k_aggregate_o(const T* __restrict__ Y, const float* __restrict__ row_gate,
   }
 }
 
-// dX[t] = sum over token t's rows (ascending) of dXt[r] + dz_r * W_r^T[e_r],
-// with the router backward of the token folded in: dS_r = sum of the row's
-// dH-epilogue partials (fixed order), dz_r = g_r (dS_r - sum_j g_j dS_j) over
-// the token's set; dS_r and dz_r are written per row and dz as the token's
-// dense row (zeros outside its set) for the router weight gradient.  One wave
-// per token; its dense dz row lives in LDS (E floats per wave).
-template <typename T, int CPL>
+// Router backward per token: dS_r = sum of the row's dH-epilogue partials
+// (fixed order), dz_r = g_r (dS_r - sum_j g_j dS_j) over the token's set;
+// dS_r and dz_r are written per row and dz as the token's dense row (zeros
+// outside its set) for the router weight gradient.  Sixteen lanes per token
+// (four tokens per wave, sixteen per workgroup): lane s takes the token's
+// rows s, s + 16, ..., the set sum is a fixed butterfly over the sixteen
+// lanes, and the dense rows are assembled in LDS (E floats per token) and
+// leave as one contiguous block per wave.  The kernel is a chain of dependent
+// loads (token CSR -> row -> partials, gate, expert); packing four tokens per
+// wave puts the whole batch in flight at once.
+template <typename T>
 __global__ void __launch_bounds__(256)
-k_aggregate_dx(const T* __restrict__ dXt, const float* __restrict__ dS_part, int nparts,
-               const float* __restrict__ row_gate, const int32_t* __restrict__ row_expert,
-               const T* __restrict__ w_rT, const int32_t* __restrict__ tok_ptr, const int32_t* __restrict__ tok_row,
-               int Tn, int d, int E, float* __restrict__ dS_row, float* __restrict__ dz_row,
-               T* __restrict__ dz_dense, T* __restrict__ dX) {
-  extern __shared__ float dzs[];  // [4][E]
-  constexpr int V = 16 / sizeof(T);
+k_router_dz(const float* __restrict__ dS_part, int nparts, const float* __restrict__ row_gate,
+            const int32_t* __restrict__ row_expert, const int32_t* __restrict__ tok_ptr,
+            const int32_t* __restrict__ tok_row, int Tn, int E, float* __restrict__ dS_row,
+            float* __restrict__ dz_row, T* __restrict__ dz_dense) {
+  extern __shared__ float dzs[];  // [16][E]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + wave);
+  const int slot = wave * 4 + (lane >> 4), sub = lane & 15;
+  const int tw = blockIdx.x * 16 + wave * 4;  // the wave's first token
+  const int t = tw + (lane >> 4);
   const bool live = t < Tn;
-  float* dense = dzs + wave * E;
-  for (int e = lane; e < E; e += 64) dense[e] = 0.f;
-  __syncthreads();
+  float* dense = dzs + slot * E;
+  for (int e = sub; e < E; e += 16) dense[e] = 0.f;
   int j0 = 0, j1 = 0;
   if (live) {
     j0 = tok_ptr[t];
     j1 = tok_ptr[t + 1];
   }
-  if (live && j1 - j0 <= 64) {
-    // one row per lane, kept in registers
-    const bool mine = j0 + lane < j1;
-    const int r = mine ? tok_row[j0 + lane] : 0;
-    float sv = 0.f, gv = 0.f;
-    int ev = 0;
-    if (mine) {
-      for (int q = 0; q < nparts; ++q) sv += dS_part[(size_t)r * nparts + q];
-      gv = row_gate[r];
-      ev = row_expert[r];
-    }
-    const float tot = wave_sum(gv * sv);
-    if (mine) {
-      const float dz = gv * (sv - tot);
-      dS_row[r] = sv;
-      dz_row[r] = dz;
-      dense[ev] = dz;
-    }
-  } else if (live) {
-    float part = 0.f;
-    for (int j = j0 + lane; j < j1; j += 64) {
-      const int r = tok_row[j];
-      float sv = 0.f;
-      for (int q = 0; q < nparts; ++q) sv += dS_part[(size_t)r * nparts + q];
-      part += row_gate[r] * sv;
-    }
-    const float tot = wave_sum(part);
-    for (int j = j0 + lane; j < j1; j += 64) {
-      const int r = tok_row[j];
-      float sv = 0.f;
-      for (int q = 0; q < nparts; ++q) sv += dS_part[(size_t)r * nparts + q];
-      const float dz = row_gate[r] * (sv - tot);
-      dS_row[r] = sv;
-      dz_row[r] = dz;
-      dense[row_expert[r]] = dz;
-    }
+  // rows sub, sub + 16, ... of the token: the first kept in registers
+  const bool mine = j0 + sub < j1;
+  const int r0 = mine ? tok_row[j0 + sub] : 0;
+  float s0 = 0.f, g0 = 0.f;
+  if (mine) {
+    for (int q = 0; q < nparts; ++q) s0 += dS_part[(size_t)r0 * nparts + q];
+    g0 = row_gate[r0];
   }
-  __syncthreads();
-  if (!live) return;
-  for (int e = lane; e < E; e += 64) dz_dense[(size_t)t * E + e] = Elem<T>::from_f(dense[e]);
-  const int nch = d / V;
-  for (int cb = 0; cb < nch; cb += 64 * CPL) {
-    float acc[CPL][V];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c)
-#pragma unroll
-      for (int i = 0; i < V; ++i) acc[c][i] = 0.f;
-    for (int j = j0; j < j1; j += UNR_DX) {
-      uint4 raw[UNR_DX][CPL], wr[UNR_DX][CPL];
-      float g[UNR_DX];
-#pragma unroll
-      for (int u = 0; u < UNR_DX; ++u) {
-        const bool ok = j + u < j1;
-        const int r = ok ? tok_row[j + u] : 0;
-        const int e = ok ? row_expert[r] : 0;
-        g[u] = ok ? dense[e] : 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int ch = cb + lane + 64 * c;
-          const bool in = ok && ch < nch;
-          raw[u][c] = in ? ld_stream(dXt + (size_t)r * d + ch * V) : make_uint4(0, 0, 0, 0);
-          wr[u][c] = in ? *reinterpret_cast<const uint4*>(w_rT + (size_t)e * d + ch * V) : make_uint4(0, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UNR_DX; ++u)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          float v[V], ww[V];
-          unpack<T>(raw[u][c], v);
-          unpack<T>(wr[u][c], ww);
-#pragma unroll
-          for (int i = 0; i < V; ++i) acc[c][i] = fmaf(g[u], ww[i], acc[c][i] + v[i]);
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int ch = cb + lane + 64 * c;
-      if (ch < nch) store_vec<T>(dX + (size_t)t * d + ch * V, acc[c]);
-    }
+  float part = g0 * s0;
+  for (int j = j0 + sub + 16; j < j1; j += 16) {
+    const int r = tok_row[j];
+    float sv = 0.f;
+    for (int q = 0; q < nparts; ++q) sv += dS_part[(size_t)r * nparts + q];
+    part += row_gate[r] * sv;
   }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, 16);
+  const float tot = part;
+  if (mine) {
+    const float dz = g0 * (s0 - tot);
+    dS_row[r0] = s0;
+    dz_row[r0] = dz;
+    dense[row_expert[r0]] = dz;
+  }
+  for (int j = j0 + sub + 16; j < j1; j += 16) {
+    const int r = tok_row[j];
+    float sv = 0.f;
+    for (int q = 0; q < nparts; ++q) sv += dS_part[(size_t)r * nparts + q];
+    const float dz = row_gate[r] * (sv - tot);
+    dS_row[r] = sv;
+    dz_row[r] = dz;
+    dense[row_expert[r]] = dz;
+  }
+  // the wave's four dense rows are one contiguous block of dz_dense (LDS
+  // accesses of one wave complete in order, so no barrier is needed)
+  const int nt = min(4, Tn - tw);
+  const float* wdense = dzs + wave * 4 * E;
+  for (int i = lane; i < nt * E; i += 64) dz_dense[(size_t)tw * E + i] = Elem<T>::from_f(wdense[i]);
 }
 
 // db[e] = sum of dz over expert e's rows (fixed per-thread split and tree).
@@ -320,25 +280,29 @@ hipError_t launch_aggregate_o(int dtype, const void* Y, const float* row_gate, c
   return hipGetLastError();
 }
 
-template <typename TE, int CPL>
-void agg_dx_launch(const AggDxArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_aggregate_dx<TE, CPL>), dim3((a.T + 3) / 4), dim3(256), (size_t)4 * a.E * sizeof(float), st,
-                     (const TE*)a.dXt, a.dS_part, a.nparts, a.row_gate, a.row_expert, (const TE*)a.w_rT, a.tok_ptr,
-                     a.tok_row, a.T, a.d, a.E, a.dS_row, a.dz_row, (TE*)a.dz_dense, (TE*)a.dX);
-}
-template <typename TE>
-void agg_dx_t(const AggDxArgs& a, hipStream_t st) {
-  switch (agg_cpl(a.d / (16 / (int)sizeof(TE)))) {
-    case 1: agg_dx_launch<TE, 1>(a, st); break;
-    case 2: agg_dx_launch<TE, 2>(a, st); break;
-    case 3: agg_dx_launch<TE, 3>(a, st); break;
-    default: agg_dx_launch<TE, 4>(a, st); break;
-  }
+hipError_t launch_aggregate_dx(int dtype, const void* dXt, const int32_t* tok_ptr, const int32_t* tok_row, int T,
+                               int d, void* dX, hipStream_t st) {
+  return launch_aggregate_o(dtype, dXt, nullptr, tok_ptr, tok_row, T, d, dX, st);
 }
 
-hipError_t launch_aggregate_dx(int dtype, const AggDxArgs& a, hipStream_t st) {
-  if (dtype == DT_BF16) agg_dx_t<bf16_t>(a, st);
-  else agg_dx_t<float>(a, st);
+hipError_t launch_router_dz(int dtype, const RouterDzArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.T + 15) / 16)), block(256);
+  const size_t lds = (size_t)16 * a.E * sizeof(float);  // 64 KB at E = 1024
+  static const hipError_t attr = [] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_router_dz<bf16_t>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 16 * 1024 * 4);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_router_dz<float>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 16 * 1024 * 4);
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(k_router_dz<bf16_t>, grid, block, lds, st, a.dS_part, a.nparts, a.row_gate, a.row_expert,
+                       a.tok_ptr, a.tok_row, a.T, a.E, a.dS_row, a.dz_row, (bf16_t*)a.dz_dense);
+  else
+    hipLaunchKernelGGL(k_router_dz<float>, grid, block, lds, st, a.dS_part, a.nparts, a.row_gate, a.row_expert,
+                       a.tok_ptr, a.tok_row, a.T, a.E, a.dS_row, a.dz_row, (float*)a.dz_dense);
   return hipGetLastError();
 }
 

@@ -22,6 +22,10 @@ struct EpiStore {
     TO* C;
     long long ldc;
     const float* bias;  // per column, may be null
+    // router term of the input-gradient rows, may be null: C[row, col] +=
+    // dz[row] * v[e, col] (v: the transposed router weights, [E][ldc])
+    const float* dz;
+    const TO* v;
   };
   static constexpr int SMEM = 0;
 
@@ -37,6 +41,12 @@ struct EpiStore {
         if (p.bias) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) x[i] += p.bias[c.n0 + ch * 8 + i];
+        }
+        if (p.dz) {
+          const float z = p.dz[c.out_row0 + r];
+          const TO* vr = p.v + (long long)c.e * p.ldc + c.n0 + ch * 8;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = fmaf(z, Elem<TO>::to_f(vr[i]), x[i]);
         }
         st8<TO>(p.C + (c.out_row0 + r) * p.ldc + c.n0 + ch * 8, x);
       }

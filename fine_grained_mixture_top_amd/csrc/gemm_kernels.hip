@@ -257,14 +257,14 @@ hipError_t dh(const GemmDims& g, const void* d_o, const void* w2, const void* H,
 
 template <typename T, int BN>
 hipError_t dxt_t(const GemmDims& g, const void* dH, const void* w1, const int32_t* offsets, void* dXt,
-                 hipStream_t st) {
+                 const float* dz, const void* w_rT, hipStream_t st) {
   constexpr int BM = ROWS<T>;
   const int n = g.n, d = g.d, E = g.E;
   using Epi = EpiStore<T, T, BM, BN>;
   GemmShape s{offsets, E, 0, d, 2 * n, d, 1};
   Operand a{dH, nullptr, 0, 2 * n};
   Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};  // W1[e] is [d][2n]: row i holds k = 0..2n-1
-  typename Epi::Params ep{reinterpret_cast<T*>(dXt), d, nullptr};
+  typename Epi::Params ep{reinterpret_cast<T*>(dXt), d, nullptr, dz, reinterpret_cast<const T*>(w_rT)};
   return run_gemm<T, BM, BN, false, B_NK, false, Epi>(s, a, b, ep, row_tiles_bound(g.cap, E, BM) * (d / BN), st);
 }
 bool dxt_g4(const GemmDims& g) {
@@ -273,21 +273,22 @@ bool dxt_g4(const GemmDims& g) {
 }
 template <typename T>
 hipError_t dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t* offsets, void* dXt,
-               hipStream_t st) {
+               const float* dz, const void* w_rT, hipStream_t st) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (dxt_g4(g)) {
       const int n = g.n, d = g.d, E = g.E;
-      using Epi = g4::G4Store;
+      using Epi = g4::G4StoreRouter;
       GemmShape s{offsets, E, 0, d, 2 * n, d, 1};
       Operand a{dH, nullptr, 0, 2 * n};
       Operand b{w1, nullptr, (long long)d * 2 * n, 2 * n};
-      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dXt), d};
+      typename Epi::Params ep{reinterpret_cast<bf16_t*>(dXt), d, dz, reinterpret_cast<const bf16_t*>(w_rT),
+                              (uint32_t)(g.cap * 4), (uint32_t)((size_t)E * d * 2)};
       return run_row256<false, false, Epi>(s, a, b, g.cap * 2 * n * 2, (size_t)d * 2 * n * 2, ep,
                                            row_tiles_bound(g.cap, E, g4::BM) * (d / g4::BN), st);
     }
   }
-  if (g.d % Cfg<T>::BIG == 0) return dxt_t<T, Cfg<T>::BIG>(g, dH, w1, offsets, dXt, st);
-  return dxt_t<T, Cfg<T>::SMALL>(g, dH, w1, offsets, dXt, st);
+  if (g.d % Cfg<T>::BIG == 0) return dxt_t<T, Cfg<T>::BIG>(g, dH, w1, offsets, dXt, dz, w_rT, st);
+  return dxt_t<T, Cfg<T>::SMALL>(g, dH, w1, offsets, dXt, dz, w_rT, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -695,8 +696,8 @@ hipError_t launch_dh(const GemmDims& g, const void* d_o, const void* w2, const v
   return MOE_GDISPATCH(g, dh, d_o, w2, H, row_token, row_gate, offsets, dH, As, dS_part, st);
 }
 hipError_t launch_dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t* offsets, void* dXt,
-                      hipStream_t st) {
-  return MOE_GDISPATCH(g, dxt, dH, w1, offsets, dXt, st);
+                      const float* dz, const void* w_rT, hipStream_t st) {
+  return MOE_GDISPATCH(g, dxt, dH, w1, offsets, dXt, dz, w_rT, st);
 }
 hipError_t launch_dw1(const GemmDims& g, const void* x, const void* dH, const int32_t* row_token,
                       const int32_t* offsets, void* dW1, void* ws, hipStream_t st) {

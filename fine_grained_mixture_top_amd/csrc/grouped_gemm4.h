@@ -229,6 +229,16 @@ __device__ __forceinline__ void mma(f32x16_v (&acc)[2][4], const Frags<AMN, BMN>
 template <class E, class = void> struct is_wave_epi : std::false_type {};
 template <class E> struct is_wave_epi<E, std::void_t<decltype(E::WAVE)>> : std::bool_constant<E::WAVE> {};
 
+// A wave epilogue may stage per-tile operands in LDS: PRE_BYTES per tile, in
+// two slots that alternate between consecutive tiles of a workgroup.
+// pre_issue (all waves) issues buffer -> LDS loads into the tile's slot just
+// before the tile's first stage, so the kernel's wait for that stage covers
+// them, and the data are in LDS long before the epilogue reads them; run
+// then takes the slot as a fifth argument.
+template <class E, class = void> struct pre_bytes : std::integral_constant<int, 0> {};
+template <class E>
+struct pre_bytes<E, std::void_t<decltype(E::PRE_BYTES)>> : std::integral_constant<int, E::PRE_BYTES> {};
+
 // 16-byte store of an output that is read again only by a later kernel:
 // non-temporal, so it does not push operand lines out of the L2
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -273,6 +283,79 @@ struct G4Store {
     }
   }
 };
+
+// Input-gradient rows with the router term: C[row, col] = acc + dz[row] *
+// v[e, col] as bf16, dz the row's score gradient (fp32, one per routed row)
+// and v the expert's row of the transposed router weights ([E][ldc] bf16).
+// The tile's 256 dz values and 256 v columns are staged in LDS with the
+// tile's first loads (rows past the buffer read as zero), and the rank-1
+// term starts the accumulators: one 32 x 32 x 16 bf16 MFMA per block, k = 0
+// and 1 carrying v against dz split into bf16 hi + lo parts (dz to about
+// 2^-17 relative), the other k zero.  In the MFMA pipe it costs 8 of the
+// tile's hundreds of MFMAs, where a per-element multiply-add in the epilogue
+// would stall the wave after its last MFMA.
+struct G4StoreRouter {
+  static constexpr bool WAVE = true;
+  static constexpr bool INIT = true;
+  static constexpr int PRE_BYTES = 256 * 4 + 256 * 2;
+  struct Params {
+    bf16_t* C;
+    long long ldc;
+    const float* dz;
+    const bf16_t* v;
+    uint32_t dz_bytes, v_bytes;
+  };
+  __device__ __forceinline__ static void pre_issue(const Params& p, const TileCtx& c, char* slot, int w, int lane) {
+    if (w < 4) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(p.dz, p.dz_bytes);
+      const uint32_t o = ((uint32_t)c.out_row0 + (uint32_t)(64 * w + lane)) * 4u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + 256 * w), 4, o, 0, 0, 0);
+    } else if (w < 6) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(p.v, p.v_bytes);
+      const uint32_t o = ((uint32_t)c.e * (uint32_t)p.ldc + (uint32_t)c.n0) * 2u + (uint32_t)(256 * (w - 4) + 4 * lane);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + 1024 + 256 * (w - 4)), 4, o, 0, 0, 0);
+    }
+  }
+  // accumulators = dz (x) v over the wave's 128 x 64 block; the slot's data
+  // must be visible (after the kernel's wait for the tile's first stage)
+  __device__ __forceinline__ static void init(const Params&, const TileCtx& c, f32x16_v (&acc)[2][4],
+                                              const char* slot) {
+    const int l32 = c.lane & 31;
+    const bool k01 = c.lane < 32;  // lanes holding k = 0..7
+    const float* zs = reinterpret_cast<const float*>(slot);
+    const bf16_t* vs = reinterpret_cast<const bf16_t*>(slot + 1024);
+    bf16x8_v nf[2], mf[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint16_t v = k01 ? vs[c.wn * 64 + 32 * i + l32] : (uint16_t)0;
+      v8i16_t x = {(short)v, (short)v, 0, 0, 0, 0, 0, 0};
+      nf[i] = __builtin_bit_cast(bf16x8_v, x);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float z = k01 ? zs[c.wm * 128 + 32 * j + l32] : 0.f;
+      const uint16_t hi = f2bf(z);
+      const uint16_t lo = f2bf(z - __uint_as_float((uint32_t)hi << 16));
+      v8i16_t x = {(short)hi, (short)lo, 0, 0, 0, 0, 0, 0};
+      mf[j] = __builtin_bit_cast(bf16x8_v, x);
+    }
+    f32x16_v zero;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(nf[i], mf[j], zero, 0, 0, 0);
+  }
+  __device__ __forceinline__ static void run(const Params& p, const TileCtx& c, const f32x16_v (&acc)[2][4],
+                                             char* area, const char*) {
+    G4Store::run(G4Store::Params{p.C, p.ldc}, c, acc, area);
+  }
+};
+
+// Epilogues whose init hook starts the accumulators (else they start at zero)
+template <class E, class = void> struct has_init : std::false_type {};
+template <class E> struct has_init<E, std::void_t<decltype(E::INIT)>> : std::bool_constant<E::INIT> {};
 
 // Weight-gradient store: tiles of an expert stored whole go to C as bf16
 // (G4Store); tiles of one chunk of a split expert write their fp32 partial
@@ -392,6 +475,8 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   // XCD-grouped id, so consecutive tiles share an XCD's L2 either way.
   __shared__ int tprefix[WGT ? 1 : MAX_E + 1];
   __shared__ __attribute__((aligned(256))) char touch_sink[WGT ? 256 : 1];  // written by the row touches, never read
+  constexpr int PREB = pre_bytes<Epi>::value;
+  __shared__ __attribute__((aligned(256))) char pre_lds[PREB > 0 ? 2 * PREB : 16];  // wave epilogues' tile operands
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -575,6 +660,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   if (t >= 0) {
     decode(t, c);
     setup(c);
+    if constexpr (PREB > 0) Epi::pre_issue(ep, c, pre_lds, w, lane);
     prime(c);
   }
   while (t >= 0) {
@@ -603,6 +689,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
         else wait_vm<0>();
       }
       __syncthreads();
+      if constexpr (has_init<Epi>::value) Epi::init(ep, c, acc, pre_lds + (r & 1) * PREB);
       Frags<AMN, BMN> f0, f1;
       f0.read(smem, 0, lane, wm, wn);
       // one k step: MFMAs of sub-step 0 while sub-step 1's fragments load,
@@ -649,9 +736,12 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     if (tn >= 0) {
       decode(tn, cn);
       setup(cn);
+      if constexpr (PREB > 0) Epi::pre_issue(ep, cn, pre_lds + ((r + 1) & 1) * PREB, w, lane);
       prime(cn);
     }
-    if constexpr (is_wave_epi<Epi>::value) {
+    if constexpr (PREB > 0) {
+      Epi::run(ep, c, acc, smem + WE_OFF + w * WAVE_LDS, pre_lds + (r & 1) * PREB);
+    } else if constexpr (is_wave_epi<Epi>::value) {
       Epi::run(ep, c, acc, smem + WE_OFF + w * WAVE_LDS);
     } else {
     // eight passes of 32 rows: pass p holds block j = p % 4 of the waves of

@@ -218,6 +218,8 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int tprefix[MAX_E + 1];
   __shared__ __attribute__((aligned(256))) char touch_sink[256];  // written by the B-line touches, never read
+  constexpr int PREB = g4::pre_bytes<Epi>::value;
+  __shared__ __attribute__((aligned(256))) char pre_lds[PREB > 0 ? 2 * PREB : 16];  // wave epilogues' tile operands
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -373,6 +375,7 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   if (t >= 0) {
     decode(t, c);
     setup(c);
+    if constexpr (PREB > 0) Epi::pre_issue(ep, c, pre_lds, w, lane);
     issue(0);
   }
   while (t >= 0) {
@@ -399,6 +402,7 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       else wait_vm<0>();
     }
     __syncthreads();
+    if constexpr (g4::has_init<Epi>::value) Epi::init(ep, c, acc, pre_lds + (r & 1) * PREB);
     Frags<BMN> f0, f1;
     f0.read(smem, 0, lane, wm, wn);
     for (int k = 0; k < nk; ++k) {
@@ -429,9 +433,12 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     if (tn >= 0) {
       decode(tn, cn);
       setup(cn);
+      if constexpr (PREB > 0) Epi::pre_issue(ep, cn, pre_lds + ((r + 1) & 1) * PREB, w, lane);
       issue(0);
     }
-    if constexpr (g4::is_wave_epi<Epi>::value) {
+    if constexpr (PREB > 0) {
+      Epi::run(ep, c, acc, smem + WE_OFF + w * g4::WAVE_LDS, pre_lds + (r & 1) * PREB);
+    } else if constexpr (g4::is_wave_epi<Epi>::value) {
       Epi::run(ep, c, acc, smem + WE_OFF + w * g4::WAVE_LDS);
     } else if constexpr (has_prefetch<Epi>::value) {
       // eight passes of 32 rows, each pass's global operands loaded one ahead

@@ -137,6 +137,8 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
                 "wave-local epilogues or the pass epilogue with prefetched operands");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int tprefix[MAX_E + 1];
+  constexpr int PREB = g4::pre_bytes<Epi>::value;
+  __shared__ __attribute__((aligned(256))) char pre_lds[PREB > 0 ? 2 * PREB : 16];  // wave epilogues' tile operands
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -248,6 +250,7 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
   if (t >= 0) {
     decode(t, c);
     setup(c);
+    if constexpr (PREB > 0) Epi::pre_issue(ep, c, pre_lds, w, lane);
     issue_ascale(c);
     issue(0);
   }
@@ -271,6 +274,7 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
       wait_vm<0>();
     }
     __syncthreads();
+    if constexpr (g4::has_init<Epi>::value) Epi::init(ep, c, acc, pre_lds + (r & 1) * PREB);
     uint32_t asc[4], bsc[2];
     read_scales(0, asc, bsc);
     // one 64-k step per iteration, two per stage; after a stage's second
@@ -294,10 +298,13 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
     if (tn >= 0) {
       decode(tn, cn);
       setup(cn);
+      if constexpr (PREB > 0) Epi::pre_issue(ep, cn, pre_lds + ((r + 1) & 1) * PREB, w, lane);
       issue_ascale(cn);
       issue(0);
     }
-    if constexpr (g4::is_wave_epi<Epi>::value) {
+    if constexpr (PREB > 0) {
+      Epi::run(ep, c, acc, smem + WE_OFF + w * g4::WAVE_LDS, pre_lds + (r & 1) * PREB);
+    } else if constexpr (g4::is_wave_epi<Epi>::value) {
       Epi::run(ep, c, acc, smem + WE_OFF + w * g4::WAVE_LDS);
     } else {
       // eight passes of 32 rows (pass p holds block j = p % 4 of the waves of

@@ -36,8 +36,10 @@ hipError_t launch_down(const GemmDims& g, const void* A, const void* w2, const i
 hipError_t launch_dh(const GemmDims& g, const void* d_o, const void* w2, const void* H,
                      const int32_t* row_token, const float* row_gate, const int32_t* offsets, void* dH,
                      void* As, float* dS_part, hipStream_t st);
+// dXt = dH W1^T plus, per row r, the router term dz[r] * w_rT[e_r] ([E][d],
+// the transposed router weights)
 hipError_t launch_dxt(const GemmDims& g, const void* dH, const void* w1, const int32_t* offsets, void* dXt,
-                      hipStream_t st);
+                      const float* dz, const void* w_rT, hipStream_t st);
 // dW1 / dW2: `ws` (wgt_ws_bytes(g) bytes, 256-byte aligned; may be null when
 // that is 0) holds the tile plan and the fp32 partial sums of experts whose
 // reduction is split.
@@ -67,9 +69,11 @@ bool mx_bwd_shape_ok(const GemmDims& g);
 // is fixed, whatever dh_block(g) picks for the bf16 dH kernel)
 int dh_mx_partials(const GemmDims& g);
 // dXt = dH W1^T on MXFP8 operands: dH codes [cap][2n] and scales [cap][2n/32],
-// W1 codes [E][d][2n] (rows along 2n) and scales [E][2n/128][d][4]
+// W1 codes [E][d][2n] (rows along 2n) and scales [E][2n/128][d][4]; the
+// router term as launch_dxt
 hipError_t launch_dxt_mx(const GemmDims& g, const uint8_t* dhq, const uint8_t* dhs, const uint8_t* w1q,
-                         const uint8_t* w1s, const int32_t* offsets, void* dXt, hipStream_t st);
+                         const uint8_t* w1s, const int32_t* offsets, void* dXt, const float* dz, const void* w_rT,
+                         hipStream_t st);
 // dA' = dO W2^T on MXFP8 operands with the dH epilogue (as launch_dh): dO
 // codes [T][d] and scales [T][d/32] gathered per row, W2 codes [E][n][d]
 // (rows along d) and scales [E][d/128][n][4]; dS partials: n / 256 per row
@@ -151,21 +155,21 @@ hipError_t launch_bias_grad(const float* dz_row, const int32_t* offsets, int E, 
                             hipStream_t st);
 hipError_t launch_transpose(int dtype, const void* src, int rows, int cols, void* dst,
                             hipStream_t st);
-// dX aggregation with the router backward folded in (see aggregate_kernels.hip)
-struct AggDxArgs {
-  const void* dXt;         // [cap][d]
+// router backward per token (see aggregate_kernels.hip)
+struct RouterDzArgs {
   const float* dS_part;    // [cap][nparts] dH-epilogue partials of dS
   int nparts;
   const float* row_gate;   // [cap]
   const int32_t* row_expert;
-  const void* w_rT;        // [E][d]
   const int32_t* tok_ptr;  // [T+1]
   const int32_t* tok_row;  // [cap]
-  int T, d, E;
+  int T, E;
   float* dS_row;           // [cap] out
   float* dz_row;           // [cap] out
   void* dz_dense;          // [T][E] out (dtype)
-  void* dX;                // [T][d] out
 };
-hipError_t launch_aggregate_dx(int dtype, const AggDxArgs& a, hipStream_t st);
+hipError_t launch_router_dz(int dtype, const RouterDzArgs& a, hipStream_t st);
+// dX[t] = sum over token t's rows of dXt[r] (rows with their router term)
+hipError_t launch_aggregate_dx(int dtype, const void* dXt, const int32_t* tok_ptr, const int32_t* tok_row, int T,
+                               int d, void* dX, hipStream_t st);
 }  // namespace moe

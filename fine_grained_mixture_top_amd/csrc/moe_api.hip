@@ -420,25 +420,29 @@ int bwd_impl(const moe_desc* desc, const void* x, const void* w_r, const void* w
   } else {
     MOE_TRY(MOE_K_DH, launch_dh(g, d_o, w2, h_cache, R.row_token, R.row_gate, R.offsets, dH, As, dS_part, st));
   }
-  // activation gradient: dXt = dH W1^T, then dX = sum of dXt + dz W_r^T, with
-  // the router backward (dS -> dz per row and dense) folded into the
-  // aggregation; then dW_r = X^T dz
+  // router backward (dS -> dz per row and dense), then the activation
+  // gradient: dXt = dH W1^T with each row's router term dz_r W_r^T[e_r] added
+  // in the GEMM's epilogue, dX = the sum of a token's dXt rows; then
+  // dW_r = X^T dz
   MOE_TRY(MOE_K_WR_T, launch_transpose(D.dtype, w_r, D.d, D.E, w_rT, st));
+  {
+    // the dS partial count is that of the dH kernel actually launched
+    const int nparts = mx ? dh_mx_partials(g) : dh_partials(g);
+    const RouterDzArgs ra{dS_part, nparts, R.row_gate, R.row_expert, R.tok_ptr, R.tok_row, D.T, D.E,
+                          dS_row,  dz_row, dz_dense};
+    MOE_TRY(MOE_K_ROUTER_GRAD, launch_router_dz(D.dtype, ra, st));
+  }
   if (mx) {
     // dH and W1 quantized along 2n (dH from the bf16 values just written)
     uint8_t *dhq = (uint8_t*)(w + L.off[10]), *dhs = (uint8_t*)(w + L.off[11]);
     uint8_t *w1q = (uint8_t*)(w + L.off[12]), *w1s = (uint8_t*)(w + L.off[13]);
     MOE_TRY(MOE_K_MX_QUANT_ROWS, launch_mx_quant_rows(dH, 2 * D.n, (long long)cap, R.offsets + D.E, dhq, dhs, st));
     MOE_TRY(MOE_K_MX_QUANT_W, launch_mx_quant_rows(w1, 2 * D.n, (long long)D.E * D.d, nullptr, w1q, w1s, st, D.d));
-    MOE_TRY(MOE_K_DXT_MX, launch_dxt_mx(g, dhq, dhs, w1q, w1s, R.offsets, dXt, st));
+    MOE_TRY(MOE_K_DXT_MX, launch_dxt_mx(g, dhq, dhs, w1q, w1s, R.offsets, dXt, dz_row, w_rT, st));
   } else {
-    MOE_TRY(MOE_K_DXT, launch_dxt(g, dH, w1, R.offsets, dXt, st));
+    MOE_TRY(MOE_K_DXT, launch_dxt(g, dH, w1, R.offsets, dXt, dz_row, w_rT, st));
   }
-  // the dS partial count is that of the dH kernel actually launched
-  const int nparts = mx ? dh_mx_partials(g) : dh_partials(g);
-  const AggDxArgs ax{dXt, dS_part, nparts, R.row_gate, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T,
-                     D.d, D.E,     dS_row, dz_row,     dz_dense,     dx};
-  MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, ax, st));
+  MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, dXt, R.tok_ptr, R.tok_row, D.T, D.d, dx, st));
   MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, (float*)(w + L.off[8]), st));
   // weight gradients
   if (mx && (D.flags & MOE_FLAG_MXFP8_WGRAD)) {
@@ -592,10 +596,11 @@ int moe_bwd_unfused(const moe_desc* desc, const void* x, const void* w_r, const 
   MOE_TRY(MOE_K_SWIGLU_BWD, launch_swiglu_bwd(D.dtype, dAp, H, A, R.row_gate, D.n, P, cap, dH, As, st));
   // input and router gradients as in the fused layer, from the one dS part
   MOE_TRY(MOE_K_WR_T, launch_transpose(D.dtype, w_r, D.d, D.E, w_rT, st));
-  MOE_TRY(MOE_K_DXT, launch_dxt(g, dH, w1, R.offsets, dXt, st));
-  const AggDxArgs ax{dXt, dS_dot, 1, R.row_gate, R.row_expert, w_rT, R.tok_ptr, R.tok_row, D.T,
-                     D.d, D.E,    dS_row, dz_row, dz_dense,   dx};
-  MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, ax, st));
+  const RouterDzArgs ra{dS_dot, 1, R.row_gate, R.row_expert, R.tok_ptr, R.tok_row, D.T, D.E,
+                        dS_row, dz_row, dz_dense};
+  MOE_TRY(MOE_K_ROUTER_GRAD, launch_router_dz(D.dtype, ra, st));
+  MOE_TRY(MOE_K_DXT, launch_dxt(g, dH, w1, R.offsets, dXt, dz_row, w_rT, st));
+  MOE_TRY(MOE_K_AGG_DX, launch_aggregate_dx(D.dtype, dXt, R.tok_ptr, R.tok_row, D.T, D.d, dx, st));
   MOE_TRY(MOE_K_DWR, launch_dwr(D.dtype, x, dz_dense, D.T, D.d, D.E, dw_r, (float*)(w + L.off[8]), st));
   // weight gradients from the cached, already gathered rows
   void* wws = wgt_ws_bytes(g) ? (void*)(w + L.off[9]) : nullptr;

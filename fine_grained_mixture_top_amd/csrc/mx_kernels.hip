@@ -302,13 +302,15 @@ hipError_t launch_up_mx(const GemmDims& g, const uint8_t* xq, const uint8_t* xs,
 }
 
 hipError_t launch_dxt_mx(const GemmDims& g, const uint8_t* dhq, const uint8_t* dhs, const uint8_t* w1q,
-                         const uint8_t* w1s, const int32_t* offsets, void* dXt, hipStream_t st) {
+                         const uint8_t* w1s, const int32_t* offsets, void* dXt, const float* dz, const void* w_rT,
+                         hipStream_t st) {
   const int n = g.n, d = g.d, E = g.E;
-  using Epi = g4::G4Store;
+  using Epi = g4::G4StoreRouter;
   GemmShape s{offsets, E, 0, d, 2 * n, d, 1};
   Operand a{dhq, nullptr, 0, 2 * n};
   Operand b{w1q, nullptr, (long long)d * 2 * n, 2 * n};
-  typename Epi::Params ep{reinterpret_cast<bf16_t*>(dXt), d};
+  typename Epi::Params ep{reinterpret_cast<bf16_t*>(dXt), d, dz, reinterpret_cast<const bf16_t*>(w_rT),
+                          (uint32_t)(g.cap * 4), (uint32_t)((size_t)E * d * 2)};
   return run_gemm_mx<false, Epi>(s, a, b, dhs, reinterpret_cast<const uint32_t*>(w1s), g.cap * 2 * n,
                                  (size_t)d * 2 * n, g.cap * (2 * n / 32), (size_t)(2 * n / 128) * d * 4, ep,
                                  tiles_bound(g.cap, E) * (d / gmx::BN), st);

@@ -82,10 +82,12 @@ def classify(name: str, wgt_seen: dict) -> str:
             wgt_seen["n"] += 1
             return "dw1" if k == 0 else "dw2"
         return "down" if bl == "1" else "dxt"
-    if "k_aggregate_o" in name:
-        return "agg_o"
-    if "k_aggregate_dx" in name:
-        return "agg_dx"
+    if "k_aggregate_o" in name:  # O (forward) and dX (backward) share the kernel: O comes first
+        k = wgt_seen.get("agg", 0)
+        wgt_seen["agg"] = k + 1
+        return "agg_o" if k % 2 == 0 else "agg_dx"
+    if "k_router_dz" in name:
+        return "router_grad"
     if "copyBuffer" in name or "elementwise_kernel" in name and "copy" in name.lower():
         return "copy"
     return None

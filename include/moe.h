@@ -88,11 +88,11 @@ extern "C" {
 #define MOE_K_DOWN          3   /* K2: A w2 -> Y                                   */
 #define MOE_K_AGG_O         4   /* K3: O = sum of gate * Y                         */
 #define MOE_K_DH            5   /* K4: dO w2^T with the dH epilogue -> dH, A_s, dS */
-#define MOE_K_ROUTER_GRAD   6   /* reserved: dS -> dz now runs inside MOE_K_AGG_DX */
+#define MOE_K_ROUTER_GRAD   6   /* dS partials -> dS, dz per row and dense dz      */
 #define MOE_K_DWR           7   /* dw_r = x^T dz                                   */
-#define MOE_K_WR_T          8   /* w_r transposed for the dX aggregation           */
-#define MOE_K_DXT           9   /* K5: dH w1^T -> dXt                              */
-#define MOE_K_AGG_DX       10   /* K6: dS -> dz, dX = sum of dXt + dz w_r^T        */
+#define MOE_K_WR_T          8   /* w_r transposed for the dXt router term          */
+#define MOE_K_DXT           9   /* K5: dH w1^T + dz w_r^T per row -> dXt           */
+#define MOE_K_AGG_DX       10   /* K6: dX = sum of a token's dXt rows              */
 #define MOE_K_DW1          11   /* K7: dw1 = x_g^T dH                              */
 #define MOE_K_DW2          12   /* K8: dw2 = A_s^T dO_g                            */
 #define MOE_K_DB           13   /* db = per-expert sum of dz                       */
@@ -129,7 +129,8 @@ extern "C" {
 #define MOE_ITEM_A        1  /* fwd: SwiGLU output A [cap, n] (dtype)             */
 #define MOE_ITEM_DH       2  /* bwd: dH [cap, 2n] (dtype)                         */
 #define MOE_ITEM_AS       3  /* bwd: gate-scaled A [cap, n] (dtype)               */
-#define MOE_ITEM_DXT      4  /* bwd: per-row input gradient dXt [cap, d] (dtype)  */
+#define MOE_ITEM_DXT      4  /* bwd: per-row input gradient with its router term,
+                                dXt_r + dz_r w_r[:, e_r]^T [cap, d] (dtype)    */
 #define MOE_ITEM_DS       5  /* bwd: per-row score gradient dS [cap] (fp32)       */
 #define MOE_ITEM_DZ       6  /* bwd: per-row router-logit gradient dz [cap] (fp32) */
 /* MXFP8 forward workspace (E4M3 codes and E8M0 scale codes are uint8) */

@@ -106,7 +106,16 @@ def oracle_layer(w: I.Workload, x, w_r, w1, w2, d_o, bias=None, round_mode=0, ro
     o = O.layer(x, w_r, w1, w2, d_o, w.dtype, w.K, bias=bias, tile=tile, round_mode=round_mode,
                 round_seed=round_seed, scores=scores)
     o["dWr_scale"] = router_column_scale(o, np.linalg.norm(O.to_f64(x, w.dtype), axis=1), w.E)
+    o["dXt_row"] = dxt_with_router_term(o["dXt"], o["dz"][o["row_token"], o["row_expert"]],
+                                        O.to_f64(w_r, w.dtype), o["row_expert"])
     return o
+
+
+def dxt_with_router_term(dXt, dz_rows, wr64, row_expert):
+    """What the library keeps per routed row as its input gradient
+    (MOE_ITEM_DXT): dXt_r plus the row's router term dz_r W_r[:, e_r]^T, so
+    that dX_t is the plain sum of its rows."""
+    return dXt + np.asarray(dz_rows)[:, None] * np.asarray(wr64)[:, np.asarray(row_expert)].T
 
 
 def router_column_scale(o: dict, x_norm: np.ndarray, E: int) -> np.ndarray:
@@ -174,7 +183,7 @@ def compare_layer(g: dict, o: dict, dtype: str, skip=()):
     expert cannot hide in a large tensor.  Returns the errors (asserts)."""
     t = tol(dtype)
     errs, rows = {}, {}
-    pairs = dict(O="O", H="H", A="A", Y="Y", dH="dH", dXt="dXt", dS="dS", dX="dX", dWr="dWr",
+    pairs = dict(O="O", H="H", A="A", Y="Y", dH="dH", dXt="dXt_row", dS="dS", dX="dX", dWr="dWr",
                  dW1="dW1", dW2="dW2", db="db")
     for gk, ok in pairs.items():
         if gk in skip:

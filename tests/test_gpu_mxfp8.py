@@ -12,7 +12,7 @@ from fine_grained_mixture_top_amd import inputs as I
 from oracle import moe_oracle as O
 from oracle import mx_oracle as M
 
-from gpu_util import assert_routing_equal, dev, host64, host_int, relF, routing_host
+from gpu_util import assert_routing_equal, dev, dxt_with_router_term, host64, host_int, relF, routing_host
 
 pytestmark = pytest.mark.gpu
 
@@ -213,7 +213,8 @@ def test_mxfp8_backward_matches_oracle(w, mode, tile, flags):
     assert np.array_equal(blocked_to_rows(u8(L, B.MOE_ITEM_MX_W1RS, E * 2 * n // 32 * d), E, 2 * n, d), o["w1rs"])
     ref = M.dxt_from_codes(dhq, dhs, o["w1rq"], o["w1rs"], rt, o["dz"], wr64)
     dXt_gpu = host64(L.ws_view(B.MOE_ITEM_DXT, P * d, torch.bfloat16, mx_bwd=True)).reshape(P, d)
-    errs = dict(dH=relF(dH_gpu, o["dH"]), dXt=relF(dXt_gpu, ref["dXt"]), dX=relF(host64(L.dx), ref["dX"]),
+    dXt_ref = dxt_with_router_term(ref["dXt"], o["dz"][rt["row_token"], rt["row_expert"]], wr64, rt["row_expert"])
+    errs = dict(dH=relF(dH_gpu, o["dH"]), dXt=relF(dXt_gpu, dXt_ref), dX=relF(host64(L.dx), ref["dX"]),
                 dW1=relF(host64(L.dw1), o["dW1"]), dW2=relF(host64(L.dw2), o["dW2"]),
                 dWr=relF(host64(L.dw_r), o["dWr"]), dS=relF(host64(L.ds[:P]), o["dS"]))
     e2e = relF(host64(L.dx), o["dX"])
@@ -244,6 +245,8 @@ def test_mxfp8_backward_full_size_expert_sample(name):
     w1q_all = L.ws_view(B.MOE_ITEM_MX_W1RQ, E * d * 2 * n, torch.uint8).view(E, d, 2 * n)
     w1s_all = blocked_to_rows(u8(L, B.MOE_ITEM_MX_W1RS, E * 2 * n // 32 * d), E, 2 * n, d)
     dXt_all = L.ws_view(B.MOE_ITEM_DXT, P * d, torch.bfloat16, mx_bwd=True).view(P, d)
+    dz_all = L.ws_view(B.MOE_ITEM_DZ, P, torch.float32, mx_bwd=True)
+    wr64 = O.to_f64(a["w_r"], "bf16")
     for e in np.random.default_rng(7).choice(E, 2, replace=False):
         s0, s1 = int(off[e]), int(off[e + 1])
         dH = host64(dH_all[s0:s1])
@@ -251,7 +254,9 @@ def test_mxfp8_backward_full_size_expert_sample(name):
         assert np.array_equal(dhq_all[s0:s1].cpu().numpy(), dhq)
         w1q, w1s = M.quantize(O.to_f64(a["w1"][e], "bf16"))
         assert np.array_equal(w1q_all[e].cpu().numpy(), w1q) and np.array_equal(w1s_all[e], w1s)
+        # plus each row's router term, from the GPU's dz (checked on whole tokens elsewhere)
         ref = M.dequantize(dhq, dhs) @ M.dequantize(w1q, w1s).T
+        ref = dxt_with_router_term(ref, host64(dz_all[s0:s1]), wr64, np.full(s1 - s0, e))
         err = relF(host64(dXt_all[s0:s1]), ref)
         print(name, int(e), s1 - s0, f"dXt {err:.2e}")
         assert err <= TOL

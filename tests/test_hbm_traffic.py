@@ -24,11 +24,12 @@ STEP = [  # one fg7b_bf16 layer step, in launch order, with the expected row
      "int const*, int const*, int, int, unsigned short*)", "agg_o"),
     ("void moe::g5::grouped_gemm5_kernel<false, false, moe::g5::G5DH>(moe::GemmShape, moe::Operand, "
      "moe::Operand, unsigned int, unsigned int, moe::g5::G5DH::Params)", "dh"),
-    ("void moe::g5::grouped_gemm5_kernel<false, false, moe::g4::G4Store>(moe::GemmShape, moe::Operand, "
-     "moe::Operand, unsigned int, unsigned int, moe::g4::G4Store::Params)", "dxt"),
-    ("void moe::(anonymous namespace)::k_aggregate_dx<unsigned short, 3>(unsigned short const*, float const*, "
-     "int, float const*, int const*, unsigned short const*, int const*, int const*, int, int, int, float*)",
-     "agg_dx"),
+    ("void moe::(anonymous namespace)::k_router_dz<unsigned short>(float const*, int, float const*, int const*, "
+     "int const*, int const*, int, int, float*, float*, unsigned short*)", "router_grad"),
+    ("void moe::g5::grouped_gemm5_kernel<false, false, moe::g4::G4StoreRouter>(moe::GemmShape, moe::Operand, "
+     "moe::Operand, unsigned int, unsigned int, moe::g4::G4StoreRouter::Params)", "dxt"),
+    ("void moe::(anonymous namespace)::k_aggregate_o<unsigned short, 3>(unsigned short const*, float const*, "
+     "int const*, int const*, int, int, unsigned short*)", "agg_dx"),
     ("void moe::grouped_gemm_kernel<unsigned short, 128, 64, true, 1, false, moe::EpiStore<unsigned short, "
      "float, 128, 64, 256>, 1>(moe::GemmShape, moe::Operand, moe::Operand, moe::EpiStore<unsigned short, "
      "float, 128, 64, 256>::Params)", "dwr"),

@@ -22,7 +22,8 @@ def case():
 def noisy(o, rel, rng):
     """The oracle's outputs with independent relative noise of size `rel`."""
     keys = ("O", "H", "A", "Y", "dH", "dXt", "dS", "dX", "dWr", "dW1", "dW2", "db")
-    return {k: o[k] * (1 + rel * rng.standard_normal(o[k].shape)) for k in keys}
+    src = dict(dXt="dXt_row")
+    return {k: o[src.get(k, k)] * (1 + rel * rng.standard_normal(o[src.get(k, k)].shape)) for k in keys}
 
 
 def test_rounding_noise_passes(case):
