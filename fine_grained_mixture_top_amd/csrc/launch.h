@@ -143,7 +143,10 @@ struct RouteScratch {
   int32_t* rowmap;     // [E][pitch] row of (e, t)
   int32_t* tokcnt;     // [T] rows per token (token rounding only)
   float* tstat;        // [2][T] set-softmax max and sum per token (token rounding only)
+  int32_t* chunk_cnt;  // [E][route_chunks(T)] member counts per chunk of 4096 tokens
 };
+// chunks of 4096 tokens of the membership rows
+int route_chunks(int T);
 hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int T, int E, int K,
                                int tile, int round_mode, uint64_t round_seed, hipStream_t st);
 

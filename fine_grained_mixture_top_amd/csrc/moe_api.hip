@@ -64,6 +64,7 @@ Layout route_layout(const moe_desc* d) {
   L.off[2] = o; o = up(o + TEp * 4);                              // rowmap
   L.off[3] = o; o = up(o + tr * (size_t)d->T * 4);                // tokcnt
   L.off[4] = o; o = up(o + tr * (size_t)d->T * 8);                // tstat
+  L.off[5] = o; o = up(o + (size_t)d->E * route_chunks(d->T) * 4); // chunk counts
   L.total = o;
   return L;
 }
@@ -324,7 +325,8 @@ int route_impl(const moe_desc* desc, const void* x, const void* w_r, const float
                routing->row_expert, routing->row_gate,  routing->tok_ptr,   routing->tok_row};
   const bool tr = desc->round_mode != 0;
   RouteScratch sc{(uint8_t*)(w + L.off[0]), tr ? (float*)(w + L.off[1]) : nullptr, (int32_t*)(w + L.off[2]),
-                  tr ? (int32_t*)(w + L.off[3]) : nullptr, tr ? (float*)(w + L.off[4]) : nullptr};
+                  tr ? (int32_t*)(w + L.off[3]) : nullptr, tr ? (float*)(w + L.off[4]) : nullptr,
+                  (int32_t*)(w + L.off[5])};
   MOE_TRY(MOE_K_ROUTE_SELECT, launch_route_select(rb, sc, desc->T, desc->E, desc->K, desc->tile,
                                                   desc->round_mode, desc->round_seed, st));
   return MOE_OK;

@@ -171,26 +171,32 @@ k_topk(const float* __restrict__ scores, int T, int E, int K, int mpitch, int32_
   }
 }
 
-// counts[e] = number of member tokens of expert e (one workgroup per expert;
-// mask rows are 16-byte aligned and zero past T).
+// Membership counts per (expert, chunk of CHUNK tokens): chunk_cnt[e][c]
+// (one 256-thread workgroup per chunk, 16 tokens per thread; mask rows are
+// 16-byte aligned and zero past T).  The per-expert counts are their sums
+// (k_scan_experts), and the chunk counts let k_compact split a heavy
+// expert's tokens over many workgroups.
+constexpr int CHUNK = 256 * 16;
 __global__ void __launch_bounds__(256)
-k_expert_count(const uint8_t* __restrict__ mask, int mpitch, int32_t* __restrict__ counts,
-               int32_t* __restrict__ counts2) {
+k_chunk_count(const uint8_t* __restrict__ mask, int mpitch, int nch, int32_t* __restrict__ chunk_cnt) {
   __shared__ int lds[8];
-  const int e = blockIdx.x;
-  const uint4* m = reinterpret_cast<const uint4*>(mask + (size_t)e * mpitch);
-  int c = 0;
-  for (int i = threadIdx.x; i < mpitch / 16; i += 256) {
-    const uint4 u = m[i];
+  const int c = blockIdx.x, e = blockIdx.y;
+  const int t0 = c * CHUNK + threadIdx.x * 16;
+  int v = 0;
+  if (t0 < mpitch) {
+    const uint4 u = *reinterpret_cast<const uint4*>(mask + (size_t)e * mpitch + t0);
     // each byte is 0 or 1: the byte sum of a word is its popcount
-    c += __popc(u.x) + __popc(u.y) + __popc(u.z) + __popc(u.w);
+    v = __popc(u.x) + __popc(u.y) + __popc(u.z) + __popc(u.w);
   }
   int total;
-  block_scan256(c, lds, &total);
-  if (threadIdx.x == 0) {
-    counts[e] = total;
-    if (counts2) counts2[e] = total;
-  }
+  block_scan256(v, lds, &total);
+  if (threadIdx.x == 0) chunk_cnt[(size_t)e * nch + c] = total;
+}
+
+__device__ __forceinline__ int expert_total(const int32_t* __restrict__ chunk_cnt, int nch, int e) {
+  int c = 0;
+  for (int i = 0; i < nch; ++i) c += chunk_cnt[(size_t)e * nch + i];
+  return c;
 }
 
 // scores [T][E] -> scoresT [E][pitch]
@@ -253,11 +259,13 @@ __device__ __forceinline__ void tr_load(const uint8_t* m, const float* z, int t0
 // depend on the order in which the histogram atomics land.
 __global__ void __launch_bounds__(TR_THREADS)
 k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int mpitch,
-              const int32_t* __restrict__ counts_raw, int T, int M, int mode, uint64_t seed) {
+              const int32_t* __restrict__ chunk_cnt, int nch, int32_t* __restrict__ counts_raw, int T, int M,
+              int mode, uint64_t seed) {
   __shared__ int hist[4096];
   __shared__ int sh[20];
   const int e = blockIdx.x;
-  const int c = counts_raw[e];
+  const int c = expert_total(chunk_cnt, nch, e);
+  if (threadIdx.x == 0) counts_raw[e] = c;
   const int rem = c % M;
   if (rem == 0) return;
   int r;
@@ -370,13 +378,18 @@ k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int
   }
 }
 
+// counts (and counts2 when set) = per-expert sums of the chunk counts;
 // offsets / tile_offsets: exclusive scans of counts and ceil(counts / tile).
 __global__ void __launch_bounds__(1024)
-k_scan_experts(const int32_t* __restrict__ counts, int E, int tile, int32_t* __restrict__ offsets,
-               int32_t* __restrict__ tile_offsets) {
+k_scan_experts(const int32_t* __restrict__ chunk_cnt, int nch, int E, int tile, int32_t* __restrict__ counts,
+               int32_t* __restrict__ counts2, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_offsets) {
   __shared__ int lds[16];
   const int e = threadIdx.x;
-  const int c = e < E ? counts[e] : 0;
+  const int c = e < E ? expert_total(chunk_cnt, nch, e) : 0;
+  if (e < E) {
+    counts[e] = c;
+    if (counts2) counts2[e] = c;
+  }
   int tot1, tot2;
   const int o = block_scan1024(c, lds, &tot1);
   const int to = block_scan1024((c + tile - 1) / tile, lds, &tot2);
@@ -391,35 +404,36 @@ k_scan_experts(const int32_t* __restrict__ counts, int E, int tile, int32_t* __r
 }
 
 // Rows of expert e: its member tokens in ascending order, at offsets[e].
-// Each thread takes 16 consecutive tokens (one 16-byte mask load) per sweep.
-// rowmap[e][t] = row of (e, t).
-__global__ void __launch_bounds__(1024)
-k_compact(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restrict__ offsets,
-          int32_t* __restrict__ row_token, int32_t* __restrict__ row_expert, int32_t* __restrict__ rowmap) {
-  __shared__ int sh[16];
-  const int e = blockIdx.x;
-  const uint8_t* m = mask + (size_t)e * mpitch;
+// One 256-thread workgroup per (chunk, expert), 16 consecutive tokens (one
+// 16-byte mask load) per thread; the chunk's first row is offsets[e] plus the
+// counts of the expert's earlier chunks, so a heavy expert's tokens spread
+// over as many workgroups as it has chunks.  rowmap[e][t] = row of (e, t).
+__global__ void __launch_bounds__(256)
+k_compact(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restrict__ chunk_cnt, int nch,
+          const int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ row_expert,
+          int32_t* __restrict__ rowmap) {
+  __shared__ int sh[8];
+  const int c = blockIdx.x, e = blockIdx.y;
+  int base = offsets[e];
+  for (int i = 0; i < c; ++i) base += chunk_cnt[(size_t)e * nch + i];
+  const int t0 = c * CHUNK + threadIdx.x * 16;
+  uint4 u = make_uint4(0, 0, 0, 0);
+  if (t0 < mpitch) u = *reinterpret_cast<const uint4*>(mask + (size_t)e * mpitch + t0);
+  const int cnt = __popc(u.x) + __popc(u.y) + __popc(u.z) + __popc(u.w);
+  int tot;
+  int row = base + block_scan256(cnt, sh, &tot);
+  if (cnt == 0) return;
   int32_t* rm = rowmap + (size_t)e * mpitch;
-  int carry = offsets[e];
-  for (int base = 0; base < mpitch; base += 1024 * 16) {
-    const int t0 = base + threadIdx.x * 16;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (t0 < mpitch) u = *reinterpret_cast<const uint4*>(m + t0);
-    const int cnt = __popc(u.x) + __popc(u.y) + __popc(u.z) + __popc(u.w);
-    int tot;
-    int row = carry + block_scan1024(cnt, sh, &tot);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if ((w[i >> 2] >> (8 * (i & 3))) & 0xffu) {
-        const int t = t0 + i;
-        row_token[row] = t;
-        row_expert[row] = e;
-        rm[t] = row;
-        ++row;
-      }
+  for (int i = 0; i < 16; ++i) {
+    if ((w[i >> 2] >> (8 * (i & 3))) & 0xffu) {
+      const int t = t0 + i;
+      row_token[row] = t;
+      row_expert[row] = e;
+      rm[t] = row;
+      ++row;
     }
-    carry += tot;
   }
 }
 
@@ -471,26 +485,29 @@ k_tok_fill_topk(const int32_t* __restrict__ topk_idx, const float* __restrict__ 
   }
 }
 
-// Per-token pass over the final membership (token rounding only).  A
-// workgroup takes 64 tokens (one per lane); wave s of its four takes the
-// contiguous expert range [s*ceil(E/4), (s+1)*ceil(E/4)), so the waves'
-// results in wave order follow ascending expert id.
+// Per-token passes over the final membership (token rounding only).  A
+// workgroup takes 64 tokens (one per lane) with TOK_SLICES waves; wave s
+// takes the contiguous expert range [s*ceil(E/S), (s+1)*ceil(E/S)), so the
+// waves' results in wave order follow ascending expert id.  Sixteen waves
+// per 64 tokens keep each lane's chain of membership loads short (E / 16
+// experts) and the chip full (T = 32768: 8192 waves).
+constexpr int TOK_SLICES = 16;
 struct TokSlice {
   int lo, hi;
 };
 __device__ __forceinline__ TokSlice tok_slice(int E, int s) {
-  const int q = (E + 3) / 4;
+  const int q = (E + TOK_SLICES - 1) / TOK_SLICES;
   const int lo = min(E, s * q);
   return TokSlice{lo, min(E, lo + q)};
 }
 
 // tokcnt[t] = rows of token t; tstat[t], tstat[T + t] = max and sum of
 // exp(score - max) over the token's final expert set (the set softmax).
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * TOK_SLICES)
 k_tok_stats(const uint8_t* __restrict__ mask, int mpitch, const float* __restrict__ scoresT, int T, int E,
             int32_t* __restrict__ tokcnt, float* __restrict__ tstat) {
-  __shared__ float smx[4][64], ssum[4][64];
-  __shared__ int scnt[4][64];
+  __shared__ float smx[TOK_SLICES][64], ssum[TOK_SLICES][64];
+  __shared__ int scnt[TOK_SLICES][64];
   const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
   const int t = blockIdx.x * 64 + lane;
   const TokSlice sl = tok_slice(E, s);
@@ -518,37 +535,61 @@ k_tok_stats(const uint8_t* __restrict__ mask, int mpitch, const float* __restric
   if (s != 0 || t >= T) return;
   float M = smx[0][lane];
   int C = scnt[0][lane];
-  for (int j = 1; j < 4; ++j) {
+  for (int j = 1; j < TOK_SLICES; ++j) {
     M = fmaxf(M, smx[j][lane]);
     C += scnt[j][lane];
   }
   float S = 0.f;
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < TOK_SLICES; ++j)
     if (scnt[j][lane]) S += ssum[j][lane] * __expf(smx[j][lane] - M);
   tokcnt[t] = C;
   tstat[t] = M;
   tstat[(size_t)T + t] = S;
 }
 
-// tok_ptr = exclusive scan of per-token row counts (one 1024-thread block;
-// each sweep takes 4096 consecutive tokens, four per thread).
+// tok_ptr = exclusive scan of per-token row counts: one 1024-thread block,
+// each sweep taking 16384 consecutive tokens, 16 per thread, read and written
+// as four 16-byte words (both arrays are 16-byte aligned; a partial last group
+// of a sweep goes element by element).
 __global__ void __launch_bounds__(1024)
 k_tok_scan(const int32_t* __restrict__ tokcnt, int T, int32_t* __restrict__ tok_ptr) {
   __shared__ int lds[16];
+  constexpr int PER = 16;
   int carry = 0;
-  for (int base = 0; base < T; base += 4096) {
-    const int t0 = base + threadIdx.x * 4;
-    int v[4];
+  for (int base = 0; base < T; base += 1024 * PER) {
+    const int t0 = base + threadIdx.x * PER;
+    const bool whole = t0 + PER <= T;
+    int v[PER];
+    if (whole) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = t0 + j < T ? tokcnt[t0 + j] : 0;
-    int tot;
-    int run = carry + block_scan1024(v[0] + v[1] + v[2] + v[3], lds, &tot);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (t0 + j < T) {
-        tok_ptr[t0 + j] = run;
-        run += v[j];
+      for (int q = 0; q < PER / 4; ++q) {
+        const int4 u = *reinterpret_cast<const int4*>(tokcnt + t0 + 4 * q);
+        v[4 * q] = u.x; v[4 * q + 1] = u.y; v[4 * q + 2] = u.z; v[4 * q + 3] = u.w;
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v[j] = t0 + j < T ? tokcnt[t0 + j] : 0;
+    }
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) sum += v[j];
+    int tot;
+    int run = carry + block_scan1024(sum, lds, &tot);
+    int o[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      o[j] = run;
+      run += v[j];
+    }
+    if (whole) {
+#pragma unroll
+      for (int q = 0; q < PER / 4; ++q)
+        *reinterpret_cast<int4*>(tok_ptr + t0 + 4 * q) = make_int4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (t0 + j < T) tok_ptr[t0 + j] = o[j];
+    }
     carry += tot;
   }
   if (threadIdx.x == 0) tok_ptr[T] = carry;
@@ -556,12 +597,12 @@ k_tok_scan(const int32_t* __restrict__ tokcnt, int T, int32_t* __restrict__ tok_
 
 // Token rounding: per token, its rows in ascending expert order and each
 // row's gate, the softmax of the token's scores over its final set.
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * TOK_SLICES)
 k_tok_fill(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restrict__ rowmap,
            const float* __restrict__ scoresT, const float* __restrict__ tstat,
            const int32_t* __restrict__ tok_ptr, int T, int E, int32_t* __restrict__ tok_row,
            float* __restrict__ row_gate) {
-  __shared__ int scnt[4][64];
+  __shared__ int scnt[TOK_SLICES][64];
   const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
   const int t = blockIdx.x * 64 + lane;
   const TokSlice sl = tok_slice(E, s);
@@ -597,6 +638,7 @@ static __global__ void k_zero16(uint4* __restrict__ p, long long n16) {
 }
 
 int mask_pitch(int T) { return (T + 15) / 16 * 16; }
+int route_chunks(int T) { return (mask_pitch(T) + CHUNK - 1) / CHUNK; }
 
 hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int T, int E, int K,
                                int tile, int round_mode, uint64_t round_seed, hipStream_t st) {
@@ -618,21 +660,19 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
   else if (E <= 256) topk(k_topk<16, 16>, 16);
   else if (E <= 512) topk(k_topk<32, 16>, 32);
   else topk(k_topk<32, 32>, 32);
-  if (round_mode == 0) {
-    hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.counts_raw, rb.counts);
-  } else {
-    hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.counts_raw,
-                       (int32_t*)nullptr);
+  const int nch = route_chunks(T);
+  const dim3 cgrid((unsigned)nch, (unsigned)E);
+  if (round_mode != 0) {
+    hipLaunchKernelGGL(k_chunk_count, cgrid, dim3(256), 0, st, sc.mask, mp, nch, sc.chunk_cnt);
     hipLaunchKernelGGL(k_transpose_scores, dim3((T + 31) / 32, (E + 31) / 32), dim3(256), 0, st,
                        rb.logits, T, E, mp, sc.scoresT);
-    hipLaunchKernelGGL(k_token_round, dim3(E), dim3(TR_THREADS), 0, st, sc.scoresT, sc.mask, mp,
-                       rb.counts_raw, T, tile, round_mode, round_seed);
-    hipLaunchKernelGGL(k_expert_count, dim3(E), dim3(256), 0, st, sc.mask, mp, rb.counts,
-                       (int32_t*)nullptr);
+    hipLaunchKernelGGL(k_token_round, dim3(E), dim3(TR_THREADS), 0, st, sc.scoresT, sc.mask, mp, sc.chunk_cnt,
+                       nch, rb.counts_raw, T, tile, round_mode, round_seed);
   }
-  hipLaunchKernelGGL(k_scan_experts, dim3(1), dim3(1024), 0, st, rb.counts, E, tile, rb.offsets,
-                     rb.tile_offsets);
-  hipLaunchKernelGGL(k_compact, dim3(E), dim3(1024), 0, st, sc.mask, mp, rb.offsets, rb.row_token,
+  hipLaunchKernelGGL(k_chunk_count, cgrid, dim3(256), 0, st, sc.mask, mp, nch, sc.chunk_cnt);
+  hipLaunchKernelGGL(k_scan_experts, dim3(1), dim3(1024), 0, st, sc.chunk_cnt, nch, E, tile, rb.counts,
+                     round_mode == 0 ? rb.counts_raw : (int32_t*)nullptr, rb.offsets, rb.tile_offsets);
+  hipLaunchKernelGGL(k_compact, cgrid, dim3(256), 0, st, sc.mask, mp, sc.chunk_cnt, nch, rb.offsets, rb.row_token,
                      rb.row_expert, sc.rowmap);
   if (round_mode == 0) {
     if (K <= 16)
@@ -643,11 +683,11 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
                          sc.rowmap, mp, T, K, rb.tok_row, rb.row_gate);
   } else {
     const unsigned blocks = (unsigned)((T + 63) / 64);
-    hipLaunchKernelGGL(k_tok_stats, dim3(blocks), dim3(256), 0, st, sc.mask, mp, sc.scoresT, T, E, sc.tokcnt,
-                       sc.tstat);
+    hipLaunchKernelGGL(k_tok_stats, dim3(blocks), dim3(64 * TOK_SLICES), 0, st, sc.mask, mp, sc.scoresT, T, E,
+                       sc.tokcnt, sc.tstat);
     hipLaunchKernelGGL(k_tok_scan, dim3(1), dim3(1024), 0, st, sc.tokcnt, T, rb.tok_ptr);
-    hipLaunchKernelGGL(k_tok_fill, dim3(blocks), dim3(256), 0, st, sc.mask, mp, sc.rowmap, sc.scoresT,
-                       sc.tstat, rb.tok_ptr, T, E, rb.tok_row, rb.row_gate);
+    hipLaunchKernelGGL(k_tok_fill, dim3(blocks), dim3(64 * TOK_SLICES), 0, st, sc.mask, mp, sc.rowmap,
+                       sc.scoresT, sc.tstat, rb.tok_ptr, T, E, rb.tok_row, rb.row_gate);
   }
   return hipGetLastError();
 }
