@@ -257,10 +257,17 @@ __device__ __forceinline__ void tr_load(const uint8_t* m, const float* z, int t0
 // in an LDS histogram); candidates with exactly the threshold key are then
 // taken in ascending token order.  Counts are exact, so the result does not
 // depend on the order in which the histogram atomics land.
+// LDSK (mask rows of at most TR_LDS_TOKENS tokens): the candidates' keys are
+// read from HBM once into LDS (0 marks a non-candidate; a candidate's key is
+// at least 1) and the radix passes and the final selection sweep LDS; else
+// every pass re-reads the expert's scores and membership bytes.
+constexpr int TR_LDS_TOKENS = 32768;
+template <bool LDSK>
 __global__ void __launch_bounds__(TR_THREADS)
 k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int mpitch,
               const int32_t* __restrict__ chunk_cnt, int nch, int32_t* __restrict__ counts_raw, int T, int M,
               int mode, uint64_t seed) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t kl[];  // LDSK: [mpitch] candidate keys
   __shared__ int hist[4096];
   __shared__ int sh[20];
   const int e = blockIdx.x;
@@ -290,6 +297,23 @@ k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int
   const int tid = threadIdx.x;
   constexpr int SWEEP = TR_THREADS * TR_GROUP;
 
+  if constexpr (LDSK) {
+    for (int base = 0; base < mpitch; base += SWEEP) {
+      const int t0 = base + tid * TR_GROUP;
+      if (t0 >= mpitch) continue;
+      TrGroup g;
+      tr_load(m, z, t0, T, want, g);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = ((g.cand >> (4 * q + i)) & 1u) ? max(g.key[4 * q + i], 1u) : 0u;
+        *reinterpret_cast<uint4*>(kl + t0 + 4 * q) = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    }
+    __syncthreads();
+  }
+
   uint32_t prefix = 0, pmask = 0;
   int kk = k_sel;
   if (k_sel > 0) {
@@ -299,15 +323,22 @@ k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int
       const int nb = 1 << width;
       for (int i = tid; i < nb; i += TR_THREADS) hist[i] = 0;
       __syncthreads();
-      for (int base = 0; base < mpitch; base += SWEEP) {
-        const int t0 = base + tid * TR_GROUP;
-        if (t0 >= mpitch) continue;
-        TrGroup g;
-        tr_load(m, z, t0, T, want, g);
+      if constexpr (LDSK) {
+        for (int t = tid; t < mpitch; t += TR_THREADS) {
+          const uint32_t k = kl[t];
+          if (k && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1);
+        }
+      } else {
+        for (int base = 0; base < mpitch; base += SWEEP) {
+          const int t0 = base + tid * TR_GROUP;
+          if (t0 >= mpitch) continue;
+          TrGroup g;
+          tr_load(m, z, t0, T, want, g);
 #pragma unroll
-        for (int i = 0; i < TR_GROUP; ++i)
-          if (((g.cand >> i) & 1u) && (g.key[i] & pmask) == prefix)
-            atomicAdd(&hist[(g.key[i] >> shift) & (nb - 1)], 1);
+          for (int i = 0; i < TR_GROUP; ++i)
+            if (((g.cand >> i) & 1u) && (g.key[i] & pmask) == prefix)
+              atomicAdd(&hist[(g.key[i] >> shift) & (nb - 1)], 1);
+        }
       }
       __syncthreads();
       // Bins in descending order: thread tid owns bins nb-1-per*tid down to
@@ -346,7 +377,19 @@ k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int
     g.cand = 0;
     uint32_t gt = 0, eq = 0;
     if (t0 < mpitch) {
-      tr_load(m, z, t0, T, want, g);
+      if constexpr (LDSK) {
+        g.mbytes = *reinterpret_cast<const uint4*>(m + t0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = *reinterpret_cast<const uint4*>(kl + t0 + 4 * q);
+          g.key[4 * q] = v.x; g.key[4 * q + 1] = v.y; g.key[4 * q + 2] = v.z; g.key[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int i = 0; i < TR_GROUP; ++i)
+          if (g.key[i]) g.cand |= 1u << i;
+      } else {
+        tr_load(m, z, t0, T, want, g);
+      }
       if (k_sel > 0) {
 #pragma unroll
         for (int i = 0; i < TR_GROUP; ++i)
@@ -666,8 +709,17 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
     hipLaunchKernelGGL(k_chunk_count, cgrid, dim3(256), 0, st, sc.mask, mp, nch, sc.chunk_cnt);
     hipLaunchKernelGGL(k_transpose_scores, dim3((T + 31) / 32, (E + 31) / 32), dim3(256), 0, st,
                        rb.logits, T, E, mp, sc.scoresT);
-    hipLaunchKernelGGL(k_token_round, dim3(E), dim3(TR_THREADS), 0, st, sc.scoresT, sc.mask, mp, sc.chunk_cnt,
-                       nch, rb.counts_raw, T, tile, round_mode, round_seed);
+    if (mp <= TR_LDS_TOKENS) {
+      static const hipError_t attr =
+          hipFuncSetAttribute(reinterpret_cast<const void*>(k_token_round<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, TR_LDS_TOKENS * 4);
+      if (attr != hipSuccess) return attr;
+      hipLaunchKernelGGL(k_token_round<true>, dim3(E), dim3(TR_THREADS), (size_t)mp * 4, st, sc.scoresT, sc.mask, mp,
+                         sc.chunk_cnt, nch, rb.counts_raw, T, tile, round_mode, round_seed);
+    } else {
+      hipLaunchKernelGGL(k_token_round<false>, dim3(E), dim3(TR_THREADS), 0, st, sc.scoresT, sc.mask, mp,
+                         sc.chunk_cnt, nch, rb.counts_raw, T, tile, round_mode, round_seed);
+    }
   }
   hipLaunchKernelGGL(k_chunk_count, cgrid, dim3(256), 0, st, sc.mask, mp, nch, sc.chunk_cnt);
   hipLaunchKernelGGL(k_scan_experts, dim3(1), dim3(1024), 0, st, sc.chunk_cnt, nch, E, tile, rb.counts,

@@ -30,6 +30,8 @@ ROUTE_CASES = [
     (700, 32, 1, 1, 8, 128), (1, 8, 2, 0, 9, 128), (5000, 1024, 7, 2, 10, 128),
     # rounding to 256-row tiles
     (4096, 16, 2, 1, 11, 256), (4096, 16, 2, 2, 12, 256), (3000, 24, 5, 2, 13, 256), (700, 8, 3, 1, 14, 256),
+    # more tokens than the rounding kernel keeps in LDS (it re-reads HBM then)
+    (40000, 32, 4, 2, 15, 128), (33000, 16, 2, 1, 16, 256),
 ]
 
 
