@@ -640,18 +640,26 @@ __global__ void k_sum_partials(const float* __restrict__ part, int splits, long 
   out[i + 3] = Elem<TO>::from_f(acc.w);
 }
 
-template <typename T>
-hipError_t dwr(const void* x, const void* dz, int T_, int d, int E, void* dWr, float* part, hipStream_t st) {
-  constexpr int BM = 128, BN = 64;
+template <typename T, int BN>
+hipError_t dwr_t(const void* x, const void* dz, int T_, int d, int E, float* part, int splits, hipStream_t st) {
+  constexpr int BM = 128;
   using Epi = EpiStore<T, float, BM, BN>;
   const int NT = (E + BN - 1) / BN;
-  const int splits = dwr_splits(T_, d, E);
   GemmShape s{nullptr, 1, d, NT * BN, T_, E, splits};
   Operand a{x, nullptr, 0, d};
   Operand b{dz, nullptr, 0, E};
   typename Epi::Params ep{part, E, nullptr};
-  hipError_t err = run_gemm<T, BM, BN, true, B_KN, false, Epi>(s, a, b, ep,
-                                                               (long long)splits * (d / BM) * NT, st);
+  return run_gemm<T, BM, BN, true, B_KN, false, Epi>(s, a, b, ep, (long long)splits * (d / BM) * NT, st);
+}
+
+// x^T dz: each column tile of dz re-reads all of x, so bf16 takes 128
+// columns of E per tile where E allows (x read E / 128 times, not E / 64)
+template <typename T>
+hipError_t dwr(const void* x, const void* dz, int T_, int d, int E, void* dWr, float* part, hipStream_t st) {
+  const int splits = dwr_splits(T_, d, E);
+  hipError_t err;
+  if (std::is_same<T, bf16_t>::value && E % 128 == 0) err = dwr_t<T, 128>(x, dz, T_, d, E, part, splits, st);
+  else err = dwr_t<T, 64>(x, dz, T_, d, E, part, splits, st);
   if (err != hipSuccess) return err;
   const long long count = (long long)d * E;  // multiple of 4: d % 128 == 0
   hipLaunchKernelGGL(k_sum_partials<T>, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0, st, part,
@@ -664,8 +672,14 @@ hipError_t dwr(const void* x, const void* dz, int T_, int d, int E, void* dWr, f
 int dh_block(const GemmDims& g) { return dh_bn(g); }
 
 int dwr_splits(int T, int d, int E) {
-  const int tiles = (d / 128) * ((E + 63) / 64);
-  int s = (512 + tiles - 1) / tiles;           // about two resident tiles per CU
+  const int bn = E % 128 == 0 ? 128 : 64;  // the column tile of the bf16 launch
+  const int tiles = (d / 128) * ((E + bn - 1) / bn);
+  // at least one tile per CU; up to two while chunks keep 1024 rows or more
+  // (shorter chunks mostly add fp32 partial traffic and per-tile overhead:
+  // measured at d = 1536, E = 128, T = 32768: 22 splits 0.055 ms, 43 splits
+  // 0.062 ms; d = 2048, E = 256: T = 32768 at 8 splits 0.100 ms and 16
+  // splits 0.069 ms, T = 16384 at 8 splits 0.056 ms and 16 splits 0.045 ms)
+  int s = std::max((256 + tiles - 1) / tiles, std::min((512 + tiles - 1) / tiles, T / 1024));
   const int kmax = (T + 255) / 256;            // at least 4 k steps of 64 per chunk
   if (s > kmax) s = kmax;
   if (s > 64) s = 64;

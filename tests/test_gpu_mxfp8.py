@@ -408,3 +408,47 @@ def test_mxfp8_weight_grads_full_size_expert_sample(name):
               "vs plain", {k: f"{v:.2e}" for k, v in (e2e or {}).items()})
         assert all(v <= TOL for v in errs.values()), errs
         assert all(v <= WG_E2E for v in (e2e or {}).values()), e2e
+
+
+def bf16_pattern_blocks(seed=31):
+    """Every finite bf16 bit pattern below 2^61 (zeros and subnormals too),
+    shuffled into blocks of 32, each with one anchor 2^0 .. 2^12 times the
+    block's largest magnitude (so the block scale sends its values to every
+    code range: saturation, normal, subnormal, zero); rows of 256."""
+    rng = np.random.default_rng(seed)
+    p = np.arange(1 << 16, dtype=np.uint32)
+    p = p[((p >> 7) & 0xFF) <= 127 + 60]
+    p = rng.permutation(p)
+    nb = (len(p) + 30) // 31
+    p = np.concatenate([p, np.zeros(nb * 31 - len(p), dtype=np.uint32)]).reshape(nb, 31)
+    ex = (p >> 7) & 0xFF
+    emax = ex.max(axis=1)
+    aexp = np.where(emax == 0, rng.integers(1, 21, nb), np.minimum(254, emax + rng.integers(0, 13, nb)))
+    anchor = (rng.integers(0, 2, nb).astype(np.uint32) << 15) | (aexp.astype(np.uint32) << 7) | \
+        rng.integers(0, 128, nb).astype(np.uint32)
+    blocks = np.empty((nb, 32), dtype=np.uint32)
+    pos = rng.integers(0, 32, nb)
+    for b in range(nb):
+        blocks[b] = np.insert(p[b], pos[b], anchor[b])
+    flat = blocks.reshape(-1)
+    rows = (len(flat) + 255) // 256
+    flat = np.concatenate([flat, np.zeros(rows * 256 - len(flat), dtype=np.uint32)])
+    return flat.astype(np.uint16).reshape(rows, 256)
+
+
+def test_mxfp8_codes_of_every_bf16_pattern():
+    """The quantizer's element codes and block scales, bit-exact against the
+    oracle's encoder, on every finite bf16 pattern below 2^61 placed in
+    blocks that send it to every code range (moe_fwd_mxfp8's x codes)."""
+    x = bf16_pattern_blocks()
+    T, d = x.shape
+    w = W("patterns", T, d, 8, 256, 2, seed=32)
+    a = I.draw_all(w)
+    a["x"] = x
+    L, _ = run_mx(w, a)
+    xq, xs = M.quantize(O.to_f64(x, "bf16"))
+    gq = u8(L, B.MOE_ITEM_MX_XQ, T * d).reshape(T, d)
+    gs = u8(L, B.MOE_ITEM_MX_XS, T * d // 32).reshape(T, d // 32)
+    bad = np.nonzero(gq != xq)
+    assert np.array_equal(gs, xs), "scales"
+    assert bad[0].size == 0, [(hex(int(x[i, j])), hex(int(gq[i, j])), hex(int(xq[i, j]))) for i, j in zip(*bad)][:10]
