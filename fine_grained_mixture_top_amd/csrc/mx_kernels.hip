@@ -168,10 +168,18 @@ k_mx_pad_offsets(const int32_t* __restrict__ offsets, int E, int32_t* __restrict
   if (tid == E - 1) ps[E] = base + incl;
   __syncthreads();
   for (int e = tid; e <= E; e += 1024) padoff[e] = ps[e];
-  // stage map: expert e owns stages ps[e]/128 .. ps[e+1]/128 - 1
-  for (int e = 0; e < E; ++e) {
-    const int g0 = ps[e] / 128, g1 = ps[e + 1] / 128;
-    for (int g = g0 + tid; g < g1; g += 1024) stage_e[g] = e;
+  // stage map: expert e owns stages ps[e]/128 .. ps[e+1]/128 - 1; stage g's
+  // expert is the last e with ps[e] <= 128 g (binary search; ps ascending,
+  // empty experts share their start with the next one)
+  const int stages = ps[E] / 128;
+  for (int g = tid; g < stages; g += 1024) {
+    int lo = 0, hi = E;  // ps[lo] <= 128 g < ps[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ps[mid] <= 128 * g) lo = mid;
+      else hi = mid;
+    }
+    stage_e[g] = lo;
   }
 }
 
@@ -180,15 +188,15 @@ k_mx_pad_offsets(const int32_t* __restrict__ offsets, int E, int32_t* __restrict
 // C * padoff[e] (Kp_e = padded segment length) and stage-blocked scales: the
 // dword (padoff[e] / 128 + s) * C + c holds column c's four block scales of
 // stage s (byte b = rows 128 s + 32 b .. +31).  One workgroup per (64
-// columns, global stage): the 128 x 64 tile is read in whole rows (zeros
-// past the segment), each thread quantizes one (column, 32-row block) from
-// LDS, and the codes leave as 128-byte rows.  Workgroups past the last stage
+// columns, global stage): the 128 x 64 tile is read in whole rows, 16 bytes
+// per thread (zeros past the segment), each thread quantizes one (column,
+// 32-row block) from LDS, and the codes leave as 128-byte rows.  Workgroups past the last stage
 // return.
 __global__ void __launch_bounds__(256)
 k_mx_quant_seg(const bf16_t* __restrict__ src, int C, const int32_t* __restrict__ idx,
                const int32_t* __restrict__ offsets, const int32_t* __restrict__ padoff,
                const int32_t* __restrict__ stage_e, int E, uint8_t* __restrict__ q, uint32_t* __restrict__ sblk) {
-  __shared__ bf16_t tin[128][64 + 2];
+  __shared__ __attribute__((aligned(16))) bf16_t tin[128][64 + 8];  // rows of 144 bytes: 16-byte stores
   __shared__ uint32_t tout[64][32 + 1];
   __shared__ uint32_t ts[4][64];
   const int tid = threadIdx.x;
@@ -199,18 +207,15 @@ k_mx_quant_seg(const bf16_t* __restrict__ src, int C, const int32_t* __restrict_
   const int pe = padoff[e], kp = padoff[e + 1] - pe;
   const int s = g - pe / 128;  // stage of the segment
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {  // 128 rows x 64 columns, 4 columns (8 bytes) per thread
-    const int v = it * 256 + tid, r = v >> 4, c4 = (v & 15) * 4;
+  for (int it = 0; it < 4; ++it) {  // 128 rows x 64 columns, 8 columns (16 bytes) per thread
+    const int v = it * 256 + tid, r = v >> 3, c8 = (v & 7) * 8;
     const int sr = 128 * s + r;
-    uint2 x = make_uint2(0u, 0u);
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
     if (sr < segn) {
       const long long row = idx ? (long long)idx[seg0 + sr] : (long long)(seg0 + sr);
-      x = *reinterpret_cast<const uint2*>(src + row * C + c0 + c4);
+      x = *reinterpret_cast<const uint4*>(src + row * C + c0 + c8);
     }
-    tin[r][c4] = (bf16_t)(x.x & 0xffffu);
-    tin[r][c4 + 1] = (bf16_t)(x.x >> 16);
-    tin[r][c4 + 2] = (bf16_t)(x.y & 0xffffu);
-    tin[r][c4 + 3] = (bf16_t)(x.y >> 16);
+    *reinterpret_cast<uint4*>(&tin[r][c8]) = x;
   }
   __syncthreads();
   const int col = tid & 63, b = tid >> 6;  // 32-row block b of the stage
