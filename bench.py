@@ -195,7 +195,7 @@ def cpu_baseline(w, a, tokens, repeats=1):
             "kind": "oracle", "cpu": cpu_model(),
             "fwd_s": round(fwd, 6), "bwd_s": round(bwd, 6),
             "fwd_tflops": 6.0 * rows * w.d * w.n / fwd / 1e12, "bwd_tflops": 12.0 * rows * w.d * w.n / bwd / 1e12,
-            "sample": f"route+fwd ({fwd:.2f} s) and bwd ({bwd:.2f} s) of {tk} of {w.T} tokens ({rows} rows), "
+            "sample": f"route+fwd ({fwd:.3g} s) and bwd ({bwd:.3g} s) of {tk} of {w.T} tokens ({rows} rows), "
                       f"same weights, fp64 numpy{med}"}
 
 
