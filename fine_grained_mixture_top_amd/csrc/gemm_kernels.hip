@@ -80,7 +80,10 @@ hipError_t run_gemm5(const GemmShape& s, const Operand& A, const Operand& B, siz
 template <bool BMN, bool PAIRED, class Epi>
 hipError_t run_row256(const GemmShape& s, const Operand& A, const Operand& B, size_t a_bytes, size_t b_bytes,
                       const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
-  if (s.K % g5::BK == 0 && s.K >= 512) {
+  // k = 64 stages from K = 512 up; K = 256 with k-contiguous weights too
+  // (dXt at n = 128: 0.509 -> 0.494 ms at T = 16384, d = 2048, E = 256; the
+  // down-projection at K = 256 is 2% faster on the k = 32 kernel)
+  if (s.K % g5::BK == 0 && s.K >= (BMN ? 512 : 256)) {
     // k-contiguous weights and A rows read without an index, shared by at
     // least four column tiles: the A-row touch variant
     if constexpr (!BMN)

@@ -141,7 +141,7 @@ struct RouteScratch {
   uint8_t* mask;       // [E][pitch] membership bytes
   float* scoresT;      // [E][pitch] scores, expert-major (token rounding only)
   int32_t* rowmap;     // [E][pitch] row of (e, t)
-  int32_t* tokcnt;     // [T] rows per token (token rounding only)
+  int32_t* tblk;       // rows per 64-token block, then their scan (token rounding only)
   float* tstat;        // [2][T] set-softmax max and sum per token (token rounding only)
   int32_t* chunk_cnt;  // [E][route_chunks(T)] member counts per chunk of 4096 tokens
 };

@@ -62,7 +62,7 @@ Layout route_layout(const moe_desc* d) {
   L.off[0] = o; o = up(o + TEp);                                  // mask
   L.off[1] = o; o = up(o + tr * TEp * 4);                         // scoresT
   L.off[2] = o; o = up(o + TEp * 4);                              // rowmap
-  L.off[3] = o; o = up(o + tr * (size_t)d->T * 4);                // tokcnt
+  L.off[3] = o; o = up(o + tr * 2 * ((size_t)(d->T + 63) / 64 + 4) * 4);  // 64-token block sums, offsets
   L.off[4] = o; o = up(o + tr * (size_t)d->T * 8);                // tstat
   L.off[5] = o; o = up(o + (size_t)d->E * route_chunks(d->T) * 4); // chunk counts
   L.total = o;

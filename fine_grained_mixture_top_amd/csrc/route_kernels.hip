@@ -265,8 +265,9 @@ constexpr int TR_LDS_TOKENS = 32768;
 template <bool LDSK>
 __global__ void __launch_bounds__(TR_THREADS)
 k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int mpitch,
-              const int32_t* __restrict__ chunk_cnt, int nch, int32_t* __restrict__ counts_raw, int T, int M,
+              int32_t* __restrict__ chunk_cnt, int nch, int32_t* __restrict__ counts_raw, int T, int M,
               int mode, uint64_t seed) {
+  static_assert(TR_THREADS * TR_GROUP == 4 * CHUNK && TR_THREADS / 64 == 16, "a sweep is four chunks");
   extern __shared__ __attribute__((aligned(16))) uint32_t kl[];  // LDSK: [mpitch] candidate keys
   __shared__ int hist[4096];
   __shared__ int sh[20];
@@ -416,8 +417,19 @@ k_token_round(const float* __restrict__ scoresT, uint8_t* __restrict__ mask, int
       for (int i = 0; i < TR_GROUP; ++i)
         if ((flip >> i) & 1u) w[i >> 2] ^= 1u << (8 * (i & 3));
       *reinterpret_cast<uint4*>(m + t0) = make_uint4(w[0], w[1], w[2], w[3]);
+      g.mbytes = make_uint4(w[0], w[1], w[2], w[3]);
     }
     carry += tot;
+    // the expert's new chunk counts: a sweep is four chunks of 256 threads
+    int c = t0 < mpitch ? __popc(g.mbytes.x) + __popc(g.mbytes.y) + __popc(g.mbytes.z) + __popc(g.mbytes.w) : 0;
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, 64);
+    if ((tid & 63) == 0) sh[tid >> 6] = c;  // sh[0..15]: free between the scans
+    __syncthreads();
+    if (tid < SWEEP / CHUNK) {
+      const int ch = base / CHUNK + tid;
+      if (ch < nch) chunk_cnt[(size_t)e * nch + ch] = sh[4 * tid] + sh[4 * tid + 1] + sh[4 * tid + 2] + sh[4 * tid + 3];
+    }
+    __syncthreads();
   }
 }
 
@@ -544,11 +556,12 @@ __device__ __forceinline__ TokSlice tok_slice(int E, int s) {
   return TokSlice{lo, min(E, lo + q)};
 }
 
-// tokcnt[t] = rows of token t; tstat[t], tstat[T + t] = max and sum of
-// exp(score - max) over the token's final expert set (the set softmax).
+// tstat[t], tstat[T + t] = max and sum of exp(score - max) over token t's
+// final expert set (the set softmax); blksum[b] = rows of the workgroup's 64
+// tokens.
 __global__ void __launch_bounds__(64 * TOK_SLICES)
 k_tok_stats(const uint8_t* __restrict__ mask, int mpitch, const float* __restrict__ scoresT, int T, int E,
-            int32_t* __restrict__ tokcnt, float* __restrict__ tstat) {
+            float* __restrict__ tstat, int32_t* __restrict__ blksum) {
   __shared__ float smx[TOK_SLICES][64], ssum[TOK_SLICES][64];
   __shared__ int scnt[TOK_SLICES][64];
   const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
@@ -575,27 +588,32 @@ k_tok_stats(const uint8_t* __restrict__ mask, int mpitch, const float* __restric
   ssum[s][lane] = sum;
   scnt[s][lane] = cnt;
   __syncthreads();
-  if (s != 0 || t >= T) return;
+  if (s != 0) return;
   float M = smx[0][lane];
   int C = scnt[0][lane];
   for (int j = 1; j < TOK_SLICES; ++j) {
     M = fmaxf(M, smx[j][lane]);
     C += scnt[j][lane];
   }
+  // rows of the workgroup's 64 tokens, for the scan of block sums
+  int bsum = C;
+  for (int o = 32; o >= 1; o >>= 1) bsum += __shfl_xor(bsum, o, 64);
+  if (lane == 0) blksum[blockIdx.x] = bsum;
+  if (t >= T) return;
   float S = 0.f;
   for (int j = 0; j < TOK_SLICES; ++j)
     if (scnt[j][lane]) S += ssum[j][lane] * __expf(smx[j][lane] - M);
-  tokcnt[t] = C;
   tstat[t] = M;
   tstat[(size_t)T + t] = S;
 }
 
-// tok_ptr = exclusive scan of per-token row counts: one 1024-thread block,
-// each sweep taking 16384 consecutive tokens, 16 per thread, read and written
-// as four 16-byte words (both arrays are 16-byte aligned; a partial last group
-// of a sweep goes element by element).
+// out[0..n] = exclusive scan of cnt[0..n-1] (out[n] = the total): one
+// 1024-thread block, each sweep taking 16384 consecutive counts, 16 per
+// thread, read and written as four 16-byte words (both arrays are 16-byte
+// aligned; a partial last group of a sweep goes element by element).  With
+// token rounding it scans the rows of the 64-token blocks.
 __global__ void __launch_bounds__(1024)
-k_tok_scan(const int32_t* __restrict__ tokcnt, int T, int32_t* __restrict__ tok_ptr) {
+k_tok_scan(const int32_t* __restrict__ cnt, int T, int32_t* __restrict__ out) {
   __shared__ int lds[16];
   constexpr int PER = 16;
   int carry = 0;
@@ -606,12 +624,12 @@ k_tok_scan(const int32_t* __restrict__ tokcnt, int T, int32_t* __restrict__ tok_
     if (whole) {
 #pragma unroll
       for (int q = 0; q < PER / 4; ++q) {
-        const int4 u = *reinterpret_cast<const int4*>(tokcnt + t0 + 4 * q);
+        const int4 u = *reinterpret_cast<const int4*>(cnt + t0 + 4 * q);
         v[4 * q] = u.x; v[4 * q + 1] = u.y; v[4 * q + 2] = u.z; v[4 * q + 3] = u.w;
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) v[j] = t0 + j < T ? tokcnt[t0 + j] : 0;
+      for (int j = 0; j < PER; ++j) v[j] = t0 + j < T ? cnt[t0 + j] : 0;
     }
     int sum = 0;
 #pragma unroll
@@ -627,24 +645,25 @@ k_tok_scan(const int32_t* __restrict__ tokcnt, int T, int32_t* __restrict__ tok_
     if (whole) {
 #pragma unroll
       for (int q = 0; q < PER / 4; ++q)
-        *reinterpret_cast<int4*>(tok_ptr + t0 + 4 * q) = make_int4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        *reinterpret_cast<int4*>(out + t0 + 4 * q) = make_int4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
     } else {
 #pragma unroll
       for (int j = 0; j < PER; ++j)
-        if (t0 + j < T) tok_ptr[t0 + j] = o[j];
+        if (t0 + j < T) out[t0 + j] = o[j];
     }
     carry += tot;
   }
-  if (threadIdx.x == 0) tok_ptr[T] = carry;
+  if (threadIdx.x == 0) out[T] = carry;
 }
 
 // Token rounding: per token, its rows in ascending expert order and each
-// row's gate, the softmax of the token's scores over its final set.
+// row's gate, the softmax of the token's scores over its final set; and
+// tok_ptr, from the scanned block sums (blkoff) and an in-wave scan.
 __global__ void __launch_bounds__(64 * TOK_SLICES)
 k_tok_fill(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restrict__ rowmap,
            const float* __restrict__ scoresT, const float* __restrict__ tstat,
-           const int32_t* __restrict__ tok_ptr, int T, int E, int32_t* __restrict__ tok_row,
-           float* __restrict__ row_gate) {
+           const int32_t* __restrict__ blkoff, int T, int E, int32_t* __restrict__ tok_ptr,
+           int32_t* __restrict__ tok_row, float* __restrict__ row_gate) {
   __shared__ int scnt[TOK_SLICES][64];
   const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
   const int t = blockIdx.x * 64 + lane;
@@ -656,9 +675,24 @@ k_tok_fill(const uint8_t* __restrict__ mask, int mpitch, const int32_t* __restri
   }
   scnt[s][lane] = cnt;
   __syncthreads();
+  // the token's first row: its block's offset plus the rows of the block's
+  // earlier tokens (an exclusive scan over the wave's lanes, one per token)
+  int before = 0, C = 0;
+  for (int q = 0; q < TOK_SLICES; ++q) {
+    const int v = scnt[q][lane];
+    C += v;
+    if (q < s) before += v;
+  }
+  int incl = C;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  const int first = blkoff[blockIdx.x] + incl - C;
+  if (s == 0 && t < T) tok_ptr[t] = first;
+  if (s == 0 && t == T - 1) tok_ptr[T] = first + C;
   if (t >= T || cnt == 0) return;
-  int j = tok_ptr[t];
-  for (int q = 0; q < s; ++q) j += scnt[q][lane];
+  int j = first + before;
   const float mx = tstat[t], inv = 1.f / tstat[(size_t)T + t];
   for (int e = sl.lo; e < sl.hi; ++e) {
     if (mask[(size_t)e * mpitch + t]) {
@@ -705,8 +739,10 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
   else topk(k_topk<32, 32>, 32);
   const int nch = route_chunks(T);
   const dim3 cgrid((unsigned)nch, (unsigned)E);
+  // membership counts per chunk (with rounding, the rounding kernel rewrites
+  // those of the experts it changes)
+  hipLaunchKernelGGL(k_chunk_count, cgrid, dim3(256), 0, st, sc.mask, mp, nch, sc.chunk_cnt);
   if (round_mode != 0) {
-    hipLaunchKernelGGL(k_chunk_count, cgrid, dim3(256), 0, st, sc.mask, mp, nch, sc.chunk_cnt);
     hipLaunchKernelGGL(k_transpose_scores, dim3((T + 31) / 32, (E + 31) / 32), dim3(256), 0, st,
                        rb.logits, T, E, mp, sc.scoresT);
     if (mp <= TR_LDS_TOKENS) {
@@ -721,7 +757,6 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
                          sc.chunk_cnt, nch, rb.counts_raw, T, tile, round_mode, round_seed);
     }
   }
-  hipLaunchKernelGGL(k_chunk_count, cgrid, dim3(256), 0, st, sc.mask, mp, nch, sc.chunk_cnt);
   hipLaunchKernelGGL(k_scan_experts, dim3(1), dim3(1024), 0, st, sc.chunk_cnt, nch, E, tile, rb.counts,
                      round_mode == 0 ? rb.counts_raw : (int32_t*)nullptr, rb.offsets, rb.tile_offsets);
   hipLaunchKernelGGL(k_compact, cgrid, dim3(256), 0, st, sc.mask, mp, sc.chunk_cnt, nch, rb.offsets, rb.row_token,
@@ -735,11 +770,13 @@ hipError_t launch_route_select(const RouteBufs& rb, const RouteScratch& sc, int 
                          sc.rowmap, mp, T, K, rb.tok_row, rb.row_gate);
   } else {
     const unsigned blocks = (unsigned)((T + 63) / 64);
+    int32_t* blksum = sc.tblk;                           // [blocks], then the scanned offsets [blocks + 1]
+    int32_t* blkoff = blksum + ((blocks + 3) / 4) * 4;
     hipLaunchKernelGGL(k_tok_stats, dim3(blocks), dim3(64 * TOK_SLICES), 0, st, sc.mask, mp, sc.scoresT, T, E,
-                       sc.tokcnt, sc.tstat);
-    hipLaunchKernelGGL(k_tok_scan, dim3(1), dim3(1024), 0, st, sc.tokcnt, T, rb.tok_ptr);
+                       sc.tstat, blksum);
+    hipLaunchKernelGGL(k_tok_scan, dim3(1), dim3(1024), 0, st, blksum, (int)blocks, blkoff);
     hipLaunchKernelGGL(k_tok_fill, dim3(blocks), dim3(64 * TOK_SLICES), 0, st, sc.mask, mp, sc.rowmap,
-                       sc.scoresT, sc.tstat, rb.tok_ptr, T, E, rb.tok_row, rb.row_gate);
+                       sc.scoresT, sc.tstat, blkoff, T, E, rb.tok_ptr, rb.tok_row, rb.row_gate);
   }
   return hipGetLastError();
 }
