@@ -262,7 +262,9 @@ def test_mxfp8_backward_full_size_expert_sample(name):
         assert err <= TOL
 
 
-WG_CASES = [CASES[0], CASES[1], CASES[3]]
+WG_CASES = [CASES[0] + (0,), CASES[1] + (0,), CASES[3] + (0,),
+            # with the bf16 kernels on 128-row tiles elsewhere in the layer
+            CASES[0] + (B.MOE_FLAG_GEMM_128,)]
 WG_E2E = 0.08      # MX dW against the plain bf16-operand product (E4M3 on both operands)
 
 
@@ -277,10 +279,10 @@ def pad128(rows):
     return np.concatenate([rows, np.zeros(((-r) % 128, rows.shape[1]))], axis=0)
 
 
-def mx_wgrad_layer(w, mode=0, tile=128):
+def mx_wgrad_layer(w, mode=0, tile=128, flags=0):
     a = I.draw_all(w)
     desc = B.make_desc(w.T, w.d, w.E, w.n, w.K, "bf16", round_mode=mode, round_seed=3, tile=tile,
-                       flags=B.MOE_FLAG_MXFP8_WGRAD)
+                       flags=B.MOE_FLAG_MXFP8_WGRAD | flags)
     L = B.Layer(desc)
     X, WR, W1, W2, DO = (dev(a[k], "bf16") for k in ("x", "w_r", "w1", "w2", "d_o"))
     L.route(X, WR)
@@ -341,15 +343,16 @@ def wgrad_views(L, w):
     return off, padoff, dH_all, As_all, wsq
 
 
-@pytest.mark.parametrize("w,mode,tile", WG_CASES, ids=[c[0].name for c in WG_CASES])
-def test_mxfp8_weight_grads_match_oracle(w, mode, tile):
+@pytest.mark.parametrize("w,mode,tile,flags", WG_CASES,
+                         ids=[c[0].name + ("-gemm128" if c[3] else "") for c in WG_CASES])
+def test_mxfp8_weight_grads_match_oracle(w, mode, tile, flags):
     """moe_bwd_mxfp8 with MOE_FLAG_MXFP8_WGRAD, every expert: padded segment
     offsets exact, the segment operands' codes and scales bit-exact, dW1 / dW2
     against the oracle on those codes (empty experts exactly zero), the whole
     dW1 / dW2 against the oracle's weight_grads_mxfp8 on the GPU's dH and A_s,
     the rest of the backward as without the flag, and every dW against the
     plain product within the MX quantization bound."""
-    a, L = mx_wgrad_layer(w, mode, tile)
+    a, L = mx_wgrad_layer(w, mode, tile, flags)
     off, padoff, dH_all, As_all, wsq = wgrad_views(L, w)
     cnt = np.diff(off)
     assert np.array_equal(padoff, np.concatenate([[0], np.cumsum((cnt + 127) // 128 * 128)]))
