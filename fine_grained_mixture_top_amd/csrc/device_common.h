@@ -73,6 +73,47 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// LDS staging next to buffer -> LDS loads in flight.
+//
+// The compiler orders LDS accesses against the loads that write LDS
+// directly (buffer_load ... lds) by waiting for all of them (vmcnt(0)):
+//  * before a __syncthreads(), whose workgroup fence covers LDS, whenever
+//    such a load may still be outstanding;
+//  * before a ds_read / ds_write that carries no type-based alias
+//    information, e.g. one through HIP's uint2 / uint4 / float4 structs.
+// The kernels that stream operand stages that way keep several stages in
+// flight on purpose and wait for exactly the stage they read with explicit
+// vmcnt waits; the LDS they write with ds_write (epilogue staging) never
+// overlaps a stage still being loaded.  So they use lds_sync() and the
+// typed accesses below, and those drains do not happen.
+// ---------------------------------------------------------------------------
+
+// Workgroup barrier for LDS: every wave's own ds_read / ds_write complete
+// (lgkmcnt(0)), then all waves meet; loads into LDS still in flight are left
+// alone.  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt at their maximum
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef uint32_t u32x2_lv __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_lv __attribute__((ext_vector_type(4)));
+
+// 8- and 16-byte LDS accesses through clang vector types
+__device__ __forceinline__ void lds_st8(void* p, uint2 v) { *reinterpret_cast<u32x2_lv*>(p) = u32x2_lv{v.x, v.y}; }
+__device__ __forceinline__ uint4 lds_ld16(const void* p) {
+  const u32x4_lv v = *reinterpret_cast<const u32x4_lv*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void lds_st_f4(void* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4_v*>(p) = f32x4_v{a, b, c, d};
+}
+__device__ __forceinline__ f32x4_v lds_ld_f4(const void* p) { return *reinterpret_cast<const f32x4_v*>(p); }
+
 // Map a workgroup id so that consecutive virtual ids land on the same XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs, so physical id b runs
 // on XCD b % 8; virtual id (b % 8) * (G / 8) + b / 8 gives each XCD one

@@ -455,10 +455,10 @@ __device__ __forceinline__ void stage_acc(float* Cs, const f32x4_v (&acc)[BM / 3
   }
 }
 
-// 8 consecutive floats of the staged tile.
+// 8 consecutive floats of the staged tile (a typed LDS access: lds_sync()).
 __device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  const f32x4_v a = lds_ld_f4(p), b = lds_ld_f4(p + 4);
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3]; v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
 }
 
 // 8 values of type TO to global memory (16 bytes for bf16, 32 for fp32).

@@ -88,7 +88,7 @@ struct KCLoad {
 
 // 16 bytes of row rb + lane % 32 at chunk c of the current stage
 __device__ __forceinline__ uint4 chunk(const char* op, int r, int c) {
-  return *reinterpret_cast<const uint4*>(op + r * BK + ((c ^ swz(r)) & 7) * 16);
+  return lds_ld16(op + r * BK + ((c ^ swz(r)) & 7) * 16);
 }
 
 // operand fragment of 32 rows for the 64-k step s of a stage
@@ -264,7 +264,7 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     // stage 1 overwrites the previous tile's epilogue areas
-    __syncthreads();
+    lds_sync();
     if (nk > 1) issue(1);
     // the A scales and stage 0 are complete once only stage 1's loads remain
     if (nk > 1) {
@@ -273,7 +273,7 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
     } else {
       wait_vm<0>();
     }
-    __syncthreads();
+    lds_sync();
     if constexpr (g4::has_init<Epi>::value) Epi::init(ep, c, acc, pre_lds + (r & 1) * PREB);
     uint32_t asc[4], bsc[2];
     read_scales(0, asc, bsc);
@@ -286,12 +286,12 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
       step(acc, smem + (k & 1) * STAGE, sidx, lane, wm, wn, asc, bsc);
       if (sidx == 1 && k + 1 < nk) {
         wait_vm<0>();
-        __syncthreads();
+        lds_sync();
         read_scales(k + 1, asc, bsc);
         if (k + 2 < nk) issue(k + 2);
       }
     }
-    __syncthreads();  // every wave is done reading the stages and the A scales
+    lds_sync();  // every wave is done reading the stages and the A scales
 
     const int tn = tile_of(r + 1);
     TileCtx cn = c;
@@ -325,17 +325,16 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
             for (int i = 0; i < 2; ++i)
 #pragma unroll
               for (int eg = 0; eg < 4; ++eg) {
-                const float4 v = make_float4(acc[i][j][4 * eg], acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2],
-                                             acc[i][j][4 * eg + 3]);
-                *reinterpret_cast<float4*>(Cs + cl * g4::LDC + wn * 64 + 32 * i + 8 * eg + 4 * hl) = v;
+                lds_st_f4(Cs + cl * g4::LDC + wn * 64 + 32 * i + 8 * eg + 4 * hl, acc[i][j][4 * eg],
+                          acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2], acc[i][j][4 * eg + 3]);
               }
           }
         }
-        __syncthreads();
+        lds_sync();
         if (p + 1 < BM / g4::EROWS) Epi::load(ep, c, p + 1, pnxt);
         Epi::run(ep, c, p, Cs, pcur);
         pcur = pnxt;
-        __syncthreads();
+        lds_sync();
       }
     }
     c = cn;
@@ -448,12 +447,12 @@ grouped_gemm_mxw_kernel(int E, int Ma, int Nb, const int32_t* __restrict__ padof
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     // stage 1 overwrites the previous tile's epilogue areas
-    __syncthreads();
+    lds_sync();
     if (nk > 0) {
       if (nk > 1) issue(1);
       if (nk > 1) wait_vm<WLPS>();
       else wait_vm<0>();
-      __syncthreads();
+      lds_sync();
       uint32_t asc[4], bsc[2];
       read_scales(0, asc, bsc);
 #pragma unroll 1
@@ -462,13 +461,13 @@ grouped_gemm_mxw_kernel(int E, int Ma, int Nb, const int32_t* __restrict__ padof
         step(acc, smem + (k & 1) * WSTAGE, sidx, lane, wm, wn, asc, bsc);
         if (sidx == 1 && k + 1 < nk) {
           wait_vm<0>();
-          __syncthreads();
+          lds_sync();
           read_scales(k + 1, asc, bsc);
           if (k + 2 < nk) issue(k + 2);
         }
       }
     }
-    __syncthreads();  // every wave is done reading the stages
+    lds_sync();  // every wave is done reading the stages
 
     const int tn = tile_of(r + 1);
     TileCtx cn = c;
