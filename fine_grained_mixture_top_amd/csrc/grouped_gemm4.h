@@ -181,6 +181,14 @@ __device__ __forceinline__ bf16x8_v frag_kc(const char* op, int rb, int s, int l
   return *reinterpret_cast<const bf16x8_v*>(op + r * 64 + ((c ^ swz_kc(r)) * 16));
 }
 
+// LDS transpose read.  Through a restrict-qualified pointer the read carries
+// alias-scope information; without any, the compiler makes it wait for every
+// buffer -> LDS load in flight (vmcnt(0)), the stages being loaded behind it
+// included (see lds_sync() in device_common.h).
+__device__ __forceinline__ v4i16_t ds_tr16(const lds_v4i16_t* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4i16_t*>(p));
+}
+
 // m/n-contiguous tile: column cb + lane%32, k = 16s + 8*(lane/32) .. +7.
 // Lane q of each 16-lane group addresses k-row (q/4) of a 4 x 16 block and
 // column chunk (q%4)*4; the transpose read hands it column q of the block.
@@ -189,8 +197,8 @@ __device__ __forceinline__ bf16x8_v frag_mn(const char* op, int cb, int s, int l
   const int col = cb + 16 * (g & 1) + (q & 3) * 4;
   const int k0 = 16 * s + 8 * (g >> 1) + (q >> 2);
   auto addr = [&](int kr) { return op + kr * 512 + ((((col >> 3) ^ swz_mn(kr)) * 16) + (col & 7) * 2); };
-  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)addr(k0));
-  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)addr(k0 + 4));
+  const v4i16_t lo = ds_tr16((const lds_v4i16_t*)addr(k0));
+  const v4i16_t hi = ds_tr16((const lds_v4i16_t*)addr(k0 + 4));
   return __builtin_bit_cast(bf16x8_v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
