@@ -102,16 +102,27 @@ struct KCLoad {
 // m/n-contiguous rows (k-rows of 256 columns).  Instruction i of wave w
 // covers k-rows (2w + i) * 2 and +1 (lanes 0..31 and 32..63), slot l % 32.
 // The column part of the offset is fixed per tile; the row part is either
-// (k0 + kr) * ld (weights) or idx[seg0 + k0 + kr] * ld (gathered rows, the
-// indices of the next stage fetched one stage ahead).
+// (k0 + kr) * ld (weights) or idx[seg0 + k0 + kr] * ld (segment rows).
+// Gathered segment rows take their indices from registers for a tile's
+// first NS - 1 stages (loaded with the tile's setup) and from an LDS ring
+// after that: while stage k's data loads are issued, one wave loads stage
+// k + 1's 32 indices into the ring with a buffer -> LDS load, which the
+// kernel's wait for stage k - 1 covers.  (An index loaded into a register
+// one stage ahead makes the wave wait for it, and so for every load issued
+// before it, as soon as the offset is formed.)
+constexpr int IRING = 64;  // ints per ring slot: one 64-lane buffer -> LDS load of 4 bytes
+// G: the rows are gathered through an index (fixed per launch)
+template <bool G>
 struct MNLoad4 {
   uint32_t coff[2];   // column byte offset of this lane's chunk (OOB if absent)
   int kr[2];          // k-row of each instruction within the stage
-  // gathered / segment rows
+  // segment rows
   const int32_t* idx;
   int seg0, segn;
   uint32_t ldb;       // row pitch in bytes
-  uint32_t rcur[2], rnext[2];  // row byte offsets of this stage / the next (OOB past the segment)
+  uint32_t rcur[2];   // row byte offsets of the stage being issued (OOB past the segment)
+  int ip0[2], ip1[2], ip2[2];     // gathered: source rows of stages 0 .. NS-2 (-1 past the segment)
+  __amdgpu_buffer_rsrc_t ridx;    // gathered: the segment's indices (records up to its end)
 
   template <class F>
   __device__ __forceinline__ void setup_cols(int w, int lane, F colmap) {
@@ -123,16 +134,18 @@ struct MNLoad4 {
       coff[i] = col < 0 ? OOB : (uint32_t)col * 2u;
     }
   }
-  // row byte offset of segment row k (OOB past the end)
-  __device__ __forceinline__ uint32_t seg_row(int k) const {
-    if (k >= segn) return OOB;
-    const int src = idx ? idx[seg0 + k] : seg0 + k;
-    return (uint32_t)src * ldb;
-  }
   __device__ __forceinline__ void setup_rows(const int32_t* idx_, int seg0_, int segn_, uint32_t ldb_) {
     idx = idx_; seg0 = seg0_; segn = segn_; ldb = ldb_;
+    if constexpr (G) {
+      ridx = make_rsrc(idx_, (uint32_t)(seg0_ + segn_) * 4u);
+      static_assert(NS == 4, "three register stages");
 #pragma unroll
-    for (int i = 0; i < 2; ++i) rnext[i] = seg_row(kr[i]);
+      for (int i = 0; i < 2; ++i) {
+        ip0[i] = kr[i] < segn ? idx[seg0 + kr[i]] : -1;
+        ip1[i] = BK + kr[i] < segn ? idx[seg0 + BK + kr[i]] : -1;
+        ip2[i] = 2 * BK + kr[i] < segn ? idx[seg0 + 2 * BK + kr[i]] : -1;
+      }
+    }
   }
   // weights: k-row kr of stage k0 sits at (k0 + kr) * ldb
   __device__ __forceinline__ void issue_w(__amdgpu_buffer_rsrc_t rs, char* op, int w, int k0) const {
@@ -142,20 +155,35 @@ struct MNLoad4 {
       dma16(rs, op + (2 * w + i) * 1024, o);
     }
   }
-  // segment rows, in two calls per stage: next_rows() takes the rows of
-  // stage k0 (fetched by the previous call) and fetches those of stage
-  // k0 + BK; dma() then issues the data loads.  Every index load of a stage
-  // is issued before any of its data loads.
-  __device__ __forceinline__ void next_rows(int k0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) rcur[i] = rnext[i];
+  // segment rows of stage k < NS - 1 (a tile's first stages): gathered ones
+  // from the registers
+  __device__ __forceinline__ void rows_pre(int k) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int k = k0 + BK + kr[i];
-      const int kc = k < segn ? k : (segn > 0 ? segn - 1 : 0);  // keeps the index load inside the segment
-      const int src = idx ? idx[seg0 + kc] : seg0 + kc;
-      rnext[i] = k < segn ? (uint32_t)src * ldb : OOB;
+      const int kk = k * BK + kr[i];
+      int src;
+      if constexpr (G) src = k == 0 ? ip0[i] : (k == 1 ? ip1[i] : ip2[i]);
+      else src = kk < segn ? seg0 + kk : -1;
+      rcur[i] = src < 0 ? OOB : (uint32_t)src * ldb;
     }
+  }
+  // segment rows of stage k >= NS - 1: gathered ones from the ring
+  __device__ __forceinline__ void rows_ring(int k, const int* ring) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int kk = k * BK + kr[i];
+      int src;
+      if constexpr (G) src = kk < segn ? ring[(k % NS) * IRING + kr[i]] : -1;
+      else src = kk < segn ? seg0 + kk : -1;
+      rcur[i] = src < 0 ? OOB : (uint32_t)src * ldb;
+    }
+  }
+  // gathered: indices of stage k into its ring slot (lanes 0..31: k-rows
+  // 0..31; the other lanes and rows past the segment read nothing and write 0)
+  __device__ __forceinline__ void idx_dma(char* ring, int k, int lane) const {
+    const int kk = k * BK + (lane & 31);
+    const uint32_t o = (lane < 32 && kk < segn) ? (uint32_t)(seg0 + kk) * 4u : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ridx, (lds_void_t*)(ring + (k % NS) * IRING * 4), 4, o, 0, 0, 0);
   }
   __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, char* op, int w) const {
 #pragma unroll
@@ -470,7 +498,9 @@ struct G4SwiGLU {
 // otherwise ROW mode with A k-contiguous and B [N][K] (BMN = false) or [K][N]
 // (BMN = true).  PAIRED: B columns arranged for G4SwiGLU (gate and up of the
 // same j in the same wave).
-template <bool WGT, bool BMN, bool PAIRED, class Epi, bool TCH = false>
+// GATH (weight gradients): bit 0 = A rows gathered through A.idx, bit 1 =
+// B rows through B.idx (A.idx / B.idx non-null exactly then)
+template <bool WGT, bool BMN, bool PAIRED, class Epi, bool TCH = false, int GATH = 0>
 __global__ void __launch_bounds__(NTH, 1)
 grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32_t b_bytes,
                      typename Epi::Params ep) {
@@ -483,6 +513,9 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   // XCD-grouped id, so consecutive tiles share an XCD's L2 either way.
   __shared__ int tprefix[WGT ? 1 : MAX_E + 1];
   __shared__ __attribute__((aligned(256))) char touch_sink[WGT ? 256 : 1];  // written by the row touches, never read
+  // weight gradients: index rings of the gathered A / B rows (see MNLoad4)
+  constexpr bool GA = WGT && (GATH & 1), GB = WGT && (GATH & 2);
+  __shared__ __attribute__((aligned(256))) int iring[2][GA || GB ? NS * IRING : 1];
   constexpr int PREB = pre_bytes<Epi>::value;
   __shared__ __attribute__((aligned(256))) char pre_lds[PREB > 0 ? 2 * PREB : 16];  // wave epilogues' tile operands
 
@@ -568,7 +601,8 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   // operand loaders (state of the tile whose loads are being issued)
   __amdgpu_buffer_rsrc_t ra, rb;
   KCLoad la_kc, lb_kc;
-  MNLoad4 la_mn, lb_mn;
+  MNLoad4<GA> la_mn;
+  MNLoad4<GB> lb_mn;
   // Row touch (weight gradients).  The tiles of one plan unit (one expert's
   // row chunk, MU x NT tiles) run side by side on one XCD and walk the same
   // rows together; a B row segment is shared by the unit's MU tiles along m,
@@ -635,7 +669,8 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       lb_mn.setup_rows(B.idx, c.seg0, c.segn, (uint32_t)B.ld * 2u);
     }
   };
-  auto issue = [&](int k) {
+  // PRE: one of a tile's first NS - 1 stages (issued by prime)
+  auto issue = [&](int k, auto PRE) {
     char* st = smem + (k % NS) * STAGE;
     const int k0 = k * BK;
     if constexpr (!WGT) {
@@ -643,15 +678,28 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       if constexpr (!BMN) lb_kc.issue(rb, st + OPB, w, k0);
       else lb_mn.issue_w(rb, st + OPB, w, k0);
     } else {
-      la_mn.next_rows(k0);
-      lb_mn.next_rows(k0);
+      // stage k's rows (from the ring from stage NS - 1 on, read before the
+      // ring's next load is issued), then wave 6 loads the indices of stage
+      // k + 1 of each gathered operand into the ring ahead of its data loads
+      // of stage k
+      if constexpr (decltype(PRE)::value) {
+        la_mn.rows_pre(k);
+        lb_mn.rows_pre(k);
+      } else {
+        la_mn.rows_ring(k, iring[0]);
+        lb_mn.rows_ring(k, iring[1]);
+      }
+      if ((GA || GB) && w == 6 && k + 1 >= NS - 1 && (k + 1) * BK < la_mn.segn) {
+        if constexpr (GA) la_mn.idx_dma(reinterpret_cast<char*>(iring[0]), k + 1, lane);
+        if constexpr (GB) lb_mn.idx_dma(reinterpret_cast<char*>(iring[1]), k + 1, lane);
+      }
       la_mn.dma(ra, st, w);
       lb_mn.dma(rb, st + OPB, w);
       if (TOUCH && touching) {
         // rows of the segment as the touched operand's loader holds them
-        const MNLoad4& ld = tch_b ? lb_mn : la_mn;
         const int rr = (k + 2) * BK + tch_row;
-        const uint32_t o = (tch_base != OOB && rr < ld.segn) ? tch_base + (uint32_t)(ld.seg0 + rr) * ld.ldb : OOB;
+        const uint32_t ldb = tch_b ? lb_mn.ldb : la_mn.ldb;
+        const uint32_t o = (tch_base != OOB && rr < la_mn.segn) ? tch_base + (uint32_t)(la_mn.seg0 + rr) * ldb : OOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(tch_b ? rb : ra, (lds_void_t*)touch_sink, 4, o, 0, 0, 0);
       }
     }
@@ -659,7 +707,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   // first stages of a tile (stages 0 .. NS-2, fewer for short reductions)
   auto prime = [&](const TileCtx& c) {
     const int nk = ksteps(c);
-    for (int k = 0; k < NS - 1 && k < nk; ++k) issue(k);
+    for (int k = 0; k < NS - 1 && k < nk; ++k) issue(k, std::true_type());
   };
 
   int r = 0;
@@ -722,7 +770,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
           else wait_vm<0>();
         }
         __syncthreads();
-        if constexpr (decltype(MAIN)::value) issue(k + NS - 1);
+        if constexpr (decltype(MAIN)::value) issue(k + NS - 1, std::false_type());
         if (k + 1 < nk) f0.read(smem + ((k + 1) % NS) * STAGE, 0, lane, wm, wn);
         mma(acc, f1);
         if constexpr (decltype(MAIN)::value) {
