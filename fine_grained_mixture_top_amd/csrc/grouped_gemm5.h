@@ -214,6 +214,11 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
                      typename Epi::Params ep) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   __shared__ int tprefix[MAX_E + 1];
+  // the experts' row offsets, and the gathered A rows' indices of the
+  // workgroup's next tile (loaded into LDS while the current tile computes,
+  // so that moving to the next tile waits for no global load)
+  __shared__ int soff[MAX_E + 1];
+  __shared__ int nidx[BM];
   __shared__ __attribute__((aligned(256))) char touch_sink[256];  // written by the B-line touches, never read
   constexpr int PREB = g4::pre_bytes<Epi>::value;
   __shared__ __attribute__((aligned(256))) char pre_lds[PREB > 0 ? 2 * PREB : 16];  // wave epilogues' tile operands
@@ -227,7 +232,9 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     int carry = 0;
     for (int e0 = 0; e0 < s.E; e0 += NTH) {
       const int e = e0 + tid;
-      const int tiles = e < s.E ? (s.offsets[e + 1] - s.offsets[e] + BM - 1) / BM : 0;
+      const int o0 = e < s.E ? s.offsets[e] : 0;
+      const int tiles = e < s.E ? (s.offsets[e + 1] - o0 + BM - 1) / BM : 0;
+      if (e < s.E) soff[e] = o0;
       int incl = tiles;
       for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(incl, o, 64);
@@ -244,7 +251,10 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       carry += tot;
       __syncthreads();
     }
-    if (tid == 0) tprefix[s.E] = carry;
+    if (tid == 0) {
+      tprefix[s.E] = carry;
+      soff[s.E] = s.offsets[s.E];
+    }
     __syncthreads();
   }
   const int total = tprefix[s.E] * NT;
@@ -265,8 +275,8 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     c.nt = t % NT;
     c.e = upper_index(tprefix, s.E + 1, mg);
     c.mt = mg - tprefix[c.e];
-    c.seg0 = s.offsets[c.e];
-    c.segn = s.offsets[c.e + 1] - c.seg0;
+    c.seg0 = soff[c.e];
+    c.segn = soff[c.e + 1] - c.seg0;
     c.m_valid = min(BM, c.segn - c.mt * BM);
     c.out_row0 = (long long)c.seg0 + (long long)c.mt * BM;
     c.slot = -1;
@@ -337,12 +347,13 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (g4::lds_void_t*)touch_sink, 4, o, 0, 0, 0);
     }
   };
-  auto setup = [&](const TileCtx& c) {
+  // pre: the gathered rows' indices are in nidx (prefetched for this tile)
+  auto setup = [&](const TileCtx& c, bool pre) {
     ra = make_rsrc(abase, a_bytes);
     la.setup(w, lane, [&](int r) -> uint32_t {
       const int m = c.mt * BM + r;
       const int row = c.seg0 + (m < c.segn ? m : c.segn - 1);  // rows past the end repeat the last one
-      const uint32_t src = A.idx ? (uint32_t)A.idx[row] : (uint32_t)row;
+      const uint32_t src = A.idx ? (uint32_t)(pre ? nidx[r] : A.idx[row]) : (uint32_t)row;
       return src * (uint32_t)A.ld * 2u;
     });
     rb = make_rsrc(bbase + (long long)c.e * B.estride * 2, b_bytes);
@@ -371,7 +382,7 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   TileCtx c;
   if (t >= 0) {
     decode(t, c);
-    setup(c);
+    setup(c, false);
     if constexpr (PREB > 0) Epi::pre_issue(ep, c, pre_lds, w, lane);
     issue(0);
   }
@@ -392,6 +403,24 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     if constexpr (has_prefetch<Epi>::value) wait_vm<0>();
     lds_sync();
     if (nk > 1) issue(1);
+    // wave 0: the gathered rows' indices of the next tile into nidx (its
+    // loads after stage 1's; its waits for stages 0 and 1 cover them: every
+    // wave reads nidx after the tile's last barrier)
+    if (A.idx && w == 0) {
+      const int tn = tile_of(r + 1);
+      if (tn >= 0) {
+        TileCtx q;
+        decode(tn, q);
+        const __amdgpu_buffer_rsrc_t ri = make_rsrc(A.idx, (uint32_t)soff[s.E] * 4u);
+#pragma unroll
+        for (int i = 0; i < BM / 64; ++i) {
+          const int m = q.mt * BM + 64 * i + lane;
+          const int row = q.seg0 + (m < q.segn ? m : q.segn - 1);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (g4::lds_void_t*)(nidx + 64 * i), 4, (uint32_t)row * 4u, 0, 0,
+                                                   0);
+        }
+      }
+    }
     // stage 0 complete: only stage 1's loads came after it (and, for tiles
     // after the first, the previous epilogue's stores before those)
     // (wave 7: also the touches issued with stages 0 and 1)
@@ -433,7 +462,7 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     TileCtx cn = c;
     if (tn >= 0) {
       decode(tn, cn);
-      setup(cn);
+      setup(cn, true);
       if constexpr (PREB > 0) Epi::pre_issue(ep, cn, pre_lds + ((r + 1) & 1) * PREB, w, lane);
       issue(0);
     }
