@@ -139,6 +139,14 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
   __shared__ int tprefix[MAX_E + 1];
   constexpr int PREB = g4::pre_bytes<Epi>::value;
   __shared__ __attribute__((aligned(256))) char pre_lds[PREB > 0 ? 2 * PREB : 16];  // wave epilogues' tile operands
+  // the experts' row offsets, and the gathered A rows' indices of the
+  // workgroup's next tile (loaded into LDS while the current tile computes,
+  // so that moving to the next tile waits for no global load)
+  __shared__ int soff[MAX_E + 1];
+  __shared__ int nidx[BM];
+  // (not with the dH epilogue, whose registers are all in use: there the
+  // extra live values of the prefetch spill)
+  constexpr bool NPRE = !g5::has_prefetch<Epi>::value;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -150,7 +158,9 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
     int carry = 0;
     for (int e0 = 0; e0 < s.E; e0 += NTH) {
       const int e = e0 + tid;
-      const int tiles = e < s.E ? (s.offsets[e + 1] - s.offsets[e] + BM - 1) / BM : 0;
+      const int o0 = e < s.E ? s.offsets[e] : 0;
+      const int tiles = e < s.E ? (s.offsets[e + 1] - o0 + BM - 1) / BM : 0;
+      if (NPRE && e < s.E) soff[e] = o0;
       int incl = tiles;
       for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(incl, o, 64);
@@ -167,7 +177,10 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
       carry += tot;
       __syncthreads();
     }
-    if (tid == 0) tprefix[s.E] = carry;
+    if (tid == 0) {
+      tprefix[s.E] = carry;
+      if (NPRE) soff[s.E] = s.offsets[s.E];
+    }
     __syncthreads();
   }
   const int total = tprefix[s.E] * NT;
@@ -187,8 +200,13 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
     c.nt = t % NT;
     c.e = upper_index(tprefix, s.E + 1, mg);
     c.mt = mg - tprefix[c.e];
-    c.seg0 = s.offsets[c.e];
-    c.segn = s.offsets[c.e + 1] - c.seg0;
+    if constexpr (NPRE) {
+      c.seg0 = soff[c.e];
+      c.segn = soff[c.e + 1] - c.seg0;
+    } else {
+      c.seg0 = s.offsets[c.e];
+      c.segn = s.offsets[c.e + 1] - c.seg0;
+    }
     c.m_valid = min(BM, c.segn - c.mt * BM);
     c.out_row0 = (long long)c.seg0 + (long long)c.mt * BM;
     c.slot = -1;
@@ -198,18 +216,20 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
   __amdgpu_buffer_rsrc_t ra, rb, ras, rbs;
   KCLoad la, lb;
   uint32_t bso = 0;          // B-scale dword offset of this lane's column (waves 0..3)
-  auto src_row = [&](const TileCtx& c, int r) -> uint32_t {
+  // source row of tile row r; pre: the gathered rows' indices are in nidx
+  auto src_row = [&](const TileCtx& c, int r, auto PRE) -> uint32_t {
     const int m = c.mt * BM + r;
     const int row = c.seg0 + (m < c.segn ? m : c.segn - 1);  // rows past the end repeat the last one
-    return A.idx ? (uint32_t)A.idx[row] : (uint32_t)row;
+    if constexpr (decltype(PRE)::value) return A.idx ? (uint32_t)nidx[r] : (uint32_t)row;
+    else return A.idx ? (uint32_t)A.idx[row] : (uint32_t)row;
   };
   auto colmap = [&](const TileCtx& c, int cc) -> int {
     if constexpr (PAIRED) return g4::G4SwiGLU::col(cc, c.nt, s.N / 2);
     return c.n0 + cc;
   };
-  auto setup = [&](const TileCtx& c) {
+  auto setup = [&](const TileCtx& c, auto pre) {
     ra = make_rsrc(abase, a_bytes);
-    la.setup(w, lane, [&](int r) -> uint32_t { return src_row(c, r) * (uint32_t)A.ld; });
+    la.setup(w, lane, [&](int r) -> uint32_t { return src_row(c, r, pre) * (uint32_t)A.ld; });
     rb = make_rsrc(bbase + (long long)c.e * B.estride, b_bytes);
     lb.setup(w, lane, [&](int r) -> uint32_t { return (uint32_t)colmap(c, r) * (uint32_t)B.ld; });
     ras = make_rsrc(ascale, as_bytes);
@@ -218,12 +238,12 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
   };
   // the tile's A scales: PA instructions of 64 dwords, wave w taking
   // w, w + 8, ...; dword q of the block is byte 4 (q % (PA/4)) of row q / (PA/4)
-  auto issue_ascale = [&](const TileCtx& c) {
+  auto issue_ascale = [&](const TileCtx& c, auto pre) {
     const int dpr = PA / 4;
 #pragma unroll 1
     for (int i = w; i < PA; i += 8) {
       const int q = i * 64 + lane;
-      dma4(ras, smem + ASC_OFF + i * 256, src_row(c, q / dpr) * (uint32_t)PA + (uint32_t)(q % dpr) * 4u);
+      dma4(ras, smem + ASC_OFF + i * 256, src_row(c, q / dpr, pre) * (uint32_t)PA + (uint32_t)(q % dpr) * 4u);
     }
   };
   auto issue = [&](int k) {
@@ -249,9 +269,9 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
   TileCtx c;
   if (t >= 0) {
     decode(t, c);
-    setup(c);
+    setup(c, std::false_type());
     if constexpr (PREB > 0) Epi::pre_issue(ep, c, pre_lds, w, lane);
-    issue_ascale(c);
+    issue_ascale(c, std::false_type());
     issue(0);
   }
   while (t >= 0) {
@@ -266,6 +286,24 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
     // stage 1 overwrites the previous tile's epilogue areas
     lds_sync();
     if (nk > 1) issue(1);
+    // wave 0: the gathered rows' indices of the next tile into nidx (its
+    // loads after stage 1's; its waits for stages 0 and 1 cover them: every
+    // wave reads nidx after the tile's last barrier)
+    if (NPRE && A.idx && w == 0) {
+      const int tn = tile_of(r + 1);
+      if (tn >= 0) {
+        TileCtx q;
+        decode(tn, q);
+        const __amdgpu_buffer_rsrc_t ri = make_rsrc(A.idx, (uint32_t)soff[s.E] * 4u);
+#pragma unroll
+        for (int i = 0; i < BM / 64; ++i) {
+          const int m = q.mt * BM + 64 * i + lane;
+          const int row = q.seg0 + (m < q.segn ? m : q.segn - 1);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (g4::lds_void_t*)(nidx + 64 * i), 4, (uint32_t)row * 4u, 0, 0,
+                                                   0);
+        }
+      }
+    }
     // the A scales and stage 0 are complete once only stage 1's loads remain
     if (nk > 1) {
       if (w < 4) wait_vm<LPS + 1>();
@@ -297,9 +335,9 @@ grouped_gemm_mx_kernel(GemmShape s, Operand A, Operand B, const uint8_t* __restr
     TileCtx cn = c;
     if (tn >= 0) {
       decode(tn, cn);
-      setup(cn);
+      setup(cn, std::bool_constant<NPRE>());
       if constexpr (PREB > 0) Epi::pre_issue(ep, cn, pre_lds + ((r + 1) & 1) * PREB, w, lane);
-      issue_ascale(cn);
+      issue_ascale(cn, std::bool_constant<NPRE>());
       issue(0);
     }
     if constexpr (PREB > 0) {
