@@ -44,10 +44,10 @@ hipError_t run_gemm(const GemmShape& s, const Operand& A, const Operand& B,
 }
 
 // 256 x 256 tile kernel: one 512-thread workgroup per CU (LDS-bound).
-template <bool WGT, bool BMN, bool PAIRED, class Epi, bool TCH = false, int GATH = 0>
+template <bool WGT, bool BMN, bool PAIRED, class Epi, int GATH = 0>
 hipError_t run_gemm4(const GemmShape& s, const Operand& A, const Operand& B, size_t a_bytes, size_t b_bytes,
                      const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
-  auto kern = g4::grouped_gemm4_kernel<WGT, BMN, PAIRED, Epi, TCH, GATH>;
+  auto kern = g4::grouped_gemm4_kernel<WGT, BMN, PAIRED, Epi, GATH>;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, g4::SMEM);
   if (attr != hipSuccess) return attr;
@@ -517,17 +517,12 @@ hipError_t wgt_g4(const GemmDims& g, const int32_t* offsets, int M, int N, const
   s.plan = WgtPlan{plan, units, pol.MU};
   using Epi = g4::G4StoreW;
   typename Epi::Params ep{reinterpret_cast<bf16_t*>(C), N, partial};
-  // the row-touch variant when a widely shared operand is read without an
-  // index (see the kernel): B when MU > NT, A when NT > MU
-  const int nt = N / g4::BN;
-  const bool tch = pol.MU != nt && (pol.MU > nt ? b.idx : a.idx) == nullptr;
   // which operand's rows are gathered (dW1: x, dW2: dO; neither when the
   // rows come pre-gathered) is a template parameter of the kernel
   const int gath = (a.idx ? 1 : 0) | (b.idx ? 2 : 0);
   auto run = [&](auto G) {
     constexpr int GA = decltype(G)::value;
-    if (tch) return run_gemm4<true, true, false, Epi, true, GA>(s, a, b, a_bytes, b_bytes, ep, num_cus(), st);
-    return run_gemm4<true, true, false, Epi, false, GA>(s, a, b, a_bytes, b_bytes, ep, num_cus(), st);
+    return run_gemm4<true, true, false, Epi, GA>(s, a, b, a_bytes, b_bytes, ep, num_cus(), st);
   };
   switch (gath) {
     case 1: err = run(std::integral_constant<int, 1>()); break;

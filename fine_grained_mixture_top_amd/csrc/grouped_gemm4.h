@@ -28,9 +28,6 @@
 //    unchanged.  The staging area lies over the last stage only: before the
 //    epilogue of a tile, the first three stages of the workgroup's next tile
 //    are already being loaded, so that tile's start does not wait for memory.
-//  * Weight gradients, host-selected TCH variant: wave 7 touches a share of
-//    the lines of the operand the plan unit's tiles share most (read without
-//    an index) two stages ahead, and its waits count the touches.
 #pragma once
 
 #include <type_traits>
@@ -500,7 +497,7 @@ struct G4SwiGLU {
 // same j in the same wave).
 // GATH (weight gradients): bit 0 = A rows gathered through A.idx, bit 1 =
 // B rows through B.idx (A.idx / B.idx non-null exactly then)
-template <bool WGT, bool BMN, bool PAIRED, class Epi, bool TCH = false, int GATH = 0>
+template <bool WGT, bool BMN, bool PAIRED, class Epi, int GATH = 0>
 __global__ void __launch_bounds__(NTH, 1)
 grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32_t b_bytes,
                      typename Epi::Params ep) {
@@ -512,7 +509,6 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   // spreads the large units' tiles evenly over the workgroups.  v is the
   // XCD-grouped id, so consecutive tiles share an XCD's L2 either way.
   __shared__ int tprefix[WGT ? 1 : MAX_E + 1];
-  __shared__ __attribute__((aligned(256))) char touch_sink[WGT ? 256 : 1];  // written by the row touches, never read
   // weight gradients: index rings of the gathered A / B rows (see MNLoad4)
   constexpr bool GA = WGT && (GATH & 1), GB = WGT && (GATH & 2);
   __shared__ __attribute__((aligned(256))) int iring[2][GA || GB ? NS * IRING : 1];
@@ -603,43 +599,12 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   KCLoad la_kc, lb_kc;
   MNLoad4<GA> la_mn;
   MNLoad4<GB> lb_mn;
-  // Row touch (weight gradients).  The tiles of one plan unit (one expert's
-  // row chunk, MU x NT tiles) run side by side on one XCD and walk the same
-  // rows together; a B row segment is shared by the unit's MU tiles along m,
-  // an A row segment by its NT tiles along n, and each stage's 128 lines of
-  // the more widely shared operand miss L2 for all of them at once.  When
-  // wave 7 issues stage k it also reads 4 bytes of 32 of those lines of stage
-  // k + 2 (the 32 chosen by the tile's index along the sharing dimension mod
-  // 4) into a scratch LDS area, provided that operand is read without an
-  // index (dH rows for dW1, A_s rows for dW2).  Past the segment the touch
-  // reads nothing (out-of-range offset) but is still issued, so that wave 7's
-  // load counts stay fixed.  Measured (A/B, two runs each): T = 32768,
-  // d = 1536, E = 128, n = 256: dW1 0.540 -> 0.526 ms (B, MU 6 > NT 2), dW2
-  // 0.296 -> 0.282 (A, NT 6 > MU 1); d = 2048, E = 64, n = 1024: dW2 1.375 ->
-  // 1.323 (A, NT 8 > MU 4), while touching B for dW1 there (MU = NT = 8) cost
-  // 3%, so equal sharing touches nothing.
-  // TCH: the launch touches (the host picks it when the rule below selects an
-  // operand; the kernel without it is the plain weight-gradient kernel).
-  constexpr bool TOUCH = WGT && TCH;
-  // which operand (fixed for the launch): B when MU > NT, A when NT > MU,
-  // none on a tie or when that operand is gathered
-  bool tch_b = false, touching = false;
-  if constexpr (TOUCH) {
-    const int mu = s.plan.MU;
-    tch_b = mu > NT;
-    touching = w == 7 && mu != NT && (tch_b ? B.idx : A.idx) == nullptr;
-  }
-  uint32_t tch_base = OOB;  // this lane's line: column byte offset (OOB for lanes 32..63)
-  int tch_row = 0;          // its row within a stage
-  auto setup_touch = [&](const TileCtx& c) {
-    const int part = (tch_b ? c.mt : c.nt) & 3;
-    const int q = part * 32 + (lane & 31);  // four lines per row, 32 rows per stage
-    tch_row = q >> 2;
-    const int col = (tch_b ? c.n0 : c.mt * BM) + 64 * (q & 3);
-    tch_base = lane < 32 ? (uint32_t)col * 2u : OOB;
-  };
+  // (A row touch for the weight gradients, wave 7 reading 4 bytes of some
+  // of a later stage's lines of the operand a plan unit's tiles share, was
+  // measured faster while the compiler drained every stage in flight; with
+  // the pipeline intact it cost 2-5% (dW1 0.398 -> 0.413 ms, dW2 0.217 ->
+  // 0.225 at T = 32768, d = 1536, E = 128, n = 256) and is gone.)
   auto setup = [&](const TileCtx& c) {
-    if (TOUCH && touching) setup_touch(c);
     if constexpr (!WGT) {
       ra = make_rsrc(abase, a_bytes);
       la_kc.setup(w, lane, [&](int r) -> uint32_t {
@@ -695,13 +660,6 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       }
       la_mn.dma(ra, st, w);
       lb_mn.dma(rb, st + OPB, w);
-      if (TOUCH && touching) {
-        // rows of the segment as the touched operand's loader holds them
-        const int rr = (k + 2) * BK + tch_row;
-        const uint32_t ldb = tch_b ? lb_mn.ldb : la_mn.ldb;
-        const uint32_t o = (tch_base != OOB && rr < la_mn.segn) ? tch_base + (uint32_t)(la_mn.seg0 + rr) * ldb : OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(tch_b ? rb : ra, (lds_void_t*)touch_sink, 4, o, 0, 0, 0);
-      }
     }
   };
   // first stages of a tile (stages 0 .. NS-2, fewer for short reductions)
@@ -734,16 +692,9 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       // every later stage of this tile and, for tiles after the first, the
       // previous epilogue's stores came after those (they only add to it)
       static_assert(NS == 4, "the waits below assume three stages in flight");
-      // (wave 7 with touches: each stage's touch came after its loads)
-      if (TOUCH && touching) {
-        if (nk >= 3) wait_vm<2 * LPS + 3>();
-        else if (nk == 2) wait_vm<LPS + 2>();
-        else wait_vm<1>();
-      } else {
-        if (nk >= 3) wait_vm<2 * LPS>();
-        else if (nk == 2) wait_vm<LPS>();
-        else wait_vm<0>();
-      }
+      if (nk >= 3) wait_vm<2 * LPS>();
+      else if (nk == 2) wait_vm<LPS>();
+      else wait_vm<0>();
       __syncthreads();
       if constexpr (has_init<Epi>::value) Epi::init(ep, c, acc, pre_lds + (r & 1) * PREB);
       Frags<AMN, BMN> f0, f1;
@@ -760,14 +711,10 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
         G4_SCHED(0x008, 2);
         if constexpr (decltype(MAIN)::value) {
           // stage k+1 complete: at least the LPS data loads of stage k+2
-          // were issued after its last load (other loads only add to that;
-          // wave 7 with touches: also the touches of stages k+1 and k+2)
-          if (TOUCH && touching) wait_vm<LPS + 2>();
-          else wait_vm<LPS>();
+          // were issued after its last load (other loads only add to that)
+          wait_vm<LPS>();
         } else {
-          // (wave 7 with touches: stage k+1's touch came after its loads)
-          if (TOUCH && touching) wait_vm<1>();
-          else wait_vm<0>();
+          wait_vm<0>();
         }
         __syncthreads();
         if constexpr (decltype(MAIN)::value) issue(k + NS - 1, std::false_type());

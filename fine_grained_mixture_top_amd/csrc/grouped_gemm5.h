@@ -20,10 +20,9 @@
 //    transpose reads of the 256 x 256 kernel.
 //  * The epilogue areas lie over stage 1: the next tile's stage 0 is loaded
 //    before the epilogue, its stage 1 once every wave has finished it.
-//  * Line touches: the tiles that share an operand tile run side by side on
-//    one XCD, so wave 7 reads 4 bytes of a share of that operand's lines two
-//    stages ahead (the [k][n] weights always; A rows in the host-selected
-//    TCHA variant), and its waits count the touches.
+//  * A-row touches (host-selected TCHA variant): the tiles that share a row
+//    block run side by side on one XCD, so wave 7 reads 4 bytes of a share
+//    of the block's A lines two stages ahead, and its waits count them.
 #pragma once
 
 #include "grouped_gemm4.h"
@@ -219,7 +218,7 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   // so that moving to the next tile waits for no global load)
   __shared__ int soff[MAX_E + 1];
   __shared__ int nidx[BM];
-  __shared__ __attribute__((aligned(256))) char touch_sink[256];  // written by the B-line touches, never read
+  __shared__ __attribute__((aligned(256))) char touch_sink[256];  // written by the A-row touches, never read
   constexpr int PREB = g4::pre_bytes<Epi>::value;
   __shared__ __attribute__((aligned(256))) char pre_lds[PREB > 0 ? 2 * PREB : 16];  // wave epilogues' tile operands
 
@@ -286,68 +285,36 @@ grouped_gemm5_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   __amdgpu_buffer_rsrc_t ra, rb;
   KCLoad5 la, lb_kc;
   MNLoad5 lb_mn;
-  // B-line touch (weights stored [k][n]).  The tiles that share an expert's
-  // weight tile run side by side on one XCD (an XCD takes 32 consecutive
-  // tiles of the list per round, so about 32 / NT blocks of an expert), and
-  // each stage of the weight tile is a fresh set of 256 lines that misses L2
-  // for all of them at once.  When wave 7 issues stage k it also reads 4
-  // bytes of 256 / S of the lines of stage k + 2 into a scratch LDS area,
-  // S = 32 / NT clamped to 4..8 and the share chosen by the block index
-  // mod S, so that the tiles of one weight tile touch different lines and
-  // bring them into L2 a stage ahead of their loads.  Past the last stage the
-  // touch reads nothing (out-of-range offset) but is still issued, so that
-  // wave 7's load counts stay fixed.  Measured at T = 32768, d = 1536,
-  // E = 128, n = 256: up-projection 0.540 -> 0.511 ms; for the k-contiguous
-  // weights of dH and dXt, and in the k = 32 kernel's down-projection, it
-  // cost 1-2%, so those do not touch.
-  //
   // A-row touch (TCHA, chosen by the host for k-contiguous weights when A's
   // rows are read without an index and NT >= 4, i.e. dXt): the NT tiles of
-  // one row block share its A rows; tile nt touches a 1/S share of the 256
-  // A lines of stage k + 2, S = NT clamped to 4..8, the same way.  dXt
-  // 0.516 -> 0.501 ms at d = 1536, n = 256 and 1.94 -> 1.88 ms at d = 2048,
-  // n = 1024.
-  static_assert(!(TCHA && BMN), "one touch kind per launch");
-  constexpr bool TOUCH = BMN || TCHA;
-  const int tshare = TCHA ? (NT < 4 ? 4 : (NT > 8 ? 8 : NT)) : (NT >= 8 ? 4 : 8);  // S
-  uint32_t tch_col = OOB;  // byte offset of this lane's line at k = 0 (column part for [k][n] weights)
-  int tch_row = 0;         // k-row of this lane's line within a stage ([k][n] weights)
+  // one row block share its A rows and run side by side on one XCD; when
+  // wave 7 issues stage k, tile nt also reads 4 bytes of a 1/S share of the
+  // 256 A lines of stage k + 2 into a scratch LDS area (S = NT clamped to
+  // 4..8, the share chosen by nt mod S), so that the row block's tiles bring
+  // different lines into L2 a stage ahead of their loads.  Past the last
+  // stage the touch reads nothing (out-of-range offset) but is still issued,
+  // so that wave 7's load counts stay fixed.  dXt 0.527 -> 0.501 ms at
+  // d = 1536, n = 256 and 2.01 -> 1.95 ms at d = 2048, n = 1024.  (A B-line
+  // touch of the [k][n] weights of the up-projection helped while the
+  // compiler drained every stage in flight; with the pipeline intact it cost
+  // about 1.5% and is gone.)
+  constexpr bool TOUCH = TCHA;
+  static_assert(!(TCHA && BMN), "A-row touches read k-contiguous A rows beside k-contiguous weights");
+  const int tshare = NT < 4 ? 4 : (NT > 8 ? 8 : NT);  // S
+  uint32_t tch_col = OOB;  // byte offset of this lane's A line at k = 0
   auto setup_touch = [&](const TileCtx& c) {
     if constexpr (!TOUCH) return;
-    if constexpr (TCHA) {
-      const int per = (256 + tshare - 1) / tshare;  // 32..64 lines per tile and stage
-      const int q = (c.nt % tshare) * per + lane;
-      const int m = c.mt * BM + q;
-      tch_row = 0;
-      tch_col = (lane < per && q < 256 && m < c.segn) ? (uint32_t)(c.seg0 + m) * (uint32_t)A.ld * 2u : OOB;
-      return;
-    }
-    const int per = 256 / tshare;  // lines per tile and stage: 32 or 64
-    const int q = (c.mt % tshare) * per + lane;
-    if (lane >= per) {
-      tch_col = OOB;
-    } else {
-      // four lines per k-row, 64 k-rows per stage
-      tch_row = q >> 2;
-      const int which = q & 3;
-      int col;
-      if constexpr (PAIRED) col = c.nt * 128 + ((which & 1) ? 64 : 0) + ((which >> 1) ? s.N / 2 : 0);
-      else col = c.n0 + 64 * which;
-      tch_col = (uint32_t)col * 2u;
-    }
+    const int per = (256 + tshare - 1) / tshare;  // 32..64 lines per tile and stage
+    const int q = (c.nt % tshare) * per + lane;
+    const int m = c.mt * BM + q;
+    tch_col = (lane < per && q < 256 && m < c.segn) ? (uint32_t)(c.seg0 + m) * (uint32_t)A.ld * 2u : OOB;
   };
   auto touch = [&](int k) {
     const int kt = k + 2;
     uint32_t o = OOB;
-    if constexpr (TCHA) {
-      if (kt < nk && tch_col != OOB) o = tch_col + (uint32_t)(kt * BK) * 2u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (g4::lds_void_t*)touch_sink, 4, o, 0, 0, 0);
-    } else {
-      if (kt < nk && tch_col != OOB) o = tch_col + (uint32_t)(kt * BK + tch_row) * ((uint32_t)B.ld * 2u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (g4::lds_void_t*)touch_sink, 4, o, 0, 0, 0);
-    }
+    if (kt < nk && tch_col != OOB) o = tch_col + (uint32_t)(kt * BK) * 2u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (g4::lds_void_t*)touch_sink, 4, o, 0, 0, 0);
   };
-  // pre: the gathered rows' indices are in nidx (prefetched for this tile)
   auto setup = [&](const TileCtx& c, bool pre) {
     ra = make_rsrc(abase, a_bytes);
     la.setup(w, lane, [&](int r) -> uint32_t {
