@@ -509,6 +509,17 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   // spreads the large units' tiles evenly over the workgroups.  v is the
   // XCD-grouped id, so consecutive tiles share an XCD's L2 either way.
   __shared__ int tprefix[WGT ? 1 : MAX_E + 1];
+  // row mode: the workgroup's next tile, looked up by wave 0 at the start
+  // of the current tile (its expert and row tile written to nxe, the
+  // expert's two row offsets loaded into nxt[0..1] by a buffer -> LDS load,
+  // the other lanes writing 0) and read by every wave once the tile is done,
+  // so that moving to the next tile waits for no LDS search and no global
+  // load.  Two slots by tile parity: no barrier separates the reads of one
+  // slot from wave 0's next write to the other.  (The barriers are
+  // lds_sync(): a __syncthreads() would make every wave wait for that load,
+  // and so for every stage in flight.)
+  __shared__ int nxe[2][2];
+  __shared__ __attribute__((aligned(256))) int nxt[2][WGT ? 1 : 64];
   // weight gradients: index rings of the gathered A / B rows (see MNLoad4)
   constexpr bool GA = WGT && (GATH & 1), GB = WGT && (GATH & 2);
   __shared__ __attribute__((aligned(256))) int iring[2][GA || GB ? NS * IRING : 1];
@@ -551,6 +562,12 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
     total = __builtin_amdgcn_readfirstlane(s.plan.nunits[0]) * UT;
   }
   const int G = gridDim.x;
+  // the tile loop's barriers: lds_sync() in row mode (see nxe / nxt above);
+  // __syncthreads() for the weight gradients, measured 2-4% faster there
+  auto tile_sync = [&]() {
+    if constexpr (WGT) __syncthreads();
+    else lds_sync();
+  };
   const int vid = xcd_virtual_id(blockIdx.x, G);
   // tile of round r, -1 past the end
   auto tile_of = [&](int r) -> int {
@@ -565,15 +582,37 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
   const char* bbase = reinterpret_cast<const char*>(B.ptr);
 
   // tile t -> expert, m tile, n tile, rows
-  auto decode = [&](int t, TileCtx& c) {
+  // wave 0 (row mode): look up tile t, the workgroup's tile of round q,
+  // into slot q & 1 of nxe / nxt (see above)
+  auto lookup_next = [&](int t, int q) {
+    if (w != 0 || t < 0) return;
+    const int mg = t / NT;
+    const int e = upper_index(tprefix, s.E + 1, mg);
+    if (lane == 0) {
+      nxe[q & 1][0] = e;
+      nxe[q & 1][1] = mg - tprefix[e];
+    }
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(s.offsets, (uint32_t)(s.E + 1) * 4u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lds_void_t*)nxt[q & 1], 4,
+                                             lane < 2 ? (uint32_t)(e + lane) * 4u : OOB, 0, 0, 0);
+  };
+  // pre (row mode): from slot q & 1 of nxe / nxt, the tile of round q
+  auto decode = [&](int t, TileCtx& c, bool pre = false, int q = 0) {
     c.tid = tid; c.lane = lane; c.wm = wm; c.wn = wn;
     if constexpr (!WGT) {
       const int mg = t / NT;
       c.nt = t % NT;
-      c.e = upper_index(tprefix, s.E + 1, mg);
-      c.mt = mg - tprefix[c.e];
-      c.seg0 = s.offsets[c.e];
-      c.segn = s.offsets[c.e + 1] - c.seg0;
+      if (pre) {
+        c.e = nxe[q & 1][0];
+        c.mt = nxe[q & 1][1];
+        c.seg0 = nxt[q & 1][0];
+        c.segn = nxt[q & 1][1] - c.seg0;
+      } else {
+        c.e = upper_index(tprefix, s.E + 1, mg);
+        c.mt = mg - tprefix[c.e];
+        c.seg0 = s.offsets[c.e];
+        c.segn = s.offsets[c.e + 1] - c.seg0;
+      }
       c.m_valid = min(BM, c.segn - c.mt * BM);
       c.out_row0 = (long long)c.seg0 + (long long)c.mt * BM;
       c.slot = -1;
@@ -687,6 +726,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+    if constexpr (!WGT) lookup_next(tile_of(r + 1), r + 1);
     if (nk > 0) {
       // stage 0 complete: at least LPS data loads were issued after it by
       // every later stage of this tile and, for tiles after the first, the
@@ -695,7 +735,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       if (nk >= 3) wait_vm<2 * LPS>();
       else if (nk == 2) wait_vm<LPS>();
       else wait_vm<0>();
-      __syncthreads();
+      tile_sync();
       if constexpr (has_init<Epi>::value) Epi::init(ep, c, acc, pre_lds + (r & 1) * PREB);
       Frags<AMN, BMN> f0, f1;
       f0.read(smem, 0, lane, wm, wn);
@@ -716,7 +756,7 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
         } else {
           wait_vm<0>();
         }
-        __syncthreads();
+        tile_sync();
         if constexpr (decltype(MAIN)::value) issue(k + NS - 1, std::false_type());
         if (k + 1 < nk) f0.read(smem + ((k + 1) % NS) * STAGE, 0, lane, wm, wn);
         mma(acc, f1);
@@ -731,13 +771,13 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
       for (; k + NS - 1 < nk; ++k) body(k, std::true_type());
       for (; k < nk; ++k) body(k, std::false_type());
     }
-    __syncthreads();  // every wave is done reading the stages
+    tile_sync();  // every wave is done reading the stages
 
     // ---- next tile's first stages, then this tile's epilogue ----
     const int tn = tile_of(r + 1);
     TileCtx cn = c;
     if (tn >= 0) {
-      decode(tn, cn);
+      decode(tn, cn, !WGT, r + 1);
       setup(cn);
       if constexpr (PREB > 0) Epi::pre_issue(ep, cn, pre_lds + ((r + 1) & 1) * PREB, w, lane);
       prime(cn);
@@ -775,9 +815,9 @@ grouped_gemm4_kernel(GemmShape s, Operand A, Operand B, uint32_t a_bytes, uint32
             }
         }
       }
-      __syncthreads();
+      tile_sync();
       Epi::run(ep, s, cp, Cs, nullptr);
-      __syncthreads();
+      tile_sync();
     }
     }
     c = cn;
