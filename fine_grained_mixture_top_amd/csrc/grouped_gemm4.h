@@ -306,12 +306,23 @@ struct G4Store {
         for (int eg = 0; eg < 4; ++eg)
           lds_st8(L + cl * LD + 32 * i + 8 * eg + 4 * hl,
                   pack4(acc[i][j][4 * eg], acc[i][j][4 * eg + 1], acc[i][j][4 * eg + 2], acc[i][j][4 * eg + 3]));
+      // rows r = lane / 8 + 8 q, chunks ch = lane % 8; a block with every
+      // row valid (all but an expert's last) reads its four chunks first, so
+      // its stores wait for LDS once
+      bf16_t* out = p.C + (c.out_row0 + rb) * p.ldc + c.n0 + c.wn * 64 + (c.lane & 7) * 8;
+      if (rb + 32 <= c.m_valid) {
+        uint4 x[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int v = c.lane + 64 * q, r = v >> 3, ch = v & 7;
-        const uint4 x = lds_ld16(L + r * LD + ch * 8);
-        if (rb + r < c.m_valid)
-          st_out(p.C + (c.out_row0 + rb + r) * p.ldc + c.n0 + c.wn * 64 + ch * 8, x);
+        for (int q = 0; q < 4; ++q) x[q] = lds_ld16(L + ((c.lane >> 3) + 8 * q) * LD + (c.lane & 7) * 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) st_out(out + ((c.lane >> 3) + 8 * q) * p.ldc, x[q]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = (c.lane >> 3) + 8 * q;
+          const uint4 x = lds_ld16(L + r * LD + (c.lane & 7) * 8);
+          if (rb + r < c.m_valid) st_out(out + r * p.ldc, x);
+        }
       }
     }
   }
