@@ -82,14 +82,15 @@ hipError_t run_row256(const GemmShape& s, const Operand& A, const Operand& B, si
                       const typename Epi::Params& ep, long long max_tiles, hipStream_t st) {
   // k = 64 stages from K = 512 up; K = 256 with k-contiguous weights too
   // (dXt at n = 128: 0.509 -> 0.494 ms at T = 16384, d = 2048, E = 256; the
-  // down-projection at K = 256 is 2% faster on the k = 32 kernel).  Weights
+  // down-projection at K = 256 is 2% faster on the k = 32 kernel, at K = 128
+  // 4% slower: 0.333 against 0.348 ms at the same shape).  Weights
   // stored [k][n] with both K and N from 1024 up go to the k = 32 kernel,
   // whose three stages in flight measured faster there: up 2.19 -> 2.14 ms,
   // down 1.17 -> 1.12 at d = 2048, E = 64, n = 1024; up 8.83 -> 8.58, down
   // 4.50 -> 4.37 at d = 7168, E = 256, n = 2048 (up at N = 512 and 256 and
   // the k-contiguous weights of dH and dXt are faster on the k = 64 one).
   const bool long_mn = BMN && s.N >= 1024 && s.K >= 1024;
-  if (!long_mn && s.K % g5::BK == 0 && s.K >= (BMN ? 512 : 256)) {
+  if (!long_mn && s.K % g5::BK == 0 && (s.K >= (BMN ? 512 : 256) || (BMN && s.K == 128))) {
     // k-contiguous weights and A rows read without an index, shared by at
     // least four column tiles: the A-row touch variant
     if constexpr (!BMN)
