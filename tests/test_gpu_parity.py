@@ -90,6 +90,11 @@ LAYER_CASES = [
     # tiles touches its A rows, dW1 with MU = 4 > NT = 2 its B rows, dW2 with
     # NT = 4 > MU = 1 its A rows, the up-projection its [k][n] weights)
     W("bf16_touch_variants", 600, 1024, 8, 256, 2, "bf16", seed=23),
+    # n = 128 and 384 (not multiples of 256) with d a multiple of 256: dW2 and
+    # dH on the 128-row kernels beside the 256 x 256 ones in the same layer;
+    # the first skewed (its heaviest expert holds 2569 of 12000 rows)
+    W("bf16_n128_split_expert", 3000, 256, 16, 128, 4, "bf16", seed=24, zipf=1.2),
+    W("bf16_n384_half_tile", 1000, 256, 8, 384, 2, "bf16", seed=25),
 ]
 
 

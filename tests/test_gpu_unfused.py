@@ -59,6 +59,9 @@ CASES = [
     (W("bf16_gemm128", 1200, 512, 16, 256, 4, "bf16", seed=7), 0, 128, B.MOE_FLAG_GEMM_128),
     (W("bf16_empty_experts", 100, 256, 64, 256, 2, "bf16", seed=8), 0, 128, 0),
     (W("bf16_rounded", 1800, 256, 16, 256, 2, "bf16", seed=9), 2, 256, 0),
+    # n = 128 with d = 256: the down-projection's K = 128 on the k = 64 row
+    # kernel and dW2 from pre-gathered dO rows on the 128-row kernel
+    (W("bf16_n128", 1000, 256, 16, 128, 4, "bf16", seed=10), 0, 128, 0),
 ]
 
 
